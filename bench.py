@@ -1,0 +1,232 @@
+"""Benchmark of the structured-mask attention forward on one MI355X.
+
+One step = one pass of the whole hot path over the ViT layer at 896 px
+(64 x 64 patch grid flattened row-major: L = 4096 tokens, batch 1, 16 heads,
+head dim 80, bf16): the three masks of that layer -- full attention, 1D chunks
+of 256 tokens and a symmetric sliding window of radius 128 -- each one launch
+of the HIP kernel on the same resident Q, K, V.  Mask plans are compiled and
+uploaded before the timed region (they are cached per mask).
+
+Metric: effective attention TFLOP/s = 4 * d * (unmasked query-key pairs) per
+head, summed over the masks, divided by the step time (2d flops for the score
+and 2d for the value mix per allowed pair; padding, masked pairs inside
+partial tiles and the exponentials are not counted).
+
+Extra workloads (skipped with --quick): the 1792-px ViT layer (L = 16384, full
+and sliding window radius 512) and 128K-token block-sparse causal prefill
+(32 heads, d = 128, block 128, about half of the causal blocks kept), timed the
+same way and reported under "extra".
+
+Prints ONE JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_softmax_amd", "csrc", "attn_fwd.hip")
+
+
+def _kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def _traffic_from_profile(workload: str, mask: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_{mask}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not b or m.group(1) != _kernel_hash():
+        return None
+    return float(b.group(1))
+
+
+def _bits_to_dev(u16, device, layout):
+    import numpy as np
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16)
+    if layout == "blhd":
+        t = t.permute(0, 2, 1, 3).contiguous()
+    return t.to(device)
+
+
+def _setup(name, device, layout):
+    import torch
+    from block_sparse_softmax_amd import inputs as gen
+    from block_sparse_softmax_amd import prepare
+    w = gen.workload(name)
+    q, k, v = gen.qkv_bf16(0, w["cfg"], w["B"], w["H"], w["L"], w["D"])
+    dev = [_bits_to_dev(x, device, layout) for x in (q, k, v)]
+    o = torch.empty_like(dev[0])
+    sink = None if w["sink"] is None else torch.from_numpy(w["sink"]).to(device)
+    masks = []
+    for label, mask in w["masks"].items():
+        pm = prepare(mask, w["L"], w["H"], w["D"], device)
+        _, pairs = pm.plan.pairs()
+        masks.append(dict(label=label, mask=mask, pm=pm, pairs=int(pairs)))
+    return dict(w=w, host=(q, k, v), dev=dev, o=o, sink=sink, masks=masks)
+
+
+def _time(setup, steps, warmup, layout):
+    """Time `steps` steps (one launch per mask each); per-launch HIP events on the launch stream."""
+    import torch
+    q, k, v = setup["dev"]
+    o, sink = setup["o"], setup["sink"]
+    stream = torch.cuda.current_stream()
+    launches = [lambda pm=m["pm"]: pm.launch(q, k, v, o, sink=sink, layout=layout, stream=stream)
+                for m in setup["masks"]]
+    for _ in range(warmup):
+        for f in launches:
+            f()
+    torch.cuda.synchronize()
+    n = len(launches)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        for i, f in enumerate(launches):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)] for i in range(n)]  # ms
+    return wall, per
+
+
+def _summarise(setup, wall, per, steps):
+    import numpy as np
+    w = setup["w"]
+    D = w["D"]
+    rows = []
+    for m, t in zip(setup["masks"], per):
+        flops = 4.0 * D * m["pairs"] * w["B"]
+        avg = float(np.mean(t))
+        rows.append(dict(mask=m["label"], pairs=m["pairs"], avg_ms=avg, min_ms=float(np.min(t)),
+                         tflops=flops / (avg * 1e-3) / 1e12,
+                         frac_bf16_peak=flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         alg_gbs=(4 * w["B"] * w["H"] * w["L"] * D * 2) / (avg * 1e-3) / 1e9))
+    total_flops = sum(4.0 * D * m["pairs"] * w["B"] for m in setup["masks"])
+    ms_per_step = wall / steps * 1e3
+    return rows, total_flops, ms_per_step
+
+
+def _cpu_baseline(setup, budget_s=20.0):
+    """The float64 oracle on a bounded sample of query rows of the same workload, on the host cores."""
+    import numpy as np
+    from oracle.attention import attention
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    w = setup["w"]
+    q, k, v = setup["host"]
+    D, H, L = w["D"], w["H"], w["L"]
+    rng = np.random.default_rng(1234)
+    done_flops, done_s, rows_done = 0.0, 0.0, 0
+    n_per_head = 16
+    while done_s < budget_s * 0.5 and n_per_head <= L:
+        rows = np.sort(np.stack([rng.choice(L, n_per_head, replace=False) for _ in range(H)]), axis=1)
+        t0 = time.perf_counter()
+        flops = 0.0
+        for m in setup["masks"]:
+            r = attention(q, k, v, m["mask"], sink=w["sink"], rows=rows)
+            flops += 4.0 * D * float(r["pairs"].sum())
+        dt = time.perf_counter() - t0
+        done_flops += flops
+        done_s += dt
+        rows_done += n_per_head * H
+        n_per_head *= 2
+    return dict(value=done_flops / done_s / 1e12, unit="TFLOP/s (effective, unmasked pairs)",
+                cores=int(threads), kind="oracle",
+                sample=f"{rows_done} query rows (random, all {H} heads) through all {len(setup['masks'])} "
+                       f"masks of the {setup['w']['L']}-token workload, float64 numpy, {done_s:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layout", default="blhd", choices=["blhd", "bhld"])
+    ap.add_argument("--quick", action="store_true", help="skip the 16K and 128K extra workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="vit896")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the kernel shards by head with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_softmax_amd import load_library
+    load_library()
+    device = torch.device("cuda:0")
+
+    setup = _setup(args.workload, device, args.layout)
+    wall, per = _time(setup, args.steps, args.warmup, args.layout)
+    rows, total_flops, ms_per_step = _summarise(setup, wall, per, args.steps)
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    dom = max(rows, key=lambda r: r["avg_ms"])
+    w = setup["w"]
+    dom_flops = 4.0 * w["D"] * dom["pairs"] * w["B"]
+    traffic = _traffic_from_profile(args.workload, dom["mask"])
+    roof = dict(bound="mfma", achieved=dom_flops / (dom["avg_ms"] * 1e-3) / 1e12, peak=PEAK_BF16_TFLOPS,
+                unit="TFLOP/s", frac=dom_flops / (dom["avg_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                traffic=traffic, kernel=f"attn_fwd_kernel<{w['D']}> ({args.workload} {dom['mask']})",
+                avg_launch_ms=dom["avg_ms"])
+
+    cpu = None if args.no_cpu_baseline else _cpu_baseline(setup)
+
+    extra = {}
+    if not args.quick:
+        for name in ("vit1792", "blocksparse128k"):
+            del setup
+            torch.cuda.empty_cache()
+            setup = _setup(name, device, args.layout)
+            wl, pr = _time(setup, max(5, args.steps // 2), args.warmup, args.layout)
+            r2, tf2, ms2 = _summarise(setup, wl, pr, max(5, args.steps // 2))
+            extra[name] = dict(ms_per_step=ms2, tflops=tf2 / (ms2 * 1e-3) / 1e12, masks=r2)
+
+    out = {
+        "metric": "effective attention TFLOP/s (unmasked pairs) and % bf16 MFMA peak, 1 MI355X",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q, K, V rounded to bf16)",
+        "config": {"workload": "ViT layer at 896 px: L=4096 tokens, batch 1, 16 heads, head dim 80; "
+                               "masks full + chunk 256 + sliding window radius 128",
+                   "layout": args.layout, "frac_bf16_peak": value / PEAK_BF16_TFLOPS},
+        "per_mask": rows,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

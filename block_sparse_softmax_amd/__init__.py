@@ -1,0 +1,19 @@
+"""Structured-mask softmax attention for AMD MI355X (gfx950).
+
+The compute path is the HIP library ``libbss_attn.so`` built from ``csrc/``
+(C ABI in ``include/bss_attn.h``); this package only marshals arguments.
+"""
+
+from ._lib import (  # noqa: F401
+    AttnError,
+    Plan,
+    PreparedMask,
+    load_library,
+    masked_fwd,
+    masked_fwd_oneshot,
+    prepare,
+    tensor_view,
+)
+
+__all__ = ["AttnError", "Plan", "PreparedMask", "load_library", "masked_fwd", "masked_fwd_oneshot",
+           "prepare", "tensor_view"]

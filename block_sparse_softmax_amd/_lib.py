@@ -1,0 +1,326 @@
+"""ctypes binding over the C ABI in include/bss_attn.h.
+
+Argument marshalling only: every step of the attention runs in the HIP
+library.  torch supplies device memory (tensors, the workspace) and the
+current stream.  If the shared library is missing or cannot be loaded, every
+entry point raises; there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbss_attn.so")
+
+ATTN_OK, ATTN_E_INVAL, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP, ATTN_E_NOMEM = 0, -1, -2, -3, -4, -5
+KINDS = {"full": 0, "chunk": 1, "window": 2, "block": 3}
+STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_E_INVAL", -2: "ATTN_E_UNSUPPORTED", -3: "ATTN_E_WORKSPACE",
+                -4: "ATTN_E_HIP", -5: "ATTN_E_NOMEM"}
+
+# every symbol the header declares
+EXPORTS = ("attn_masked_fwd", "attn_workspace_bytes", "attn_plan_create", "attn_plan_tiles",
+           "attn_plan_pairs", "attn_plan_schedule", "attn_plan_workspace_bytes", "attn_plan_upload",
+           "attn_masked_fwd_plan", "attn_plan_destroy", "attn_last_error", "attn_version")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class AttnTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p),
+                ("B", ctypes.c_int64), ("L", ctypes.c_int64), ("H", ctypes.c_int64), ("D", ctypes.c_int64),
+                ("stride_b", ctypes.c_int64), ("stride_l", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class MaskDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("chunk", ctypes.c_int64), ("left", ctypes.c_int64), ("right", ctypes.c_int64),
+                ("head_left", ctypes.POINTER(ctypes.c_int64)),
+                ("block", ctypes.c_int64), ("block_mask", ctypes.POINTER(ctypes.c_uint8)),
+                ("block_mask_heads", ctypes.c_int32)]
+
+
+class Launch(ctypes.Structure):
+    _fields_ = [("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("softmax_scale", ctypes.c_float)]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it is not built."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(f"HIP library not built: {path} is missing (run __graft_entry__.build())")
+        lib = ctypes.CDLL(path)
+        P = ctypes.POINTER
+        i64, i32, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        vp = ctypes.c_void_p
+        plan_p = vp
+        sig = {
+            "attn_masked_fwd": [P(AttnTensor), P(AttnTensor), P(AttnTensor), P(MaskDesc), vp, P(AttnTensor), P(Launch)],
+            "attn_workspace_bytes": [P(MaskDesc), i64, i64, i64, P(sz)],
+            "attn_plan_create": [P(MaskDesc), i64, i64, i64, P(plan_p)],
+            "attn_plan_tiles": [plan_p, P(i32), P(i32), P(i64), P(i64), P(P(i32)), P(P(i32)), P(P(ctypes.c_uint8))],
+            "attn_plan_pairs": [plan_p, P(i64), P(i64)],
+            "attn_plan_schedule": [plan_p, P(i64), P(P(i32))],
+            "attn_plan_workspace_bytes": [plan_p, P(sz)],
+            "attn_plan_upload": [plan_p, vp, sz, vp],
+            "attn_masked_fwd_plan": [plan_p, P(AttnTensor), P(AttnTensor), P(AttnTensor), vp, P(AttnTensor), P(Launch)],
+        }
+        for name, args in sig.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        lib.attn_plan_destroy.argtypes = [plan_p]
+        lib.attn_plan_destroy.restype = None
+        lib.attn_last_error.restype = ctypes.c_char_p
+        lib.attn_version.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        msg = load_library().attn_last_error().decode()
+        raise AttnError(status, msg)
+
+
+def mask_key(mask: dict) -> tuple:
+    """Hashable content key of a mask dict (arrays by value)."""
+    items = []
+    for k in sorted(mask):
+        v = mask[k]
+        if isinstance(v, np.ndarray):
+            v = (v.shape, str(v.dtype), hash(v.tobytes()))
+        elif isinstance(v, (list, tuple)):
+            v = tuple(int(x) for x in v)
+        items.append((k, v))
+    return tuple(items)
+
+
+def build_desc(mask: dict, H: int):
+    """MaskDesc plus the numpy arrays it points into (keep them alive)."""
+    d = MaskDesc()
+    keep = []
+    kind = mask["kind"]
+    if kind not in KINDS:
+        raise ValueError(f"unknown mask kind {kind!r}")
+    d.kind = KINDS[kind]
+    d.causal = 1 if mask.get("causal", False) else 0
+    d.chunk = int(mask.get("chunk", 0))
+    d.left = int(mask.get("left", 0))
+    d.right = int(mask.get("right", 0))
+    hl = mask.get("head_left")
+    if hl is not None:
+        arr = np.ascontiguousarray(np.asarray(hl, dtype=np.int64))
+        if arr.shape != (H,):
+            raise ValueError("head_left must have one entry per head")
+        keep.append(arr)
+        d.head_left = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    d.block = int(mask.get("block", 0))
+    bm = mask.get("block_mask")
+    if bm is not None:
+        arr = np.ascontiguousarray(np.asarray(bm, dtype=np.uint8))
+        if arr.ndim == 2:
+            arr = arr[None]
+        keep.append(arr)
+        d.block_mask = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+        d.block_mask_heads = arr.shape[0]
+    return d, keep
+
+
+class Plan:
+    """A compiled mask for (L, H, D): tile lists, schedule, pair counts, device image."""
+
+    def __init__(self, mask: dict, L: int, H: int, D: int):
+        lib = load_library()
+        self.mask, self.L, self.H, self.D = mask, L, H, D
+        desc, keep = build_desc(mask, H)
+        h = ctypes.c_void_p()
+        _check(lib.attn_plan_create(ctypes.byref(desc), L, H, D, ctypes.byref(h)))
+        self._h = h
+        del keep
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.attn_plan_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def tiles(self):
+        lib = load_library()
+        bm, bn = ctypes.c_int32(), ctypes.c_int32()
+        nr, nnz = ctypes.c_int64(), ctypes.c_int64()
+        rp, kv = ctypes.POINTER(ctypes.c_int32)(), ctypes.POINTER(ctypes.c_int32)()
+        fl = ctypes.POINTER(ctypes.c_uint8)()
+        _check(lib.attn_plan_tiles(self._h, ctypes.byref(bm), ctypes.byref(bn), ctypes.byref(nr),
+                                   ctypes.byref(nnz), ctypes.byref(rp), ctypes.byref(kv), ctypes.byref(fl)))
+        n_rows, n = nr.value, nnz.value
+        row_ptr = np.ctypeslib.as_array(rp, shape=(n_rows + 1,)).copy()
+        kv_tile = np.ctypeslib.as_array(kv, shape=(n,)).copy() if n else np.zeros(0, np.int32)
+        flags = np.ctypeslib.as_array(fl, shape=(n,)).copy() if n else np.zeros(0, np.uint8)
+        return bm.value, bn.value, row_ptr, kv_tile, flags
+
+    def pairs(self):
+        lib = load_library()
+        per = np.zeros(self.H, dtype=np.int64)
+        tot = ctypes.c_int64()
+        _check(lib.attn_plan_pairs(self._h, per.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), ctypes.byref(tot)))
+        return per, tot.value
+
+    def schedule(self):
+        lib = load_library()
+        n = ctypes.c_int64()
+        it = ctypes.POINTER(ctypes.c_int32)()
+        _check(lib.attn_plan_schedule(self._h, ctypes.byref(n), ctypes.byref(it)))
+        return np.ctypeslib.as_array(it, shape=(n.value, 4)).copy() if n.value else np.zeros((0, 4), np.int32)
+
+    def workspace_bytes(self) -> int:
+        lib = load_library()
+        b = ctypes.c_size_t()
+        _check(lib.attn_plan_workspace_bytes(self._h, ctypes.byref(b)))
+        return b.value
+
+    def upload(self, workspace, stream=None):
+        """Copy the device image into `workspace` (a uint8 CUDA tensor)."""
+        lib = load_library()
+        _check(lib.attn_plan_upload(self._h, ctypes.c_void_p(workspace.data_ptr()),
+                                    workspace.numel() * workspace.element_size(), _stream_ptr(stream, workspace)))
+
+
+# ---------------------------------------------------------------------------
+# torch-facing helpers
+# ---------------------------------------------------------------------------
+
+def _stream_ptr(stream, like):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(like.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def tensor_view(t, layout: str = "blhd") -> AttnTensor:
+    """AttnTensor over a bf16 CUDA tensor stored as [B, L, H, D] ('blhd') or [B, H, L, D] ('bhld')."""
+    import torch
+    if t.dtype != torch.bfloat16:
+        raise TypeError("attention tensors must be bfloat16")
+    if not t.is_cuda:
+        raise TypeError("attention tensors must be on the GPU")
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a 4-d tensor with a contiguous last dimension")
+    a = AttnTensor()
+    a.data = t.data_ptr()
+    if layout == "blhd":
+        a.B, a.L, a.H, a.D = t.shape
+        a.stride_b, a.stride_l, a.stride_h = t.stride(0), t.stride(1), t.stride(2)
+    elif layout == "bhld":
+        a.B, a.H, a.L, a.D = t.shape
+        a.stride_b, a.stride_h, a.stride_l = t.stride(0), t.stride(1), t.stride(2)
+    else:
+        raise ValueError(layout)
+    return a
+
+
+class PreparedMask:
+    """A plan plus a device workspace holding its uploaded image."""
+
+    def __init__(self, mask: dict, L: int, H: int, D: int, device):
+        import torch
+        self.plan = Plan(mask, L, H, D)
+        self.workspace = torch.empty(max(256, self.plan.workspace_bytes()), dtype=torch.uint8, device=device)
+        self.plan.upload(self.workspace)
+        torch.cuda.synchronize(device)
+
+    def launch(self, q, k, v, o, sink=None, layout="blhd", stream=None, softmax_scale: float = 0.0):
+        lib = load_library()
+        qv, kv, vv, ov = (tensor_view(x, layout) for x in (q, k, v, o))
+        ln = Launch()
+        ln.stream = _stream_ptr(stream, q).value
+        ln.workspace = self.workspace.data_ptr()
+        ln.workspace_bytes = self.workspace.numel()
+        ln.softmax_scale = softmax_scale
+        sp = None
+        if sink is not None:
+            import torch
+            if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() != self.plan.H:
+                raise TypeError("sink must be a float32 CUDA tensor with one entry per head")
+            sp = ctypes.c_void_p(sink.data_ptr())
+        _check(lib.attn_masked_fwd_plan(self.plan.handle, ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv),
+                                        sp, ctypes.byref(ov), ctypes.byref(ln)))
+        return o
+
+
+_prepared = {}
+_prepared_lock = threading.Lock()
+
+
+def prepare(mask: dict, L: int, H: int, D: int, device) -> PreparedMask:
+    key = (mask_key(mask), L, H, D, str(device))
+    with _prepared_lock:
+        pm = _prepared.get(key)
+        if pm is None:
+            pm = PreparedMask(mask, L, H, D, device)
+            _prepared[key] = pm
+        return pm
+
+
+def masked_fwd(q, k, v, mask: dict, sink=None, out=None, layout: str = "blhd", stream=None,
+               softmax_scale: float = 0.0):
+    """O = masked softmax attention of bf16 CUDA tensors q, k, v (see include/bss_attn.h).
+
+    layout 'blhd' = [B, L, H, D] (the default) or 'bhld' = [B, H, L, D].
+    The compiled plan and its uploaded workspace are cached per (mask, L, H, D, device).
+    """
+    import torch
+    if layout == "blhd":
+        B, L, H, D = q.shape
+    else:
+        B, H, L, D = q.shape
+    pm = prepare(mask, L, H, D, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    return pm.launch(q, k, v, out, sink=sink, layout=layout, stream=stream, softmax_scale=softmax_scale)
+
+
+def masked_fwd_oneshot(q, k, v, mask: dict, sink=None, out=None, layout: str = "blhd", stream=None,
+                       softmax_scale: float = 0.0):
+    """The one-shot C entry point attn_masked_fwd (compile-or-cache, upload, launch per call)."""
+    import torch
+    lib = load_library()
+    qv, kv, vv = (tensor_view(x, layout) for x in (q, k, v))
+    if out is None:
+        out = torch.empty_like(q)
+    ov = tensor_view(out, layout)
+    desc, keep = build_desc(mask, qv.H)
+    nbytes = ctypes.c_size_t()
+    _check(lib.attn_workspace_bytes(ctypes.byref(desc), qv.L, qv.H, qv.D, ctypes.byref(nbytes)))
+    ws = torch.empty(max(256, nbytes.value), dtype=torch.uint8, device=q.device)
+    ln = Launch()
+    ln.stream = _stream_ptr(stream, q).value
+    ln.workspace = ws.data_ptr()
+    ln.workspace_bytes = ws.numel()
+    ln.softmax_scale = softmax_scale
+    sp = None if sink is None else ctypes.c_void_p(sink.data_ptr())
+    _check(lib.attn_masked_fwd(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), ctypes.byref(desc), sp,
+                               ctypes.byref(ov), ctypes.byref(ln)))
+    torch.cuda.current_stream(q.device).synchronize()  # keep ws alive until the kernel has run
+    del keep
+    return out

@@ -1,0 +1,63 @@
+"""Build the HIP library in-tree: block_sparse_softmax_amd/libbss_attn.so (gfx950).
+
+Host files (plan compiler, C ABI) are compiled with g++; the kernels with
+hipcc for gfx950; hipcc links the shared object against the HIP runtime.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libbss_attn.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
+    # no packed-FP32 instructions are generated
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+              f"-I{ROCM}/include"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
+    os.makedirs(BUILD, exist_ok=True)
+    inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
+    jobs = [
+        [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "attn_fwd.hip"), "-o", os.path.join(BUILD, "attn_fwd.o")],
+        ["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "plan.cpp"), "-o", os.path.join(BUILD, "plan.o")],
+        ["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "capi.cpp"), "-o", os.path.join(BUILD, "capi.o")],
+    ]
+    with ThreadPoolExecutor(3) as ex:
+        outs = list(ex.map(_run, jobs))
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
+    tmp = LIB + ".tmp"
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
+          os.path.join(BUILD, "attn_fwd.o"), os.path.join(BUILD, "plan.o"), os.path.join(BUILD, "capi.o")])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

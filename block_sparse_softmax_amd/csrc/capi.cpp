@@ -1,0 +1,286 @@
+// C ABI of the library: validation, the plan cache, uploads and launches.
+// Every entry point returns an attn_status; nothing throws across the ABI.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <memory>
+#include <mutex>
+#include <new>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "bss_attn.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+namespace bss {
+
+namespace {
+thread_local std::string g_last_error;
+
+// Compiled plans keyed by descriptor content; entries live until process exit.
+std::mutex g_cache_mu;
+std::unordered_map<uint64_t, std::unique_ptr<attn_plan>> g_cache;
+
+attn_status hip_fail(hipError_t e, const char* what) {
+  set_error(std::string(what) + ": " + hipGetErrorString(e));
+  return ATTN_E_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+attn_status check_tensor(const attn_tensor* t, const char* name, int64_t B, int64_t L, int64_t H,
+                         int64_t D) {
+  if (!t) { set_error(std::string(name) + " is NULL"); return ATTN_E_INVAL; }
+  if (!t->data) { set_error(std::string(name) + ".data is NULL"); return ATTN_E_INVAL; }
+  if (t->B != B || t->L != L || t->H != H || t->D != D) {
+    set_error(std::string(name) + " shape differs from q (or from the plan)");
+    return ATTN_E_INVAL;
+  }
+  if (t->stride_b < 0 || t->stride_l < D || t->stride_h < 0) {
+    set_error(std::string(name) + " has a negative or overlapping stride");
+    return ATTN_E_INVAL;
+  }
+  if (!aligned16(t->data) || (t->stride_b % 8) || (t->stride_l % 8) || (t->stride_h % 8)) {
+    set_error(std::string(name) + " rows must start on 16-byte boundaries (strides multiple of 8)");
+    return ATTN_E_INVAL;
+  }
+  if (t->stride_l * 2 * 64 > INT32_MAX) {
+    set_error(std::string(name) + " token stride too large");
+    return ATTN_E_UNSUPPORTED;
+  }
+  return ATTN_OK;
+}
+
+attn_status launch_with_plan(const attn_plan& p, const attn_tensor* q, const attn_tensor* k,
+                             const attn_tensor* v, const float* sink, attn_tensor* o,
+                             const attn_launch* launch) {
+  if (!launch) { set_error("launch is NULL"); return ATTN_E_INVAL; }
+  if (!q) { set_error("q is NULL"); return ATTN_E_INVAL; }
+  const int64_t B = q->B;
+  if (B < 1 || B > 65535) { set_error("batch must be in [1, 65535]"); return ATTN_E_INVAL; }
+  attn_status st;
+  if ((st = check_tensor(q, "q", B, p.L, p.H, p.D)) != ATTN_OK) return st;
+  if ((st = check_tensor(k, "k", B, p.L, p.H, p.D)) != ATTN_OK) return st;
+  if ((st = check_tensor(v, "v", B, p.L, p.H, p.D)) != ATTN_OK) return st;
+  if ((st = check_tensor(o, "o", B, p.L, p.H, p.D)) != ATTN_OK) return st;
+  if (o->data == q->data || o->data == k->data || o->data == v->data) {
+    set_error("o must not alias q, k or v");
+    return ATTN_E_INVAL;
+  }
+  if (p.kind == ATTN_MASK_BLOCK && !p.block_aligned) {
+    set_error("block size must be a multiple of 128 for the GPU kernel");
+    return ATTN_E_UNSUPPORTED;
+  }
+  if (!launch->workspace || launch->workspace_bytes < p.layout.bytes) {
+    set_error("workspace smaller than attn_plan_workspace_bytes (" + std::to_string(p.layout.bytes) +
+              " bytes)");
+    return ATTN_E_WORKSPACE;
+  }
+  if (!aligned16(launch->workspace)) { set_error("workspace must be 16-byte aligned"); return ATTN_E_INVAL; }
+
+  const uint8_t* ws = static_cast<const uint8_t*>(launch->workspace);
+  FwdParams f{};
+  f.q = static_cast<const uint16_t*>(q->data);
+  f.k = static_cast<const uint16_t*>(k->data);
+  f.v = static_cast<const uint16_t*>(v->data);
+  f.o = static_cast<uint16_t*>(o->data);
+  f.q_sb = q->stride_b; f.q_sl = q->stride_l; f.q_sh = q->stride_h;
+  f.k_sb = k->stride_b; f.k_sl = k->stride_l; f.k_sh = k->stride_h;
+  f.v_sb = v->stride_b; f.v_sl = v->stride_l; f.v_sh = v->stride_h;
+  f.o_sb = o->stride_b; f.o_sl = o->stride_l; f.o_sh = o->stride_h;
+  f.items = reinterpret_cast<const int32_t*>(ws + p.layout.off_items);
+  f.kv = reinterpret_cast<const int32_t*>(ws + p.layout.off_kv);
+  f.head_left = reinterpret_cast<const int32_t*>(ws + p.layout.off_head_left);
+  f.block_bits = reinterpret_cast<const uint32_t*>(ws + p.layout.off_bits);
+  f.sink = sink;
+  const float scale = launch->softmax_scale > 0.f ? launch->softmax_scale
+                                                  : static_cast<float>(1.0 / std::sqrt(double(p.D)));
+  f.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
+  f.L = static_cast<int32_t>(p.L);
+  f.H = static_cast<int32_t>(p.H);
+  f.n_items = static_cast<int32_t>(p.items.size());
+  f.kind = p.kind;
+  f.causal = p.causal;
+  f.chunk = static_cast<int32_t>(std::min<int64_t>(p.chunk, p.L));
+  if (f.chunk < 1) f.chunk = 1;
+  f.right = static_cast<int32_t>(p.right);
+  hipError_t e = launch_fwd(f, static_cast<int>(p.D), static_cast<int>(B),
+                            static_cast<hipStream_t>(launch->stream));
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return ATTN_OK;
+}
+
+attn_status upload(const attn_plan& p, void* workspace, size_t bytes, void* stream) {
+  if (!workspace || bytes < p.layout.bytes) {
+    set_error("workspace smaller than attn_plan_workspace_bytes (" + std::to_string(p.layout.bytes) +
+              " bytes)");
+    return ATTN_E_WORKSPACE;
+  }
+  std::vector<uint8_t> img;
+  try {
+    img.resize(p.layout.bytes);
+  } catch (const std::bad_alloc&) {
+    set_error("host allocation failed for the plan image");
+    return ATTN_E_NOMEM;
+  }
+  write_image(p, img.data());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan image)");
+  // The staging buffer is pageable host memory that goes out of scope here.
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize (plan image)");
+  return ATTN_OK;
+}
+
+attn_status cached_plan(const attn_mask_desc* mask, int64_t L, int64_t H, int64_t D,
+                        const attn_plan** out) {
+  if (!mask) { set_error("mask descriptor is NULL"); return ATTN_E_INVAL; }
+  // Validate pointers needed by the fingerprint before hashing them.
+  if (mask->kind == ATTN_MASK_BLOCK && (!mask->block_mask || mask->block < 1 ||
+                                        (mask->block_mask_heads != 1 && mask->block_mask_heads != H))) {
+    set_error("BLOCK descriptor needs block >= 1, block_mask and block_mask_heads in {1, H}");
+    return ATTN_E_INVAL;
+  }
+  if (H < 1 || L < 1) { set_error("L and H must be >= 1"); return ATTN_E_INVAL; }
+  const uint64_t key = fingerprint(mask, L, H, D);
+  std::lock_guard<std::mutex> g(g_cache_mu);
+  auto it = g_cache.find(key);
+  if (it != g_cache.end()) {
+    *out = it->second.get();
+    return ATTN_OK;
+  }
+  attn_plan* p = nullptr;
+  attn_status st = compile_plan(mask, L, H, D, &p);
+  if (st != ATTN_OK) return st;
+  try {
+    g_cache.emplace(key, std::unique_ptr<attn_plan>(p));
+  } catch (const std::bad_alloc&) {
+    delete p;
+    set_error("host allocation failed for the plan cache");
+    return ATTN_E_NOMEM;
+  }
+  *out = p;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+}  // namespace bss
+
+using namespace bss;
+
+extern "C" {
+
+attn_status attn_plan_create(const attn_mask_desc* mask, int64_t L, int64_t H, int64_t D,
+                             attn_plan** out) {
+  try {
+    return compile_plan(mask, L, H, D, out);
+  } catch (...) {
+    set_error("unexpected exception while compiling the plan");
+    return ATTN_E_NOMEM;
+  }
+}
+
+attn_status attn_plan_tiles(const attn_plan* p, int32_t* bm, int32_t* bn, int64_t* n_rows, int64_t* nnz,
+                            const int32_t** row_ptr, const int32_t** kv_tile, const uint8_t** flags) {
+  if (!p) { set_error("plan is NULL"); return ATTN_E_INVAL; }
+  if (bm) *bm = p->bm;
+  if (bn) *bn = p->bn;
+  if (n_rows) *n_rows = static_cast<int64_t>(p->row_ptr.size()) - 1;
+  if (nnz) *nnz = static_cast<int64_t>(p->kv_tile.size());
+  if (row_ptr) *row_ptr = p->row_ptr.data();
+  if (kv_tile) *kv_tile = p->kv_tile.data();
+  if (flags) *flags = p->flags.data();
+  return ATTN_OK;
+}
+
+attn_status attn_plan_pairs(const attn_plan* p, int64_t* pairs_per_head, int64_t* total) {
+  if (!p) { set_error("plan is NULL"); return ATTN_E_INVAL; }
+  if (pairs_per_head) std::memcpy(pairs_per_head, p->pairs.data(), p->pairs.size() * sizeof(int64_t));
+  if (total) *total = p->pairs_total;
+  return ATTN_OK;
+}
+
+attn_status attn_plan_schedule(const attn_plan* p, int64_t* n_items, const int32_t** items) {
+  if (!p) { set_error("plan is NULL"); return ATTN_E_INVAL; }
+  if (n_items) *n_items = static_cast<int64_t>(p->items.size());
+  if (items) *items = reinterpret_cast<const int32_t*>(p->items.data());
+  return ATTN_OK;
+}
+
+attn_status attn_plan_workspace_bytes(const attn_plan* p, size_t* bytes) {
+  if (!p || !bytes) { set_error("plan or bytes is NULL"); return ATTN_E_INVAL; }
+  *bytes = p->layout.bytes;
+  return ATTN_OK;
+}
+
+attn_status attn_plan_upload(const attn_plan* p, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!p) { set_error("plan is NULL"); return ATTN_E_INVAL; }
+  try {
+    return upload(*p, workspace, workspace_bytes, stream);
+  } catch (...) {
+    set_error("unexpected exception during upload");
+    return ATTN_E_NOMEM;
+  }
+}
+
+attn_status attn_masked_fwd_plan(const attn_plan* p, const attn_tensor* q, const attn_tensor* k,
+                                 const attn_tensor* v, const float* sink, attn_tensor* o,
+                                 const attn_launch* launch) {
+  if (!p) { set_error("plan is NULL"); return ATTN_E_INVAL; }
+  try {
+    return launch_with_plan(*p, q, k, v, sink, o, launch);
+  } catch (...) {
+    set_error("unexpected exception during launch");
+    return ATTN_E_NOMEM;
+  }
+}
+
+attn_status attn_workspace_bytes(const attn_mask_desc* mask, int64_t L, int64_t H, int64_t D,
+                                 size_t* bytes) {
+  if (!bytes) { set_error("bytes is NULL"); return ATTN_E_INVAL; }
+  try {
+    const attn_plan* p = nullptr;
+    attn_status st = cached_plan(mask, L, H, D, &p);
+    if (st != ATTN_OK) return st;
+    *bytes = p->layout.bytes;
+    return ATTN_OK;
+  } catch (...) {
+    set_error("unexpected exception");
+    return ATTN_E_NOMEM;
+  }
+}
+
+attn_status attn_masked_fwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                            const attn_mask_desc* mask, const float* sink, attn_tensor* o,
+                            const attn_launch* launch) {
+  try {
+    if (!q) { set_error("q is NULL"); return ATTN_E_INVAL; }
+    if (!launch) { set_error("launch is NULL"); return ATTN_E_INVAL; }
+    const attn_plan* p = nullptr;
+    attn_status st = cached_plan(mask, q->L, q->H, q->D, &p);
+    if (st != ATTN_OK) return st;
+    if ((st = check_tensor(q, "q", q->B, p->L, p->H, p->D)) != ATTN_OK) return st;
+    st = upload(*p, launch->workspace, launch->workspace_bytes, launch->stream);
+    if (st != ATTN_OK) return st;
+    return launch_with_plan(*p, q, k, v, sink, o, launch);
+  } catch (...) {
+    set_error("unexpected exception");
+    return ATTN_E_NOMEM;
+  }
+}
+
+void attn_plan_destroy(attn_plan* p) { delete p; }
+
+const char* attn_last_error(void) { return bss::g_last_error.c_str(); }
+
+const char* attn_version(void) { return "bss_attn 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,334 @@
+// Mask-descriptor compiler and tile scheduler.  Host C++17, no HIP calls.
+//
+// Mask semantics (0-based tokens i = query, j = key, both < L):
+//   FULL    all j                                  (SHS slides, mask slide)
+//   CHUNK   floor(i/C) == floor(j/C)               (same slide, "chunk window")
+//   WINDOW  i - left_h <= j <= i + right           (inclusive; the serialisation
+//                                                   slide's 7..23 example)
+//   BLOCK   B_h[i/Bs][j/Bs] == 1 and j <= i         (RRAttention Eq. 2)
+//   causal = 1 additionally requires j <= i.
+// For FULL, CHUNK and WINDOW the allowed keys of row i form one interval
+// [lo(i), hi(i)) whose ends never decrease as i grows; the compiler works on
+// those intervals.  BLOCK walks the kept blocks of each block row.
+
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <numeric>
+
+namespace bss {
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// FNV-1a over bytes.
+struct Hasher {
+  uint64_t h = 1469598103934665603ull;
+  void bytes(const void* p, size_t n) {
+    const uint8_t* b = static_cast<const uint8_t*>(p);
+    for (size_t i = 0; i < n; ++i) {
+      h ^= b[i];
+      h *= 1099511628211ull;
+    }
+  }
+  template <class T>
+  void pod(const T& v) { bytes(&v, sizeof(T)); }
+};
+
+// Allowed interval [lo, hi) of row i for the interval kinds.
+inline void row_interval(const attn_plan& p, int64_t h, int64_t i, int64_t* lo, int64_t* hi) {
+  int64_t a = 0, b = p.L;
+  if (p.kind == ATTN_MASK_CHUNK) {
+    a = (i / p.chunk) * p.chunk;
+    b = std::min(p.L, a + p.chunk);
+  } else if (p.kind == ATTN_MASK_WINDOW) {
+    a = std::max<int64_t>(0, i - p.head_left[h]);
+    b = std::min(p.L, i + p.right + 1);
+  }
+  if (p.causal) b = std::min(b, i + 1);
+  *lo = a;
+  *hi = b;
+}
+
+attn_status validate(const attn_mask_desc* m, int64_t L, int64_t H, int64_t D) {
+  if (!m) { set_error("mask descriptor is NULL"); return ATTN_E_INVAL; }
+  if (L < 1 || H < 1) { set_error("L and H must be >= 1"); return ATTN_E_INVAL; }
+  if (L > (int64_t(1) << 30)) { set_error("L above 2^30 is not supported"); return ATTN_E_UNSUPPORTED; }
+  if (H > 65535) { set_error("H above 65535 is not supported"); return ATTN_E_UNSUPPORTED; }
+  if (D != 64 && D != 80 && D != 128) {
+    set_error("head dim " + std::to_string(D) + " is not supported (64, 80, 128)");
+    return ATTN_E_UNSUPPORTED;
+  }
+  if (m->causal != 0 && m->causal != 1) { set_error("causal must be 0 or 1"); return ATTN_E_INVAL; }
+  switch (m->kind) {
+    case ATTN_MASK_FULL:
+      break;
+    case ATTN_MASK_CHUNK:
+      if (m->chunk < 1) { set_error("chunk size must be >= 1"); return ATTN_E_INVAL; }
+      break;
+    case ATTN_MASK_WINDOW:
+      if (m->left < 0 || m->right < 0) { set_error("window reach must be >= 0"); return ATTN_E_INVAL; }
+      if (m->head_left) {
+        for (int64_t h = 0; h < H; ++h)
+          if (m->head_left[h] < 0) { set_error("head_left entries must be >= 0"); return ATTN_E_INVAL; }
+      }
+      break;
+    case ATTN_MASK_BLOCK: {
+      if (m->block < 1) { set_error("block size must be >= 1"); return ATTN_E_INVAL; }
+      if (!m->block_mask) { set_error("block_mask is NULL"); return ATTN_E_INVAL; }
+      if (m->block_mask_heads != 1 && m->block_mask_heads != H) {
+        set_error("block_mask_heads must be 1 or H");
+        return ATTN_E_INVAL;
+      }
+      const int64_t nb = ceil_div(L, m->block);
+      for (int64_t hb = 0; hb < m->block_mask_heads; ++hb) {
+        const uint8_t* b = m->block_mask + hb * nb * nb;
+        for (int64_t r = 0; r < nb; ++r)
+          for (int64_t c = r + 1; c < nb; ++c)
+            if (b[r * nb + c]) {
+              set_error("block_mask has B[" + std::to_string(r) + "][" + std::to_string(c) +
+                        "] = 1 above the diagonal (causality, RRAttention Eq. 5)");
+              return ATTN_E_INVAL;
+            }
+      }
+      break;
+    }
+    default:
+      set_error("unknown mask kind " + std::to_string(m->kind));
+      return ATTN_E_INVAL;
+  }
+  return ATTN_OK;
+}
+
+// Lists for FULL / CHUNK / WINDOW.
+void compile_intervals(attn_plan& p) {
+  const int64_t bm = p.bm, bn = p.bn;
+  std::vector<int32_t> diff(p.nk + 1);
+  p.row_ptr.assign(1, 0);
+  p.pairs.assign(p.H, 0);
+  for (int64_t h = 0; h < p.H; ++h) {
+    for (int64_t qt = 0; qt < p.nq; ++qt) {
+      const int64_t i0 = qt * bm, i1 = std::min(p.L, i0 + bm);
+      std::fill(diff.begin(), diff.end(), 0);
+      int64_t max_lo = 0, min_hi = p.L;
+      for (int64_t i = i0; i < i1; ++i) {
+        int64_t lo, hi;
+        row_interval(p, h, i, &lo, &hi);
+        max_lo = std::max(max_lo, lo);
+        min_hi = std::min(min_hi, hi);
+        if (hi <= lo) continue;
+        p.pairs[h] += hi - lo;
+        diff[lo / bn] += 1;
+        diff[(hi - 1) / bn + 1] -= 1;
+      }
+      int32_t run = 0;
+      const bool rows_full = (i1 - i0) == bm;
+      for (int64_t kt = 0; kt < p.nk; ++kt) {
+        run += diff[kt];
+        if (run <= 0) continue;
+        const int64_t j0 = kt * bn, j1 = j0 + bn;
+        const bool full = rows_full && j1 <= p.L && max_lo <= j0 && min_hi >= j1;
+        p.kv_tile.push_back(static_cast<int32_t>(kt));
+        p.flags.push_back(full ? 1 : 0);
+      }
+      p.row_ptr.push_back(static_cast<int32_t>(p.kv_tile.size()));
+    }
+  }
+}
+
+// Lists for BLOCK: walk the kept blocks of each block row overlapping the query tile.
+void compile_blocks(attn_plan& p) {
+  const int64_t bm = p.bm, bn = p.bn, bs = p.block, nb = p.nb;
+  std::vector<uint8_t> present(p.nk);
+  p.row_ptr.assign(1, 0);
+  p.pairs.assign(p.H, 0);
+  for (int64_t h = 0; h < p.H; ++h) {
+    const uint8_t* B = p.block_mask.data() + (p.block_heads > 1 ? h : 0) * nb * nb;
+    // pairs: per block row, full-width kept blocks to the left plus the causal diagonal block
+    for (int64_t br = 0; br < nb; ++br) {
+      const int64_t r0 = br * bs, r1 = std::min(p.L, r0 + bs);
+      int64_t width = 0;
+      for (int64_t bc = 0; bc < br; ++bc)
+        if (B[br * nb + bc]) width += std::min(p.L, (bc + 1) * bs) - bc * bs;
+      int64_t pr = (r1 - r0) * width;
+      if (B[br * nb + br]) {
+        const int64_t n = r1 - r0;
+        pr += n * (n + 1) / 2;
+      }
+      p.pairs[h] += pr;
+    }
+    for (int64_t qt = 0; qt < p.nq; ++qt) {
+      const int64_t i0 = qt * bm, i1 = std::min(p.L, i0 + bm);
+      std::fill(present.begin(), present.end(), 0);
+      for (int64_t br = i0 / bs; br <= (i1 - 1) / bs; ++br) {
+        const int64_t r1 = std::min(i1, (br + 1) * bs);     // rows of this tile in block row br
+        for (int64_t bc = 0; bc <= br; ++bc) {
+          if (!B[br * nb + bc]) continue;
+          const int64_t c0 = bc * bs;
+          const int64_t c1 = std::min({p.L, (bc + 1) * bs, r1});  // j <= i < r1
+          if (c1 <= c0) continue;
+          for (int64_t kt = c0 / bn; kt <= (c1 - 1) / bn; ++kt) present[kt] = 1;
+        }
+      }
+      for (int64_t kt = 0; kt < p.nk; ++kt) {
+        if (!present[kt]) continue;
+        const int64_t j0 = kt * bn, j1 = j0 + bn;
+        bool full = (i1 - i0) == bm && j1 <= p.L && (j1 - 1) <= i0;
+        for (int64_t br = i0 / bs; full && br <= (i1 - 1) / bs; ++br)
+          for (int64_t bc = j0 / bs; full && bc <= (j1 - 1) / bs; ++bc)
+            if (!B[br * nb + bc]) full = false;
+        p.kv_tile.push_back(static_cast<int32_t>(kt));
+        p.flags.push_back(full ? 1 : 0);
+      }
+      p.row_ptr.push_back(static_cast<int32_t>(p.kv_tile.size()));
+    }
+  }
+}
+
+// Work order: heads by descending total cost, and inside a head the query
+// tiles by descending cost, so that long items start first while work items
+// that run at the same time share one head's keys and values in cache.
+void schedule(attn_plan& p) {
+  const int64_t rows = p.H * p.nq;
+  std::vector<double> cost(rows);
+  std::vector<double> head_cost(p.H, 0.0);
+  for (int64_t r = 0; r < rows; ++r) {
+    double c = 0.5;  // Q load and epilogue
+    for (int32_t e = p.row_ptr[r]; e < p.row_ptr[r + 1]; ++e) c += p.flags[e] ? 1.0 : 1.25;
+    cost[r] = c;
+    head_cost[r / p.nq] += c;
+  }
+  std::vector<int64_t> heads(p.H);
+  std::iota(heads.begin(), heads.end(), 0);
+  std::stable_sort(heads.begin(), heads.end(),
+                   [&](int64_t a, int64_t b) { return head_cost[a] > head_cost[b]; });
+  p.items.clear();
+  p.items.reserve(rows);
+  std::vector<int64_t> qts(p.nq);
+  for (int64_t h : heads) {
+    std::iota(qts.begin(), qts.end(), 0);
+    std::stable_sort(qts.begin(), qts.end(),
+                     [&](int64_t a, int64_t b) { return cost[h * p.nq + a] > cost[h * p.nq + b]; });
+    for (int64_t qt : qts) {
+      const int64_t r = h * p.nq + qt;
+      p.items.push_back(Item{static_cast<int32_t>(h), static_cast<int32_t>(qt), p.row_ptr[r],
+                             p.row_ptr[r + 1]});
+    }
+  }
+}
+
+void build_image(attn_plan& p) {
+  p.kv_entries.resize(p.kv_tile.size());
+  for (size_t e = 0; e < p.kv_tile.size(); ++e) p.kv_entries[e] = (p.kv_tile[e] << 1) | p.flags[e];
+  p.head_left32.assign(p.H, 0);
+  if (p.kind == ATTN_MASK_WINDOW)
+    for (int64_t h = 0; h < p.H; ++h)
+      p.head_left32[h] = static_cast<int32_t>(std::min<int64_t>(p.head_left[h], p.L));
+  if (p.kind == ATTN_MASK_BLOCK && !p.block_aligned) {
+    const int64_t words = ceil_div(p.nb, 32);
+    p.block_bits.assign(static_cast<size_t>(p.block_heads) * p.nb * words, 0u);
+    for (int64_t hb = 0; hb < p.block_heads; ++hb)
+      for (int64_t r = 0; r < p.nb; ++r)
+        for (int64_t c = 0; c <= r; ++c)
+          if (p.block_mask[(hb * p.nb + r) * p.nb + c])
+            p.block_bits[(hb * p.nb + r) * words + c / 32] |= 1u << (c % 32);
+  }
+  ImageLayout& l = p.layout;
+  l.off_items = 0;
+  l.off_kv = align_up(l.off_items + p.items.size() * sizeof(Item));
+  l.off_head_left = align_up(l.off_kv + std::max<size_t>(1, p.kv_entries.size()) * sizeof(int32_t));
+  l.off_bits = align_up(l.off_head_left + p.head_left32.size() * sizeof(int32_t));
+  l.bytes = align_up(l.off_bits + p.block_bits.size() * sizeof(uint32_t));
+}
+
+}  // namespace
+
+uint64_t fingerprint(const attn_mask_desc* m, int64_t L, int64_t H, int64_t D) {
+  Hasher hs;
+  hs.pod(L); hs.pod(H); hs.pod(D);
+  hs.pod(m->kind); hs.pod(m->causal);
+  switch (m->kind) {
+    case ATTN_MASK_CHUNK: hs.pod(m->chunk); break;
+    case ATTN_MASK_WINDOW:
+      hs.pod(m->left); hs.pod(m->right);
+      if (m->head_left) hs.bytes(m->head_left, sizeof(int64_t) * H);
+      else hs.pod(int64_t(-1));
+      break;
+    case ATTN_MASK_BLOCK: {
+      hs.pod(m->block); hs.pod(m->block_mask_heads);
+      const int64_t nb = ceil_div(L, m->block);
+      if (m->block_mask) hs.bytes(m->block_mask, static_cast<size_t>(m->block_mask_heads) * nb * nb);
+      break;
+    }
+    default: break;
+  }
+  return hs.h;
+}
+
+attn_status compile_plan(const attn_mask_desc* m, int64_t L, int64_t H, int64_t D, attn_plan** out) {
+  if (!out) { set_error("output pointer is NULL"); return ATTN_E_INVAL; }
+  attn_status st = validate(m, L, H, D);
+  if (st != ATTN_OK) return st;
+  attn_plan* p = nullptr;
+  try {
+    p = new attn_plan();
+    p->kind = m->kind;
+    p->causal = m->causal;
+    p->L = L; p->H = H; p->D = D;
+    p->nq = ceil_div(L, p->bm);
+    p->nk = ceil_div(L, p->bn);
+    if (m->kind == ATTN_MASK_CHUNK) p->chunk = m->chunk;
+    if (m->kind == ATTN_MASK_WINDOW) {
+      p->left = m->left;
+      p->right = std::min<int64_t>(m->right, L);
+      p->head_left.resize(H);
+      for (int64_t h = 0; h < H; ++h)
+        p->head_left[h] = std::min<int64_t>(m->head_left ? m->head_left[h] : m->left, L);
+    }
+    if (m->kind == ATTN_MASK_BLOCK) {
+      p->block = m->block;
+      p->block_heads = m->block_mask_heads;
+      p->nb = ceil_div(L, m->block);
+      p->block_mask.resize(static_cast<size_t>(p->block_heads) * p->nb * p->nb);
+      for (size_t i = 0; i < p->block_mask.size(); ++i) p->block_mask[i] = m->block_mask[i] ? 1 : 0;
+      p->block_aligned = (p->block % p->bm == 0) && (p->block % p->bn == 0);
+      compile_blocks(*p);
+    } else {
+      compile_intervals(*p);
+    }
+    p->pairs_total = std::accumulate(p->pairs.begin(), p->pairs.end(), int64_t(0));
+    if (p->kv_tile.size() > static_cast<size_t>(INT32_MAX)) {
+      delete p;
+      set_error("tile list longer than 2^31 entries");
+      return ATTN_E_UNSUPPORTED;
+    }
+    schedule(*p);
+    build_image(*p);
+    p->fingerprint = fingerprint(m, L, H, D);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    set_error("host allocation failed while compiling the plan");
+    return ATTN_E_NOMEM;
+  }
+  *out = p;
+  return ATTN_OK;
+}
+
+void write_image(const attn_plan& p, uint8_t* dst) {
+  std::memset(dst, 0, p.layout.bytes);
+  std::memcpy(dst + p.layout.off_items, p.items.data(), p.items.size() * sizeof(Item));
+  std::memcpy(dst + p.layout.off_kv, p.kv_entries.data(), p.kv_entries.size() * sizeof(int32_t));
+  std::memcpy(dst + p.layout.off_head_left, p.head_left32.data(), p.head_left32.size() * sizeof(int32_t));
+  if (!p.block_bits.empty())
+    std::memcpy(dst + p.layout.off_bits, p.block_bits.data(), p.block_bits.size() * sizeof(uint32_t));
+}
+
+}  // namespace bss

@@ -1,0 +1,82 @@
+// Mask-descriptor compiler and tile scheduler (host side).
+//
+// A plan turns a mask descriptor (full / chunk / sliding window / per-head
+// causal window / block-selection matrix) into, for every (head, query tile),
+// the ascending list of key tiles that contain at least one allowed pair, each
+// flagged FULL or PARTIAL.  Masked-out tiles never appear, so the kernel never
+// loads or multiplies them.  The tile partition is the block partition of
+// "RRAttention", section 2.1 (contiguous blocks, ceil(L/B) of them), applied
+// with query tiles of BM rows and key tiles of BN columns.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "bss_attn.h"
+
+namespace bss {
+
+constexpr int kBM = 128;  // query rows per work item (4 waves x 32 rows)
+constexpr int kBN = 64;   // keys per KV tile
+
+// Device record of one work item (16 bytes).
+struct Item {
+  int32_t head, qtile, begin, end;
+};
+
+// Layout of the plan's device image inside the caller's workspace.
+struct ImageLayout {
+  size_t off_items = 0, off_kv = 0, off_head_left = 0, off_bits = 0, bytes = 0;
+};
+
+void set_error(const std::string& msg);
+
+}  // namespace bss
+
+struct attn_plan {
+  // descriptor (copied)
+  int32_t kind = 0, causal = 0;
+  int64_t chunk = 0, left = 0, right = 0, block = 0;
+  int32_t block_heads = 0;
+  std::vector<int64_t> head_left;     // [H] for WINDOW (left broadcast when no per-head array)
+  std::vector<uint8_t> block_mask;    // [Hb][Nb][Nb] for BLOCK
+  int64_t nb = 0;                     // ceil(L / block)
+  bool block_aligned = true;          // block % BM == 0 and block % BN == 0
+
+  int64_t L = 0, H = 0, D = 0;
+  int32_t bm = bss::kBM, bn = bss::kBN;
+  int64_t nq = 0, nk = 0;
+
+  // canonical lists
+  std::vector<int32_t> row_ptr, kv_tile;
+  std::vector<uint8_t> flags;
+  std::vector<int64_t> pairs;         // allowed pairs per head
+  int64_t pairs_total = 0;
+
+  // schedule and device image
+  std::vector<bss::Item> items;
+  std::vector<int32_t> kv_entries;    // (kv_tile << 1) | full, in canonical order
+  std::vector<int32_t> head_left32;   // [H]
+  std::vector<uint32_t> block_bits;   // [Hb][Nb][ceil(Nb/32)] when not block_aligned
+  bss::ImageLayout layout;
+
+  // content fingerprint (cache key)
+  uint64_t fingerprint = 0;
+};
+
+namespace bss {
+
+// Validate and compile.  Returns ATTN_OK and a new plan, or an error status
+// with the message set.
+attn_status compile_plan(const attn_mask_desc* mask, int64_t L, int64_t H, int64_t D,
+                         attn_plan** out);
+
+// Hash of the descriptor content together with (L, H, D).
+uint64_t fingerprint(const attn_mask_desc* mask, int64_t L, int64_t H, int64_t D);
+
+// Serialise the device image into `dst` (layout.bytes long).
+void write_image(const attn_plan& p, uint8_t* dst);
+
+}  // namespace bss

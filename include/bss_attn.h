@@ -1,0 +1,181 @@
+/*
+ * bss_attn.h — C ABI of the structured-mask softmax attention library (gfx950).
+ *
+ * The library computes the forward pass
+ *
+ *     O = Softmax( Q K^T / sqrt(d)  restricted to the allowed keys N(i),
+ *                  optionally with a per-head sink logit in the denominator ) V
+ *
+ * for bf16 Q, K, V with float32 accumulation, writing bf16 O.
+ *   - Scores and the row-wise softmax follow "Vision transformers and hybrid
+ *     architectures", section 2 (score_ij = q_i.k_j/sqrt(d), row softmax, z_i = sum_j a_ij v_j).
+ *   - The allowed-key sets N(i) (full, chunk window, sliding window with l left
+ *     and r right) follow the mask slide of "Semantic Head Specialization Guides
+ *     Hybrid ViT Attention for Multimodal LLMs"; the sliding window is inclusive
+ *     at both ends (that page's serialisation slide: anchor 15 with 8 per side
+ *     covers tokens 7..23).
+ *   - Per-head causal windows of W keys ("Asymmetric Attention Heads", Table 2)
+ *     are the WINDOW kind with causal = 1 and head_left[h] = W_h - 1.
+ *   - The block-selection matrix B in {0,1}^{Nb x Nb}, Nb = ceil(L/Bs), is
+ *     expanded to tokens as M[i,j] = B[i/Bs][j/Bs] and j <= i ("RRAttention",
+ *     section 2.1, Eq. 1-2); B[m][n] = 1 with n > m violates Eq. 5 and is rejected.
+ *     A zero entry of B skips the pair (its weight is exactly 0).
+ *   - The sink s_aux[h] is a logit with no value that only enlarges the
+ *     denominator; -inf means no sink (SHS slides, the sink-bias slide, "Eq. 1").
+ *   - A row with no allowed key is written as zeros.
+ *
+ * Conventions shared by every entry point
+ *   - Device tensors are views: element strides for batch, token and head; the
+ *     head dimension is contiguous (stride 1).  Every row start must be 16-byte
+ *     aligned (D and all strides multiples of 8 elements, 16-byte aligned base).
+ *   - The caller owns every device buffer (Q, K, V, O, sink, workspace).  The
+ *     library never allocates or frees device memory.  Host arrays passed in a
+ *     mask descriptor are only read during the call; a plan copies what it needs.
+ *   - Launches are asynchronous on the given HIP stream: they enqueue the
+ *     kernel and return.  A kernel fault surfaces at the caller's next
+ *     synchronisation as a HIP error.  Copying a plan's device image
+ *     (attn_plan_upload, and attn_masked_fwd which uploads on every call)
+ *     stages it in pageable host memory and synchronises the stream once.
+ *   - Functions return attn_status and never throw or abort.  On a non-OK status
+ *     attn_last_error() returns a message (thread-local, valid until the next call
+ *     on that thread).
+ *   - Supported head dims: 64, 80, 128.  Batch B >= 1.  Lq == Lk.  GQA is not
+ *     supported (K and V have as many heads as Q).
+ */
+#ifndef BSS_ATTN_H
+#define BSS_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_INVAL = -1,       /* malformed argument: shapes, strides, alignment, descriptor fields */
+  ATTN_E_UNSUPPORTED = -2, /* well-formed but outside what the kernels implement (e.g. D = 96)   */
+  ATTN_E_WORKSPACE = -3,   /* workspace missing or smaller than attn_plan_workspace_bytes        */
+  ATTN_E_HIP = -4,         /* a HIP runtime call failed; the message carries hipGetErrorString   */
+  ATTN_E_NOMEM = -5        /* host allocation failed while compiling a plan                      */
+} attn_status;
+
+typedef enum {
+  ATTN_MASK_FULL = 0,   /* every key                                                   */
+  ATTN_MASK_CHUNK = 1,  /* floor(i/chunk) == floor(j/chunk): non-overlapping chunks     */
+  ATTN_MASK_WINDOW = 2, /* i - left_h <= j <= i + right (inclusive)                      */
+  ATTN_MASK_BLOCK = 3   /* B_h[i/block][j/block] == 1 and j <= i                         */
+} attn_mask_kind;
+
+/* A bf16 device tensor view of logical shape [B, L, H, D]. */
+typedef struct {
+  void* data;                 /* device pointer to element [0,0,0,0]                  */
+  int64_t B, L, H, D;         /* batch, tokens, heads, head dim                       */
+  int64_t stride_b, stride_l, stride_h; /* element strides; the D stride is 1          */
+} attn_tensor;
+
+/* Which keys each query may see.  Unused fields are ignored for a given kind. */
+typedef struct {
+  int32_t kind;               /* attn_mask_kind                                        */
+  int32_t causal;             /* 1: additionally require j <= i (FULL, CHUNK, WINDOW); BLOCK is always causal */
+  int64_t chunk;              /* CHUNK: C >= 1                                         */
+  int64_t left, right;        /* WINDOW: reach to the left and to the right, >= 0      */
+  const int64_t* head_left;   /* WINDOW, optional host [H]: per-head left reach (overrides left) */
+  int64_t block;              /* BLOCK: token block size Bs >= 1                       */
+  const uint8_t* block_mask;  /* BLOCK: host [Hb][Nb][Nb] row-major 0/1, Nb = ceil(L/Bs) */
+  int32_t block_mask_heads;   /* BLOCK: Hb = 1 (shared by all heads) or H             */
+} attn_mask_desc;
+
+/* Launch context. */
+typedef struct {
+  void* stream;               /* hipStream_t; NULL = the default stream               */
+  void* workspace;            /* device memory of at least workspace_bytes            */
+  size_t workspace_bytes;
+  float softmax_scale;        /* <= 0 selects 1/sqrt(D)                                */
+} attn_launch;
+
+/* Opaque compiled mask: tile lists, schedule and the device image layout. */
+typedef struct attn_plan attn_plan;
+
+/*
+ * One-shot forward.  Compiles (or finds in an internal cache keyed by the
+ * descriptor's content, L, H and D) the plan for `mask`, copies its device
+ * image into launch->workspace and launches the kernel on launch->stream.
+ *   q, k, v : bf16 [B, L, H, D] inputs (same B, L, H, D).
+ *   mask    : host descriptor.
+ *   sink    : NULL, or device float32 [H] sink logits.
+ *   o       : bf16 [B, L, H, D] output (may not alias q, k or v).
+ * Required workspace: attn_plan_workspace_bytes of the same plan (query it with
+ * attn_workspace_bytes below).  Errors: ATTN_E_INVAL, ATTN_E_UNSUPPORTED,
+ * ATTN_E_WORKSPACE, ATTN_E_HIP, ATTN_E_NOMEM.
+ */
+attn_status attn_masked_fwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                            const attn_mask_desc* mask, const float* sink, attn_tensor* o,
+                            const attn_launch* launch);
+
+/* Workspace bytes attn_masked_fwd needs for this descriptor and shape. */
+attn_status attn_workspace_bytes(const attn_mask_desc* mask, int64_t L, int64_t H, int64_t D,
+                                 size_t* bytes);
+
+/*
+ * Mask-descriptor compiler.  Validates `mask` against (L, H, D) and builds, for
+ * every (head, query tile), the ascending list of key tiles that hold at least
+ * one allowed pair, each flagged FULL or PARTIAL, plus the work schedule.
+ * Errors: ATTN_E_INVAL (bad descriptor; B violating Eq. 5), ATTN_E_UNSUPPORTED
+ * (D not in {64, 80, 128}), ATTN_E_NOMEM.  *out is set only on ATTN_OK.
+ */
+attn_status attn_plan_create(const attn_mask_desc* mask, int64_t L, int64_t H, int64_t D,
+                             attn_plan** out);
+
+/*
+ * Canonical tile lists (host views owned by the plan, valid until destroy).
+ * Rows are (head, query tile) in row-major order, n_rows = H * ceil(L/bm);
+ * row_ptr[n_rows+1]; kv_tile[nnz] ascending within a row; flags[nnz]: 1 = FULL
+ * (the whole bm x bn rectangle is inside the sequence and allowed), 0 = PARTIAL.
+ */
+attn_status attn_plan_tiles(const attn_plan* plan, int32_t* bm, int32_t* bn, int64_t* n_rows,
+                            int64_t* nnz, const int32_t** row_ptr, const int32_t** kv_tile,
+                            const uint8_t** flags);
+
+/* Allowed (query, key) pairs: per head into pairs_per_head[H] (may be NULL) and in total. */
+attn_status attn_plan_pairs(const attn_plan* plan, int64_t* pairs_per_head, int64_t* total);
+
+/*
+ * Work schedule: n_items records of 4 int32 {head, query tile, first list
+ * entry, one past the last list entry}, in the order the grid consumes them.
+ * Every (head, query tile) row appears exactly once (empty rows too: they
+ * write zeros).  Host view owned by the plan.
+ */
+attn_status attn_plan_schedule(const attn_plan* plan, int64_t* n_items, const int32_t** items);
+
+/* Device bytes the plan's image needs in the workspace. */
+attn_status attn_plan_workspace_bytes(const attn_plan* plan, size_t* bytes);
+
+/* Copy the plan's device image into `workspace` on `stream` (asynchronous). */
+attn_status attn_plan_upload(const attn_plan* plan, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * Forward with a compiled plan whose image the caller has already uploaded
+ * into launch->workspace with attn_plan_upload.  Same tensors and errors as
+ * attn_masked_fwd; q/k/v/o must match the plan's L, H, D.
+ */
+attn_status attn_masked_fwd_plan(const attn_plan* plan, const attn_tensor* q, const attn_tensor* k,
+                                 const attn_tensor* v, const float* sink, attn_tensor* o,
+                                 const attn_launch* launch);
+
+/* Free a plan (NULL is allowed). */
+void attn_plan_destroy(attn_plan* plan);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Library version string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSS_ATTN_H */

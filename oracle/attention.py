@@ -99,8 +99,7 @@ def attention(q, k, v, mask: dict, sink=None, rows=None, scale=None, row_chunk: 
       pairs    [H] number of allowed (i, j) pairs over the evaluated rows,
       rows     [H, n] the evaluated rows.
     """
-    qf, kf, vf = _as_f64(q), _as_f64(k), _as_f64(v)
-    B, H, L, D = qf.shape
+    B, H, L, D = np.shape(q)
     sigma = (1.0 / np.sqrt(D)) if scale is None else float(scale)
     if rows is None:
         rows = np.tile(np.arange(L, dtype=np.int64), (H, 1))
@@ -114,12 +113,14 @@ def attention(q, k, v, mask: dict, sink=None, rows=None, scale=None, row_chunk: 
     pairs = np.zeros(H, dtype=np.int64)
     for h in range(H):
         sa = -np.inf if s_aux is None else s_aux[h]
-        for r0 in range(0, n, row_chunk):
-            rr = rows[h, r0:r0 + row_chunk]
-            allowed = allowed_rows(mask, h, rr, L)
-            pairs[h] += int(allowed.sum())
-            for b in range(B):
-                s = sigma * (qf[b, h, rr] @ kf[b, h].T)          # [r, L]
+        for b in range(B):
+            kf, vf = _as_f64(k[b, h]), _as_f64(v[b, h])
+            for r0 in range(0, n, row_chunk):
+                rr = rows[h, r0:r0 + row_chunk]
+                allowed = allowed_rows(mask, h, rr, L)
+                if b == 0:
+                    pairs[h] += int(allowed.sum())
+                s = sigma * (_as_f64(q[b, h, rr]) @ kf.T)        # [r, L]
                 s = np.where(allowed, s, -np.inf)
                 m = np.maximum(s.max(axis=1), sa)                  # row max incl. the sink logit
                 empty = ~np.isfinite(m)                            # no allowed key and no sink
@@ -128,7 +129,7 @@ def attention(q, k, v, mask: dict, sink=None, rows=None, scale=None, row_chunk: 
                 z = e.sum(axis=1) + np.exp(sa - m)
                 zsafe = np.where(z > 0, z, 1.0)
                 p = e / zsafe[:, None]
-                out[b, h, r0:r0 + len(rr)] = p @ vf[b, h]
+                out[b, h, r0:r0 + len(rr)] = p @ vf
                 rowsum[b, h, r0:r0 + len(rr)] = p.sum(axis=1)
                 sink_mass[b, h, r0:r0 + len(rr)] = np.where(z > 0, np.exp(sa - m) / zsafe, 0.0)
     return dict(out=out, rowsum=rowsum, sink_mass=sink_mass, pairs=pairs, rows=rows)

@@ -13,9 +13,9 @@ N_b = ceil(L/B)) applied to any of the masks.
 
 Two independent derivations:
 * dense:  reshape the explicit L x L mask into [nq, BM, nk, BN] and use any/all;
-* block:  for a block matrix whose block size equals BM and BN, by index
-          arithmetic on B (a kept block strictly below the diagonal is FULL,
-          the diagonal block is PARTIAL because of j <= i, Eq. 2).
+* block:  for a block matrix whose block size is a multiple of BM and BN, by
+          index arithmetic on B (each tile sits inside one block; Eq. 2's
+          j <= i decides PARTIAL against FULL).
 """
 
 from __future__ import annotations
@@ -57,25 +57,35 @@ def tile_lists_dense(mask: dict, H: int, L: int, bm: int, bn: int, heads=None):
 
 
 def tile_lists_block(mask: dict, H: int, L: int, bm: int, bn: int):
-    """Index-arithmetic derivation for block masks when BM == BN == block size."""
+    """Index-arithmetic derivation for block masks whose block size is a multiple of BM and BN.
+
+    Each tile then lies inside one block (m, n) = (i0 // Bs, j0 // Bs).  It holds
+    an allowed pair iff B[m][n] = 1 and some key is not after some query
+    (j0 <= i1 - 1, Eq. 2's j <= i); it is FULL iff in addition every key is at or
+    before every query (j1 - 1 <= i0) and the rectangle lies inside the sequence.
+    """
     bs = int(mask["block"])
-    if not (bm == bn == bs):
-        raise ValueError("block derivation needs BM == BN == block size")
+    if bs % bm or bs % bn:
+        raise ValueError("block derivation needs the block size to be a multiple of BM and BN")
     bmat = np.asarray(mask["block_mask"]) != 0
-    nb = math.ceil(L / bs)
+    nq, nk = math.ceil(L / bm), math.ceil(L / bn)
+    i0 = np.arange(nq)[:, None] * bm
+    i1 = np.minimum(L, i0 + bm)
+    j0 = np.arange(nk)[None, :] * bn
+    j1 = j0 + bn
+    causal_some = j0 <= i1 - 1
+    causal_all = (j1 - 1 <= i0) & (j1 <= L) & (i0 + bm <= L)
     pres, full = [], []
-    n_idx = np.arange(nb)
     for h in range(H):
         bh = bmat[h] if bmat.shape[0] > 1 else bmat[0]
-        for m in range(nb):
-            p = bh[m] & (n_idx <= m)
-            f = p & (n_idx < m) & ((n_idx + 1) * bs <= L) & ((m + 1) * bs <= L)
-            pres.append(p)
-            full.append(f)
-    return _csr(np.array(pres), np.array(full))
+        kept = bh[(i0 // bs), (j0 // bs)]                      # [nq, nk]
+        p = kept & causal_some
+        pres.append(p)
+        full.append(p & causal_all)
+    return _csr(np.concatenate(pres), np.concatenate(full))
 
 
 def tile_lists(mask: dict, H: int, L: int, bm: int, bn: int):
-    if mask["kind"] == "block" and bm == bn == int(mask["block"]) and L > 16384:
+    if mask["kind"] == "block" and int(mask["block"]) % bm == 0 and int(mask["block"]) % bn == 0 and L > 16384:
         return tile_lists_block(mask, H, L, bm, bn)
     return tile_lists_dense(mask, H, L, bm, bn)

@@ -409,10 +409,11 @@ def test_tile_lists_block_vs_dense():
     bs, nb, H = 16, 20, 3
     mask = dict(kind="block", block=bs, block_mask=block_matrix_top_half(0, 5, H, nb))
     for L in (nb * bs, nb * bs - 5):
-        a = tile_lists_block(mask, H, L, bs, bs)
-        b = tile_lists_dense(mask, H, L, bs, bs)
-        for x, y in zip(a, b):
-            assert np.array_equal(x, y)
+        for bm, bn in ((16, 16), (16, 8), (8, 16), (4, 2), (2, 8)):
+            a = tile_lists_block(mask, H, L, bm, bn)
+            b = tile_lists_dense(mask, H, L, bm, bn)
+            for x, y in zip(a, b):
+                assert np.array_equal(x, y)
 
 
 def test_block_matrix_generator_shape():

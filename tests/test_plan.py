@@ -1,0 +1,224 @@
+"""Host-side checks of the C-ABI library: it loads, exports what the header
+declares, and its mask-descriptor compiler (tile lists, pair counts, schedule,
+error handling) matches the oracle's independent derivation bit for bit.
+No GPU needed: nothing here launches a kernel."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_sparse_softmax_amd import _lib
+from block_sparse_softmax_amd.inputs import block_matrix_top_half, head_windows, workload
+from oracle.counts import pair_count
+from oracle.tiles import tile_lists, tile_lists_dense
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bss_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(attn_[a-z_]+)\s*\(", text, re.M))
+    assert declared == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.attn_version().decode().startswith("bss_attn")
+
+
+def _compare(mask, L, H, D=64):
+    plan = _lib.Plan(mask, L, H, D)
+    bm, bn, rp, kv, fl = plan.tiles()
+    ref = tile_lists(mask, H, L, bm, bn)
+    assert rp.dtype == ref[0].dtype and np.array_equal(rp, ref[0])
+    assert kv.dtype == ref[1].dtype and np.array_equal(kv, ref[1])
+    assert fl.dtype == ref[2].dtype and np.array_equal(fl, ref[2])
+    return plan, (bm, bn, rp, kv, fl)
+
+
+SMALL_MASKS = [
+    (dict(kind="full"), 300, 2),
+    (dict(kind="full", causal=True), 300, 2),
+    (dict(kind="chunk", chunk=64), 256, 2),
+    (dict(kind="chunk", chunk=100), 333, 1),
+    (dict(kind="chunk", chunk=1), 130, 1),
+    (dict(kind="chunk", chunk=50, causal=True), 250, 1),
+    (dict(kind="window", left=0, right=0), 200, 1),
+    (dict(kind="window", left=17, right=3), 500, 2),
+    (dict(kind="window", left=128, right=128), 1000, 1),
+    (dict(kind="window", left=5000, right=5000), 700, 1),
+    (dict(kind="window", left=0, right=0, causal=True, head_left=[0, 63, 64, 1000]), 777, 4),
+    (dict(kind="window", left=40, right=9, causal=True), 411, 1),
+]
+
+
+@pytest.mark.parametrize("mi", range(len(SMALL_MASKS)))
+def test_tile_lists_match_oracle_small(lib, mi):
+    mask, L, H = SMALL_MASKS[mi]
+    _compare(mask, L, H)
+
+
+@pytest.mark.parametrize("bs,nb,L", [(128, 8, 1024), (128, 8, 1000), (256, 6, 1536), (64, 20, 1280),
+                                     (100, 10, 1000), (48, 25, 1190), (384, 3, 1100)])
+def test_tile_lists_match_oracle_block(lib, bs, nb, L):
+    H = 2
+    bm = block_matrix_top_half(7, 5, H, nb)
+    bm[1, nb // 2, :] = 0          # an empty block row
+    mask = dict(kind="block", block=bs, block_mask=bm)
+    plan = _lib.Plan(mask, L, H, 128)
+    bmt, bnt, rp, kv, fl = plan.tiles()
+    ref = tile_lists_dense(mask, H, L, bmt, bnt)
+    for a, b in zip((rp, kv, fl), ref):
+        assert np.array_equal(a, b)
+
+
+def test_random_descriptors_match_oracle(lib):
+    rng = np.random.default_rng(11)
+    for _ in range(25):
+        L = int(rng.integers(1, 700))
+        H = int(rng.integers(1, 3))
+        kind = rng.choice(["full", "chunk", "window", "block"])
+        causal = bool(rng.integers(0, 2))
+        if kind == "full":
+            mask = dict(kind="full", causal=causal)
+        elif kind == "chunk":
+            mask = dict(kind="chunk", chunk=int(rng.integers(1, 300)), causal=causal)
+        elif kind == "window":
+            mask = dict(kind="window", left=int(rng.integers(0, 400)), right=int(rng.integers(0, 400)),
+                        causal=causal)
+            if rng.integers(0, 2):
+                mask["head_left"] = rng.integers(0, 800, H)
+        else:
+            bs = int(rng.integers(1, 200))
+            nb = -(-L // bs)
+            b = np.tril(rng.integers(0, 2, (H, nb, nb))).astype(np.uint8)
+            mask = dict(kind="block", block=bs, block_mask=b)
+        plan = _lib.Plan(mask, L, H, 80)
+        bm, bn, rp, kv, fl = plan.tiles()
+        ref = tile_lists_dense(mask, H, L, bm, bn)
+        for a, b in zip((rp, kv, fl), ref):
+            assert np.array_equal(a, b), mask
+        per, tot = plan.pairs()
+        assert np.array_equal(per, pair_count(mask, H, L)), mask
+        assert tot == per.sum()
+
+
+@pytest.mark.parametrize("name", ["tiny_chunk", "vit896", "vit1792", "lm_headwin"])
+def test_workload_tile_lists_and_pairs(lib, name):
+    w = workload(name)
+    for label, mask in w["masks"].items():
+        plan, _ = _compare(mask, w["L"], w["H"], w["D"])
+        per, tot = plan.pairs()
+        if w["L"] <= 4096:
+            assert np.array_equal(per, pair_count(mask, w["H"], w["L"]))
+        else:  # closed forms at 16K tokens
+            L = w["L"]
+            exp = L * L if mask["kind"] == "full" else L * (2 * mask["left"] + 1) - mask["left"] * (mask["left"] + 1)
+            assert np.all(per == exp)
+
+
+def test_blocksparse_128k_tile_lists(lib):
+    w = workload("blocksparse128k")
+    mask = w["masks"]["block50"]
+    plan = _lib.Plan(mask, w["L"], w["H"], w["D"])
+    bm, bn, rp, kv, fl = plan.tiles()
+    assert mask["block"] % bm == 0 and mask["block"] % bn == 0
+    ref = tile_lists(mask, w["H"], w["L"], bm, bn)   # index-arithmetic derivation at 128K
+    for a, b in zip((rp, kv, fl), ref):
+        assert np.array_equal(a, b)
+    per, tot = plan.pairs()
+    nb = w["L"] // mask["block"]
+    bsz = mask["block"]
+    kept = mask["block_mask"].reshape(w["H"], -1).sum(axis=1).astype(np.int64)
+    assert np.array_equal(per, nb * bsz * (bsz + 1) // 2 + (kept - nb) * bsz * bsz)
+    assert int(kept[0]) == 263679
+
+
+def test_schedule_covers_every_row_once(lib):
+    for name in ("vit896", "lm_headwin"):
+        w = workload(name)
+        for mask in w["masks"].values():
+            plan = _lib.Plan(mask, w["L"], w["H"], w["D"])
+            bm, bn, rp, kv, fl = plan.tiles()
+            items = plan.schedule()
+            nq = -(-w["L"] // bm)
+            assert items.shape == (w["H"] * nq, 4)
+            rows = items[:, 0] * nq + items[:, 1]
+            assert np.array_equal(np.sort(rows), np.arange(w["H"] * nq))
+            assert np.array_equal(items[:, 2], rp[rows]) and np.array_equal(items[:, 3], rp[rows + 1])
+            # heads with more work come first; inside a head, longer lists first
+            cost = (items[:, 3] - items[:, 2]).astype(float)
+            for h in np.unique(items[:, 0]):
+                c = cost[items[:, 0] == h]
+                assert np.all(np.diff(c) <= 0)
+
+
+def _status(lib, mask, L, H, D):
+    desc, keep = _lib.build_desc(mask, H)
+    h = ctypes.c_void_p()
+    st = lib.attn_plan_create(ctypes.byref(desc), L, H, D, ctypes.byref(h))
+    if st == 0:
+        lib.attn_plan_destroy(h)
+    return st, lib.attn_last_error().decode()
+
+
+def test_descriptor_errors(lib):
+    ok, _ = _status(lib, dict(kind="full"), 64, 1, 64)
+    assert ok == _lib.ATTN_OK
+    st, msg = _status(lib, dict(kind="full"), 64, 1, 96)
+    assert st == _lib.ATTN_E_UNSUPPORTED and "96" in msg
+    assert _status(lib, dict(kind="chunk", chunk=0), 64, 1, 64)[0] == _lib.ATTN_E_INVAL
+    assert _status(lib, dict(kind="window", left=-1, right=0), 64, 1, 64)[0] == _lib.ATTN_E_INVAL
+    assert _status(lib, dict(kind="window", left=0, right=0, head_left=[3, -2]), 64, 2, 64)[0] == _lib.ATTN_E_INVAL
+    upper = np.tril(np.ones((1, 4, 4), np.uint8))
+    upper[0, 1, 3] = 1
+    st, msg = _status(lib, dict(kind="block", block=16, block_mask=upper), 64, 1, 64)
+    assert st == _lib.ATTN_E_INVAL and "diagonal" in msg
+    st, _ = _status(lib, dict(kind="block", block=16, block_mask=np.ones((3, 4, 4), np.uint8)), 64, 2, 64)
+    assert st == _lib.ATTN_E_INVAL
+    assert _status(lib, dict(kind="full"), 0, 1, 64)[0] == _lib.ATTN_E_INVAL
+    d = _lib.MaskDesc()
+    d.kind = 9
+    h = ctypes.c_void_p()
+    assert lib.attn_plan_create(ctypes.byref(d), 64, 1, 64, ctypes.byref(h)) == _lib.ATTN_E_INVAL
+    assert lib.attn_plan_create(None, 64, 1, 64, ctypes.byref(h)) == _lib.ATTN_E_INVAL
+
+
+def test_launch_argument_errors_without_gpu(lib):
+    """Validation runs before any HIP call: bad shapes and a short workspace are rejected."""
+    plan = _lib.Plan(dict(kind="full"), 256, 2, 64)
+    fake = 1 << 20  # never dereferenced: validation fails first
+
+    def t(L=256, H=2, D=64, stride_l=128, data=fake):
+        a = _lib.AttnTensor()
+        a.data, a.B, a.L, a.H, a.D = data, 1, L, H, D
+        a.stride_b, a.stride_l, a.stride_h = L * stride_l, stride_l, 64
+        return a
+
+    ln = _lib.Launch()
+    ln.workspace = fake
+    ln.workspace_bytes = 16
+    q, k, v, o = t(), t(), t(), t(data=fake * 2)
+    st = lib.attn_masked_fwd_plan(plan.handle, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), None,
+                                  ctypes.byref(o), ctypes.byref(ln))
+    assert st == _lib.ATTN_E_WORKSPACE
+    k_bad = t(L=128)
+    ln.workspace_bytes = plan.workspace_bytes()
+    st = lib.attn_masked_fwd_plan(plan.handle, ctypes.byref(q), ctypes.byref(k_bad), ctypes.byref(v), None,
+                                  ctypes.byref(o), ctypes.byref(ln))
+    assert st == _lib.ATTN_E_INVAL
+    q_mis = t(stride_l=130)
+    st = lib.attn_masked_fwd_plan(plan.handle, ctypes.byref(q_mis), ctypes.byref(k), ctypes.byref(v), None,
+                                  ctypes.byref(o), ctypes.byref(ln))
+    assert st == _lib.ATTN_E_INVAL and "16-byte" in lib.attn_last_error().decode()
+    o_alias = t()
+    st = lib.attn_masked_fwd_plan(plan.handle, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), None,
+                                  ctypes.byref(o_alias), ctypes.byref(ln))
+    assert st == _lib.ATTN_E_INVAL
