@@ -45,6 +45,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
@@ -55,8 +56,14 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;
+constexpr int kListCap = 1024;  // KV-list entries staged in LDS at a time
 
 constexpr int kMaskFull = 0, kMaskChunk = 1, kMaskWindow = 2, kMaskBlock = 3;
+
+template <bool B>
+struct Bool {
+  static constexpr bool value = B;
+};
 
 template <int D>
 struct Shape {
@@ -66,6 +73,8 @@ struct Shape {
   static constexpr int DT = (D + 31) / 32;                   // 32-row tiles of O^T
   static constexpr int TILE = kBN * RB;                      // bytes of one K (or V) tile
   static constexpr int LOADS = 2 * kBN * CPR / 64 / kWaves;  // LDS-DMA loads per lane per tile
+  // waves 0-1 fill the K tile, waves 2-3 the V tile, LOADS wave-instructions each
+  static_assert(2 * LOADS == CPR, "each wave must cover half of one tensor's tile");
   static constexpr bool PAD_ROWSUM = (D % 32) != 0;
   static_assert((2 * kBN * CPR) % (64 * kWaves) == 0, "tile must split evenly over the waves");
 };
@@ -81,6 +90,30 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 16, "vmcnt immediate");
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
+// One 16-byte global -> LDS copy per lane: lane l writes LDS bytes
+// [lds_base + 16 l, lds_base + 16 l + 16).  Issued as inline assembly so the
+// compiler does not treat every later LDS read as aliasing it (it would then
+// wait for the whole prefetch before any LDS read); completion is tracked by
+// the explicit vmcnt waits in the main loop.
+__device__ __forceinline__ void dma16(const void* base_ptr, uint32_t voffset, uint32_t lds_base) {
+  // readfirstlane yields int: widen through uint32_t so the low half is not sign-extended
+  const uint64_t a = reinterpret_cast<uint64_t>(base_ptr);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32)));
+  const uint64_t base = (static_cast<uint64_t>(hi) << 32) | lo;
+  __asm__ volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voffset), "s"(base), "s"(lds_base)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)(p)));
 }
 
 __device__ __forceinline__ void wg_barrier() {
@@ -111,15 +144,29 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p) {
   using S = Shape<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * S::TILE];  // [buffer][K, V]
+  // LDS: K tiles in buffers 0-1, V tiles in buffers 2-3; for d = 80 two more
+  // tile-sized regions (4-5) hold the constant V^T pad rows read by the pad
+  // lanes of the last O^T tile (column 0 = 1, columns 1..15 = 0 on every row),
+  // placed two tiles after each V buffer so one lane offset serves both.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[(S::PAD_ROWSUM ? 6 : 4) * S::TILE];
+  __shared__ int list_lds[kListCap];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h2 = lane >> 5;    // half of the wave
   const int l31 = lane & 31;
 
-  const int4 item = reinterpret_cast<const int4*>(p.items)[blockIdx.x];
-  const int head = item.x, qtile = item.y, e_begin = item.z, e_end = item.w;
+  // Work-groups are dealt to the 8 XCDs round-robin (block i runs on XCD i mod 8);
+  // XCD x takes the x-th contiguous chunk of the schedule, so the items that
+  // share an XCD's L2 at any time come from the same head.
+  const int xcd_chunk = (p.n_items + 7) / 8;
+  const int item_idx = (blockIdx.x % 8) * xcd_chunk + blockIdx.x / 8;
+  if (item_idx >= p.n_items) return;
+  const int4 item = reinterpret_cast<const int4*>(p.items)[item_idx];
+  const int head = __builtin_amdgcn_readfirstlane(item.x);
+  const int qtile = __builtin_amdgcn_readfirstlane(item.y);
+  const int e_begin = __builtin_amdgcn_readfirstlane(item.z);
+  const int e_end = __builtin_amdgcn_readfirstlane(item.w);
   const int b = blockIdx.y;
 
   const unsigned char* qbase =
@@ -132,14 +179,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   const int64_t q_row_bytes = p.q_sl * 2, k_row_bytes = p.k_sl * 2, v_row_bytes = p.v_sl * 2,
                 o_row_bytes = p.o_sl * 2;
 
-  // ---- this lane's query and its Q fragments (B operand of S^T = K Q^T) ----
+  // ---- the KV list of this item, staged in LDS kListCap entries at a time ----
+  const int n = e_end - e_begin;
+  auto stage_list = [&](int first) {
+    const int cnt = min(kListCap, n - first);
+    for (int i = threadIdx.x; i < cnt; i += kThreads) list_lds[i] = p.kv[e_begin + first + i];
+  };
+  if (n > 0) stage_list(0);
+
+  // ---- this lane's query; Q fragments (B operand of S^T = K Q^T), pre-scaled ----
+  // by softmax_scale * log2(e) so that the MFMA yields log2-domain logits.
   const int qi = qtile * kBM + wave * 32 + l31;
   const int qrow = qi < p.L ? qi : p.L - 1;
   bf16x8 qf[S::KS];
   {
     const unsigned char* src = qbase + qrow * q_row_bytes + 16 * h2;
 #pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(src + 32 * ks);
+    for (int ks = 0; ks < S::KS; ++ks) {
+      const bf16x8 raw = *reinterpret_cast<const bf16x8*>(src + 32 * ks);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ks][e] = (__bf16)((float)raw[e] * p.scale_log2);
+    }
   }
 
   // ---- allowed key interval [lo, hi) of this query (used on PARTIAL tiles) ----
@@ -156,6 +216,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   const unsigned width = static_cast<unsigned>(hi - lo);
 
   // ---- running softmax state (log2 domain) ----
+  // m_run: reference max; l_run: row sum of this lane's keys (d != 80);
+  // sink_l: the sink's term exp2(s_aux log2e - m_run).
   float m_run = -INFINITY, l_run = 0.f, sink_l = 0.f;
   if (p.sink != nullptr) {
     const float s = p.sink[head] * kLog2e;
@@ -170,131 +232,185 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
 
   // ---- LDS addressing ----
   // K fragment for k-step ks: row l31 (and l31 + 32), logical chunk 2*ks + h2.
-  int koff[S::KS];
+  // For d = 128 k-steps 4..7 sit 128 bytes after k-steps 0..3 (the swizzle keeps bit 3 of the chunk).
+  constexpr int kKoffRegs = (D == 128) ? 4 : S::KS;
+  int koff[kKoffRegs];
 #pragma unroll
-  for (int ks = 0; ks < S::KS; ++ks) koff[ks] = l31 * S::RB + phys_chunk<D>(l31, 2 * ks + h2) * 16;
+  for (int ks = 0; ks < kKoffRegs; ++ks) koff[ks] = l31 * S::RB + phys_chunk<D>(l31, 2 * ks + h2) * 16;
+  auto koff_of = [&](int ks) { return koff[ks % kKoffRegs] + (ks / kKoffRegs) * 128; };
   // V^T fragment for O^T tile dt: transposed read; source lane (j, c) of each
   // 16-lane group points at row 4*h2 + j, columns 32*dt + 16*dhalf + 4*c .. +3.
   const int tr_j = (lane & 15) >> 2, tr_c = lane & 3, dhalf = (lane >> 4) & 1;
-  int voff[S::DT];
+  constexpr int kVoffRegs = (D == 128) ? 2 : S::DT;
+  int voff[kVoffRegs];
 #pragma unroll
-  for (int dt = 0; dt < S::DT; ++dt) {
+  for (int dt = 0; dt < kVoffRegs; ++dt) {
     const int row = 4 * h2 + tr_j;
     int c = 4 * dt + 2 * dhalf + (tr_c >> 1);
     if (S::PAD_ROWSUM && 8 * c >= D) c = 2 * dhalf + (tr_c >> 1);  // pad lanes: any valid address
     voff[dt] = row * S::RB + phys_chunk<D>(row, c) * 16 + (tr_c & 1) * 8;
   }
-  // Pad lanes of the last O^T tile use a constant V^T: row D is all ones, the rest zero.
-  bf16x8 pad_ones;
-  {
-    const __bf16 one = (dhalf == 1 && (lane & 15) == 0) ? (__bf16)1.0f : (__bf16)0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pad_ones[e] = one;
+  if constexpr (S::PAD_ROWSUM) {
+    // Pad lanes of the last O^T tile read the constant regions: V^T row D is all
+    // ones (its O^T row is the row sum), rows D+1 .. D+15 are zero.
+    if (dhalf == 1) voff[S::DT - 1] = 2 * S::TILE + (4 * h2 + tr_j) * S::RB + tr_c * 8;
+    for (int i = threadIdx.x; i < 2 * kBN * 4; i += kThreads) {  // 2 regions x 64 rows x 4 x 8 bytes
+      const int region = i / (kBN * 4), row = (i / 4) % kBN, q4 = i % 4;
+      uint2 v = make_uint2(0u, 0u);
+      if (q4 == 0) v.x = 0x3F80u;  // bf16 1.0 in element 0
+      *reinterpret_cast<uint2*>(smem + (4 + region) * S::TILE + row * S::RB + q4 * 8) = v;
+    }
   }
-  const bool pad_lane = S::PAD_ROWSUM && dhalf == 1;
 
-  // LDS-DMA: wave-instruction idx = wave + 4*i fills 64 consecutive 16-byte slots.
-  int goff[S::LOADS];
+  // LDS-DMA: waves 0-1 fill K tiles and waves 2-3 V tiles; wave-instruction i
+  // of a wave fills 64 consecutive 16-byte LDS slots of its half of the tile.
+  const int dma_tensor = wave >> 1;
+  const uint32_t dma_row_bytes = static_cast<uint32_t>(dma_tensor ? v_row_bytes : k_row_bytes);
+  const unsigned char* dma_base = dma_tensor ? vbase : kbase;
+  // Lane part of each load's source offset.  Rows whose XOR swizzle repeats
+  // share a lane offset; the rest of the offset is uniform.
+  constexpr int kGoffRegs = (D == 128) ? 2 : (D == 64) ? 1 : S::LOADS;
+  uint32_t goff[kGoffRegs];
 #pragma unroll
-  for (int i = 0; i < S::LOADS; ++i) {
-    const int idx = wave + kWaves * i;
-    const int tensor = idx >= S::CPR;
-    const int blk = tensor ? idx - S::CPR : idx;
-    const int slot = blk * 64 + lane;
+  for (int i = 0; i < kGoffRegs; ++i) {
+    const int slot = ((wave & 1) * S::LOADS + i) * 64 + lane;
     const int row = slot / S::CPR;
-    const int c = phys_chunk<D>(row, slot % S::CPR);
-    goff[i] = row * static_cast<int>(tensor ? v_row_bytes : k_row_bytes) + c * 16;
+    goff[i] = row * dma_row_bytes + phys_chunk<D>(row, slot % S::CPR) * 16;
   }
-
+  const uint32_t smem_lds = lds_addr(smem);
+  // Issue this wave's share of tile kt into LDS buffer buf (0-1 K, 2-3 V).
   auto issue_tile = [&](int kt, int buf) {
     const int kv0 = kt * kBN;
-    const unsigned char* kp = kbase + kv0 * k_row_bytes;
-    const unsigned char* vp = vbase + kv0 * v_row_bytes;
-    unsigned char* dst = smem + buf * 2 * S::TILE;
-    const bool ragged = kv0 + kBN > p.L;
+    const unsigned char* src = dma_base + static_cast<uint32_t>(kv0) * dma_row_bytes;
+    const uint32_t dst =
+        __builtin_amdgcn_readfirstlane(smem_lds + buf * S::TILE + (wave & 1) * S::LOADS * 1024);
+    if (kv0 + kBN <= p.L) {
 #pragma unroll
-    for (int i = 0; i < S::LOADS; ++i) {
-      const int idx = wave + kWaves * i;
-      const int tensor = idx >= S::CPR;
-      const int blk = tensor ? idx - S::CPR : idx;
-      int off = goff[i];
-      if (ragged) {  // clamp rows past the end of the sequence (their keys are masked)
-        const int slot = blk * 64 + lane;
-        const int row = min(slot / S::CPR, p.L - 1 - kv0);
-        const int c = phys_chunk<D>(slot / S::CPR, slot % S::CPR);
-        off = row * static_cast<int>(tensor ? v_row_bytes : k_row_bytes) + c * 16;
+      for (int i = 0; i < S::LOADS; ++i) {
+        // rows advance by 64 / CPR per load; the swizzle period is kGoffRegs loads
+        const uint32_t rows_ahead = static_cast<uint32_t>((i / kGoffRegs) * kGoffRegs * 64 / S::CPR);
+        dma16(src + rows_ahead * dma_row_bytes, goff[i % kGoffRegs], dst + i * 1024);
       }
-      const unsigned char* src = (tensor ? vp : kp) + off;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + tensor * S::TILE + blk * 1024), 16, 0, 0);
+    } else {  // ragged last tile: clamp rows past the end of the sequence (their keys are masked)
+      const int last = p.L - 1 - kv0;
+#pragma unroll
+      for (int i = 0; i < S::LOADS; ++i) {
+        const int slot = ((wave & 1) * S::LOADS + i) * 64 + lane;
+        const int row = slot / S::CPR;
+        const uint32_t off = min(row, last) * dma_row_bytes +
+                             phys_chunk<D>(row, slot % S::CPR) * 16;
+        dma16(src, off, dst + i * 1024);
+      }
     }
   };
 
-  const int n = e_end - e_begin;
-  if (n > 0) issue_tile(p.kv[e_begin] >> 1, 0);
-
-  for (int e = 0; e < n; ++e) {
-    const int ent = p.kv[e_begin + e];
-    const int kt = ent >> 1;
-    const bool full = ent & 1;
-    const int buf = e & 1;
-    if (e + 1 < n) {
-      issue_tile(p.kv[e_begin + e + 1] >> 1, buf ^ 1);
-      wait_vmcnt<S::LOADS>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    wg_barrier();
-
-    const unsigned char* kt_lds = smem + buf * 2 * S::TILE;
-    const unsigned char* vt_lds = kt_lds + S::TILE;
-
-    // ---- S^T = K Q^T for two 32-key blocks ----
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+  // S^T = K Q^T + seed (log2-domain logits minus the reference max) for a
+  // 64-key tile; the seed block is the C operand of the first k-step.
+  auto qk = [&](int kbuf, const f32x16& seed, f32x16& s0, f32x16& s1) {
+    const unsigned char* kt_lds = smem + kbuf * S::TILE;
 #pragma unroll
     for (int ks = 0; ks < S::KS; ++ks) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kt_lds + koff[ks]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kt_lds + koff[ks] + 32 * S::RB);
-      s0 = mfma32(a0, qf[ks], s0);
-      s1 = mfma32(a1, qf[ks], s1);
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kt_lds + koff_of(ks));
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kt_lds + koff_of(ks) + 32 * S::RB);
+      s0 = mfma32(a0, qf[ks], ks == 0 ? seed : s0);
+      s1 = mfma32(a1, qf[ks], ks == 0 ? seed : s1);
+    }
+  };
+  // O^T += V^T P^T for a 64-key tile.
+  auto pv = [&](int vbuf, const bf16x8 (&pb)[4]) {
+    const unsigned char* vt_lds = smem + vbuf * S::TILE;
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const unsigned char* src = vt_lds + voff[dt % kVoffRegs] + (dt / kVoffRegs) * 128 + 16 * t * S::RB;
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 8 * S::RB));
+        const s16x8 x = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[dt] = mfma32(__builtin_bit_cast(bf16x8, x), pb[t], acc[dt]);
+      }
+    }
+  };
+  // Seed of a tile's S^T accumulators: minus the current reference max (0 while
+  // none), kept as a 16-register block rewritten only when the max moves.
+  f32x16 seedv;
+  auto set_seed = [&]() {
+    const float sd = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) seedv[r] = sd;
+  };
+  set_seed();
+
+  // ---- main loop: one listed tile per iteration ----
+  // K and V of tile j sit in buffers (j&1) and 2 + (j&1); the DMA for tile
+  // j+1 is issued at the top of iteration j, right after the barrier that
+  // guarantees every wave is done with the buffers of tile j-1.
+  int list_base = 0;
+  int ent_c = 0;
+  if (n > 0) {
+    __syncthreads();  // list staged, pad regions written
+    ent_c = __builtin_amdgcn_readfirstlane(list_lds[0]);
+    issue_tile(ent_c >> 1, 2 * dma_tensor);
+  }
+  for (int j = 0; j < n; ++j) {
+    const int ent = __builtin_amdgcn_readfirstlane(ent_c);
+    wait_vmcnt<0>();   // this wave's share of tile j (and, at j = 0, the Q fragments)
+    wg_barrier();      // everyone's share of tile j; buffers of tile j-1 are free
+    if (j + 1 < n) {
+      if (j + 1 - list_base == kListCap) {  // next chunk of the list
+        list_base += kListCap;
+        stage_list(list_base);
+        __syncthreads();
+      }
+      ent_c = __builtin_amdgcn_readfirstlane(list_lds[j + 1 - list_base]);
+      issue_tile(ent_c >> 1, 2 * dma_tensor + ((j + 1) & 1));
     }
 
-    // ---- mask (PARTIAL tiles only) ----
-    if (!full) {
-      const unsigned base = static_cast<unsigned>(kt * kBN + 4 * h2 - lo);
+    // ---- S^T of tile j, relative to the reference max (seeded C operand) ----
+    f32x16 s0, s1;
+    qk(j & 1, seedv, s0, s1);
+
+    // ---- mask (PARTIAL tiles only), row max, lazy rescale ----
+    if (!(ent & 1)) {
+      const unsigned base = static_cast<unsigned>((ent >> 1) * kBN + 4 * h2 - lo);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const unsigned u = base + 8 * (r >> 2) + (r & 3);
-        if (u >= width) s0[r] = -INFINITY;
-        if (u + 32 >= width) s1[r] = -INFINITY;
+        s0[r] = (u >= width) ? -INFINITY : s0[r];
+        s1[r] = (u + 32 >= width) ? -INFINITY : s1[r];
       }
     }
-
-    // ---- online softmax ----
-    float mx = -INFINITY;
+    float mt = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = halves_max(mx) * p.scale_log2;
-    const bool need = mx > m_run + kRescaleThreshold;
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
+    mt = halves_max(mt);
+    const bool need = (m_run == -INFINITY) ? (mt > -INFINITY) : (mt > kRescaleThreshold);
     if (__builtin_amdgcn_ballot_w64(need)) {
-      const float m_new = need ? mx : m_run;
-      const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
+      float alpha = 1.f, shift = 0.f;
+      if (need) {
+        const float m_new = (m_run == -INFINITY ? 0.f : m_run) + mt;
+        alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        shift = mt;
+      }
+      s0 -= shift;
+      s1 -= shift;
       l_run *= alpha;
       sink_l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt) acc[dt] *= alpha;
+      set_seed();
     }
-    const float mneg = (m_run == -INFINITY) ? 0.f : -m_run;
+
+    // ---- P = exp2(S), O^T += V^T P^T ----
     float rs = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], p.scale_log2, mneg));
-      s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], p.scale_log2, mneg));
+      s0[r] = __builtin_amdgcn_exp2f(s0[r]);
+      s1[r] = __builtin_amdgcn_exp2f(s1[r]);
       if (!S::PAD_ROWSUM) rs += s0[r] + s1[r];
     }
     if (!S::PAD_ROWSUM) l_run += rs;
-
-    // P^T operands for the four 16-key k-steps of this tile
     bf16x8 pb[4];
 #pragma unroll
     for (int e8 = 0; e8 < 8; ++e8) {
@@ -303,24 +419,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
       pb[2][e8] = (__bf16)s1[e8];
       pb[3][e8] = (__bf16)s1[8 + e8];
     }
-
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int dt = 0; dt < S::DT; ++dt) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const unsigned char* src = vt_lds + voff[dt] + 16 * t * S::RB;
-        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
-        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 8 * S::RB));
-        bf16x8 a;
-        const bf16x4 y0 = __builtin_bit_cast(bf16x4, x0), y1 = __builtin_bit_cast(bf16x4, x1);
-        a[0] = y0[0]; a[1] = y0[1]; a[2] = y0[2]; a[3] = y0[3];
-        a[4] = y1[0]; a[5] = y1[1]; a[6] = y1[2]; a[7] = y1[3];
-        if (S::PAD_ROWSUM && dt == S::DT - 1 && pad_lane) a = pad_ones;
-        acc[dt] = mfma32(a, pb[t], acc[dt]);
-      }
-    }
-    wg_barrier();
+    pv(2 + (j & 1), pb);
   }
 
   // ---- epilogue: O = acc / (row sum + sink term) ----
@@ -353,7 +452,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
 
 template <int D>
 hipError_t launch_d(const FwdParams& p, int B, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(p.n_items), static_cast<unsigned>(B));
+  dim3 grid(static_cast<unsigned>(8 * ((p.n_items + 7) / 8)), static_cast<unsigned>(B));
   hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
