@@ -67,23 +67,37 @@ struct Bool {
 
 template <int D>
 struct Shape {
-  static constexpr int CPR = D / 8;                          // 16-byte chunks per token row
-  static constexpr int RB = D * 2;                           // bytes per token row
+  static constexpr int CPR = D / 8;                          // 16-byte chunks per token row in memory
+  static constexpr int RB = D * 2;                           // bytes per token row in memory
+  // 16-byte chunks per row in LDS: d = 80 rows get two extra chunks whose V
+  // slots hold the constant pad of the last O^T tile (element 80 = 1, so that
+  // O^T row 80 is the row sum of P); the DMA never writes them.
+  static constexpr int LCPR = (D == 80) ? 12 : CPR;
+  static constexpr int LRB = LCPR * 16;                      // bytes per row in LDS
   static constexpr int KS = D / 16;                          // k-steps of the Q.K product
   static constexpr int DT = (D + 31) / 32;                   // 32-row tiles of O^T
-  static constexpr int TILE = kBN * RB;                      // bytes of one K (or V) tile
-  static constexpr int LOADS = 2 * kBN * CPR / 64 / kWaves;  // LDS-DMA loads per lane per tile
+  static constexpr int TILE = kBN * LRB;                     // bytes of one K (or V) tile in LDS
+  static constexpr int LOADS = 2 * kBN * LCPR / 64 / kWaves; // LDS-DMA wave-instructions per wave per tile
   // waves 0-1 fill the K tile, waves 2-3 the V tile, LOADS wave-instructions each
-  static_assert(2 * LOADS == CPR, "each wave must cover half of one tensor's tile");
+  static_assert(2 * LOADS == LCPR, "each wave must cover half of one tensor's tile");
+  // the XOR swizzle repeats every 16 rows; that many rows span DMA_PERIOD loads
+  static constexpr int DMA_PERIOD = 16 * LCPR / 64;
+  static_assert(LOADS % DMA_PERIOD == 0, "loads per wave must be whole swizzle periods");
   static constexpr bool PAD_ROWSUM = (D % 32) != 0;
-  static_assert((2 * kBN * CPR) % (64 * kWaves) == 0, "tile must split evenly over the waves");
 };
 
-// Physical 16-byte chunk of logical chunk c in LDS row `row` (an involution).
+// Physical 16-byte chunk of logical chunk c in LDS row `row` (an XOR, so its
+// own inverse).  Chosen so that the 16 rows read by one K-fragment load, and
+// the 4 rows x 64 bytes read by 32 lanes of one transposed V load, fall in
+// distinct banks of a 64-bank LDS:
+//   d = 128 (16 chunks):  c ^ {row bits 0-1 -> bits 2-3, row bits 2-3 -> bits 0-1}
+//   d = 64  (8 chunks):   c ^ {row bit 1 -> bit 2, row bits 2-3 -> bits 0-1}
+//   d = 80  (12 chunks):  c ^ row bits 2-3  (stays inside each aligned group of 4)
 template <int D>
 __device__ __forceinline__ int phys_chunk(int row, int c) {
-  if (D == 80 && c >= 8) return c ^ (row & 1);
-  return c ^ (row & 7);
+  if constexpr (D == 128) return c ^ (((row & 3) << 2) | ((row >> 2) & 3));
+  else if constexpr (D == 64) return c ^ ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  else return c ^ ((row >> 2) & 3);
 }
 
 template <int N>
@@ -144,11 +158,8 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p) {
   using S = Shape<D>;
-  // LDS: K tiles in buffers 0-1, V tiles in buffers 2-3; for d = 80 two more
-  // tile-sized regions (4-5) hold the constant V^T pad rows read by the pad
-  // lanes of the last O^T tile (column 0 = 1, columns 1..15 = 0 on every row),
-  // placed two tiles after each V buffer so one lane offset serves both.
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[(S::PAD_ROWSUM ? 6 : 4) * S::TILE];
+  // LDS: K tiles in buffers 0-1, V tiles in buffers 2-3 (row pitch LRB).
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * S::TILE];
   __shared__ int list_lds[kListCap];
 
   const int lane = threadIdx.x & 63;
@@ -231,34 +242,33 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   for (int dt = 0; dt < S::DT; ++dt) acc[dt] = f32x16{};
 
   // ---- LDS addressing ----
-  // K fragment for k-step ks: row l31 (and l31 + 32), logical chunk 2*ks + h2.
-  // For d = 128 k-steps 4..7 sit 128 bytes after k-steps 0..3 (the swizzle keeps bit 3 of the chunk).
-  constexpr int kKoffRegs = (D == 128) ? 4 : S::KS;
-  int koff[kKoffRegs];
+  // K fragment for k-step ks: row l31 (and l31 + 32: same swizzle), logical chunk 2*ks + h2.
+  int koff[S::KS];
 #pragma unroll
-  for (int ks = 0; ks < kKoffRegs; ++ks) koff[ks] = l31 * S::RB + phys_chunk<D>(l31, 2 * ks + h2) * 16;
-  auto koff_of = [&](int ks) { return koff[ks % kKoffRegs] + (ks / kKoffRegs) * 128; };
-  // V^T fragment for O^T tile dt: transposed read; source lane (j, c) of each
-  // 16-lane group points at row 4*h2 + j, columns 32*dt + 16*dhalf + 4*c .. +3.
+  for (int ks = 0; ks < S::KS; ++ks) koff[ks] = l31 * S::LRB + phys_chunk<D>(l31, 2 * ks + h2) * 16;
+  // V^T fragment for O^T tile dt and half u of a 16-key k-step: transposed
+  // read; source lane (j, c) of each 16-lane group points at row
+  // 8*u + 4*h2 + j (+16 per k-step), columns 32*dt + 16*dhalf + 4*c .. +3.
   const int tr_j = (lane & 15) >> 2, tr_c = lane & 3, dhalf = (lane >> 4) & 1;
-  constexpr int kVoffRegs = (D == 128) ? 2 : S::DT;
-  int voff[kVoffRegs];
+  int voff[S::DT][2];
 #pragma unroll
-  for (int dt = 0; dt < kVoffRegs; ++dt) {
-    const int row = 4 * h2 + tr_j;
-    int c = 4 * dt + 2 * dhalf + (tr_c >> 1);
-    if (S::PAD_ROWSUM && 8 * c >= D) c = 2 * dhalf + (tr_c >> 1);  // pad lanes: any valid address
-    voff[dt] = row * S::RB + phys_chunk<D>(row, c) * 16 + (tr_c & 1) * 8;
+  for (int dt = 0; dt < S::DT; ++dt) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int row = 8 * u + 4 * h2 + tr_j;
+      const int c = 4 * dt + 2 * dhalf + (tr_c >> 1);
+      voff[dt][u] = row * S::LRB + phys_chunk<D>(row, c) * 16 + (tr_c & 1) * 8;
+    }
   }
   if constexpr (S::PAD_ROWSUM) {
-    // Pad lanes of the last O^T tile read the constant regions: V^T row D is all
-    // ones (its O^T row is the row sum), rows D+1 .. D+15 are zero.
-    if (dhalf == 1) voff[S::DT - 1] = 2 * S::TILE + (4 * h2 + tr_j) * S::RB + tr_c * 8;
-    for (int i = threadIdx.x; i < 2 * kBN * 4; i += kThreads) {  // 2 regions x 64 rows x 4 x 8 bytes
-      const int region = i / (kBN * 4), row = (i / 4) % kBN, q4 = i % 4;
+    // Constant pad chunks 10-11 of every V row in both V buffers: element 80 = 1, the rest 0.
+    for (int i = threadIdx.x; i < 2 * kBN * 4; i += kThreads) {  // 2 buffers x 64 rows x 4 x 8 bytes
+      const int buf = i / (kBN * 4), row = (i / 4) % kBN, q4 = i % 4;
+      const int c = 10 + (q4 >> 1);
       uint2 v = make_uint2(0u, 0u);
-      if (q4 == 0) v.x = 0x3F80u;  // bf16 1.0 in element 0
-      *reinterpret_cast<uint2*>(smem + (4 + region) * S::TILE + row * S::RB + q4 * 8) = v;
+      if (q4 == 0) v.x = 0x3F80u;  // bf16 1.0 in element 80
+      *reinterpret_cast<uint2*>(smem + (2 + buf) * S::TILE + row * S::LRB +
+                                phys_chunk<D>(row, c) * 16 + (q4 & 1) * 8) = v;
     }
   }
 
@@ -267,15 +277,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   const int dma_tensor = wave >> 1;
   const uint32_t dma_row_bytes = static_cast<uint32_t>(dma_tensor ? v_row_bytes : k_row_bytes);
   const unsigned char* dma_base = dma_tensor ? vbase : kbase;
-  // Lane part of each load's source offset.  Rows whose XOR swizzle repeats
-  // share a lane offset; the rest of the offset is uniform.
-  constexpr int kGoffRegs = (D == 128) ? 2 : (D == 64) ? 1 : S::LOADS;
-  uint32_t goff[kGoffRegs];
+  // Lane part of each load's source offset for one swizzle period (16 rows);
+  // later periods add 16 rows to the uniform base.  Lanes whose slot is a
+  // pad chunk (d = 80) load nothing.
+  uint32_t goff[S::DMA_PERIOD];
+  bool gpad[S::DMA_PERIOD];
 #pragma unroll
-  for (int i = 0; i < kGoffRegs; ++i) {
+  for (int i = 0; i < S::DMA_PERIOD; ++i) {
     const int slot = ((wave & 1) * S::LOADS + i) * 64 + lane;
-    const int row = slot / S::CPR;
-    goff[i] = row * dma_row_bytes + phys_chunk<D>(row, slot % S::CPR) * 16;
+    const int row = slot / S::LCPR;
+    const int c = phys_chunk<D>(row, slot % S::LCPR);
+    gpad[i] = c >= S::CPR;
+    goff[i] = row * dma_row_bytes + (gpad[i] ? 0 : c) * 16;
   }
   const uint32_t smem_lds = lds_addr(smem);
   // Issue this wave's share of tile kt into LDS buffer buf (0-1 K, 2-3 V).
@@ -287,19 +300,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     if (kv0 + kBN <= p.L) {
 #pragma unroll
       for (int i = 0; i < S::LOADS; ++i) {
-        // rows advance by 64 / CPR per load; the swizzle period is kGoffRegs loads
-        const uint32_t rows_ahead = static_cast<uint32_t>((i / kGoffRegs) * kGoffRegs * 64 / S::CPR);
-        dma16(src + rows_ahead * dma_row_bytes, goff[i % kGoffRegs], dst + i * 1024);
+        const uint32_t rows_ahead = static_cast<uint32_t>((i / S::DMA_PERIOD) * 16);
+        if (!S::PAD_ROWSUM || !gpad[i % S::DMA_PERIOD])
+          dma16(src + rows_ahead * dma_row_bytes, goff[i % S::DMA_PERIOD], dst + i * 1024);
       }
     } else {  // ragged last tile: clamp rows past the end of the sequence (their keys are masked)
       const int last = p.L - 1 - kv0;
 #pragma unroll
       for (int i = 0; i < S::LOADS; ++i) {
         const int slot = ((wave & 1) * S::LOADS + i) * 64 + lane;
-        const int row = slot / S::CPR;
-        const uint32_t off = min(row, last) * dma_row_bytes +
-                             phys_chunk<D>(row, slot % S::CPR) * 16;
-        dma16(src, off, dst + i * 1024);
+        const int row = slot / S::LCPR;
+        const int c = phys_chunk<D>(row, slot % S::LCPR);
+        const uint32_t off = min(row, last) * dma_row_bytes + c * 16;
+        if (!S::PAD_ROWSUM || c < S::CPR) dma16(src, off, dst + i * 1024);
       }
     }
   };
@@ -310,8 +323,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     const unsigned char* kt_lds = smem + kbuf * S::TILE;
 #pragma unroll
     for (int ks = 0; ks < S::KS; ++ks) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kt_lds + koff_of(ks));
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kt_lds + koff_of(ks) + 32 * S::RB);
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kt_lds + koff[ks]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kt_lds + koff[ks] + 32 * S::LRB);
       s0 = mfma32(a0, qf[ks], ks == 0 ? seed : s0);
       s1 = mfma32(a1, qf[ks], ks == 0 ? seed : s1);
     }
@@ -323,9 +336,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     for (int dt = 0; dt < S::DT; ++dt) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const unsigned char* src = vt_lds + voff[dt % kVoffRegs] + (dt / kVoffRegs) * 128 + 16 * t * S::RB;
-        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
-        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 8 * S::RB));
+        const unsigned char* src = vt_lds + 16 * t * S::LRB;
+        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + voff[dt][0]));
+        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + voff[dt][1]));
         const s16x8 x = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
         acc[dt] = mfma32(__builtin_bit_cast(bf16x8, x), pb[t], acc[dt]);
       }
