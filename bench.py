@@ -87,8 +87,7 @@ def _time(setup, steps, warmup, layout):
     q, k, v = setup["dev"]
     o, sink = setup["o"], setup["sink"]
     stream = torch.cuda.current_stream()
-    launches = [lambda pm=m["pm"]: pm.launch(q, k, v, o, sink=sink, layout=layout, stream=stream)
-                for m in setup["masks"]]
+    launches = [m["pm"].bind(q, k, v, o, sink=sink, layout=layout, stream=stream) for m in setup["masks"]]
     for _ in range(warmup):
         for f in launches:
             f()
@@ -163,10 +162,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--layout", default="blhd", choices=["blhd", "bhld"])
+    ap.add_argument("--layout", default="bhld", choices=["blhd", "bhld"],
+                    help="bhld = [B, H, L, D] (each head contiguous), blhd = [B, L, H, D]")
     ap.add_argument("--quick", action="store_true", help="skip the 16K and 128K extra workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="vit896")
+    ap.add_argument("--only", default=None, help="time only this mask of the workload (profiling)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="run only a plain device copy of MIB mebibytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
@@ -174,11 +177,22 @@ def main():
         sys.exit(2)
 
     import torch
+    device = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": args.steps}))
+        return
     from block_sparse_softmax_amd import load_library
     load_library()
-    device = torch.device("cuda:0")
 
     setup = _setup(args.workload, device, args.layout)
+    if args.only:
+        setup["masks"] = [m for m in setup["masks"] if m["label"] == args.only]
     wall, per = _time(setup, args.steps, args.warmup, args.layout)
     rows, total_flops, ms_per_step = _summarise(setup, wall, per, args.steps)
     value = total_flops / (ms_per_step * 1e-3) / 1e12

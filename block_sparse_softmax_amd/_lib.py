@@ -249,6 +249,34 @@ class PreparedMask:
         self.plan.upload(self.workspace)
         torch.cuda.synchronize(device)
 
+    def bind(self, q, k, v, o, sink=None, layout="blhd", stream=None, softmax_scale: float = 0.0):
+        """Marshal the arguments once; the returned callable launches with a single C call.
+
+        The tensors must stay alive (and keep their storage) while the callable is used.
+        """
+        lib = load_library()
+        qv, kv, vv, ov = (tensor_view(x, layout) for x in (q, k, v, o))
+        ln = Launch()
+        ln.stream = _stream_ptr(stream, q).value
+        ln.workspace = self.workspace.data_ptr()
+        ln.workspace_bytes = self.workspace.numel()
+        ln.softmax_scale = softmax_scale
+        sp = None
+        if sink is not None:
+            import torch
+            if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() != self.plan.H:
+                raise TypeError("sink must be a float32 CUDA tensor with one entry per head")
+            sp = ctypes.c_void_p(sink.data_ptr())
+        args = (self.plan.handle, ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), sp,
+                ctypes.byref(ov), ctypes.byref(ln))
+        keep = (qv, kv, vv, ov, ln, q, k, v, o, sink)
+        fn = lib.attn_masked_fwd_plan
+
+        def run():
+            _check(fn(*args))
+            return keep[8]
+        return run
+
     def launch(self, q, k, v, o, sink=None, layout="blhd", stream=None, softmax_scale: float = 0.0):
         lib = load_library()
         qv, kv, vv, ov = (tensor_view(x, layout) for x in (q, k, v, o))

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   // XCD x takes the x-th contiguous chunk of the schedule, so the items that
   // share an XCD's L2 at any time come from the same head.
   const int xcd_chunk = (p.n_items + 7) / 8;
-  const int item_idx = (blockIdx.x % 8) * xcd_chunk + blockIdx.x / 8;
+  const int item_idx = p.xcd_chunked ? (blockIdx.x % 8) * xcd_chunk + blockIdx.x / 8 : blockIdx.x;
   if (item_idx >= p.n_items) return;
   const int4 item = reinterpret_cast<const int4*>(p.items)[item_idx];
   const int head = __builtin_amdgcn_readfirstlane(item.x);
@@ -333,9 +333,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   auto pv = [&](int vbuf, const bf16x8 (&pb)[4]) {
     const unsigned char* vt_lds = smem + vbuf * S::TILE;
 #pragma unroll
-    for (int dt = 0; dt < S::DT; ++dt) {
+    for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int dt = 0; dt < S::DT; ++dt) {  // consecutive MFMAs use different accumulators
         const unsigned char* src = vt_lds + 16 * t * S::LRB;
         const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + voff[dt][0]));
         const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + voff[dt][1]));

@@ -108,6 +108,7 @@ attn_status launch_with_plan(const attn_plan& p, const attn_tensor* q, const att
   f.chunk = static_cast<int32_t>(std::min<int64_t>(p.chunk, p.L));
   if (f.chunk < 1) f.chunk = 1;
   f.right = static_cast<int32_t>(p.right);
+  f.xcd_chunked = 1;
   hipError_t e = launch_fwd(f, static_cast<int>(p.D), static_cast<int>(B),
                             static_cast<hipStream_t>(launch->stream));
   if (e != hipSuccess) return hip_fail(e, "kernel launch");

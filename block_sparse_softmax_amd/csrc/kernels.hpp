@@ -26,6 +26,7 @@ struct FwdParams {
   int32_t L, H, n_items;
   int32_t kind, causal;
   int32_t chunk, right;
+  int32_t xcd_chunked;        // 1: XCD x runs the x-th contiguous eighth of the schedule
 };
 
 // Launch the forward kernel for head dim D on `stream` with grid (n_items, B).
