@@ -36,6 +36,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "kernels.hpp"
 
@@ -44,6 +45,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -84,6 +86,14 @@ struct Shape {
   static constexpr int DMA_PERIOD = 16 * LCPR / 64;
   static_assert(LOADS % DMA_PERIOD == 0, "loads per wave must be whole swizzle periods");
   static constexpr bool PAD_ROWSUM = (D % 32) != 0;
+  // S^T tiles start from minus the reference (the C operand of the first
+  // k-step), so the scores come out of the MFMA already shifted.
+  static constexpr bool SEEDED = true;
+  // d = 64 and 80 software-pipeline the tiles (the VALU work of one tile
+  // runs beside the MFMAs of the next); at d = 128 the second score block
+  // that needs does not fit in 256 VGPRs, so each tile runs QK, softmax, PV
+  // in turn and the second wave on the SIMD provides the overlap.
+  static constexpr bool PIPELINED = D != 128;
 };
 
 // Physical 16-byte chunk of logical chunk c in LDS row `row` (an XOR, so its
@@ -106,17 +116,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-// One 16-byte global -> LDS copy per lane: lane l writes LDS bytes
-// [lds_base + 16 l, lds_base + 16 l + 16).  Issued as inline assembly so the
-// compiler does not treat every later LDS read as aliasing it (it would then
-// wait for the whole prefetch before any LDS read); completion is tracked by
-// the explicit vmcnt waits in the main loop.
-__device__ __forceinline__ void dma16(const void* base_ptr, uint32_t voffset, uint32_t lds_base) {
-  // readfirstlane yields int: widen through uint32_t so the low half is not sign-extended
-  const uint64_t a = reinterpret_cast<uint64_t>(base_ptr);
+// A wave-uniform 64-bit value moved to scalar registers (readfirstlane yields
+// int: widen through uint32_t so the low half is not sign-extended).
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t a) {
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a)));
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32)));
-  const uint64_t base = (static_cast<uint64_t>(hi) << 32) | lo;
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// One 16-byte global -> LDS copy per lane: lane l writes LDS bytes
+// [lds_base + 16 l, lds_base + 16 l + 16) from base + voffset.  base and
+// lds_base must be wave-uniform.  Issued as inline assembly so the compiler
+// does not treat every later LDS read as aliasing it (it would then wait for
+// the whole prefetch before any LDS read); completion is tracked by the
+// explicit vmcnt waits in the main loop.
+__device__ __forceinline__ void dma16(uint64_t base, uint32_t voffset, uint32_t lds_base) {
   __asm__ volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
@@ -124,6 +138,22 @@ __device__ __forceinline__ void dma16(const void* base_ptr, uint32_t voffset, ui
       :
       : "v"(voffset), "s"(base), "s"(lds_base)
       : "memory", "m0");
+}
+// Same, with the lanes set in `skip` left out (exec is narrowed and restored
+// inside the statement, so no branch is needed).
+__device__ __forceinline__ void dma16_skip(uint64_t base, uint32_t voffset, uint32_t lds_base,
+                                           uint64_t skip) {
+  uint64_t saved;
+  __asm__ volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_andn2_b64 exec, exec, %4\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"(voffset), "s"(base), "s"(lds_base), "s"(skip)
+      : "memory", "m0", "scc");  // s_andn2_b64 writes SCC
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -149,6 +179,21 @@ __device__ __forceinline__ float halves_sum(float x) {
 __device__ __forceinline__ float low_half(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]);
+}
+
+// An empty asm that claims to modify x: values derived from x inside a loop
+// can then not be hoisted out of it (used to recompute cheap addresses
+// instead of keeping a register for each).
+template <typename T>
+__device__ __forceinline__ void opaque(T& x) {
+  __asm__ volatile("" : "+v"(x));
+}
+
+// max(a, b, c) in one instruction.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -192,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
 
   // ---- the KV list of this item, staged in LDS kListCap entries at a time ----
   const int n = e_end - e_begin;
-  auto stage_list = [&](int first) {
+  auto stage_list = [&](int first) __attribute__((always_inline)) {
     const int cnt = min(kListCap, n - first);
     for (int i = threadIdx.x; i < cnt; i += kThreads) list_lds[i] = p.kv[e_begin + first + i];
   };
@@ -213,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     }
   }
 
-  // ---- allowed key interval [lo, hi) of this query (used on PARTIAL tiles) ----
+  // ---- allowed key interval [lo, lo + width) of this query (PARTIAL tiles) ----
   int lo = 0, hi = p.L;
   if (p.kind == kMaskChunk) {
     lo = (qi / p.chunk) * p.chunk;
@@ -227,8 +272,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   const unsigned width = static_cast<unsigned>(hi - lo);
 
   // ---- running softmax state (log2 domain) ----
-  // m_run: reference max; l_run: row sum of this lane's keys (d != 80);
-  // sink_l: the sink's term exp2(s_aux log2e - m_run).
+  // m_run: reference max (-inf while no allowed key and no sink has been seen);
+  // l_run: sum of this lane's probabilities (d != 80: d = 80 reads the row sum
+  // off O^T row 80); sink_l: the sink's term exp2(s_aux log2e - m_run).
   float m_run = -INFINITY, l_run = 0.f, sink_l = 0.f;
   if (p.sink != nullptr) {
     const float s = p.sink[head] * kLog2e;
@@ -243,9 +289,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
 
   // ---- LDS addressing ----
   // K fragment for k-step ks: row l31 (and l31 + 32: same swizzle), logical chunk 2*ks + h2.
+  // d = 128 keeps one base per table and rebuilds the others with an XOR per
+  // use (its swizzle XORs k-step / O^T-tile bits into address bits that are
+  // otherwise lane-only), which saves 14 registers.
   int koff[S::KS];
 #pragma unroll
   for (int ks = 0; ks < S::KS; ++ks) koff[ks] = l31 * S::LRB + phys_chunk<D>(l31, 2 * ks + h2) * 16;
+  int kbase_off = koff[0];
   // V^T fragment for O^T tile dt and half u of a 16-key k-step: transposed
   // read; source lane (j, c) of each 16-lane group points at row
   // 8*u + 4*h2 + j (+16 per k-step), columns 32*dt + 16*dhalf + 4*c .. +3.
@@ -260,6 +310,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
       voff[dt][u] = row * S::LRB + phys_chunk<D>(row, c) * 16 + (tr_c & 1) * 8;
     }
   }
+  int vbase_off = voff[0][0];
   if constexpr (S::PAD_ROWSUM) {
     // Constant pad chunks 10-11 of every V row in both V buffers: element 80 = 1, the rest 0.
     for (int i = threadIdx.x; i < 2 * kBN * 4; i += kThreads) {  // 2 buffers x 64 rows x 4 x 8 bytes
@@ -278,161 +329,365 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   const uint32_t dma_row_bytes = static_cast<uint32_t>(dma_tensor ? v_row_bytes : k_row_bytes);
   const unsigned char* dma_base = dma_tensor ? vbase : kbase;
   // Lane part of each load's source offset for one swizzle period (16 rows);
-  // later periods add 16 rows to the uniform base.  Lanes whose slot is a
-  // pad chunk (d = 80) load nothing.
+  // later periods add 16 rows to the uniform base.  d = 80: lanes whose slot
+  // is a pad chunk read chunk 0 of their row instead; for V they are left out
+  // of the copy (the pad holds the constant ones row), for K the copy is
+  // harmless (K pad chunks are never read).
   uint32_t goff[S::DMA_PERIOD];
-  bool gpad[S::DMA_PERIOD];
+  uint64_t gskip[S::DMA_PERIOD];
 #pragma unroll
   for (int i = 0; i < S::DMA_PERIOD; ++i) {
     const int slot = ((wave & 1) * S::LOADS + i) * 64 + lane;
     const int row = slot / S::LCPR;
     const int c = phys_chunk<D>(row, slot % S::LCPR);
-    gpad[i] = c >= S::CPR;
-    goff[i] = row * dma_row_bytes + (gpad[i] ? 0 : c) * 16;
+    const bool pad = c >= S::CPR;
+    goff[i] = row * dma_row_bytes + (pad ? 0 : c) * 16;
+    gskip[i] = (S::PAD_ROWSUM && dma_tensor == 1) ? __builtin_amdgcn_ballot_w64(pad) : 0;
   }
   const uint32_t smem_lds = lds_addr(smem);
   // Issue this wave's share of tile kt into LDS buffer buf (0-1 K, 2-3 V).
-  auto issue_tile = [&](int kt, int buf) {
-    const int kv0 = kt * kBN;
-    const unsigned char* src = dma_base + static_cast<uint32_t>(kv0) * dma_row_bytes;
+  auto issue_tile = [&](int kt, int buf) __attribute__((always_inline)) {
+    const uint32_t kv0 = static_cast<uint32_t>(kt * kBN);
+    const uint64_t tb = uniform_u64(reinterpret_cast<uint64_t>(dma_base) + static_cast<uint64_t>(kv0) * dma_row_bytes);
     const uint32_t dst =
         __builtin_amdgcn_readfirstlane(smem_lds + buf * S::TILE + (wave & 1) * S::LOADS * 1024);
-    if (kv0 + kBN <= p.L) {
+    if (static_cast<int>(kv0) + kBN <= p.L) {
 #pragma unroll
       for (int i = 0; i < S::LOADS; ++i) {
-        const uint32_t rows_ahead = static_cast<uint32_t>((i / S::DMA_PERIOD) * 16);
-        if (!S::PAD_ROWSUM || !gpad[i % S::DMA_PERIOD])
-          dma16(src + rows_ahead * dma_row_bytes, goff[i % S::DMA_PERIOD], dst + i * 1024);
+        const uint64_t b = tb + static_cast<uint64_t>((i / S::DMA_PERIOD) * 16) * dma_row_bytes;
+        if constexpr (S::PAD_ROWSUM) dma16_skip(b, goff[i % S::DMA_PERIOD], dst + i * 1024, gskip[i % S::DMA_PERIOD]);
+        else dma16(b, goff[i % S::DMA_PERIOD], dst + i * 1024);
       }
     } else {  // ragged last tile: clamp rows past the end of the sequence (their keys are masked)
-      const int last = p.L - 1 - kv0;
+      const int last = p.L - 1 - static_cast<int>(kv0);
 #pragma unroll
       for (int i = 0; i < S::LOADS; ++i) {
         const int slot = ((wave & 1) * S::LOADS + i) * 64 + lane;
         const int row = slot / S::LCPR;
         const int c = phys_chunk<D>(row, slot % S::LCPR);
-        const uint32_t off = min(row, last) * dma_row_bytes + c * 16;
-        if (!S::PAD_ROWSUM || c < S::CPR) dma16(src, off, dst + i * 1024);
+        const uint32_t off = min(row, last) * dma_row_bytes + (c < S::CPR ? c : 0) * 16;
+        if constexpr (S::PAD_ROWSUM) dma16_skip(tb, off, dst + i * 1024, gskip[i % S::DMA_PERIOD]);
+        else dma16(tb, off, dst + i * 1024);
       }
     }
   };
 
-  // S^T = K Q^T + seed (log2-domain logits minus the reference max) for a
-  // 64-key tile; the seed block is the C operand of the first k-step.
-  auto qk = [&](int kbuf, const f32x16& seed, f32x16& s0, f32x16& s1) {
-    const unsigned char* kt_lds = smem + kbuf * S::TILE;
-#pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kt_lds + koff[ks]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kt_lds + koff[ks] + 32 * S::LRB);
-      s0 = mfma32(a0, qf[ks], ks == 0 ? seed : s0);
-      s1 = mfma32(a1, qf[ks], ks == 0 ? seed : s1);
-    }
+  // ---- LDS fragment reads ----
+  // d = 128: XOR of a per-use constant into one base; d = 80: its swizzle
+  // only touches the two low chunk bits, so addresses are one of two bases
+  // plus an immediate (32 bytes per k-step, 64 bytes per O^T tile).
+  auto k_addr = [&](int ks) __attribute__((always_inline)) {
+    if constexpr (D == 128) return kbase_off ^ (ks << 5);
+    else if constexpr (D == 80) return koff[ks & 1] + 32 * (ks & ~1);
+    else return koff[ks];
   };
-  // O^T += V^T P^T for a 64-key tile.
-  auto pv = [&](int vbuf, const bf16x8 (&pb)[4]) {
-    const unsigned char* vt_lds = smem + vbuf * S::TILE;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int dt = 0; dt < S::DT; ++dt) {  // consecutive MFMAs use different accumulators
-        const unsigned char* src = vt_lds + 16 * t * S::LRB;
-        const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + voff[dt][0]));
-        const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + voff[dt][1]));
-        const s16x8 x = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[dt] = mfma32(__builtin_bit_cast(bf16x8, x), pb[t], acc[dt]);
-      }
-    }
+  auto v_addr = [&](int dt, int u) __attribute__((always_inline)) {
+    if constexpr (D == 128) return vbase_off ^ (dt << 6) ^ (u ? 0x820 : 0);
+    else if constexpr (D == 80) return voff[0][u] + 64 * dt;
+    else return voff[dt][u];
   };
-  // Seed of a tile's S^T accumulators: minus the current reference max (0 while
-  // none), kept as a 16-register block rewritten only when the max moves.
+  // K fragment (A operand of S^T = K Q^T) for k-step ks, keys 32*half .. +31.
+  auto kfrag = [&](int kbuf, int ks, int half) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(smem + kbuf * S::TILE + k_addr(ks) + half * 32 * S::LRB);
+  };
+  // V^T fragment for PV step p = t * DT + dt (keys 16t .. 16t+15, O^T tile dt).
+  auto vfrag = [&](int vbuf, int p) __attribute__((always_inline)) {
+    const int t = p / S::DT, dt = p % S::DT;
+    const unsigned char* src = smem + vbuf * S::TILE + 16 * t * S::LRB;
+    const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + v_addr(dt, 0)));
+    const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + v_addr(dt, 1)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // Seed of a tile's S^T accumulators (C operand of its first k-step): minus
+  // the reference, so the MFMA output is already relative to it.
   f32x16 seedv;
-  auto set_seed = [&]() {
-    const float sd = m_run == -INFINITY ? 0.f : -m_run;
+  auto ref_of = [&]() __attribute__((always_inline)) { return m_run == -INFINITY ? 0.f : m_run; };
+  auto set_seed = [&]() __attribute__((always_inline)) {
+    if constexpr (S::SEEDED) {
+      const float sd = -ref_of();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) seedv[r] = sd;
+      for (int r = 0; r < 16; ++r) seedv[r] = sd;
+    }
   };
   set_seed();
 
-  // ---- main loop: one listed tile per iteration ----
-  // K and V of tile j sit in buffers (j&1) and 2 + (j&1); the DMA for tile
-  // j+1 is issued at the top of iteration j, right after the barrier that
-  // guarantees every wave is done with the buffers of tile j-1.
+  // ---- main loop: software pipeline over the listed tiles, scheduled by hand ----
+  // Iteration j (0 <= j <= n):
+  //   part 1: S^T of tile j (2 KS MFMAs), each MFMA followed by a share of
+  //           the exponentials of tile j-1, keys 0-31;
+  //   part 2: O^T += V^T P^T of tile j-1 (4 DT MFMAs); the first half of them
+  //           carry the exponentials of keys 32-63, the second half the mask
+  //           (PARTIAL tiles) and row max of tile j.
+  // An MFMA hides about four full-rate VALU instructions (VALU work issued
+  // while an MFMA runs proceeds at half rate), which sets the shares.  LDS
+  // fragments are read two MFMAs ahead; scheduling fences keep this order.
+  // A rare branch at the end moves the reference when tile j's max exceeds
+  // it by more than 2^kRescaleThreshold (scaling acc, which then holds tile
+  // j-1, the row sum, the sink term and tile j's scores).
+  // K of tile t sits in buffer t&1 (DMA issued at the top of iteration t-1),
+  // V of tile t in buffer 2 + (t&1) (DMA issued at the top of iteration t);
+  // the barrier at the top of iteration j guarantees that the buffers of K
+  // tile j-1 and V tile j-2 are no longer read.
+  // Scores of the newest tile relative to the reference: two register
+  // blocks that trade roles every iteration (the loop is unrolled by two),
+  // so the hand-over needs no copies and buffer offsets are immediates.
+  f32x16 sA[2], sB[2];
   int list_base = 0;
-  int ent_c = 0;
-  if (n > 0) {
-    __syncthreads();  // list staged, pad regions written
-    ent_c = __builtin_amdgcn_readfirstlane(list_lds[0]);
-    issue_tile(ent_c >> 1, 2 * dma_tensor);
-  }
-  for (int j = 0; j < n; ++j) {
-    const int ent = __builtin_amdgcn_readfirstlane(ent_c);
-    wait_vmcnt<0>();   // this wave's share of tile j (and, at j = 0, the Q fragments)
-    wg_barrier();      // everyone's share of tile j; buffers of tile j-1 are free
+  int ent_cur = 0;  // list entry (kv_tile << 1 | full) of tile j
+  const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // sc: scores of tile j-1 (read); sn: scores of tile j (written).
+  auto iteration = [&](int j, auto cur_tag, auto prev_tag, auto mask_tag, auto par_tag,
+                       f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    constexpr bool kCur = decltype(cur_tag)::value;    // tile j exists
+    constexpr bool kPrev = decltype(prev_tag)::value;  // tile j-1 exists
+    constexpr bool kMask = decltype(mask_tag)::value;  // tile j is PARTIAL
+    constexpr int kPar = decltype(par_tag)::value;     // j & 1
+    constexpr int NQ = 2 * S::KS;  // QK MFMAs
+    constexpr int NP = 4 * S::DT;  // PV MFMAs
+    wait_vmcnt<0>();   // this wave's share of K tile j / V tile j-1
+    wg_barrier();      // ... and everyone else's
+    const int ent = __builtin_amdgcn_readfirstlane(ent_cur);
     if (j + 1 < n) {
       if (j + 1 - list_base == kListCap) {  // next chunk of the list
         list_base += kListCap;
         stage_list(list_base);
         __syncthreads();
       }
-      ent_c = __builtin_amdgcn_readfirstlane(list_lds[j + 1 - list_base]);
-      issue_tile(ent_c >> 1, 2 * dma_tensor + ((j + 1) & 1));
+      ent_cur = __builtin_amdgcn_readfirstlane(list_lds[j + 1 - list_base]);
+      if (dma_tensor == 0) issue_tile(ent_cur >> 1, kPar ^ 1);
+    }
+    if constexpr (kCur) {
+      if (dma_tensor == 1) issue_tile(ent >> 1, 2 + kPar);
+    }
+    if constexpr (D == 128) {
+      opaque(kbase_off);
+      opaque(vbase_off);
+    }
+    constexpr int kb = kPar, vb = 2 + (kPar ^ 1);
+
+    // exponentials of tile j-1: pair i (0..7) of key block h -> P^T elements
+    bf16x8 pb[4];
+    float rs = 0.f;
+    // (unseeded scores are raw logits: the reference comes off here)
+    const float eref = S::SEEDED ? 0.f : ref_of();
+    auto exp_pair = [&](int h, int i) __attribute__((always_inline)) {
+      const int t = 2 * h + i / 4, e = 2 * (i % 4);
+      pb[t][e] = (__bf16)__builtin_amdgcn_exp2f(sc[h][2 * i] - eref);
+      pb[t][e + 1] = (__bf16)__builtin_amdgcn_exp2f(sc[h][2 * i + 1] - eref);
+      if constexpr (!S::PAD_ROWSUM)
+        rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[t][e], pb[t][e + 1]}, ones2, rs, false);
+    };
+    // mask (PARTIAL) and row max of tile j: step r (0..15)
+    float x = 0.f;
+    const unsigned mbase = static_cast<unsigned>((ent >> 1) * kBN + 4 * h2 - lo);
+    auto mask_step = [&](int r) __attribute__((always_inline)) {
+      const unsigned u = mbase + 8 * (r >> 2) + (r & 3);
+      sn[0][r] = (u >= width) ? -INFINITY : sn[0][r];
+      sn[1][r] = (u + 32 >= width) ? -INFINITY : sn[1][r];
+    };
+    auto max_step = [&](int r) __attribute__((always_inline)) {
+      x = (r == 0) ? fmaxf(sn[0][0], sn[1][0]) : max3(x, sn[0][r], sn[1][r]);
+    };
+    // QK MFMA number q: k-step and key half
+    auto q_ks = [](int q) __attribute__((always_inline)) { return q / 2; };
+    auto q_half = [](int q) __attribute__((always_inline)) { return q % 2; };
+
+    // ---- part 1 ----
+    bf16x8 ka[NQ + 2];
+    if constexpr (kCur) {
+      ka[0] = kfrag(kb, q_ks(0), q_half(0));
+      ka[1] = kfrag(kb, q_ks(1), q_half(1));
+    }
+    bf16x8 va[NP + 2];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int ks = q_ks(q), half = q_half(q);
+      if constexpr (kCur) {
+        if (q + 2 < NQ) ka[q + 2] = kfrag(kb, q_ks(q + 2), q_half(q + 2));
+        sn[half] = mfma32(ka[q], qf[ks], ks == 0 ? (S::SEEDED ? seedv : f32x16{}) : sn[half]);
+      }
+      if constexpr (kPrev) {
+        if (q == NQ - 2) va[0] = vfrag(vb, 0);
+        if (q == NQ - 1) va[1] = vfrag(vb, 1);
+#pragma unroll
+        for (int i = q * 8 / NQ; i < (q + 1) * 8 / NQ; ++i) exp_pair(0, i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- S^T of tile j, relative to the reference max (seeded C operand) ----
-    f32x16 s0, s1;
-    qk(j & 1, seedv, s0, s1);
+    // ---- part 2 ----
+    constexpr int NB = kMask ? 32 : 16;  // mask + max steps
+#pragma unroll
+    for (int pidx = 0; pidx < NP; ++pidx) {
+      if constexpr (kPrev) {
+        if (pidx + 2 < NP) va[pidx + 2] = vfrag(vb, pidx + 2);
+        const int t = pidx / S::DT, dt = pidx % S::DT;
+        acc[dt] = mfma32(va[pidx], pb[t], acc[dt]);
+        if (pidx < 2 * S::DT) {
+          constexpr int H = 2 * S::DT;
+#pragma unroll
+          for (int i = pidx * 8 / H; i < (pidx + 1) * 8 / H; ++i) exp_pair(1, i);
+        }
+      }
+      if constexpr (kCur) {
+        constexpr int H = 2 * S::DT;
+        if (!kPrev || pidx >= H) {
+          const int slot = !kPrev ? pidx : pidx - H;
+          const int nslots = !kPrev ? NP : H;
+#pragma unroll
+          for (int i = slot * NB / nslots; i < (slot + 1) * NB / nslots; ++i) {
+            if (kMask && i < 16) mask_step(i);
+            else max_step(kMask ? i - 16 : i);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (!S::PAD_ROWSUM && kPrev) l_run += rs;
 
-    // ---- mask (PARTIAL tiles only), row max, lazy rescale ----
-    if (!(ent & 1)) {
-      const unsigned base = static_cast<unsigned>((ent >> 1) * kBN + 4 * h2 - lo);
+    if constexpr (kCur) {
+      // ---- rare: move the reference ----
+      const float ref = ref_of();
+      const float mx = halves_max(x);  // tile max (SEEDED: relative to the reference)
+      const float mt = S::SEEDED ? mx : mx - ref;
+      const bool need = (m_run == -INFINITY) ? (mt > -INFINITY) : (mt > kRescaleThreshold);
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+        const float m_new = need ? ref + mt : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 while m_run = -inf
+        const float shift = (m_new == -INFINITY ? 0.f : m_new) - ref;
+        m_run = m_new;
+        l_run *= alpha;
+        sink_l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt) acc[dt] *= alpha;
+        if constexpr (S::SEEDED) {
+          sn[0] -= shift;
+          sn[1] -= shift;
+        }
+        set_seed();
+      }
+    }
+  };
+  // steady-state iteration: the FULL / PARTIAL variant of tile j
+  auto steady = [&](int j, auto par_tag, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    if (__builtin_amdgcn_readfirstlane(ent_cur) & 1)
+      iteration(j, Bool<true>{}, Bool<true>{}, Bool<false>{}, par_tag, sc, sn);
+    else
+      iteration(j, Bool<true>{}, Bool<true>{}, Bool<true>{}, par_tag, sc, sn);
+  };
+
+  // ---- d = 128: one tile per iteration, QK -> softmax -> PV ----
+  // (one loop body with the mask under a uniform branch: separate FULL and
+  // PARTIAL copies raise the register pressure past 256 here)
+  // K and V of tile j sit in buffers (j&1) and 2 + (j&1); the DMA for tile
+  // j+1 is issued at the top of iteration j, right after the barrier that
+  // guarantees every wave is done with the buffers of tile j-1.
+  auto serial = [&](int j) __attribute__((always_inline)) {
+    const int kPar = j & 1;
+    constexpr int NQ = 2 * S::KS;
+    constexpr int NP = 4 * S::DT;
+    wait_vmcnt<0>();   // this wave's share of tile j
+    wg_barrier();      // ... and everyone else's; buffers of tile j-1 are free
+    const int ent = __builtin_amdgcn_readfirstlane(ent_cur);
+    if (j + 1 < n) {
+      if (j + 1 - list_base == kListCap) {  // next chunk of the list
+        list_base += kListCap;
+        stage_list(list_base);
+        __syncthreads();
+      }
+      ent_cur = __builtin_amdgcn_readfirstlane(list_lds[j + 1 - list_base]);
+      issue_tile(ent_cur >> 1, 2 * dma_tensor + (kPar ^ 1));
+    }
+    if constexpr (D == 128) {
+      opaque(kbase_off);
+      opaque(vbase_off);
+    }
+    // S^T of tile j relative to the reference (seeded C operand)
+    f32x16 sn[2];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int ks = q / 2, half = q % 2;
+      sn[half] = mfma32(kfrag(kPar, ks, half), qf[ks], ks == 0 ? seedv : sn[half]);
+    }
+    if (!(ent & 1)) {  // PARTIAL tile
+      const unsigned mbase = static_cast<unsigned>((ent >> 1) * kBN + 4 * h2 - lo);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const unsigned u = base + 8 * (r >> 2) + (r & 3);
-        s0[r] = (u >= width) ? -INFINITY : s0[r];
-        s1[r] = (u + 32 >= width) ? -INFINITY : s1[r];
+        const unsigned u = mbase + 8 * (r >> 2) + (r & 3);
+        sn[0][r] = (u >= width) ? -INFINITY : sn[0][r];
+        sn[1][r] = (u + 32 >= width) ? -INFINITY : sn[1][r];
       }
     }
-    float mt = fmaxf(s0[0], s1[0]);
+    float x = fmaxf(sn[0][0], sn[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
-    mt = halves_max(mt);
+    for (int r = 1; r < 16; ++r) x = max3(x, sn[0][r], sn[1][r]);
+    const float mt = halves_max(x);  // tile max relative to the reference
     const bool need = (m_run == -INFINITY) ? (mt > -INFINITY) : (mt > kRescaleThreshold);
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      float alpha = 1.f, shift = 0.f;
-      if (need) {
-        const float m_new = (m_run == -INFINITY ? 0.f : m_run) + mt;
-        alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        shift = mt;
-      }
-      s0 -= shift;
-      s1 -= shift;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+      const float ref = ref_of();
+      const float m_new = need ? ref + mt : m_run;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 while m_run = -inf
+      const float shift = (m_new == -INFINITY ? 0.f : m_new) - ref;
+      m_run = m_new;
       l_run *= alpha;
       sink_l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt) acc[dt] *= alpha;
+      sn[0] -= shift;
+      sn[1] -= shift;
       set_seed();
     }
-
-    // ---- P = exp2(S), O^T += V^T P^T ----
+    // P^T = exp2(S^T) in bf16; row sum of the bf16 values
+    bf16x8 pb[4];
     float rs = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] = __builtin_amdgcn_exp2f(s0[r]);
-      s1[r] = __builtin_amdgcn_exp2f(s1[r]);
-      if (!S::PAD_ROWSUM) rs += s0[r] + s1[r];
-    }
-    if (!S::PAD_ROWSUM) l_run += rs;
-    bf16x8 pb[4];
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int e8 = 0; e8 < 8; ++e8) {
-      pb[0][e8] = (__bf16)s0[e8];
-      pb[1][e8] = (__bf16)s0[8 + e8];
-      pb[2][e8] = (__bf16)s1[e8];
-      pb[3][e8] = (__bf16)s1[8 + e8];
+      for (int i = 0; i < 8; ++i) {
+        const int t = 2 * h + i / 4, e = 2 * (i % 4);
+        pb[t][e] = (__bf16)__builtin_amdgcn_exp2f(sn[h][2 * i]);
+        pb[t][e + 1] = (__bf16)__builtin_amdgcn_exp2f(sn[h][2 * i + 1]);
+        if constexpr (!S::PAD_ROWSUM)
+          rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[t][e], pb[t][e + 1]}, ones2, rs, false);
+      }
     }
-    pv(2 + (j & 1), pb);
+    if constexpr (!S::PAD_ROWSUM) l_run += rs;
+    // O^T += V^T P^T
+#pragma unroll
+    for (int pidx = 0; pidx < NP; ++pidx) {
+      const int t = pidx / S::DT, dt = pidx % S::DT;
+      acc[dt] = mfma32(vfrag(2 + kPar, pidx), pb[t], acc[dt]);
+    }
+  };
+
+  if constexpr (!S::PIPELINED) {
+   if (n > 0) {
+    __syncthreads();  // list staged, pad regions written
+    ent_cur = __builtin_amdgcn_readfirstlane(list_lds[0]);
+    issue_tile(ent_cur >> 1, 2 * dma_tensor);
+    for (int j = 0; j < n; ++j) serial(j);
+   }
+  } else {
+   if (n > 0) {
+    __syncthreads();  // list staged, pad regions written
+    ent_cur = __builtin_amdgcn_readfirstlane(list_lds[0]);
+    if (dma_tensor == 0) issue_tile(ent_cur >> 1, 0);
+    if (ent_cur & 1) iteration(0, Bool<true>{}, Bool<false>{}, Bool<false>{}, std::integral_constant<int, 0>{}, sB, sA);
+    else iteration(0, Bool<true>{}, Bool<false>{}, Bool<true>{}, std::integral_constant<int, 0>{}, sB, sA);
+    int j = 1;
+    for (; j + 1 < n; j += 2) {
+      steady(j, std::integral_constant<int, 1>{}, sA, sB);
+      steady(j + 1, std::integral_constant<int, 0>{}, sB, sA);
+    }
+    if (j < n) {  // j = n - 1 (odd)
+      steady(j, std::integral_constant<int, 1>{}, sA, sB);
+      iteration(n, Bool<false>{}, Bool<true>{}, Bool<false>{}, std::integral_constant<int, 0>{}, sB, sA);
+    } else {  // j = n (odd)
+      iteration(n, Bool<false>{}, Bool<true>{}, Bool<false>{}, std::integral_constant<int, 1>{}, sA, sB);
+    }
+   }
   }
 
   // ---- epilogue: O = acc / (row sum + sink term) ----
