@@ -55,6 +55,30 @@ def _traffic_from_profile(workload: str, mask: str):
     return float(b.group(1))
 
 
+WORKLOADS = {
+    "tiny_chunk": "Tiny chunk-window attention: L=256 tokens, batch 1, 2 heads, head dim 64; chunks of 64",
+    "vit896": "ViT layer at 896 px: L=4096 tokens, batch 1, 16 heads, head dim 80; "
+              "masks full + chunk 256 + sliding window radius 128",
+    "vit1792": "ViT layer at 1792 px: L=16384 tokens, batch 1, 16 heads, head dim 80; "
+               "masks full + sliding window radius 512",
+    "lm_headwin": "Causal LM prefill: L=4096, batch 1, 16 heads, head dim 128; per-head causal windows "
+                  "{512, 1024, 2048, 4096} and a sink logit per head",
+    "blocksparse128k": "Block-sparse causal prefill: L=131072, batch 1, 32 heads, head dim 128; block 128, "
+                       "diagonal + first block + top half of the remaining causal blocks per block row",
+}
+
+
+def _roofline(setup, rows, workload):
+    """Roofline object for the launch with the largest average duration."""
+    dom = max(rows, key=lambda r: r["avg_ms"])
+    w = setup["w"]
+    dom_flops = 4.0 * w["D"] * dom["pairs"] * w["B"]
+    achieved = dom_flops / (dom["avg_ms"] * 1e-3) / 1e12
+    return dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                frac=achieved / PEAK_BF16_TFLOPS, traffic=_traffic_from_profile(workload, dom["mask"]),
+                kernel=f"attn_fwd_kernel<{w['D']}> ({workload} {dom['mask']})", avg_launch_ms=dom["avg_ms"])
+
+
 def _bits_to_dev(u16, device, layout):
     import numpy as np
     import torch
@@ -197,14 +221,7 @@ def main():
     rows, total_flops, ms_per_step = _summarise(setup, wall, per, args.steps)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
-    dom = max(rows, key=lambda r: r["avg_ms"])
-    w = setup["w"]
-    dom_flops = 4.0 * w["D"] * dom["pairs"] * w["B"]
-    traffic = _traffic_from_profile(args.workload, dom["mask"])
-    roof = dict(bound="mfma", achieved=dom_flops / (dom["avg_ms"] * 1e-3) / 1e12, peak=PEAK_BF16_TFLOPS,
-                unit="TFLOP/s", frac=dom_flops / (dom["avg_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                traffic=traffic, kernel=f"attn_fwd_kernel<{w['D']}> ({args.workload} {dom['mask']})",
-                avg_launch_ms=dom["avg_ms"])
+    roof = _roofline(setup, rows, args.workload)
 
     cpu = None if args.no_cpu_baseline else _cpu_baseline(setup)
 
@@ -216,7 +233,9 @@ def main():
             setup = _setup(name, device, args.layout)
             wl, pr = _time(setup, max(5, args.steps // 2), args.warmup, args.layout)
             r2, tf2, ms2 = _summarise(setup, wl, pr, max(5, args.steps // 2))
-            extra[name] = dict(ms_per_step=ms2, tflops=tf2 / (ms2 * 1e-3) / 1e12, masks=r2)
+            extra[name] = dict(workload=WORKLOADS[name], ms_per_step=ms2, tflops=tf2 / (ms2 * 1e-3) / 1e12,
+                               frac_bf16_peak=tf2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, masks=r2,
+                               roofline=_roofline(setup, r2, name))
 
     out = {
         "metric": "effective attention TFLOP/s (unmasked pairs) and % bf16 MFMA peak, 1 MI355X",
@@ -231,8 +250,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) Q, K, V rounded to bf16)",
-        "config": {"workload": "ViT layer at 896 px: L=4096 tokens, batch 1, 16 heads, head dim 80; "
-                               "masks full + chunk 256 + sliding window radius 128",
+        "config": {"workload": WORKLOADS[args.workload] + (f" (mask {args.only} only)" if args.only else ""),
                    "layout": args.layout, "frac_bf16_peak": value / PEAK_BF16_TFLOPS},
         "per_mask": rows,
         "roofline": roof,
