@@ -275,17 +275,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   // m_run: reference max (-inf while no allowed key and no sink has been seen);
   // l_run: sum of this lane's probabilities (d != 80: d = 80 reads the row sum
   // off O^T row 80); sink_l: the sink's term exp2(s_aux log2e - m_run).
-  float m_run = -INFINITY, l_run = 0.f, sink_l = 0.f;
-  if (p.sink != nullptr) {
-    const float s = p.sink[head] * kLog2e;
-    if (s > -INFINITY) {
-      m_run = s;
+  float m_run, l_run, sink_l;
+  f32x16 acc[S::DT];
+  const float sink_log2 = p.sink != nullptr ? p.sink[head] * kLog2e : -INFINITY;
+  auto init_state = [&]() __attribute__((always_inline)) {
+    m_run = -INFINITY;
+    l_run = 0.f;
+    sink_l = 0.f;
+    if (sink_log2 > -INFINITY) {
+      m_run = sink_log2;
       sink_l = 1.f;
     }
-  }
-  f32x16 acc[S::DT];
 #pragma unroll
-  for (int dt = 0; dt < S::DT; ++dt) acc[dt] = f32x16{};
+    for (int dt = 0; dt < S::DT; ++dt) acc[dt] = f32x16{};
+  };
+  init_state();
 
   // ---- LDS addressing ----
   // K fragment for k-step ks: row l31 (and l31 + 32: same swizzle), logical chunk 2*ks + h2.
@@ -438,12 +442,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   // sc: scores of tile j-1 (read); sn: scores of tile j (written).
-  auto iteration = [&](int j, auto cur_tag, auto prev_tag, auto mask_tag, auto par_tag,
-                       f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+  auto iteration = [&](int j, auto cur_tag, auto prev_tag, auto mask_tag, auto par_tag, auto safe_tag,
+                       f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
     constexpr bool kCur = decltype(cur_tag)::value;    // tile j exists
     constexpr bool kPrev = decltype(prev_tag)::value;  // tile j-1 exists
     constexpr bool kMask = decltype(mask_tag)::value;  // tile j is PARTIAL
     constexpr int kPar = decltype(par_tag)::value;     // j & 1
+    // Row max and reference update: on the first tile always; on later tiles
+    // only in the safe pass (the fast pass keeps the first tile's reference).
+    constexpr bool kMax = decltype(safe_tag)::value || !kPrev;
     constexpr int NQ = 2 * S::KS;  // QK MFMAs
     constexpr int NP = 4 * S::DT;  // PV MFMAs
     wait_vmcnt<0>();   // this wave's share of K tile j / V tile j-1
@@ -518,7 +525,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     }
 
     // ---- part 2 ----
-    constexpr int NB = kMask ? 32 : 16;  // mask + max steps
+    constexpr int NB = (kMask ? 16 : 0) + (kMax ? 16 : 0);  // mask + max steps
 #pragma unroll
     for (int pidx = 0; pidx < NP; ++pidx) {
       if constexpr (kPrev) {
@@ -539,7 +546,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
 #pragma unroll
           for (int i = slot * NB / nslots; i < (slot + 1) * NB / nslots; ++i) {
             if (kMask && i < 16) mask_step(i);
-            else max_step(kMask ? i - 16 : i);
+            else if constexpr (kMax) max_step(kMask ? i - 16 : i);
           }
         }
       }
@@ -547,7 +554,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     }
     if constexpr (!S::PAD_ROWSUM && kPrev) l_run += rs;
 
-    if constexpr (kCur) {
+    if constexpr (kCur && kMax) {
       // ---- rare: move the reference ----
       const float ref = ref_of();
       const float mx = halves_max(x);  // tile max (SEEDED: relative to the reference)
@@ -571,11 +578,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     }
   };
   // steady-state iteration: the FULL / PARTIAL variant of tile j
-  auto steady = [&](int j, auto par_tag, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+  auto steady = [&](int j, auto par_tag, auto safe_tag, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
     if (__builtin_amdgcn_readfirstlane(ent_cur) & 1)
-      iteration(j, Bool<true>{}, Bool<true>{}, Bool<false>{}, par_tag, sc, sn);
+      iteration(j, Bool<true>{}, Bool<true>{}, Bool<false>{}, par_tag, safe_tag, sc, sn);
     else
-      iteration(j, Bool<true>{}, Bool<true>{}, Bool<true>{}, par_tag, sc, sn);
+      iteration(j, Bool<true>{}, Bool<true>{}, Bool<true>{}, par_tag, safe_tag, sc, sn);
   };
 
   // ---- d = 128: one tile per iteration, QK -> softmax -> PV ----
@@ -662,30 +669,120 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     }
   };
 
-  if constexpr (!S::PIPELINED) {
-   if (n > 0) {
-    __syncthreads();  // list staged, pad regions written
+  // Rare path: this wave's 32 query rows recomputed exactly in fp32, K and V
+  // read straight from global memory (no LDS, no other wave involved).
+  // Lanes l and l+32 share a query and produce one half of its output each.
+  auto exact_rows = [&]() __attribute__((always_inline)) {
+    constexpr int DH = D / 2;
+    const unsigned char* qr = qbase + (qi < p.L ? qi : p.L - 1) * q_row_bytes;
+    float qv[D];
+#pragma unroll
+    for (int c = 0; c < S::CPR; ++c) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[8 * c + e] = (float)x[e];
+    }
+    float m = -INFINITY, l = 0.f, o[DH];
+#pragma unroll
+    for (int d = 0; d < DH; ++d) o[d] = 0.f;
+    for (int e = e_begin; e < e_end; ++e) {
+      const int ent = p.kv[e];
+      const int kv0 = (ent >> 1) * kBN;
+      for (int kk = 0; kk < kBN; ++kk) {
+        const int key = kv0 + kk;
+        const bool allowed = key < p.L && ((ent & 1) || static_cast<unsigned>(key - lo) < width);
+        if (!allowed) continue;
+        const unsigned char* kr = kbase + static_cast<int64_t>(key) * k_row_bytes;
+        float sdot = 0.f;
+#pragma unroll
+        for (int c = 0; c < S::CPR; ++c) {
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(kr + 16 * c);
+#pragma unroll
+          for (int e8 = 0; e8 < 8; ++e8) sdot = __builtin_fmaf(qv[8 * c + e8], (float)x[e8], sdot);
+        }
+        const float sc2 = sdot * p.scale_log2;
+        const float m_new = fmaxf(m, sc2);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 while m = -inf
+        const float pr = __builtin_amdgcn_exp2f(sc2 - m_new);
+        l = l * alpha + pr;
+        const unsigned char* vr = vbase + static_cast<int64_t>(key) * v_row_bytes + h2 * DH * 2;
+#pragma unroll
+        for (int c = 0; c < DH / 8; ++c) {
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(vr + 16 * c);
+#pragma unroll
+          for (int e8 = 0; e8 < 8; ++e8) o[8 * c + e8] = __builtin_fmaf(o[8 * c + e8], alpha, pr * (float)x[e8]);
+        }
+        m = m_new;
+      }
+    }
+    if (sink_log2 > -INFINITY) {  // the sink adds exp2(s_aux log2 e - m) to the denominator
+      const float m_new = fmaxf(m, sink_log2);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      l = l * alpha + __builtin_amdgcn_exp2f(sink_log2 - m_new);
+#pragma unroll
+      for (int d = 0; d < DH; ++d) o[d] *= alpha;
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    if (qi < p.L) {
+      unsigned char* dst = obase + qi * o_row_bytes + h2 * DH * 2;
+#pragma unroll
+      for (int c = 0; c < DH / 4; ++c) {
+        bf16x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = (__bf16)(o[4 * c + e] * inv);
+        *reinterpret_cast<bf16x4*>(dst + 8 * c) = out;
+      }
+    }
+  };
+
+  // A whole item with the serial loop (running max on every tile).
+  auto serial_pass = [&]() __attribute__((always_inline)) {
+    __syncthreads();  // list staged, pad regions written; previous pass done with LDS
     ent_cur = __builtin_amdgcn_readfirstlane(list_lds[0]);
     issue_tile(ent_cur >> 1, 2 * dma_tensor);
     for (int j = 0; j < n; ++j) serial(j);
-   }
+  };
+  if constexpr (!S::PIPELINED) {
+   if (n > 0) serial_pass();
   } else {
-   if (n > 0) {
+   // One pass over the item's tiles; `safe` selects the pass that tracks the
+   // row max on every tile.
+   auto pass = [&](auto safe) __attribute__((always_inline)) {
     __syncthreads();  // list staged, pad regions written
     ent_cur = __builtin_amdgcn_readfirstlane(list_lds[0]);
     if (dma_tensor == 0) issue_tile(ent_cur >> 1, 0);
-    if (ent_cur & 1) iteration(0, Bool<true>{}, Bool<false>{}, Bool<false>{}, std::integral_constant<int, 0>{}, sB, sA);
-    else iteration(0, Bool<true>{}, Bool<false>{}, Bool<true>{}, std::integral_constant<int, 0>{}, sB, sA);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    if (ent_cur & 1) iteration(0, Bool<true>{}, Bool<false>{}, Bool<false>{}, I0{}, safe, sB, sA);
+    else iteration(0, Bool<true>{}, Bool<false>{}, Bool<true>{}, I0{}, safe, sB, sA);
     int j = 1;
     for (; j + 1 < n; j += 2) {
-      steady(j, std::integral_constant<int, 1>{}, sA, sB);
-      steady(j + 1, std::integral_constant<int, 0>{}, sB, sA);
+      steady(j, I1{}, safe, sA, sB);
+      steady(j + 1, I0{}, safe, sB, sA);
     }
     if (j < n) {  // j = n - 1 (odd)
-      steady(j, std::integral_constant<int, 1>{}, sA, sB);
-      iteration(n, Bool<false>{}, Bool<true>{}, Bool<false>{}, std::integral_constant<int, 0>{}, sB, sA);
+      steady(j, I1{}, safe, sA, sB);
+      iteration(n, Bool<false>{}, Bool<true>{}, Bool<false>{}, I0{}, safe, sB, sA);
     } else {  // j = n (odd)
-      iteration(n, Bool<false>{}, Bool<true>{}, Bool<false>{}, std::integral_constant<int, 1>{}, sA, sB);
+      iteration(n, Bool<false>{}, Bool<true>{}, Bool<false>{}, I1{}, safe, sA, sB);
+    }
+   };
+   if (n > 0) {
+    // Fast pass: the reference is fixed after the first tile, so later tiles
+    // need no row max.  Probabilities relative to it stay far inside the
+    // bf16 / fp32 range unless a later score exceeds it by more than 2^64.
+    // The reference is a score of the row (or its sink) whenever the first
+    // tile allows one of the row's keys, which makes the total at least 1;
+    // a row that starts from the placeholder reference 0 instead can end far
+    // below it.  A wave with a row (inside the sequence) whose row sum is not
+    // finite or above 2^64, or whose total is below 2^-64, recomputes its
+    // rows exactly (exact_rows; no other wave is involved).
+    pass(Bool<false>{});
+    const float lrow = S::PAD_ROWSUM ? low_half(acc[S::DT - 1][8]) : halves_sum(l_run);
+    const bool off_range = !(lrow <= 0x1p64f) || !(lrow + sink_l >= 0x1p-64f);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(qi < p.L && off_range) != 0, 0)) {
+      exact_rows();
+      return;
     }
    }
   }

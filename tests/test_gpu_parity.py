@@ -169,3 +169,61 @@ def test_v_ones_probe_and_determinism():
     assert np.max(np.abs(got - exp)) <= 8e-3
     got2 = _run_gpu(q, k, v, mask, sink)
     assert np.array_equal(got, got2)
+
+
+def _offset_case(seed, H, L, D, first_sign):
+    """Q, K with a shared direction u: the first 64 keys score about first_sign * 40 (log2 units) against
+    every query, all other keys about -first_sign * 40, plus N(0, 1) noise in every element."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    a = np.sqrt(40.0 * np.sqrt(D) / np.log2(np.e))
+    q = rng.standard_normal((1, H, L, D)) + a * u
+    k = rng.standard_normal((1, H, L, D)) - first_sign * a * u
+    k[:, :, :64] += 2 * first_sign * a * u
+    v = rng.standard_normal((1, H, L, D))
+    return tuple(gen.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("D", [64, 80, 128])
+@pytest.mark.parametrize("first_sign", [-1, 1])
+def test_wide_logit_range(D, first_sign):
+    """Scores of later tiles far above (-1) or below (+1) those of the first listed tile: the first case
+    makes the probabilities relative to the first tile's reference overflow the fast pass's bound, so the
+    work-group redoes the item with a running max; the second underflows harmlessly."""
+    L, H = 700, 2
+    q, k, v = _offset_case(31 + D, H, L, D, first_sign)
+    for mask in (dict(kind="full"), dict(kind="window", left=300, right=300)):
+        print(f"[case] wide logit range D={D} sign={first_sign} {mask['kind']}", flush=True)
+        got = _run_gpu(q, k, v, mask, layout="bhld")
+        ref = attention(q, k, v, mask)["out"]
+        _compare(got, ref, f"wide-range-d{D}-{first_sign}-{mask['kind']}")
+
+
+def _far_below_case(seed, H, L, D):
+    """Every score about 200 below zero (log2 units), spread about +-3 by the keys: q = n1 + a u,
+    k = n2 / 2 - a u for one shared unit direction u (the rounding of the large shared part shifts
+    all scores of a row alike, which the softmax ignores)."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    a = np.sqrt(200.0 * np.sqrt(D) / np.log2(np.e))
+    q = rng.standard_normal((1, H, L, D)) + a * u
+    k = 0.5 * rng.standard_normal((1, H, L, D)) - a * u
+    v = rng.standard_normal((1, H, L, D))
+    return tuple(gen.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("D", [64, 80, 128])
+def test_scores_far_below_placeholder_reference(D):
+    """Rows whose first listed tile holds none of their keys start from the placeholder reference 0;
+    with every score about 2^-200 relative to it the probabilities underflow, and the work-group must
+    still return the exact softmax (its rows are recomputed)."""
+    L, H = 700, 2
+    q, k, v = _far_below_case(57 + D, H, L, D)
+    for mask in (dict(kind="window", left=300, right=300), dict(kind="chunk", chunk=100),
+                 dict(kind="window", left=0, right=0, causal=True, head_left=[150, 333])):
+        print(f"[case] far below reference D={D} {mask['kind']}", flush=True)
+        got = _run_gpu(q, k, v, mask, layout="bhld")
+        ref = attention(q, k, v, mask)["out"]
+        _compare(got, ref, f"far-below-d{D}-{mask['kind']}")
