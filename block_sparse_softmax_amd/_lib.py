@@ -191,7 +191,7 @@ class Plan:
         n = ctypes.c_int64()
         it = ctypes.POINTER(ctypes.c_int32)()
         _check(lib.attn_plan_schedule(self._h, ctypes.byref(n), ctypes.byref(it)))
-        return np.ctypeslib.as_array(it, shape=(n.value, 4)).copy() if n.value else np.zeros((0, 4), np.int32)
+        return np.ctypeslib.as_array(it, shape=(n.value, 8)).copy() if n.value else np.zeros((0, 8), np.int32)
 
     def workspace_bytes(self) -> int:
         lib = load_library()

@@ -203,6 +203,10 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p) {
   using S = Shape<D>;
+  constexpr int64_t kSlotFloats = partial_slot_floats(D);
+  constexpr int kSlotM = 4 * S::DT * 16 * 64;  // m of every lane of the 4 waves
+  constexpr int kSlotL = kSlotM + 4 * 64;       // l of every lane
+  static_assert(kSlotL + 4 * 64 == kSlotFloats, "partial slot layout");
   // LDS: K tiles in buffers 0-1, V tiles in buffers 2-3 (row pitch LRB).
   __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * S::TILE];
   __shared__ int list_lds[kListCap];
@@ -218,11 +222,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   const int xcd_chunk = (p.n_items + 7) / 8;
   const int item_idx = p.xcd_chunked ? (blockIdx.x % 8) * xcd_chunk + blockIdx.x / 8 : blockIdx.x;
   if (item_idx >= p.n_items) return;
-  const int4 item = reinterpret_cast<const int4*>(p.items)[item_idx];
+  const int4 item = reinterpret_cast<const int4*>(p.items)[2 * item_idx];
+  const int4 split = reinterpret_cast<const int4*>(p.items)[2 * item_idx + 1];
   const int head = __builtin_amdgcn_readfirstlane(item.x);
+  if (head < 0) return;  // queue padding
   const int qtile = __builtin_amdgcn_readfirstlane(item.y);
   const int e_begin = __builtin_amdgcn_readfirstlane(item.z);
   const int e_end = __builtin_amdgcn_readfirstlane(item.w);
+  // A piece of a split row: its list range is a part of the row's list; the
+  // sink enters piece 0 only.
+  const int slot0 = __builtin_amdgcn_readfirstlane(split.x);
+  const int piece = __builtin_amdgcn_readfirstlane(split.y);
+  const int npieces = __builtin_amdgcn_readfirstlane(split.z);
+  const int counter = __builtin_amdgcn_readfirstlane(split.w);
   const int b = blockIdx.y;
 
   const unsigned char* qbase =
@@ -277,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   // off O^T row 80); sink_l: the sink's term exp2(s_aux log2e - m_run).
   float m_run, l_run, sink_l;
   f32x16 acc[S::DT];
-  const float sink_log2 = p.sink != nullptr ? p.sink[head] * kLog2e : -INFINITY;
+  const float sink_log2 = (p.sink != nullptr && piece == 0) ? p.sink[head] * kLog2e : -INFINITY;
   auto init_state = [&]() __attribute__((always_inline)) {
     m_run = -INFINITY;
     l_run = 0.f;
@@ -722,6 +734,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
 #pragma unroll
       for (int d = 0; d < DH; ++d) o[d] *= alpha;
     }
+    if (npieces > 1) {  // partial state of this piece, in the accumulator layout
+      float* sp = p.partials + static_cast<int64_t>(slot0 + piece) * kSlotFloats;
+#pragma unroll
+      for (int dd = 0; dd < DH; ++dd) {
+        const int d = h2 * DH + dd;
+        const int idx = ((((wave * S::DT + (d >> 5)) * 4 + ((d >> 3) & 3)) * 64) + l31 + 32 * ((d >> 2) & 1)) * 4 + (d & 3);
+        sp[idx] = o[dd];
+      }
+      sp[kSlotM + wave * 64 + lane] = l > 0.f ? m : -INFINITY;
+      sp[kSlotL + wave * 64 + lane] = l;
+      return;
+    }
     const float inv = l > 0.f ? 1.f / l : 0.f;
     if (qi < p.L) {
       unsigned char* dst = obase + qi * o_row_bytes + h2 * DH * 2;
@@ -734,6 +758,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
       }
     }
   };
+  // Whether some listed tile of this item holds an allowed key of this row.
+  auto row_has_key = [&]() __attribute__((always_inline)) {
+    bool has = false;
+    const int hi_row = lo + static_cast<int>(width);
+    for (int e = e_begin; e < e_end; ++e) {
+      const int ent = p.kv[e];
+      const int j0 = (ent >> 1) * kBN;
+      has = has || (ent & 1) || (j0 < hi_row && j0 + kBN > lo);
+    }
+    return has;
+  };
 
   // A whole item with the serial loop (running max on every tile).
   auto serial_pass = [&]() __attribute__((always_inline)) {
@@ -742,6 +777,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     issue_tile(ent_cur >> 1, 2 * dma_tensor);
     for (int j = 0; j < n; ++j) serial(j);
   };
+  bool rows_written = false;  // this wave's rows were finished by the exact path
   if constexpr (!S::PIPELINED) {
    if (n > 0) serial_pass();
   } else {
@@ -775,44 +811,114 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     // tile allows one of the row's keys, which makes the total at least 1;
     // a row that starts from the placeholder reference 0 instead can end far
     // below it.  A wave with a row (inside the sequence) whose row sum is not
-    // finite or above 2^64, or whose total is below 2^-64, recomputes its
-    // rows exactly (exact_rows; no other wave is involved).
+    // finite or above 2^64, or whose total is below 2^-64 although the item
+    // lists one of its keys, recomputes its rows exactly (exact_rows; no
+    // other wave is involved).  A piece of a split row may legitimately hold
+    // none of a row's keys: that row's total is 0 and it is left as is.
     pass(Bool<false>{});
     const float lrow = S::PAD_ROWSUM ? low_half(acc[S::DT - 1][8]) : halves_sum(l_run);
-    const bool off_range = !(lrow <= 0x1p64f) || !(lrow + sink_l >= 0x1p-64f);
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(qi < p.L && off_range) != 0, 0)) {
-      exact_rows();
-      return;
+    const bool off_range = qi < p.L && (!(lrow <= 0x1p64f) || !(lrow + sink_l >= 0x1p-64f));
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(off_range) != 0, 0)) {
+      const bool redo = off_range && (!(lrow <= 0x1p64f) || row_has_key());
+      if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+        exact_rows();
+        rows_written = true;
+      }
     }
    }
   }
 
   // ---- epilogue: O = acc / (row sum + sink term) ----
-  float lsum;
-  if (S::PAD_ROWSUM) {
-    lsum = low_half(acc[S::DT - 1][8]);  // O^T row D (ones row of V^T), held by lanes 0..31
-  } else {
-    lsum = halves_sum(l_run);
+  auto store_o = [&](float inv) __attribute__((always_inline)) {
+    if (qi < p.L) {
+      unsigned char* dst = obase + qi * o_row_bytes;
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * dt + 8 * g + 4 * h2;
+          if (S::PAD_ROWSUM && 32 * dt + 8 * g >= D) continue;
+          bf16x4 out;
+          out[0] = (__bf16)(acc[dt][4 * g + 0] * inv);
+          out[1] = (__bf16)(acc[dt][4 * g + 1] * inv);
+          out[2] = (__bf16)(acc[dt][4 * g + 2] * inv);
+          out[3] = (__bf16)(acc[dt][4 * g + 3] * inv);
+          *reinterpret_cast<bf16x4*>(dst + d * 2) = out;
+        }
+      }
+    }
+  };
+  float ltot = 0.f;
+  if (!rows_written) {
+    const float lsum = S::PAD_ROWSUM ? low_half(acc[S::DT - 1][8])  // O^T row D (ones row of V^T), lanes 0..31
+                                     : halves_sum(l_run);
+    ltot = lsum + sink_l;
   }
-  const float ltot = lsum + sink_l;
-  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-  if (qi < p.L) {
-    unsigned char* dst = obase + qi * o_row_bytes;
+  if (npieces == 1) {
+    if (!rows_written) store_o(ltot > 0.f ? 1.f / ltot : 0.f);
+    return;
+  }
+
+  // ---- a piece of a split row: leave the partial state, the last piece merges ----
+  // Slot layout (per wave): acc as float4 [DT][4][64 lanes], then m and l per lane.
+  float* slots = p.partials + static_cast<int64_t>(slot0) * kSlotFloats;
+  if (!rows_written) {
+    float* sp = slots + static_cast<int64_t>(piece) * kSlotFloats;
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d = 32 * dt + 8 * g + 4 * h2;
-        if (S::PAD_ROWSUM && 32 * dt + 8 * g >= D) continue;
-        bf16x4 out;
-        out[0] = (__bf16)(acc[dt][4 * g + 0] * inv);
-        out[1] = (__bf16)(acc[dt][4 * g + 1] * inv);
-        out[2] = (__bf16)(acc[dt][4 * g + 2] * inv);
-        out[3] = (__bf16)(acc[dt][4 * g + 3] * inv);
-        *reinterpret_cast<bf16x4*>(dst + d * 2) = out;
+        const float4 a = make_float4(acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]);
+        *reinterpret_cast<float4*>(sp + (((wave * S::DT + dt) * 4 + g) * 64 + lane) * 4) = a;
+      }
+    }
+    sp[kSlotM + wave * 64 + lane] = ltot > 0.f ? ref_of() : -INFINITY;
+    sp[kSlotL + wave * 64 + lane] = ltot;
+  }
+  // Publication: every wave's stores are ordered before the barrier
+  // (work-group scope); thread 0 then releases them at device scope (one
+  // write-back of the XCD's L2) and counts the piece.  The piece that counts
+  // last acquires at device scope (one invalidation), so after the second
+  // barrier its waves read every piece's state.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int* cnt = p.counters + counter;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int done = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = done == npieces - 1;
+    if (last) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next launch
+    }
+    list_lds[0] = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (list_lds[0] == 0) return;
+  // Merge in piece order (fixed, whichever piece finishes last).
+  float mmax = -INFINITY;
+  for (int i = 0; i < npieces; ++i) mmax = fmaxf(mmax, slots[static_cast<int64_t>(i) * kSlotFloats + kSlotM + wave * 64 + lane]);
+#pragma unroll
+  for (int dt = 0; dt < S::DT; ++dt) acc[dt] = f32x16{};
+  float lm = 0.f;
+  for (int i = 0; i < npieces; ++i) {
+    const float* sp = slots + static_cast<int64_t>(i) * kSlotFloats;
+    const float mi = sp[kSlotM + wave * 64 + lane];
+    const float w = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - mmax);
+    lm = __builtin_fmaf(w, sp[kSlotL + wave * 64 + lane], lm);
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 a = *reinterpret_cast<const float4*>(sp + (((wave * S::DT + dt) * 4 + g) * 64 + lane) * 4);
+        acc[dt][4 * g + 0] = __builtin_fmaf(w, a.x, acc[dt][4 * g + 0]);
+        acc[dt][4 * g + 1] = __builtin_fmaf(w, a.y, acc[dt][4 * g + 1]);
+        acc[dt][4 * g + 2] = __builtin_fmaf(w, a.z, acc[dt][4 * g + 2]);
+        acc[dt][4 * g + 3] = __builtin_fmaf(w, a.w, acc[dt][4 * g + 3]);
       }
     }
   }
+  store_o(lm > 0.f ? 1.f / lm : 0.f);
 }
 
 template <int D>

@@ -75,10 +75,17 @@ attn_status launch_with_plan(const attn_plan& p, const attn_tensor* q, const att
     set_error("block size must be a multiple of 128 for the GPU kernel");
     return ATTN_E_UNSUPPORTED;
   }
-  if (!launch->workspace || launch->workspace_bytes < p.layout.bytes) {
-    set_error("workspace smaller than attn_plan_workspace_bytes (" + std::to_string(p.layout.bytes) +
+  // batch 1 runs the split schedule, whose partial states follow the image
+  const bool split = (B == 1);
+  const size_t need = split ? p.layout.total : p.layout.bytes;
+  if (!launch->workspace || launch->workspace_bytes < need) {
+    set_error("workspace smaller than attn_plan_workspace_bytes (" + std::to_string(p.layout.total) +
               " bytes)");
     return ATTN_E_WORKSPACE;
+  }
+  if ((split ? p.items.size() : p.items_unsplit.size()) > static_cast<size_t>(INT32_MAX)) {
+    set_error("too many work items");
+    return ATTN_E_UNSUPPORTED;
   }
   if (!aligned16(launch->workspace)) { set_error("workspace must be 16-byte aligned"); return ATTN_E_INVAL; }
 
@@ -92,7 +99,9 @@ attn_status launch_with_plan(const attn_plan& p, const attn_tensor* q, const att
   f.k_sb = k->stride_b; f.k_sl = k->stride_l; f.k_sh = k->stride_h;
   f.v_sb = v->stride_b; f.v_sl = v->stride_l; f.v_sh = v->stride_h;
   f.o_sb = o->stride_b; f.o_sl = o->stride_l; f.o_sh = o->stride_h;
-  f.items = reinterpret_cast<const int32_t*>(ws + p.layout.off_items);
+  f.items = reinterpret_cast<const int32_t*>(ws + (split ? p.layout.off_items : p.layout.off_items_unsplit));
+  f.partials = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + p.layout.off_partials);
+  f.counters = reinterpret_cast<int32_t*>(const_cast<uint8_t*>(ws) + p.layout.off_counters);
   f.kv = reinterpret_cast<const int32_t*>(ws + p.layout.off_kv);
   f.head_left = reinterpret_cast<const int32_t*>(ws + p.layout.off_head_left);
   f.block_bits = reinterpret_cast<const uint32_t*>(ws + p.layout.off_bits);
@@ -102,7 +111,7 @@ attn_status launch_with_plan(const attn_plan& p, const attn_tensor* q, const att
   f.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
   f.L = static_cast<int32_t>(p.L);
   f.H = static_cast<int32_t>(p.H);
-  f.n_items = static_cast<int32_t>(p.items.size());
+  f.n_items = static_cast<int32_t>(split ? p.items.size() : p.items_unsplit.size());
   f.kind = p.kind;
   f.causal = p.causal;
   f.chunk = static_cast<int32_t>(std::min<int64_t>(p.chunk, p.L));
@@ -218,7 +227,7 @@ attn_status attn_plan_schedule(const attn_plan* p, int64_t* n_items, const int32
 
 attn_status attn_plan_workspace_bytes(const attn_plan* p, size_t* bytes) {
   if (!p || !bytes) { set_error("plan or bytes is NULL"); return ATTN_E_INVAL; }
-  *bytes = p->layout.bytes;
+  *bytes = p->layout.total;
   return ATTN_OK;
 }
 
@@ -251,7 +260,7 @@ attn_status attn_workspace_bytes(const attn_mask_desc* mask, int64_t L, int64_t 
     const attn_plan* p = nullptr;
     attn_status st = cached_plan(mask, L, H, D, &p);
     if (st != ATTN_OK) return st;
-    *bytes = p->layout.bytes;
+    *bytes = p->layout.total;
     return ATTN_OK;
   } catch (...) {
     set_error("unexpected exception");

@@ -13,6 +13,8 @@
 
 #include "plan.hpp"
 
+#include "kernels.hpp"
+
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -193,36 +195,120 @@ void compile_blocks(attn_plan& p) {
   }
 }
 
-// Work order: heads by descending total cost, and inside a head the query
-// tiles by descending cost, so that long items start first while work items
-// that run at the same time share one head's keys and values in cache.
+// Work schedule.
+//
+// Cost of a (head, query tile) row: its listed tiles (a PARTIAL tile counts
+// 1.25 for the masking) plus 0.5 for the Q load and the epilogue.  Rows much
+// longer than the launch's fair share T = max(total / kSlots, kMinPiece) are
+// cut into pieces of about T tiles (batch 1 only), so that a causal or
+// per-head-window launch with about as many rows as resident work-groups is
+// not held up by its longest rows.  Items are then laid out as kXcds queues:
+// heads in descending cost, rows of a head in descending cost, and the
+// sequence cut into kXcds consecutive runs of equal total cost (so the work
+// that shares an XCD's L2 comes from as few heads as possible).  A queue
+// short enough to run in a few rounds of its work-groups is ordered by
+// descending cost instead (longest first).  Queues are padded to equal length
+// with null items.
+constexpr double kMinPiece = 12.0;     // tiles: below this a piece's merge costs more than it saves
+constexpr double kPieceOverhead = 2.0; // tiles: writing the partial state and the merge
+constexpr int kMaxPieces = 16;
+
+std::vector<Item> layout_queues(const std::vector<int64_t>& head_order, const std::vector<Item>& all,
+                                const std::vector<double>& icost) {
+  // items of each head, in descending cost (stable: query tile, then piece)
+  int64_t H = static_cast<int64_t>(head_order.size());
+  std::vector<std::vector<int64_t>> by_head(H);
+  for (size_t i = 0; i < all.size(); ++i) by_head[all[i].head].push_back(static_cast<int64_t>(i));
+  std::vector<int64_t> seq;
+  seq.reserve(all.size());
+  for (int64_t h : head_order) {
+    auto& v = by_head[h];
+    std::stable_sort(v.begin(), v.end(), [&](int64_t a, int64_t b) { return icost[a] > icost[b]; });
+    seq.insert(seq.end(), v.begin(), v.end());
+  }
+  double total = 0.0;
+  for (int64_t i : seq) total += icost[i];
+  std::vector<std::vector<int64_t>> q(kXcds);
+  double cum = 0.0;
+  for (int64_t i : seq) {
+    const double mid = cum + 0.5 * icost[i];
+    int x = total > 0.0 ? static_cast<int>(mid / total * kXcds) : 0;
+    x = std::min(std::max(x, 0), kXcds - 1);
+    q[x].push_back(i);
+    cum += icost[i];
+  }
+  size_t len = 0;
+  for (auto& v : q) {
+    if (v.size() <= static_cast<size_t>(4 * kSlots / kXcds))
+      std::stable_sort(v.begin(), v.end(), [&](int64_t a, int64_t b) { return icost[a] > icost[b]; });
+    len = std::max(len, v.size());
+  }
+  std::vector<Item> out;
+  out.reserve(len * kXcds);
+  const Item null_item{-1, 0, 0, 0, 0, 0, 1, 0};
+  for (auto& v : q) {
+    for (int64_t i : v) out.push_back(all[i]);
+    out.insert(out.end(), len - v.size(), null_item);
+  }
+  return out;
+}
+
 void schedule(attn_plan& p) {
   const int64_t rows = p.H * p.nq;
   std::vector<double> cost(rows);
   std::vector<double> head_cost(p.H, 0.0);
+  double total = 0.0;
   for (int64_t r = 0; r < rows; ++r) {
     double c = 0.5;  // Q load and epilogue
     for (int32_t e = p.row_ptr[r]; e < p.row_ptr[r + 1]; ++e) c += p.flags[e] ? 1.0 : 1.25;
     cost[r] = c;
     head_cost[r / p.nq] += c;
+    total += c;
   }
   std::vector<int64_t> heads(p.H);
   std::iota(heads.begin(), heads.end(), 0);
   std::stable_sort(heads.begin(), heads.end(),
                    [&](int64_t a, int64_t b) { return head_cost[a] > head_cost[b]; });
-  p.items.clear();
-  p.items.reserve(rows);
-  std::vector<int64_t> qts(p.nq);
-  for (int64_t h : heads) {
-    std::iota(qts.begin(), qts.end(), 0);
-    std::stable_sort(qts.begin(), qts.end(),
-                     [&](int64_t a, int64_t b) { return cost[h * p.nq + a] > cost[h * p.nq + b]; });
-    for (int64_t qt : qts) {
-      const int64_t r = h * p.nq + qt;
-      p.items.push_back(Item{static_cast<int32_t>(h), static_cast<int32_t>(qt), p.row_ptr[r],
-                             p.row_ptr[r + 1]});
+
+  // unsplit schedule (batch > 1)
+  std::vector<Item> whole(rows);
+  for (int64_t r = 0; r < rows; ++r)
+    whole[r] = Item{static_cast<int32_t>(r / p.nq), static_cast<int32_t>(r % p.nq), p.row_ptr[r],
+                    p.row_ptr[r + 1], 0, 0, 1, 0};
+  p.items_unsplit = layout_queues(heads, whole, cost);
+
+  // batch-1 schedule: long rows cut into pieces
+  const double share = std::max(total / kSlots, kMinPiece);
+  std::vector<Item> all;
+  std::vector<double> icost;
+  all.reserve(rows);
+  icost.reserve(rows);
+  int64_t slots = 0, groups = 0;
+  for (int64_t r = 0; r < rows; ++r) {
+    const int32_t b = p.row_ptr[r], e = p.row_ptr[r + 1], n = e - b;
+    int np = 1;
+    if (cost[r] > 1.25 * share)
+      np = static_cast<int>(std::min<double>({std::ceil(cost[r] / share), double(kMaxPieces), double(n)}));
+    if (np <= 1) {
+      all.push_back(whole[r]);
+      icost.push_back(cost[r]);
+      continue;
     }
+    for (int k = 0; k < np; ++k) {
+      const int32_t pb = b + static_cast<int32_t>(int64_t(n) * k / np);
+      const int32_t pe = b + static_cast<int32_t>(int64_t(n) * (k + 1) / np);
+      double c = 0.5 + kPieceOverhead;
+      for (int32_t x = pb; x < pe; ++x) c += p.flags[x] ? 1.0 : 1.25;
+      all.push_back(Item{whole[r].head, whole[r].qtile, pb, pe, static_cast<int32_t>(slots), k, np,
+                         static_cast<int32_t>(groups)});
+      icost.push_back(c);
+    }
+    slots += np;
+    groups += 1;
   }
+  p.n_partial_slots = slots;
+  p.n_counters = groups;
+  p.items = layout_queues(heads, all, icost);
 }
 
 void build_image(attn_plan& p) {
@@ -243,10 +329,15 @@ void build_image(attn_plan& p) {
   }
   ImageLayout& l = p.layout;
   l.off_items = 0;
-  l.off_kv = align_up(l.off_items + p.items.size() * sizeof(Item));
+  l.off_items_unsplit = align_up(l.off_items + p.items.size() * sizeof(Item));
+  l.off_kv = align_up(l.off_items_unsplit + p.items_unsplit.size() * sizeof(Item));
   l.off_head_left = align_up(l.off_kv + std::max<size_t>(1, p.kv_entries.size()) * sizeof(int32_t));
   l.off_bits = align_up(l.off_head_left + p.head_left32.size() * sizeof(int32_t));
-  l.bytes = align_up(l.off_bits + p.block_bits.size() * sizeof(uint32_t));
+  l.off_counters = align_up(l.off_bits + p.block_bits.size() * sizeof(uint32_t));
+  l.bytes = align_up(l.off_counters + p.n_counters * sizeof(int32_t));
+  l.off_partials = l.bytes;
+  l.total = align_up(l.off_partials + static_cast<size_t>(p.n_partial_slots) *
+                                          static_cast<size_t>(partial_slot_floats(p.D)) * sizeof(float));
 }
 
 }  // namespace
@@ -325,6 +416,7 @@ attn_status compile_plan(const attn_mask_desc* m, int64_t L, int64_t H, int64_t 
 void write_image(const attn_plan& p, uint8_t* dst) {
   std::memset(dst, 0, p.layout.bytes);
   std::memcpy(dst + p.layout.off_items, p.items.data(), p.items.size() * sizeof(Item));
+  std::memcpy(dst + p.layout.off_items_unsplit, p.items_unsplit.data(), p.items_unsplit.size() * sizeof(Item));
   std::memcpy(dst + p.layout.off_kv, p.kv_entries.data(), p.kv_entries.size() * sizeof(int32_t));
   std::memcpy(dst + p.layout.off_head_left, p.head_left32.data(), p.head_left32.size() * sizeof(int32_t));
   if (!p.block_bits.empty())

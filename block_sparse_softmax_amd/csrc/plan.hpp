@@ -20,15 +20,26 @@ namespace bss {
 
 constexpr int kBM = 128;  // query rows per work item (4 waves x 32 rows)
 constexpr int kBN = 64;   // keys per KV tile
+constexpr int kXcds = 8;  // MI355X: 8 accelerator dies, each with its own L2
+constexpr int kSlots = 512;  // resident work-groups: 256 CUs x 2
 
-// Device record of one work item (16 bytes).
+// Device record of one work item (32 bytes).  A (head, query tile) row whose
+// list is long compared with the whole launch is cut into `npieces`
+// contiguous pieces of its list; each piece leaves its partial softmax state
+// in partial slot `slot + piece`, and the last piece to finish (counted on
+// counters[counter]) merges them.  Unsplit items have npieces = 1.  Items
+// with head = -1 pad the per-XCD queues to equal length and do nothing.
 struct Item {
   int32_t head, qtile, begin, end;
+  int32_t slot, piece, npieces, counter;
 };
 
-// Layout of the plan's device image inside the caller's workspace.
+// Layout of the plan's device image inside the caller's workspace, followed
+// by the partial-state slots of split items (not part of the image).
 struct ImageLayout {
-  size_t off_items = 0, off_kv = 0, off_head_left = 0, off_bits = 0, bytes = 0;
+  size_t off_items = 0, off_items_unsplit = 0, off_kv = 0, off_head_left = 0, off_bits = 0,
+         off_counters = 0, bytes = 0;
+  size_t off_partials = 0, total = 0;
 };
 
 void set_error(const std::string& msg);
@@ -55,8 +66,11 @@ struct attn_plan {
   std::vector<int64_t> pairs;         // allowed pairs per head
   int64_t pairs_total = 0;
 
-  // schedule and device image
-  std::vector<bss::Item> items;
+  // schedule and device image: `items` (batch 1, long rows split) and
+  // `items_unsplit` (batch > 1: every row one item), each laid out as
+  // kXcds equal-length queues
+  std::vector<bss::Item> items, items_unsplit;
+  int64_t n_partial_slots = 0, n_counters = 0;
   std::vector<int32_t> kv_entries;    // (kv_tile << 1) | full, in canonical order
   std::vector<int32_t> head_left32;   // [H]
   std::vector<uint32_t> block_bits;   // [Hb][Nb][ceil(Nb/32)] when not block_aligned

@@ -142,17 +142,31 @@ attn_status attn_plan_tiles(const attn_plan* plan, int32_t* bm, int32_t* bn, int
 attn_status attn_plan_pairs(const attn_plan* plan, int64_t* pairs_per_head, int64_t* total);
 
 /*
- * Work schedule: n_items records of 4 int32 {head, query tile, first list
- * entry, one past the last list entry}, in the order the grid consumes them.
- * Every (head, query tile) row appears exactly once (empty rows too: they
- * write zeros).  Host view owned by the plan.
+ * Work schedule of a batch-1 launch: n_items records of 8 int32 {head, query
+ * tile, first list entry, one past the last list entry, partial slot, piece,
+ * pieces, counter}, laid out as 8 equal-length queues (queue x = records
+ * [x n_items/8, (x+1) n_items/8), run by the work-groups of XCD x in order).
+ * Every (head, query tile) row is covered once: by one record (pieces = 1;
+ * empty rows too: they write zeros) or, when its list is long compared with
+ * the launch, by `pieces` records that cut the list into consecutive ranges;
+ * each piece leaves its partial softmax state in partial slot (slot + piece)
+ * of the workspace and the last piece to finish merges them in piece order.
+ * Records with head = -1 pad the queues.  Launches with batch > 1 run an
+ * unsplit schedule of the same layout.  Host view owned by the plan.
  */
 attn_status attn_plan_schedule(const attn_plan* plan, int64_t* n_items, const int32_t** items);
 
-/* Device bytes the plan's image needs in the workspace. */
+/*
+ * Device bytes a launch needs in the workspace: the plan's image (tile lists,
+ * schedules, per-row piece counters) followed, for batch-1 launches, by the
+ * partial states of split rows.  Launches that share a workspace must not
+ * overlap in time (the counters and partial states are per launch; launches
+ * on one stream are ordered); every completed launch leaves the counters at
+ * zero, as the upload does.
+ */
 attn_status attn_plan_workspace_bytes(const attn_plan* plan, size_t* bytes);
 
-/* Copy the plan's device image into `workspace` on `stream` (asynchronous). */
+/* Copy the plan's device image into `workspace` on `stream` (returns once copied). */
 attn_status attn_plan_upload(const attn_plan* plan, void* workspace, size_t workspace_bytes,
                              void* stream);
 

@@ -227,3 +227,30 @@ def test_scores_far_below_placeholder_reference(D):
         got = _run_gpu(q, k, v, mask, layout="bhld")
         ref = attention(q, k, v, mask)["out"]
         _compare(got, ref, f"far-below-d{D}-{mask['kind']}")
+
+
+SPLIT = [
+    # (mask, L, sink): rows long enough that the batch-1 schedule cuts them into pieces
+    (dict(kind="chunk", chunk=1000), 3000, False),    # pieces with rows that see none of their keys
+    (dict(kind="full", causal=True), 2500, True),
+    (dict(kind="window", left=700, right=50), 2200, True),
+]
+
+
+@pytest.mark.parametrize("D", [64, 80, 128])
+@pytest.mark.parametrize("ci", range(len(SPLIT)))
+def test_split_rows_merge(D, ci):
+    """Long rows split into pieces whose partial states the last piece merges (batch 1)."""
+    from block_sparse_softmax_amd import _lib
+    mask, L, with_sink = SPLIT[ci]
+    H = 2
+    items = _lib.Plan(mask, L, H, D).schedule()
+    assert np.any(items[:, 6] > 1), "the schedule should split some rows"
+    print(f"[case] split rows {mask['kind']} L={L} D={D} sink={with_sink}", flush=True)
+    q, k, v = _random_case(300 + ci, 1, H, L, D)
+    sink = np.random.default_rng(400 + ci).standard_normal(H).astype(np.float32) if with_sink else None
+    got = _run_gpu(q, k, v, mask, sink)
+    ref = attention(q, k, v, mask, sink=sink)["out"]
+    _compare(got, ref, f"split-{ci}-d{D}")
+    got2 = _run_gpu(q, k, v, mask, sink)   # counters returned to zero: the same result again
+    assert np.array_equal(got, got2)

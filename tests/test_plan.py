@@ -141,23 +141,53 @@ def test_blocksparse_128k_tile_lists(lib):
     assert int(kept[0]) == 263679
 
 
+def _schedule_cost(flags, b, e):
+    return float(np.sum(np.where(flags[b:e] == 1, 1.0, 1.25)))
+
+
 def test_schedule_covers_every_row_once(lib):
-    for name in ("vit896", "lm_headwin"):
+    """The batch-1 schedule: 8 equal-length XCD queues (padding items have head -1); every (head, query
+    tile) row's list is covered exactly once, by one item or by pieces that cut it into contiguous ranges
+    in piece order; split rows own distinct partial slots and counters; the queues carry equal cost."""
+    split_seen = {}
+    for name in ("vit896", "vit1792", "lm_headwin"):
         w = workload(name)
-        for mask in w["masks"].values():
+        for label, mask in w["masks"].items():
             plan = _lib.Plan(mask, w["L"], w["H"], w["D"])
             bm, bn, rp, kv, fl = plan.tiles()
             items = plan.schedule()
             nq = -(-w["L"] // bm)
-            assert items.shape == (w["H"] * nq, 4)
-            rows = items[:, 0] * nq + items[:, 1]
-            assert np.array_equal(np.sort(rows), np.arange(w["H"] * nq))
-            assert np.array_equal(items[:, 2], rp[rows]) and np.array_equal(items[:, 3], rp[rows + 1])
-            # heads with more work come first; inside a head, longer lists first
-            cost = (items[:, 3] - items[:, 2]).astype(float)
-            for h in np.unique(items[:, 0]):
-                c = cost[items[:, 0] == h]
-                assert np.all(np.diff(c) <= 0)
+            assert items.shape[1] == 8 and items.shape[0] % 8 == 0
+            real = items[items[:, 0] >= 0]
+            assert np.all(items[items[:, 0] < 0][:, 3] == items[items[:, 0] < 0][:, 2])
+            rows = real[:, 0] * nq + real[:, 1]
+            assert np.array_equal(np.unique(rows), np.arange(w["H"] * nq))
+            slots, counters = [], []
+            for r in np.unique(rows):
+                its = real[rows == r]
+                its = its[np.argsort(its[:, 5])]
+                npc = its[0, 6]
+                assert len(its) == npc and np.all(its[:, 6] == npc) and np.array_equal(its[:, 5], np.arange(npc))
+                assert its[0, 2] == rp[r] and its[-1, 3] == rp[r + 1]
+                assert np.all(its[1:, 2] == its[:-1, 3]) and np.all(its[:, 3] > its[:, 2] - (npc == 1))
+                if npc > 1:
+                    assert np.all(its[:, 4] == its[0, 4]) and np.all(its[:, 7] == its[0, 7])
+                    slots.extend(its[0, 4] + np.arange(npc))
+                    counters.append(its[0, 7])
+            assert len(set(slots)) == len(slots) and len(set(counters)) == len(counters)
+            if slots:
+                assert sorted(slots) == list(range(len(slots))) and sorted(counters) == list(range(len(counters)))
+            split_seen[(name, label)] = len(counters)
+            # per-XCD queues of equal total cost (within one item's cost)
+            q = items.reshape(8, -1, 8)
+            cost = np.array([[0.0 if it[0] < 0 else 0.5 + _schedule_cost(fl, it[2], it[3]) + (2.0 if it[6] > 1 else 0.0)
+                              for it in qq] for qq in q])
+            tot = cost.sum(axis=1)
+            assert tot.max() - tot.min() <= 2 * cost.max() + 1e-9, (name, label, tot)
+    # uniform ViT masks are never split; the causal per-head windows are
+    assert split_seen[("vit896", "full")] == 0 and split_seen[("vit1792", "full")] == 0
+    assert split_seen[("vit1792", "swa512")] == 0
+    assert split_seen[("lm_headwin", "headwin")] > 0
 
 
 def _status(lib, mask, L, H, D):
