@@ -450,7 +450,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   // so the hand-over needs no copies and buffer offsets are immediates.
   f32x16 sA[2], sB[2];
   int list_base = 0;
-  int ent_cur = 0;  // list entry (kv_tile << 1 | full) of tile j
+  // List entries (kv_tile << 1 | full) of tiles j and j+1.  Entry j+2 is read
+  // from LDS during iteration j and moved to a scalar register only at its
+  // end, so the DMA address of the next tile never waits on an LDS read.
+  int ent_cur = 0, ent_nxt = 0;
+  // Read list entry i (i < n) from the staged list; crossing into the next
+  // staged chunk restages it (every wave is past the barrier of this
+  // iteration, so no entry of the old chunk is still to be read).
+  auto list_entry = [&](int i) __attribute__((always_inline)) {
+    if (i - list_base == kListCap) {
+      list_base += kListCap;
+      stage_list(list_base);
+      __syncthreads();
+    }
+    return list_lds[i - list_base];
+  };
   const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   // sc: scores of tile j-1 (read); sn: scores of tile j (written).
@@ -467,24 +481,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     constexpr int NP = 4 * S::DT;  // PV MFMAs
     wait_vmcnt<0>();   // this wave's share of K tile j / V tile j-1
     wg_barrier();      // ... and everyone else's
-    const int ent = __builtin_amdgcn_readfirstlane(ent_cur);
+    constexpr int kb = kPar, vb = 2 + (kPar ^ 1);
+    // the first K fragments of tile j go out before the DMA instructions
+    // (whose memory clobber would otherwise hold them back)
+    bf16x8 ka[NQ + 2];
+    if constexpr (kCur) {
+      ka[0] = kfrag(kb, 0, 0);
+      ka[1] = kfrag(kb, 0, 1);
+    }
+    const int ent = ent_cur, ent1 = ent_nxt;
     if (j + 1 < n) {
-      if (j + 1 - list_base == kListCap) {  // next chunk of the list
-        list_base += kListCap;
-        stage_list(list_base);
-        __syncthreads();
-      }
-      ent_cur = __builtin_amdgcn_readfirstlane(list_lds[j + 1 - list_base]);
-      if (dma_tensor == 0) issue_tile(ent_cur >> 1, kPar ^ 1);
+      if (dma_tensor == 0) issue_tile(ent1 >> 1, kPar ^ 1);
     }
     if constexpr (kCur) {
       if (dma_tensor == 1) issue_tile(ent >> 1, 2 + kPar);
     }
+    const int raw2 = (j + 2 < n) ? list_entry(j + 2) : 0;
     if constexpr (D == 128) {
       opaque(kbase_off);
       opaque(vbase_off);
     }
-    constexpr int kb = kPar, vb = 2 + (kPar ^ 1);
 
     // exponentials of tile j-1: pair i (0..7) of key block h -> P^T elements
     bf16x8 pb[4];
@@ -514,11 +530,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     auto q_half = [](int q) __attribute__((always_inline)) { return q % 2; };
 
     // ---- part 1 ----
-    bf16x8 ka[NQ + 2];
-    if constexpr (kCur) {
-      ka[0] = kfrag(kb, q_ks(0), q_half(0));
-      ka[1] = kfrag(kb, q_ks(1), q_half(1));
-    }
     bf16x8 va[NP + 2];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
@@ -588,10 +599,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
         set_seed();
       }
     }
+    ent_cur = ent1;
+    ent_nxt = __builtin_amdgcn_readfirstlane(raw2);
   };
   // steady-state iteration: the FULL / PARTIAL variant of tile j
   auto steady = [&](int j, auto par_tag, auto safe_tag, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
-    if (__builtin_amdgcn_readfirstlane(ent_cur) & 1)
+    if (ent_cur & 1)
       iteration(j, Bool<true>{}, Bool<true>{}, Bool<false>{}, par_tag, safe_tag, sc, sn);
     else
       iteration(j, Bool<true>{}, Bool<true>{}, Bool<true>{}, par_tag, safe_tag, sc, sn);
@@ -609,26 +622,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     constexpr int NP = 4 * S::DT;
     wait_vmcnt<0>();   // this wave's share of tile j
     wg_barrier();      // ... and everyone else's; buffers of tile j-1 are free
-    const int ent = __builtin_amdgcn_readfirstlane(ent_cur);
-    if (j + 1 < n) {
-      if (j + 1 - list_base == kListCap) {  // next chunk of the list
-        list_base += kListCap;
-        stage_list(list_base);
-        __syncthreads();
-      }
-      ent_cur = __builtin_amdgcn_readfirstlane(list_lds[j + 1 - list_base]);
-      issue_tile(ent_cur >> 1, 2 * dma_tensor + (kPar ^ 1));
-    }
     if constexpr (D == 128) {
       opaque(kbase_off);
       opaque(vbase_off);
     }
+    // the first K fragments go out before the DMA instructions
+    const bf16x8 k00 = kfrag(kPar, 0, 0), k01 = kfrag(kPar, 0, 1);
+    const int ent = ent_cur, ent1 = ent_nxt;
+    if (j + 1 < n) issue_tile(ent1 >> 1, 2 * dma_tensor + (kPar ^ 1));
+    const int raw2 = (j + 2 < n) ? list_entry(j + 2) : 0;
     // S^T of tile j relative to the reference (seeded C operand)
     f32x16 sn[2];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int ks = q / 2, half = q % 2;
-      sn[half] = mfma32(kfrag(kPar, ks, half), qf[ks], ks == 0 ? seedv : sn[half]);
+      const bf16x8 kf = q == 0 ? k00 : q == 1 ? k01 : kfrag(kPar, ks, half);
+      sn[half] = mfma32(kf, qf[ks], ks == 0 ? seedv : sn[half]);
     }
     if (!(ent & 1)) {  // PARTIAL tile
       const unsigned mbase = static_cast<unsigned>((ent >> 1) * kBN + 4 * h2 - lo);
@@ -679,6 +688,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
       const int t = pidx / S::DT, dt = pidx % S::DT;
       acc[dt] = mfma32(vfrag(2 + kPar, pidx), pb[t], acc[dt]);
     }
+    ent_cur = ent1;
+    ent_nxt = __builtin_amdgcn_readfirstlane(raw2);
   };
 
   // Rare path: this wave's 32 query rows recomputed exactly in fp32, K and V
@@ -774,6 +785,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   auto serial_pass = [&]() __attribute__((always_inline)) {
     __syncthreads();  // list staged, pad regions written; previous pass done with LDS
     ent_cur = __builtin_amdgcn_readfirstlane(list_lds[0]);
+    ent_nxt = n > 1 ? __builtin_amdgcn_readfirstlane(list_lds[1]) : 0;
     issue_tile(ent_cur >> 1, 2 * dma_tensor);
     for (int j = 0; j < n; ++j) serial(j);
   };
@@ -786,6 +798,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
    auto pass = [&](auto safe) __attribute__((always_inline)) {
     __syncthreads();  // list staged, pad regions written
     ent_cur = __builtin_amdgcn_readfirstlane(list_lds[0]);
+    ent_nxt = n > 1 ? __builtin_amdgcn_readfirstlane(list_lds[1]) : 0;
     if (dma_tensor == 0) issue_tile(ent_cur >> 1, 0);
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;

@@ -205,10 +205,12 @@ void compile_blocks(attn_plan& p) {
 // not held up by its longest rows.  Items are then laid out as kXcds queues:
 // heads in descending cost, rows of a head in descending cost, and the
 // sequence cut into kXcds consecutive runs of equal total cost (so the work
-// that shares an XCD's L2 comes from as few heads as possible).  A queue
-// short enough to run in a few rounds of its work-groups is ordered by
-// descending cost instead (longest first).  Queues are padded to equal length
-// with null items.
+// that shares an XCD's L2 comes from as few heads as possible; measured
+// better than dealing a head's rows to all XCDs for the 16K-token windows and
+// the 128K-token block masks).  A queue short enough to run in a few rounds of
+// its work-groups is ordered by descending cost.  A launch of at most two
+// rounds is dealt longest-first to the least-loaded queue instead.  Queues are
+// padded to equal length with null items.
 constexpr double kMinPiece = 12.0;     // tiles: below this a piece's merge costs more than it saves
 constexpr double kPieceOverhead = 2.0; // tiles: writing the partial state and the merge
 constexpr int kMaxPieces = 16;
@@ -226,16 +228,30 @@ std::vector<Item> layout_queues(const std::vector<int64_t>& head_order, const st
     std::stable_sort(v.begin(), v.end(), [&](int64_t a, int64_t b) { return icost[a] > icost[b]; });
     seq.insert(seq.end(), v.begin(), v.end());
   }
-  double total = 0.0;
-  for (int64_t i : seq) total += icost[i];
   std::vector<std::vector<int64_t>> q(kXcds);
-  double cum = 0.0;
-  for (int64_t i : seq) {
-    const double mid = cum + 0.5 * icost[i];
-    int x = total > 0.0 ? static_cast<int>(mid / total * kXcds) : 0;
-    x = std::min(std::max(x, 0), kXcds - 1);
-    q[x].push_back(i);
-    cum += icost[i];
+  if (seq.size() <= static_cast<size_t>(2 * kSlots)) {
+    // at most two rounds of work-groups: longest first over all queues (LPT)
+    std::stable_sort(seq.begin(), seq.end(), [&](int64_t a, int64_t b) { return icost[a] > icost[b]; });
+    std::vector<double> load(kXcds, 0.0);
+    for (int64_t i : seq) {
+      int x = 0;
+      for (int y = 1; y < kXcds; ++y)
+        if (load[y] < load[x]) x = y;
+      q[x].push_back(i);
+      load[x] += icost[i];
+    }
+  } else {
+    // consecutive runs of equal cost: an XCD works through few heads at a time
+    double total = 0.0;
+    for (int64_t i : seq) total += icost[i];
+    double cum = 0.0;
+    for (int64_t i : seq) {
+      const double mid = cum + 0.5 * icost[i];
+      int x = total > 0.0 ? static_cast<int>(mid / total * kXcds) : 0;
+      x = std::min(std::max(x, 0), kXcds - 1);
+      q[x].push_back(i);
+      cum += icost[i];
+    }
   }
   size_t len = 0;
   for (auto& v : q) {
