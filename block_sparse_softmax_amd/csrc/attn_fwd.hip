@@ -282,6 +282,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   if (p.causal || p.kind == kMaskBlock) hi = min(hi, qi + 1);
   hi = max(hi, lo);
   const unsigned width = static_cast<unsigned>(hi - lo);
+  // A tile flagged PARTIAL for the 128 rows of the item can still allow every
+  // pair for this wave's 32 rows: the intervals' ends never decrease with the
+  // row, so the wave's rows all allow keys [lo of its last row, hi of its
+  // first row).  Such tiles take the unmasked path.
+  const int wave_lo_max = __builtin_amdgcn_readlane(lo, 31);
+  const int wave_hi_min = __builtin_amdgcn_readlane(hi, 0);
+  auto unmasked = [&](int ent) __attribute__((always_inline)) {
+    const int kv0 = (ent >> 1) * kBN;
+    return (ent & 1) || (kv0 >= wave_lo_max && kv0 + kBN <= wave_hi_min);
+  };
 
   // ---- running softmax state (log2 domain) ----
   // m_run: reference max (-inf while no allowed key and no sink has been seen);
@@ -604,19 +614,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   };
   // steady-state iteration: the FULL / PARTIAL variant of tile j
   auto steady = [&](int j, auto par_tag, auto safe_tag, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
-    if (ent_cur & 1)
+    if (unmasked(ent_cur))
       iteration(j, Bool<true>{}, Bool<true>{}, Bool<false>{}, par_tag, safe_tag, sc, sn);
     else
       iteration(j, Bool<true>{}, Bool<true>{}, Bool<true>{}, par_tag, safe_tag, sc, sn);
   };
 
   // ---- d = 128: one tile per iteration, QK -> softmax -> PV ----
-  // (one loop body with the mask under a uniform branch: separate FULL and
-  // PARTIAL copies raise the register pressure past 256 here)
   // K and V of tile j sit in buffers (j&1) and 2 + (j&1); the DMA for tile
   // j+1 is issued at the top of iteration j, right after the barrier that
-  // guarantees every wave is done with the buffers of tile j-1.
-  auto serial = [&](int j) __attribute__((always_inline)) {
+  // guarantees every wave is done with the buffers of tile j-1.  Separate
+  // bodies for FULL and PARTIAL tiles (a uniform branch inside one body is
+  // turned into predicated code, which runs the mask on every tile); the
+  // row max and the reference update run on the first tile only (the same
+  // fast pass as the pipelined loop).
+  auto serial = [&](int j, auto mask_tag, auto first_tag) __attribute__((always_inline)) {
+    constexpr bool kMask = decltype(mask_tag)::value;    // tile j is PARTIAL
+    constexpr bool kFirst = decltype(first_tag)::value;  // j == 0: sets the reference
     const int kPar = j & 1;
     constexpr int NQ = 2 * S::KS;
     constexpr int NP = 4 * S::DT;
@@ -631,15 +645,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     const int ent = ent_cur, ent1 = ent_nxt;
     if (j + 1 < n) issue_tile(ent1 >> 1, 2 * dma_tensor + (kPar ^ 1));
     const int raw2 = (j + 2 < n) ? list_entry(j + 2) : 0;
-    // S^T of tile j relative to the reference (seeded C operand)
+    // S^T of tile j relative to the reference (seeded C operand); K fragments
+    // are read two MFMAs ahead, the first V fragments during the last QK MFMAs
     f32x16 sn[2];
+    bf16x8 ka[NQ];
+    ka[0] = k00;
+    ka[1] = k01;
+    bf16x8 va[NP];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int ks = q / 2, half = q % 2;
-      const bf16x8 kf = q == 0 ? k00 : q == 1 ? k01 : kfrag(kPar, ks, half);
-      sn[half] = mfma32(kf, qf[ks], ks == 0 ? seedv : sn[half]);
+      if (q + 2 < NQ) ka[q + 2] = kfrag(kPar, (q + 2) / 2, (q + 2) % 2);
+      if (q == NQ - 2) va[0] = vfrag(2 + kPar, 0);
+      if (q == NQ - 1) va[1] = vfrag(2 + kPar, 1);
+      sn[half] = mfma32(ka[q], qf[ks], ks == 0 ? seedv : sn[half]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (!(ent & 1)) {  // PARTIAL tile
+    if constexpr (kMask) {
       const unsigned mbase = static_cast<unsigned>((ent >> 1) * kBN + 4 * h2 - lo);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -648,87 +670,96 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
         sn[1][r] = (u + 32 >= width) ? -INFINITY : sn[1][r];
       }
     }
-    float x = fmaxf(sn[0][0], sn[1][0]);
+    if constexpr (kFirst) {
+      float x = fmaxf(sn[0][0], sn[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) x = max3(x, sn[0][r], sn[1][r]);
-    const float mt = halves_max(x);  // tile max relative to the reference
-    const bool need = (m_run == -INFINITY) ? (mt > -INFINITY) : (mt > kRescaleThreshold);
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-      const float ref = ref_of();
-      const float m_new = need ? ref + mt : m_run;
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 while m_run = -inf
-      const float shift = (m_new == -INFINITY ? 0.f : m_new) - ref;
-      m_run = m_new;
-      l_run *= alpha;
-      sink_l *= alpha;
+      for (int r = 1; r < 16; ++r) x = max3(x, sn[0][r], sn[1][r]);
+      const float mt = halves_max(x);  // tile max relative to the reference
+      const bool need = (m_run == -INFINITY) ? (mt > -INFINITY) : (mt > kRescaleThreshold);
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+        const float ref = ref_of();
+        const float m_new = need ? ref + mt : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 while m_run = -inf
+        const float shift = (m_new == -INFINITY ? 0.f : m_new) - ref;
+        m_run = m_new;
+        l_run *= alpha;
+        sink_l *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < S::DT; ++dt) acc[dt] *= alpha;
-      sn[0] -= shift;
-      sn[1] -= shift;
-      set_seed();
-    }
-    // P^T = exp2(S^T) in bf16; row sum of the bf16 values
-    bf16x8 pb[4];
-    float rs = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int t = 2 * h + i / 4, e = 2 * (i % 4);
-        pb[t][e] = (__bf16)__builtin_amdgcn_exp2f(sn[h][2 * i]);
-        pb[t][e + 1] = (__bf16)__builtin_amdgcn_exp2f(sn[h][2 * i + 1]);
-        if constexpr (!S::PAD_ROWSUM)
-          rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[t][e], pb[t][e + 1]}, ones2, rs, false);
+        for (int dt = 0; dt < S::DT; ++dt) acc[dt] *= alpha;
+        sn[0] -= shift;
+        sn[1] -= shift;
+        set_seed();
       }
     }
-    if constexpr (!S::PAD_ROWSUM) l_run += rs;
+    // P^T = exp2(S^T) in bf16, 16 keys (one B operand pb[t]) at a time: the
+    // exponentials of keys 16(t+1) .. +15 run beside the PV MFMAs of keys
+    // 16t .. +15; row sum of the bf16 values
+    bf16x8 pb[4];
+    float rs = 0.f;
+    auto exp_pair = [&](int t, int i) __attribute__((always_inline)) {  // pair i (0..3) of pb[t]
+      const int h = t >> 1, src = 8 * (t & 1) + 2 * i;
+      pb[t][2 * i] = (__bf16)__builtin_amdgcn_exp2f(sn[h][src]);
+      pb[t][2 * i + 1] = (__bf16)__builtin_amdgcn_exp2f(sn[h][src + 1]);
+      if constexpr (!S::PAD_ROWSUM)
+        rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[t][2 * i], pb[t][2 * i + 1]}, ones2, rs, false);
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) exp_pair(0, i);
+    __builtin_amdgcn_sched_barrier(0);
     // O^T += V^T P^T
 #pragma unroll
     for (int pidx = 0; pidx < NP; ++pidx) {
       const int t = pidx / S::DT, dt = pidx % S::DT;
-      acc[dt] = mfma32(vfrag(2 + kPar, pidx), pb[t], acc[dt]);
+      if (pidx + 2 < NP) va[pidx + 2] = vfrag(2 + kPar, pidx + 2);
+      acc[dt] = mfma32(va[pidx], pb[t], acc[dt]);
+      if (t + 1 < 4) {
+#pragma unroll
+        for (int i = dt * 4 / S::DT; i < (dt + 1) * 4 / S::DT; ++i) exp_pair(t + 1, i);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (!S::PAD_ROWSUM) l_run += rs;
     ent_cur = ent1;
     ent_nxt = __builtin_amdgcn_readfirstlane(raw2);
   };
 
   // Rare path: this wave's 32 query rows recomputed exactly in fp32, K and V
   // read straight from global memory (no LDS, no other wave involved).
-  // Lanes l and l+32 share a query and produce one half of its output each.
+  // Lanes l and l+32 share a query: each takes half of the head dimension,
+  // for the dot products (summed over the pair) and for the output.
   auto exact_rows = [&]() __attribute__((always_inline)) {
     constexpr int DH = D / 2;
-    const unsigned char* qr = qbase + (qi < p.L ? qi : p.L - 1) * q_row_bytes;
-    float qv[D];
+    const unsigned char* qr = qbase + (qi < p.L ? qi : p.L - 1) * q_row_bytes + h2 * DH * 2;
+    bf16x8 qv[DH / 8];
 #pragma unroll
-    for (int c = 0; c < S::CPR; ++c) {
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[8 * c + e] = (float)x[e];
-    }
+    for (int c = 0; c < DH / 8; ++c) qv[c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
     float m = -INFINITY, l = 0.f, o[DH];
 #pragma unroll
     for (int d = 0; d < DH; ++d) o[d] = 0.f;
+#pragma unroll 1
     for (int e = e_begin; e < e_end; ++e) {
       const int ent = p.kv[e];
       const int kv0 = (ent >> 1) * kBN;
+#pragma unroll 1
       for (int kk = 0; kk < kBN; ++kk) {
         const int key = kv0 + kk;
         const bool allowed = key < p.L && ((ent & 1) || static_cast<unsigned>(key - lo) < width);
-        if (!allowed) continue;
-        const unsigned char* kr = kbase + static_cast<int64_t>(key) * k_row_bytes;
-        float sdot = 0.f;
+        const int krow = key < p.L ? key : p.L - 1;
+        const unsigned char* kr = kbase + static_cast<int64_t>(krow) * k_row_bytes + h2 * DH * 2;
+        float part = 0.f;
 #pragma unroll
-        for (int c = 0; c < S::CPR; ++c) {
+        for (int c = 0; c < DH / 8; ++c) {
           const bf16x8 x = *reinterpret_cast<const bf16x8*>(kr + 16 * c);
 #pragma unroll
-          for (int e8 = 0; e8 < 8; ++e8) sdot = __builtin_fmaf(qv[8 * c + e8], (float)x[e8], sdot);
+          for (int e8 = 0; e8 < 8; ++e8) part = __builtin_fmaf((float)qv[c][e8], (float)x[e8], part);
         }
-        const float sc2 = sdot * p.scale_log2;
+        const float sdot = halves_sum(part);
+        const float sc2 = allowed ? sdot * p.scale_log2 : -INFINITY;
         const float m_new = fmaxf(m, sc2);
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 while m = -inf
-        const float pr = __builtin_amdgcn_exp2f(sc2 - m_new);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+        const float pr = allowed ? __builtin_amdgcn_exp2f(sc2 - m_new) : 0.f;
         l = l * alpha + pr;
-        const unsigned char* vr = vbase + static_cast<int64_t>(key) * v_row_bytes + h2 * DH * 2;
+        const unsigned char* vr = vbase + static_cast<int64_t>(krow) * v_row_bytes + h2 * DH * 2;
 #pragma unroll
         for (int c = 0; c < DH / 8; ++c) {
           const bf16x8 x = *reinterpret_cast<const bf16x8*>(vr + 16 * c);
@@ -740,10 +771,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     }
     if (sink_log2 > -INFINITY) {  // the sink adds exp2(s_aux log2 e - m) to the denominator
       const float m_new = fmaxf(m, sink_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
       l = l * alpha + __builtin_amdgcn_exp2f(sink_log2 - m_new);
 #pragma unroll
       for (int d = 0; d < DH; ++d) o[d] *= alpha;
+      m = m_new;
     }
     if (npieces > 1) {  // partial state of this piece, in the accumulator layout
       float* sp = p.partials + static_cast<int64_t>(slot0 + piece) * kSlotFloats;
@@ -781,66 +813,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     return has;
   };
 
-  // A whole item with the serial loop (running max on every tile).
+  // A whole item with the serial loop.
   auto serial_pass = [&]() __attribute__((always_inline)) {
     __syncthreads();  // list staged, pad regions written; previous pass done with LDS
     ent_cur = __builtin_amdgcn_readfirstlane(list_lds[0]);
     ent_nxt = n > 1 ? __builtin_amdgcn_readfirstlane(list_lds[1]) : 0;
     issue_tile(ent_cur >> 1, 2 * dma_tensor);
-    for (int j = 0; j < n; ++j) serial(j);
+    if (unmasked(ent_cur)) serial(0, Bool<false>{}, Bool<true>{});
+    else serial(0, Bool<true>{}, Bool<true>{});
+    for (int j = 1; j < n; ++j) {
+      if (unmasked(ent_cur)) serial(j, Bool<false>{}, Bool<false>{});
+      else serial(j, Bool<true>{}, Bool<false>{});
+    }
   };
-  bool rows_written = false;  // this wave's rows were finished by the exact path
-  if constexpr (!S::PIPELINED) {
-   if (n > 0) serial_pass();
-  } else {
-   // One pass over the item's tiles; `safe` selects the pass that tracks the
-   // row max on every tile.
-   auto pass = [&](auto safe) __attribute__((always_inline)) {
-    __syncthreads();  // list staged, pad regions written
-    ent_cur = __builtin_amdgcn_readfirstlane(list_lds[0]);
-    ent_nxt = n > 1 ? __builtin_amdgcn_readfirstlane(list_lds[1]) : 0;
-    if (dma_tensor == 0) issue_tile(ent_cur >> 1, 0);
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    if (ent_cur & 1) iteration(0, Bool<true>{}, Bool<false>{}, Bool<false>{}, I0{}, safe, sB, sA);
-    else iteration(0, Bool<true>{}, Bool<false>{}, Bool<true>{}, I0{}, safe, sB, sA);
-    int j = 1;
-    for (; j + 1 < n; j += 2) {
-      steady(j, I1{}, safe, sA, sB);
-      steady(j + 1, I0{}, safe, sB, sA);
-    }
-    if (j < n) {  // j = n - 1 (odd)
-      steady(j, I1{}, safe, sA, sB);
-      iteration(n, Bool<false>{}, Bool<true>{}, Bool<false>{}, I0{}, safe, sB, sA);
-    } else {  // j = n (odd)
-      iteration(n, Bool<false>{}, Bool<true>{}, Bool<false>{}, I1{}, safe, sA, sB);
-    }
-   };
-   if (n > 0) {
-    // Fast pass: the reference is fixed after the first tile, so later tiles
-    // need no row max.  Probabilities relative to it stay far inside the
-    // bf16 / fp32 range unless a later score exceeds it by more than 2^64.
-    // The reference is a score of the row (or its sink) whenever the first
-    // tile allows one of the row's keys, which makes the total at least 1;
-    // a row that starts from the placeholder reference 0 instead can end far
-    // below it.  A wave with a row (inside the sequence) whose row sum is not
-    // finite or above 2^64, or whose total is below 2^-64 although the item
-    // lists one of its keys, recomputes its rows exactly (exact_rows; no
-    // other wave is involved).  A piece of a split row may legitimately hold
-    // none of a row's keys: that row's total is 0 and it is left as is.
-    pass(Bool<false>{});
-    const float lrow = S::PAD_ROWSUM ? low_half(acc[S::DT - 1][8]) : halves_sum(l_run);
-    const bool off_range = qi < p.L && (!(lrow <= 0x1p64f) || !(lrow + sink_l >= 0x1p-64f));
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(off_range) != 0, 0)) {
-      const bool redo = off_range && (!(lrow <= 0x1p64f) || row_has_key());
-      if (__builtin_amdgcn_ballot_w64(redo) != 0) {
-        exact_rows();
-        rows_written = true;
-      }
-    }
-   }
-  }
-
   // ---- epilogue: O = acc / (row sum + sink term) ----
   auto store_o = [&](float inv) __attribute__((always_inline)) {
     if (qi < p.L) {
@@ -861,21 +846,121 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
       }
     }
   };
-  float ltot = 0.f;
-  if (!rows_written) {
-    const float lsum = S::PAD_ROWSUM ? low_half(acc[S::DT - 1][8])  // O^T row D (ones row of V^T), lanes 0..31
-                                     : halves_sum(l_run);
-    ltot = lsum + sink_l;
+
+  // ---- a piece of a split row: publish the partial state, the last piece merges ----
+  // Slot layout (per wave): acc as float4 [DT][4][64 lanes], then m and l per
+  // lane.  Every wave has written its part of this piece's slot (from its
+  // registers, or from the exact path) before the call.
+  float* slots = p.partials + static_cast<int64_t>(slot0) * kSlotFloats;
+  auto publish_and_merge = [&]() __attribute__((always_inline)) {
+    // Publication: every wave's stores are ordered before the barrier
+    // (work-group scope); thread 0 then releases them at device scope (one
+    // write-back of the XCD's L2) and counts the piece.  The piece that
+    // counts last acquires at device scope (one invalidation), so after the
+    // second barrier its waves read every piece's state.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int* cnt = p.counters + counter;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const int done = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = done == npieces - 1;
+      if (last) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next launch
+      }
+      list_lds[0] = last ? 1 : 0;
+    }
+    __syncthreads();
+    if (list_lds[0] == 0) return;
+    // Merge in piece order (fixed, whichever piece finishes last).
+    float mmax = -INFINITY;
+    for (int i = 0; i < npieces; ++i) mmax = fmaxf(mmax, slots[static_cast<int64_t>(i) * kSlotFloats + kSlotM + wave * 64 + lane]);
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) acc[dt] = f32x16{};
+    float lm = 0.f;
+    for (int i = 0; i < npieces; ++i) {
+      const float* sp = slots + static_cast<int64_t>(i) * kSlotFloats;
+      const float mi = sp[kSlotM + wave * 64 + lane];
+      const float w = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - mmax);
+      lm = __builtin_fmaf(w, sp[kSlotL + wave * 64 + lane], lm);
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 a = *reinterpret_cast<const float4*>(sp + (((wave * S::DT + dt) * 4 + g) * 64 + lane) * 4);
+          acc[dt][4 * g + 0] = __builtin_fmaf(w, a.x, acc[dt][4 * g + 0]);
+          acc[dt][4 * g + 1] = __builtin_fmaf(w, a.y, acc[dt][4 * g + 1]);
+          acc[dt][4 * g + 2] = __builtin_fmaf(w, a.z, acc[dt][4 * g + 2]);
+          acc[dt][4 * g + 3] = __builtin_fmaf(w, a.w, acc[dt][4 * g + 3]);
+        }
+      }
+    }
+    store_o(lm > 0.f ? 1.f / lm : 0.f);
+  };
+
+  // After the pass (fast pass: the reference is fixed after the first tile,
+  // so later tiles need no row max).  Probabilities relative to it stay far
+  // inside the bf16 / fp32 range unless a later score exceeds it by more than
+  // 2^64.  The reference is a score of the row (or its sink) whenever the
+  // first tile allows one of the row's keys, which makes the total at least
+  // 1; a row that starts from the placeholder reference 0 instead can end far
+  // below it.  A wave with a row (inside the sequence) whose row sum is not
+  // finite or above 2^64, or whose total is below 2^-64 although the item
+  // lists one of its keys, recomputes its rows exactly (exact_rows; no other
+  // wave is involved) and finishes from there.  A piece of a split row may
+  // legitimately hold none of a row's keys: that row's total is 0 and it is
+  // left as is.
+  auto finish_or_redo = [&](float lrow) __attribute__((always_inline)) {
+    const bool off_range = qi < p.L && (!(lrow <= 0x1p64f) || !(lrow + sink_l >= 0x1p-64f));
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(off_range) != 0, 0)) {
+      const bool redo = off_range && (!(lrow <= 0x1p64f) || row_has_key());
+      if (__builtin_amdgcn_ballot_w64(redo) != 0) return true;
+    }
+    return false;
+  };
+
+  if constexpr (!S::PIPELINED) {
+    if (n > 0) serial_pass();
+  } else {
+   // One pass over the item's tiles; `safe` selects the pass that tracks the
+   // row max on every tile.
+   auto pass = [&](auto safe) __attribute__((always_inline)) {
+    __syncthreads();  // list staged, pad regions written
+    ent_cur = __builtin_amdgcn_readfirstlane(list_lds[0]);
+    ent_nxt = n > 1 ? __builtin_amdgcn_readfirstlane(list_lds[1]) : 0;
+    if (dma_tensor == 0) issue_tile(ent_cur >> 1, 0);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    if (unmasked(ent_cur)) iteration(0, Bool<true>{}, Bool<false>{}, Bool<false>{}, I0{}, safe, sB, sA);
+    else iteration(0, Bool<true>{}, Bool<false>{}, Bool<true>{}, I0{}, safe, sB, sA);
+    int j = 1;
+    for (; j + 1 < n; j += 2) {
+      steady(j, I1{}, safe, sA, sB);
+      steady(j + 1, I0{}, safe, sB, sA);
+    }
+    if (j < n) {  // j = n - 1 (odd)
+      steady(j, I1{}, safe, sA, sB);
+      iteration(n, Bool<false>{}, Bool<true>{}, Bool<false>{}, I0{}, safe, sB, sA);
+    } else {  // j = n (odd)
+      iteration(n, Bool<false>{}, Bool<true>{}, Bool<false>{}, I1{}, safe, sA, sB);
+    }
+   };
+   if (n > 0) pass(Bool<false>{});
   }
-  if (npieces == 1) {
-    if (!rows_written) store_o(ltot > 0.f ? 1.f / ltot : 0.f);
+  const float lrow = S::PAD_ROWSUM ? low_half(acc[S::DT - 1][8])  // O^T row D (ones row of V^T), lanes 0..31
+                                   : halves_sum(l_run);
+  if (n > 0 && finish_or_redo(lrow)) {
+    exact_rows();  // writes O, or this piece's partial state
+    if (npieces > 1) publish_and_merge();
     return;
   }
-
-  // ---- a piece of a split row: leave the partial state, the last piece merges ----
-  // Slot layout (per wave): acc as float4 [DT][4][64 lanes], then m and l per lane.
-  float* slots = p.partials + static_cast<int64_t>(slot0) * kSlotFloats;
-  if (!rows_written) {
+  const float ltot = lrow + sink_l;
+  if (npieces == 1) {
+    store_o(ltot > 0.f ? 1.f / ltot : 0.f);
+    return;
+  }
+  {
     float* sp = slots + static_cast<int64_t>(piece) * kSlotFloats;
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt) {
@@ -888,50 +973,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
     sp[kSlotM + wave * 64 + lane] = ltot > 0.f ? ref_of() : -INFINITY;
     sp[kSlotL + wave * 64 + lane] = ltot;
   }
-  // Publication: every wave's stores are ordered before the barrier
-  // (work-group scope); thread 0 then releases them at device scope (one
-  // write-back of the XCD's L2) and counts the piece.  The piece that counts
-  // last acquires at device scope (one invalidation), so after the second
-  // barrier its waves read every piece's state.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int* cnt = p.counters + counter;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const int done = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = done == npieces - 1;
-    if (last) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next launch
-    }
-    list_lds[0] = last ? 1 : 0;
-  }
-  __syncthreads();
-  if (list_lds[0] == 0) return;
-  // Merge in piece order (fixed, whichever piece finishes last).
-  float mmax = -INFINITY;
-  for (int i = 0; i < npieces; ++i) mmax = fmaxf(mmax, slots[static_cast<int64_t>(i) * kSlotFloats + kSlotM + wave * 64 + lane]);
-#pragma unroll
-  for (int dt = 0; dt < S::DT; ++dt) acc[dt] = f32x16{};
-  float lm = 0.f;
-  for (int i = 0; i < npieces; ++i) {
-    const float* sp = slots + static_cast<int64_t>(i) * kSlotFloats;
-    const float mi = sp[kSlotM + wave * 64 + lane];
-    const float w = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - mmax);
-    lm = __builtin_fmaf(w, sp[kSlotL + wave * 64 + lane], lm);
-#pragma unroll
-    for (int dt = 0; dt < S::DT; ++dt) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 a = *reinterpret_cast<const float4*>(sp + (((wave * S::DT + dt) * 4 + g) * 64 + lane) * 4);
-        acc[dt][4 * g + 0] = __builtin_fmaf(w, a.x, acc[dt][4 * g + 0]);
-        acc[dt][4 * g + 1] = __builtin_fmaf(w, a.y, acc[dt][4 * g + 1]);
-        acc[dt][4 * g + 2] = __builtin_fmaf(w, a.z, acc[dt][4 * g + 2]);
-        acc[dt][4 * g + 3] = __builtin_fmaf(w, a.w, acc[dt][4 * g + 3]);
-      }
-    }
-  }
-  store_o(lm > 0.f ? 1.f / lm : 0.f);
+  publish_and_merge();
 }
 
 template <int D>
