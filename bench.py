@@ -3,9 +3,11 @@
 One step = one pass of the whole hot path over the ViT layer at 896 px
 (64 x 64 patch grid flattened row-major: L = 4096 tokens, batch 1, 16 heads,
 head dim 80, bf16): the three masks of that layer -- full attention, 1D chunks
-of 256 tokens and a symmetric sliding window of radius 128 -- each one launch
-of the HIP kernel on the same resident Q, K, V.  Mask plans are compiled and
-uploaded before the timed region (they are cached per mask).
+of 256 tokens and a symmetric sliding window of radius 128 -- on the same
+resident Q, K, V, run as one grouped launch of the HIP kernel (each mask writes
+its own output).  Mask plans are compiled and uploaded before the timed region
+(they are cached per mask).  Each mask is also timed alone, after the timed
+steps, for the per-mask table.
 
 Metric: effective attention TFLOP/s = 4 * d * (unmasked query-key pairs) per
 head, summed over the masks, divided by the step time (2d flops for the score
@@ -13,9 +15,10 @@ and 2d for the value mix per allowed pair; padding, masked pairs inside
 partial tiles and the exponentials are not counted).
 
 Extra workloads (skipped with --quick): the 1792-px ViT layer (L = 16384, full
-and sliding window radius 512) and 128K-token block-sparse causal prefill
-(32 heads, d = 128, block 128, about half of the causal blocks kept), timed the
-same way and reported under "extra".
+and sliding window radius 512), causal LM prefill with per-head windows and
+sinks (L = 4096, d = 128) and 128K-token block-sparse causal prefill (32 heads,
+d = 128, block 128, about half of the causal blocks kept), timed the same way
+and reported under "extra".
 
 Prints ONE JSON line.
 """
@@ -68,15 +71,15 @@ WORKLOADS = {
 }
 
 
-def _roofline(setup, rows, workload):
-    """Roofline object for the launch with the largest average duration."""
-    dom = max(rows, key=lambda r: r["avg_ms"])
+def _roofline(setup, group, total_flops, workload):
+    """Roofline object for the step's kernel: the grouped launch of all masks of the workload."""
     w = setup["w"]
-    dom_flops = 4.0 * w["D"] * dom["pairs"] * w["B"]
-    achieved = dom_flops / (dom["avg_ms"] * 1e-3) / 1e12
+    achieved = total_flops / (group["avg_ms"] * 1e-3) / 1e12
+    label = "+".join(group["masks"])
     return dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                frac=achieved / PEAK_BF16_TFLOPS, traffic=_traffic_from_profile(workload, dom["mask"]),
-                kernel=f"attn_fwd_kernel<{w['D']}> ({workload} {dom['mask']})", avg_launch_ms=dom["avg_ms"])
+                frac=achieved / PEAK_BF16_TFLOPS, traffic=_traffic_from_profile(workload, label),
+                kernel=f"attn_fwd_kernel<{w['D']}> grouped launch ({workload}: {', '.join(group['masks'])})",
+                avg_launch_ms=group["avg_ms"])
 
 
 def _bits_to_dev(u16, device, layout):
@@ -95,48 +98,72 @@ def _setup(name, device, layout):
     w = gen.workload(name)
     q, k, v = gen.qkv_bf16(0, w["cfg"], w["B"], w["H"], w["L"], w["D"])
     dev = [_bits_to_dev(x, device, layout) for x in (q, k, v)]
-    o = torch.empty_like(dev[0])
     sink = None if w["sink"] is None else torch.from_numpy(w["sink"]).to(device)
     masks = []
     for label, mask in w["masks"].items():
         pm = prepare(mask, w["L"], w["H"], w["D"], device)
         _, pairs = pm.plan.pairs()
-        masks.append(dict(label=label, mask=mask, pm=pm, pairs=int(pairs)))
-    return dict(w=w, host=(q, k, v), dev=dev, o=o, sink=sink, masks=masks)
+        masks.append(dict(label=label, mask=mask, pm=pm, pairs=int(pairs), o=torch.empty_like(dev[0])))
+    return dict(w=w, host=(q, k, v), dev=dev, sink=sink, masks=masks)
+
+
+def _events(n):
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:             # a torch event exists once it has been recorded
+        a.record()
+        b.record()
+    return ev
 
 
 def _time(setup, steps, warmup, layout):
-    """Time `steps` steps (one launch per mask each); per-launch HIP events on the launch stream."""
+    """Time `steps` steps.  A step is ONE grouped launch (attn_masked_fwd_group) of every mask of
+    the workload, each mask writing its own output.
+
+    Launch durations come from HIP events that the launch attaches to the kernel's own dispatch
+    (hipExtLaunchKernel), so nothing is recorded between the kernels of the timed steps; the step
+    time is the host wall clock between two device synchronisations.  After the timed steps each
+    mask is also launched alone (same events) for the per-mask table.
+    """
     import torch
+    from block_sparse_softmax_amd import bind_group
     q, k, v = setup["dev"]
-    o, sink = setup["o"], setup["sink"]
+    sink = setup["sink"]
+    ms = setup["masks"]
     stream = torch.cuda.current_stream()
-    launches = [m["pm"].bind(q, k, v, o, sink=sink, layout=layout, stream=stream) for m in setup["masks"]]
+    n = len(ms)
+    group = bind_group([m["pm"] for m in ms], [q] * n, [k] * n, [v] * n, [m["o"] for m in ms],
+                       sinks=[sink] * n, layout=layout, stream=stream)
     for _ in range(warmup):
-        for f in launches:
-            f()
-    torch.cuda.synchronize()
-    n = len(launches)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+        group()
+    ev = _events(steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
-        ev[s][0].record(stream)
-        for i, f in enumerate(launches):
-            f()
-            ev[s][i + 1].record(stream)
+        group(*ev[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [[ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)] for i in range(n)]  # ms
-    return wall, per
+    per_group = [a.elapsed_time(b) for a, b in ev]  # ms
+    # each mask alone (not part of the timed steps)
+    per_mask = []
+    reps = max(3, min(steps, 10))
+    for m in ms:
+        f = m["pm"].bind(q, k, v, m["o"], sink=sink, layout=layout, stream=stream)
+        f()
+        e1 = _events(reps)
+        for a, b in e1:
+            f(a, b)
+        torch.cuda.synchronize()
+        per_mask.append([a.elapsed_time(b) for a, b in e1])
+    return wall, per_group, per_mask
 
 
-def _summarise(setup, wall, per, steps):
+def _summarise(setup, wall, per_group, per_mask, steps):
     import numpy as np
     w = setup["w"]
     D = w["D"]
     rows = []
-    for m, t in zip(setup["masks"], per):
+    for m, t in zip(setup["masks"], per_mask):
         flops = 4.0 * D * m["pairs"] * w["B"]
         avg = float(np.mean(t))
         rows.append(dict(mask=m["label"], pairs=m["pairs"], avg_ms=avg, min_ms=float(np.min(t)),
@@ -145,7 +172,9 @@ def _summarise(setup, wall, per, steps):
                          alg_gbs=(4 * w["B"] * w["H"] * w["L"] * D * 2) / (avg * 1e-3) / 1e9))
     total_flops = sum(4.0 * D * m["pairs"] * w["B"] for m in setup["masks"])
     ms_per_step = wall / steps * 1e3
-    return rows, total_flops, ms_per_step
+    group = dict(avg_ms=float(np.mean(per_group)), min_ms=float(np.min(per_group)),
+                 masks=[m["label"] for m in setup["masks"]])
+    return rows, total_flops, ms_per_step, group
 
 
 def _cpu_baseline(setup, budget_s=20.0):
@@ -217,25 +246,26 @@ def main():
     setup = _setup(args.workload, device, args.layout)
     if args.only:
         setup["masks"] = [m for m in setup["masks"] if m["label"] == args.only]
-    wall, per = _time(setup, args.steps, args.warmup, args.layout)
-    rows, total_flops, ms_per_step = _summarise(setup, wall, per, args.steps)
+    wall, per_group, per_mask = _time(setup, args.steps, args.warmup, args.layout)
+    rows, total_flops, ms_per_step, group = _summarise(setup, wall, per_group, per_mask, args.steps)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
-    roof = _roofline(setup, rows, args.workload)
+    roof = _roofline(setup, group, total_flops, args.workload)
 
     cpu = None if args.no_cpu_baseline else _cpu_baseline(setup)
 
     extra = {}
     if not args.quick:
-        for name in ("vit1792", "blocksparse128k"):
+        for name in ("vit1792", "lm_headwin", "blocksparse128k"):
             del setup
             torch.cuda.empty_cache()
             setup = _setup(name, device, args.layout)
-            wl, pr = _time(setup, max(5, args.steps // 2), args.warmup, args.layout)
-            r2, tf2, ms2 = _summarise(setup, wl, pr, max(5, args.steps // 2))
+            nst = max(5, args.steps // 2)
+            wl, pg, pm = _time(setup, nst, args.warmup, args.layout)
+            r2, tf2, ms2, g2 = _summarise(setup, wl, pg, pm, nst)
             extra[name] = dict(workload=WORKLOADS[name], ms_per_step=ms2, tflops=tf2 / (ms2 * 1e-3) / 1e12,
                                frac_bf16_peak=tf2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, masks=r2,
-                               roofline=_roofline(setup, r2, name))
+                               grouped_launch=g2, roofline=_roofline(setup, g2, tf2, name))
 
     out = {
         "metric": "effective attention TFLOP/s (unmasked pairs) and % bf16 MFMA peak, 1 MI355X",
@@ -252,6 +282,7 @@ def main():
         "data": "synthetic (seeded N(0,1) Q, K, V rounded to bf16)",
         "config": {"workload": WORKLOADS[args.workload] + (f" (mask {args.only} only)" if args.only else ""),
                    "layout": args.layout, "frac_bf16_peak": value / PEAK_BF16_TFLOPS},
+        "grouped_launch": group,
         "per_mask": rows,
         "roofline": roof,
         "cpu_baseline": cpu,

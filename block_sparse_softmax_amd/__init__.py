@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     AttnError,
     Plan,
     PreparedMask,
+    bind_group,
     load_library,
     masked_fwd,
     masked_fwd_oneshot,
@@ -15,5 +16,5 @@ from ._lib import (  # noqa: F401
     tensor_view,
 )
 
-__all__ = ["AttnError", "Plan", "PreparedMask", "load_library", "masked_fwd", "masked_fwd_oneshot",
+__all__ = ["AttnError", "Plan", "PreparedMask", "bind_group", "load_library", "masked_fwd", "masked_fwd_oneshot",
            "prepare", "tensor_view"]

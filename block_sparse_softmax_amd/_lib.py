@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_E_INVAL", -2: "ATTN_E_UNSUPPORTED", -3: 
 # every symbol the header declares
 EXPORTS = ("attn_masked_fwd", "attn_workspace_bytes", "attn_plan_create", "attn_plan_tiles",
            "attn_plan_pairs", "attn_plan_schedule", "attn_plan_workspace_bytes", "attn_plan_upload",
-           "attn_masked_fwd_plan", "attn_plan_destroy", "attn_last_error", "attn_version")
+           "attn_masked_fwd_plan", "attn_masked_fwd_group", "attn_plan_destroy", "attn_last_error",
+           "attn_version")
 
 
 class AttnError(RuntimeError):
@@ -50,7 +51,8 @@ class MaskDesc(ctypes.Structure):
 
 class Launch(ctypes.Structure):
     _fields_ = [("stream", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t), ("softmax_scale", ctypes.c_float)]
+                ("workspace_bytes", ctypes.c_size_t), ("softmax_scale", ctypes.c_float),
+                ("start_event", ctypes.c_void_p), ("stop_event", ctypes.c_void_p)]
 
 
 _lib = None
@@ -80,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "attn_plan_workspace_bytes": [plan_p, P(sz)],
             "attn_plan_upload": [plan_p, vp, sz, vp],
             "attn_masked_fwd_plan": [plan_p, P(AttnTensor), P(AttnTensor), P(AttnTensor), vp, P(AttnTensor), P(Launch)],
+            "attn_masked_fwd_group": [i32, P(vp), P(AttnTensor), P(AttnTensor), P(AttnTensor), P(vp), P(AttnTensor),
+                                      P(vp), P(sz), P(Launch)],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -272,7 +276,11 @@ class PreparedMask:
         keep = (qv, kv, vv, ov, ln, q, k, v, o, sink)
         fn = lib.attn_masked_fwd_plan
 
-        def run():
+        def run(start_event=None, stop_event=None):
+            """Launch; optional torch.cuda.Events (already created, e.g. recorded once) are set at
+            the kernel's start and end by the launch itself."""
+            ln.start_event = None if start_event is None else start_event.cuda_event
+            ln.stop_event = None if stop_event is None else stop_event.cuda_event
             _check(fn(*args))
             return keep[8]
         return run
@@ -294,6 +302,39 @@ class PreparedMask:
         _check(lib.attn_masked_fwd_plan(self.plan.handle, ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv),
                                         sp, ctypes.byref(ov), ctypes.byref(ln)))
         return o
+
+
+def bind_group(prepared, qs, ks, vs, outs, sinks=None, layout="blhd", stream=None, softmax_scale: float = 0.0):
+    """Marshal a grouped launch (attn_masked_fwd_group) of PreparedMasks once; the returned callable
+    launches all of them as one kernel.  Lists are per launch; outputs must be distinct tensors."""
+    lib = load_library()
+    n = len(prepared)
+    if not (len(qs) == len(ks) == len(vs) == len(outs) == n):
+        raise ValueError("one q, k, v and output per prepared mask")
+    sinks = [None] * n if sinks is None else list(sinks)
+    ta = AttnTensor * n
+    qv, kv, vv, ov = (ta(*(tensor_view(x, layout) for x in xs)) for xs in (qs, ks, vs, outs))
+    for j, sk in enumerate(sinks):
+        if sk is not None:
+            import torch
+            if sk.dtype != torch.float32 or not sk.is_cuda or sk.numel() != prepared[j].plan.H:
+                raise TypeError("sink must be a float32 CUDA tensor with one entry per head")
+    plans = (ctypes.c_void_p * n)(*(pm.plan.handle.value for pm in prepared))
+    sk = (ctypes.c_void_p * n)(*(None if x is None else x.data_ptr() for x in sinks))
+    ws = (ctypes.c_void_p * n)(*(pm.workspace.data_ptr() for pm in prepared))
+    wb = (ctypes.c_size_t * n)(*(pm.workspace.numel() for pm in prepared))
+    ln = Launch()
+    ln.stream = _stream_ptr(stream, qs[0]).value
+    ln.softmax_scale = softmax_scale
+    keep = (qv, kv, vv, ov, plans, sk, ws, wb, ln, prepared, qs, ks, vs, outs, sinks)
+    fn = lib.attn_masked_fwd_group
+
+    def run(start_event=None, stop_event=None):
+        ln.start_event = None if start_event is None else start_event.cuda_event
+        ln.stop_event = None if stop_event is None else stop_event.cuda_event
+        _check(fn(n, plans, qv, kv, vv, sk, ov, ws, wb, ctypes.byref(ln)))
+        return keep[13]
+    return run
 
 
 _prepared = {}

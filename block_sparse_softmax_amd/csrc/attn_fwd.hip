@@ -32,6 +32,7 @@
 //     more than 2^8; probabilities stay below 256 and the result is the same
 //     softmax (every term shares the reference point).
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -201,7 +202,7 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p) {
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams g) {
   using S = Shape<D>;
   constexpr int64_t kSlotFloats = partial_slot_floats(D);
   constexpr int kSlotM = 4 * S::DT * 16 * 64;  // m of every lane of the 4 waves
@@ -219,9 +220,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   // Work-groups are dealt to the 8 XCDs round-robin (block i runs on XCD i mod 8);
   // XCD x takes the x-th contiguous chunk of the schedule, so the items that
   // share an XCD's L2 at any time come from the same head.
-  const int xcd_chunk = (p.n_items + 7) / 8;
-  const int item_idx = p.xcd_chunked ? (blockIdx.x % 8) * xcd_chunk + blockIdx.x / 8 : blockIdx.x;
-  if (item_idx >= p.n_items) return;
+  // XCD x (blockIdx mod 8) runs queue x of job 0, then of job 1, ...
+  int pos = static_cast<int>(blockIdx.x / 8), jb = 0;
+  while (jb + 1 < g.n_jobs && pos >= g.queue_len[jb]) pos -= g.queue_len[jb++];
+  const int job = __builtin_amdgcn_readfirstlane(jb);
+  pos = __builtin_amdgcn_readfirstlane(pos);
+  if (pos >= g.queue_len[job]) return;
+  const FwdParams& p = g.job[job];
+  const int item_idx = static_cast<int>(blockIdx.x % 8) * g.queue_len[job] + pos;
   const int4 item = reinterpret_cast<const int4*>(p.items)[2 * item_idx];
   const int4 split = reinterpret_cast<const int4*>(p.items)[2 * item_idx + 1];
   const int head = __builtin_amdgcn_readfirstlane(item.x);
@@ -352,7 +358,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
   // LDS-DMA: waves 0-1 fill K tiles and waves 2-3 V tiles; wave-instruction i
   // of a wave fills 64 consecutive 16-byte LDS slots of its half of the tile.
   const int dma_tensor = wave >> 1;
-  const uint32_t dma_row_bytes = static_cast<uint32_t>(dma_tensor ? v_row_bytes : k_row_bytes);
+  const uint32_t dma_row_bytes =
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(dma_tensor ? v_row_bytes : k_row_bytes)));
   const unsigned char* dma_base = dma_tensor ? vbase : kbase;
   // Lane part of each load's source offset for one swizzle period (16 rows);
   // later periods add 16 rows to the uniform base.  d = 80: lanes whose slot
@@ -977,20 +984,31 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const FwdParams p
 }
 
 template <int D>
-hipError_t launch_d(const FwdParams& p, int B, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(8 * ((p.n_items + 7) / 8)), static_cast<unsigned>(B));
-  hipLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(kThreads), 0, stream, p);
+hipError_t launch_d(const GroupParams& g, int blocks, int B, hipStream_t stream, hipEvent_t start,
+                    hipEvent_t stop) {
+  dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(B));
+  // the extended launch attaches the events to the kernel's own dispatch
+  hipExtLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(kThreads), 0, stream, start, stop, 0, g);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd(const FwdParams& p, int D, int B, hipStream_t stream) {
-  if (p.n_items == 0 || B == 0) return hipSuccess;
+hipError_t launch_fwd(const GroupParams& g, int D, int B, hipStream_t stream, hipEvent_t start,
+                      hipEvent_t stop) {
+  int64_t blocks = 0;
+  for (int j = 0; j < g.n_jobs; ++j) blocks += 8 * static_cast<int64_t>(g.queue_len[j]);
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  if (blocks == 0 || B == 0) {  // nothing to run: the events still mark this point of the stream
+    hipError_t e = hipSuccess;
+    if (start != nullptr) e = hipEventRecord(start, stream);
+    if (e == hipSuccess && stop != nullptr) e = hipEventRecord(stop, stream);
+    return e;
+  }
   switch (D) {
-    case 64: return launch_d<64>(p, B, stream);
-    case 80: return launch_d<80>(p, B, stream);
-    case 128: return launch_d<128>(p, B, stream);
+    case 64: return launch_d<64>(g, static_cast<int>(blocks), B, stream, start, stop);
+    case 80: return launch_d<80>(g, static_cast<int>(blocks), B, stream, start, stop);
+    case 128: return launch_d<128>(g, static_cast<int>(blocks), B, stream, start, stop);
     default: return hipErrorInvalidValue;
   }
 }

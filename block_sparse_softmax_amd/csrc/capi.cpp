@@ -55,10 +55,11 @@ attn_status check_tensor(const attn_tensor* t, const char* name, int64_t B, int6
   return ATTN_OK;
 }
 
-attn_status launch_with_plan(const attn_plan& p, const attn_tensor* q, const attn_tensor* k,
-                             const attn_tensor* v, const float* sink, attn_tensor* o,
-                             const attn_launch* launch) {
-  if (!launch) { set_error("launch is NULL"); return ATTN_E_INVAL; }
+// Validate one launch of plan p and fill its kernel parameters.  ws/ws_bytes:
+// the workspace holding p's uploaded image (and the partial states).
+attn_status make_job(const attn_plan& p, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                     const float* sink, attn_tensor* o, void* ws_ptr, size_t ws_bytes, float softmax_scale,
+                     FwdParams* out, int32_t* queue_len) {
   if (!q) { set_error("q is NULL"); return ATTN_E_INVAL; }
   const int64_t B = q->B;
   if (B < 1 || B > 65535) { set_error("batch must be in [1, 65535]"); return ATTN_E_INVAL; }
@@ -78,18 +79,18 @@ attn_status launch_with_plan(const attn_plan& p, const attn_tensor* q, const att
   // batch 1 runs the split schedule, whose partial states follow the image
   const bool split = (B == 1);
   const size_t need = split ? p.layout.total : p.layout.bytes;
-  if (!launch->workspace || launch->workspace_bytes < need) {
+  if (!ws_ptr || ws_bytes < need) {
     set_error("workspace smaller than attn_plan_workspace_bytes (" + std::to_string(p.layout.total) +
               " bytes)");
     return ATTN_E_WORKSPACE;
   }
-  if ((split ? p.items.size() : p.items_unsplit.size()) > static_cast<size_t>(INT32_MAX)) {
+  const size_t n_items = split ? p.items.size() : p.items_unsplit.size();
+  if (n_items % 8 != 0 || n_items / 8 > static_cast<size_t>(INT32_MAX / 8)) {
     set_error("too many work items");
     return ATTN_E_UNSUPPORTED;
   }
-  if (!aligned16(launch->workspace)) { set_error("workspace must be 16-byte aligned"); return ATTN_E_INVAL; }
-
-  const uint8_t* ws = static_cast<const uint8_t*>(launch->workspace);
+  if (!aligned16(ws_ptr)) { set_error("workspace must be 16-byte aligned"); return ATTN_E_INVAL; }
+  const uint8_t* ws = static_cast<const uint8_t*>(ws_ptr);
   FwdParams f{};
   f.q = static_cast<const uint16_t*>(q->data);
   f.k = static_cast<const uint16_t*>(k->data);
@@ -100,28 +101,45 @@ attn_status launch_with_plan(const attn_plan& p, const attn_tensor* q, const att
   f.v_sb = v->stride_b; f.v_sl = v->stride_l; f.v_sh = v->stride_h;
   f.o_sb = o->stride_b; f.o_sl = o->stride_l; f.o_sh = o->stride_h;
   f.items = reinterpret_cast<const int32_t*>(ws + (split ? p.layout.off_items : p.layout.off_items_unsplit));
-  f.partials = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + p.layout.off_partials);
-  f.counters = reinterpret_cast<int32_t*>(const_cast<uint8_t*>(ws) + p.layout.off_counters);
   f.kv = reinterpret_cast<const int32_t*>(ws + p.layout.off_kv);
   f.head_left = reinterpret_cast<const int32_t*>(ws + p.layout.off_head_left);
   f.block_bits = reinterpret_cast<const uint32_t*>(ws + p.layout.off_bits);
+  f.partials = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + p.layout.off_partials);
+  f.counters = reinterpret_cast<int32_t*>(const_cast<uint8_t*>(ws) + p.layout.off_counters);
   f.sink = sink;
-  const float scale = launch->softmax_scale > 0.f ? launch->softmax_scale
-                                                  : static_cast<float>(1.0 / std::sqrt(double(p.D)));
+  const float scale = softmax_scale > 0.f ? softmax_scale : static_cast<float>(1.0 / std::sqrt(double(p.D)));
   f.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
   f.L = static_cast<int32_t>(p.L);
   f.H = static_cast<int32_t>(p.H);
-  f.n_items = static_cast<int32_t>(split ? p.items.size() : p.items_unsplit.size());
+  f.n_items = static_cast<int32_t>(n_items);
   f.kind = p.kind;
   f.causal = p.causal;
   f.chunk = static_cast<int32_t>(std::min<int64_t>(p.chunk, p.L));
   if (f.chunk < 1) f.chunk = 1;
   f.right = static_cast<int32_t>(p.right);
-  f.xcd_chunked = 1;
-  hipError_t e = launch_fwd(f, static_cast<int>(p.D), static_cast<int>(B),
-                            static_cast<hipStream_t>(launch->stream));
+  *out = f;
+  *queue_len = static_cast<int32_t>(n_items / 8);
+  return ATTN_OK;
+}
+
+attn_status run_group(const GroupParams& g, int64_t D, int64_t B, const attn_launch* launch) {
+  hipError_t e = launch_fwd(g, static_cast<int>(D), static_cast<int>(B), static_cast<hipStream_t>(launch->stream),
+                            static_cast<hipEvent_t>(launch->start_event),
+                            static_cast<hipEvent_t>(launch->stop_event));
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
   return ATTN_OK;
+}
+
+attn_status launch_with_plan(const attn_plan& p, const attn_tensor* q, const attn_tensor* k,
+                             const attn_tensor* v, const float* sink, attn_tensor* o,
+                             const attn_launch* launch) {
+  if (!launch) { set_error("launch is NULL"); return ATTN_E_INVAL; }
+  GroupParams g{};
+  g.n_jobs = 1;
+  attn_status st = make_job(p, q, k, v, sink, o, launch->workspace, launch->workspace_bytes,
+                            launch->softmax_scale, &g.job[0], &g.queue_len[0]);
+  if (st != ATTN_OK) return st;
+  return run_group(g, p.D, q->B, launch);
 }
 
 attn_status upload(const attn_plan& p, void* workspace, size_t bytes, void* stream) {
@@ -283,6 +301,45 @@ attn_status attn_masked_fwd(const attn_tensor* q, const attn_tensor* k, const at
     return launch_with_plan(*p, q, k, v, sink, o, launch);
   } catch (...) {
     set_error("unexpected exception");
+    return ATTN_E_NOMEM;
+  }
+}
+
+attn_status attn_masked_fwd_group(int32_t n, const attn_plan* const* plans, const attn_tensor* q,
+                                  const attn_tensor* k, const attn_tensor* v, const float* const* sinks,
+                                  attn_tensor* o, void* const* workspaces, const size_t* workspace_bytes,
+                                  const attn_launch* launch) {
+  try {
+    if (n < 1 || n > kMaxJobs) {
+      set_error("a group holds 1 to " + std::to_string(kMaxJobs) + " launches");
+      return n < 1 ? ATTN_E_INVAL : ATTN_E_UNSUPPORTED;
+    }
+    if (!plans || !q || !k || !v || !o || !workspaces || !workspace_bytes || !launch) {
+      set_error("NULL array argument");
+      return ATTN_E_INVAL;
+    }
+    GroupParams g{};
+    g.n_jobs = n;
+    for (int32_t j = 0; j < n; ++j) {
+      if (!plans[j]) { set_error("plan " + std::to_string(j) + " is NULL"); return ATTN_E_INVAL; }
+      if (plans[j]->D != plans[0]->D || q[j].B != q[0].B) {
+        set_error("the launches of a group need the same head dim and batch");
+        return ATTN_E_INVAL;
+      }
+      for (int32_t i = 0; i < j; ++i) {
+        if (workspaces[i] == workspaces[j]) { set_error("the launches of a group need distinct workspaces"); return ATTN_E_INVAL; }
+        if (o[i].data == o[j].data) { set_error("the launches of a group need distinct outputs"); return ATTN_E_INVAL; }
+      }
+      attn_status st = make_job(*plans[j], &q[j], &k[j], &v[j], sinks ? sinks[j] : nullptr, &o[j], workspaces[j],
+                                workspace_bytes[j], launch->softmax_scale, &g.job[j], &g.queue_len[j]);
+      if (st != ATTN_OK) {
+        set_error("launch " + std::to_string(j) + " of the group: " + attn_last_error());
+        return st;
+      }
+    }
+    return run_group(g, plans[0]->D, q[0].B, launch);
+  } catch (...) {
+    set_error("unexpected exception during launch");
     return ATTN_E_NOMEM;
   }
 }

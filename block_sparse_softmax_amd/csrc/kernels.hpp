@@ -34,10 +34,22 @@ struct FwdParams {
   int32_t L, H, n_items;
   int32_t kind, causal;
   int32_t chunk, right;
-  int32_t xcd_chunked;        // 1: XCD x runs the x-th of 8 equal-length queues of the schedule
 };
 
-// Launch the forward kernel for head dim D on `stream` with grid (n_items, B).
-hipError_t launch_fwd(const FwdParams& p, int D, int B, hipStream_t stream);
+// Several launches (jobs) with the same head dim and batch run as one kernel.
+// Every job's schedule is 8 equal-length XCD queues of n_items / 8 items; the
+// grid's XCD x takes, in job order, queue x of every job.
+constexpr int kMaxJobs = 8;
+struct GroupParams {
+  int32_t n_jobs;
+  int32_t queue_len[kMaxJobs];  // job j: items per XCD queue (n_items / 8)
+  FwdParams job[kMaxJobs];
+};
+static_assert(sizeof(GroupParams) <= 4096, "kernel arguments are limited to 4 KiB");
+
+// Launch the forward kernel for head dim D on `stream` with grid
+// (8 * sum of queue lengths, B); non-null events record the kernel's start and end.
+hipError_t launch_fwd(const GroupParams& g, int D, int B, hipStream_t stream, hipEvent_t start,
+                      hipEvent_t stop);
 
 }  // namespace bss

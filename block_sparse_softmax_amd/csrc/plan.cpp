@@ -209,8 +209,9 @@ void compile_blocks(attn_plan& p) {
 // better than dealing a head's rows to all XCDs for the 16K-token windows and
 // the 128K-token block masks).  A queue short enough to run in a few rounds of
 // its work-groups is ordered by descending cost.  A launch of at most two
-// rounds is dealt longest-first to the least-loaded queue instead.  Queues are
-// padded to equal length with null items.
+// rounds whose item costs are uneven is dealt longest-first to the
+// least-loaded queue instead.  Queues are padded to equal length with null
+// items.
 constexpr double kMinPiece = 12.0;     // tiles: below this a piece's merge costs more than it saves
 constexpr double kPieceOverhead = 2.0; // tiles: writing the partial state and the merge
 constexpr int kMaxPieces = 16;
@@ -229,7 +230,13 @@ std::vector<Item> layout_queues(const std::vector<int64_t>& head_order, const st
     seq.insert(seq.end(), v.begin(), v.end());
   }
   std::vector<std::vector<int64_t>> q(kXcds);
-  if (seq.size() <= static_cast<size_t>(2 * kSlots)) {
+  double cmax = 0.0, csum = 0.0;
+  for (int64_t i : seq) {
+    cmax = std::max(cmax, icost[i]);
+    csum += icost[i];
+  }
+  const bool uneven = !seq.empty() && cmax > 1.5 * csum / static_cast<double>(seq.size());
+  if (uneven && seq.size() <= static_cast<size_t>(2 * kSlots)) {
     // at most two rounds of work-groups: longest first over all queues (LPT)
     std::stable_sort(seq.begin(), seq.end(), [&](int64_t a, int64_t b) { return icost[a] > icost[b]; });
     std::vector<double> load(kXcds, 0.0);

@@ -93,6 +93,9 @@ typedef struct {
   void* workspace;            /* device memory of at least workspace_bytes            */
   size_t workspace_bytes;
   float softmax_scale;        /* <= 0 selects 1/sqrt(D)                                */
+  void* start_event;          /* optional hipEvent_t (created by the caller): records when the
+                                 attention kernel starts (hipExtLaunchKernel); NULL = none   */
+  void* stop_event;           /* optional hipEvent_t: records when the kernel ends          */
 } attn_launch;
 
 /* Opaque compiled mask: tile lists, schedule and the device image layout. */
@@ -178,6 +181,29 @@ attn_status attn_plan_upload(const attn_plan* plan, void* workspace, size_t work
 attn_status attn_masked_fwd_plan(const attn_plan* plan, const attn_tensor* q, const attn_tensor* k,
                                  const attn_tensor* v, const float* sink, attn_tensor* o,
                                  const attn_launch* launch);
+
+/*
+ * Grouped forward: n (1..8) independent launches with the same head dim D and
+ * batch B run as one kernel, whose work-groups take the items of every launch
+ * (the per-XCD queues of launch 0, then of launch 1, ...).  It serves a layer
+ * whose heads use different masks (the hybrid ViT of "Semantic Head
+ * Specialization ...": full, chunk and sliding-window heads side by side) and
+ * any set of masks applied together, with one dispatch instead of n.
+ *   plans[j], q[j], k[j], v[j], sinks[j] (sinks may be NULL, or hold NULL
+ *   entries), o[j]: as for attn_masked_fwd_plan; plans[j]'s image must have
+ *   been uploaded into workspaces[j] (workspace_bytes[j] long, at least
+ *   attn_plan_workspace_bytes).  Workspaces and outputs must be distinct
+ *   (outputs must not overlap at all: that is not checked beyond the base
+ *   pointers).  launch: stream, softmax_scale and the optional events; its
+ *   workspace fields are ignored.
+ * Errors: as attn_masked_fwd_plan for each launch (the message names it);
+ * ATTN_E_INVAL for n < 1, NULL arrays, differing D or B, shared workspaces or
+ * outputs; ATTN_E_UNSUPPORTED for n > 8.
+ */
+attn_status attn_masked_fwd_group(int32_t n, const attn_plan* const* plans, const attn_tensor* q,
+                                  const attn_tensor* k, const attn_tensor* v, const float* const* sinks,
+                                  attn_tensor* o, void* const* workspaces, const size_t* workspace_bytes,
+                                  const attn_launch* launch);
 
 /* Free a plan (NULL is allowed). */
 void attn_plan_destroy(attn_plan* plan);

@@ -254,3 +254,55 @@ def test_split_rows_merge(D, ci):
     _compare(got, ref, f"split-{ci}-d{D}")
     got2 = _run_gpu(q, k, v, mask, sink)   # counters returned to zero: the same result again
     assert np.array_equal(got, got2)
+
+
+def test_launch_events_bracket_the_kernel():
+    """Events handed to the launch are recorded at the kernel's start and end: their interval is
+    positive and lies inside an interval bracketed by ordinary stream events around the launch."""
+    from block_sparse_softmax_amd import prepare
+    L, H, D = 2048, 4, 80
+    q, k, v = (_bits_to_bf16(x) for x in _random_case(11, 1, H, L, D))
+    o = torch.empty_like(q)
+    pm = prepare(dict(kind="full"), L, H, D, q.device)
+    run = pm.bind(q, k, v, o, layout="bhld")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    ev[0].record()
+    run(ev[1], ev[2])
+    ev[3].record()
+    torch.cuda.synchronize()
+    inner, outer = ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
+    print(f"[events] kernel {inner * 1e3:.1f} us inside {outer * 1e3:.1f} us", flush=True)
+    assert 0.0 < inner <= outer + 1e-3
+    assert torch.isfinite(o.float()).all()
+
+
+def test_grouped_launch_matches_single_launches():
+    """One grouped launch of several masks (split rows and a sink among them) writes exactly what
+    the single launches write."""
+    from block_sparse_softmax_amd import bind_group, prepare
+    L, H, D = 2500, 2, 80
+    q, k, v = (_bits_to_bf16(x) for x in _random_case(21, 1, H, L, D))
+    sink = torch.as_tensor(np.random.default_rng(22).standard_normal(H).astype(np.float32)).cuda()
+    masks = [dict(kind="full"), dict(kind="chunk", chunk=256), dict(kind="window", left=128, right=128),
+             dict(kind="full", causal=True)]
+    sinks = [None, None, None, sink]
+    pms = [prepare(m, L, H, D, q.device) for m in masks]
+    single = []
+    for pm, s in zip(pms, sinks):
+        o = torch.empty_like(q)
+        pm.launch(q, k, v, o, sink=s, layout="bhld")
+        single.append(o)
+    outs = [torch.empty_like(q) for _ in masks]
+    run = bind_group(pms, [q] * 4, [k] * 4, [v] * 4, outs, sinks=sinks, layout="bhld")
+    for _ in range(2):  # twice: the split rows' counters are back at zero after a launch
+        for o in outs:
+            o.zero_()
+        run()
+        torch.cuda.synchronize()
+        for j in range(len(masks)):
+            assert torch.equal(outs[j], single[j]), masks[j]
+    ref = attention(*(x for x in _random_case(21, 1, H, L, D)), masks[1])["out"]
+    _compare(outs[1].float().cpu().double().numpy(), ref, "group-chunk")

@@ -252,3 +252,39 @@ def test_launch_argument_errors_without_gpu(lib):
     st = lib.attn_masked_fwd_plan(plan.handle, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), None,
                                   ctypes.byref(o_alias), ctypes.byref(ln))
     assert st == _lib.ATTN_E_INVAL
+
+
+def test_group_argument_errors_without_gpu(lib):
+    """The grouped entry point validates before any HIP call."""
+    plan = _lib.Plan(dict(kind="full"), 256, 2, 64)
+    plan2 = _lib.Plan(dict(kind="full"), 256, 2, 80)
+    fake = 1 << 20
+
+    def t(data=fake, D=64):
+        a = _lib.AttnTensor()
+        a.data, a.B, a.L, a.H, a.D = data, 1, 256, 2, D
+        a.stride_b, a.stride_l, a.stride_h = 256 * 128, 128, 64
+        return a
+
+    ln = _lib.Launch()
+    P = ctypes.c_void_p
+
+    def call(n, plans, outs, wss, D=64):
+        ta = _lib.AttnTensor * max(n, 1)
+        q = ta(*[t(D=D) for _ in range(max(n, 1))])
+        o = ta(*outs)
+        pl = (P * max(n, 1))(*plans)
+        ws = (P * max(n, 1))(*wss)
+        wb = (ctypes.c_size_t * max(n, 1))(*[plan.workspace_bytes()] * max(n, 1))
+        return lib.attn_masked_fwd_group(n, pl, q, q, q, None, o, ws, wb, ctypes.byref(ln))
+
+    h = plan.handle.value
+    assert call(0, [h], [t(fake * 2)], [fake * 4]) == _lib.ATTN_E_INVAL
+    assert call(9, [h] * 9, [t(fake * (2 + j)) for j in range(9)], [fake * (20 + j) for j in range(9)]) == \
+        _lib.ATTN_E_UNSUPPORTED
+    # shared workspace, shared output
+    assert call(2, [h, h], [t(fake * 2), t(fake * 3)], [fake * 4, fake * 4]) == _lib.ATTN_E_INVAL
+    assert call(2, [h, h], [t(fake * 2), t(fake * 2)], [fake * 4, fake * 5]) == _lib.ATTN_E_INVAL
+    # differing head dims
+    assert call(2, [h, plan2.handle.value], [t(fake * 2), t(fake * 3)], [fake * 4, fake * 5]) == _lib.ATTN_E_INVAL
+    assert "same head dim" in lib.attn_last_error().decode()
