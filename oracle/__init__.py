@@ -14,6 +14,9 @@ attention.py  the definition: explicit token mask from index predicates,
 tiles.py      the per-query-tile KV tile lists in canonical CSR form, derived
               from the dense mask (and, for block matrices, by index arithmetic).
 counts.py     unmasked-pair counts by enumeration of the explicit mask.
+rr_search.py  RRAttention's block-pattern search (Eq. 6-12): sampled queries,
+              stride-summed keys, stride softmax, block scores, top-tau, the
+              last-row protection.
 
 Every function is pinned by ``tests/test_oracle*.py`` against brute force,
 closed forms, invariants and the worked numbers printed on the pages; see the
@@ -23,3 +26,4 @@ module docstrings for the passage each function follows.
 from .attention import attention, allowed_rows, bf16_to_f64, dense_mask  # noqa: F401
 from .tiles import tile_lists  # noqa: F401
 from .counts import pair_count  # noqa: F401
+from .rr_search import rr_search  # noqa: F401
