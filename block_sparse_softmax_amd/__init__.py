@@ -8,13 +8,15 @@ from ._lib import (  # noqa: F401
     AttnError,
     Plan,
     PreparedMask,
+    RrSearch,
     bind_group,
     load_library,
     masked_fwd,
     masked_fwd_oneshot,
     prepare,
+    rr_search,
     tensor_view,
 )
 
-__all__ = ["AttnError", "Plan", "PreparedMask", "bind_group", "load_library", "masked_fwd", "masked_fwd_oneshot",
-           "prepare", "tensor_view"]
+__all__ = ["AttnError", "Plan", "PreparedMask", "RrSearch", "bind_group", "load_library", "masked_fwd",
+           "masked_fwd_oneshot", "prepare", "rr_search", "tensor_view"]

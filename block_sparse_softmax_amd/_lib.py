@@ -25,8 +25,8 @@ STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_E_INVAL", -2: "ATTN_E_UNSUPPORTED", -3: 
 # every symbol the header declares
 EXPORTS = ("attn_masked_fwd", "attn_workspace_bytes", "attn_plan_create", "attn_plan_tiles",
            "attn_plan_pairs", "attn_plan_schedule", "attn_plan_workspace_bytes", "attn_plan_upload",
-           "attn_masked_fwd_plan", "attn_masked_fwd_group", "attn_plan_destroy", "attn_last_error",
-           "attn_version")
+           "attn_masked_fwd_plan", "attn_masked_fwd_group", "attn_rr_workspace_bytes", "attn_rr_search",
+           "attn_plan_destroy", "attn_last_error", "attn_version")
 
 
 class AttnError(RuntimeError):
@@ -39,6 +39,11 @@ class AttnTensor(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p),
                 ("B", ctypes.c_int64), ("L", ctypes.c_int64), ("H", ctypes.c_int64), ("D", ctypes.c_int64),
                 ("stride_b", ctypes.c_int64), ("stride_l", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class RrParams(ctypes.Structure):
+    _fields_ = [("stride", ctypes.c_int64), ("block", ctypes.c_int64), ("tau", ctypes.c_float),
+                ("protect_last", ctypes.c_int32)]
 
 
 class MaskDesc(ctypes.Structure):
@@ -84,6 +89,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "attn_masked_fwd_plan": [plan_p, P(AttnTensor), P(AttnTensor), P(AttnTensor), vp, P(AttnTensor), P(Launch)],
             "attn_masked_fwd_group": [i32, P(vp), P(AttnTensor), P(AttnTensor), P(AttnTensor), P(vp), P(AttnTensor),
                                       P(vp), P(sz), P(Launch)],
+            "attn_rr_workspace_bytes": [P(AttnTensor), P(RrParams), P(sz)],
+            "attn_rr_search": [P(AttnTensor), P(AttnTensor), P(RrParams), vp, vp, P(Launch)],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -335,6 +342,45 @@ def bind_group(prepared, qs, ks, vs, outs, sinks=None, layout="blhd", stream=Non
         _check(fn(n, plans, qv, kv, vv, sk, ov, ws, wb, ctypes.byref(ln)))
         return keep[13]
     return run
+
+
+class RrSearch:
+    """RRAttention's block-pattern search (attn_rr_search) for one q/k shape and parameter set, with
+    its workspace and outputs allocated once."""
+
+    def __init__(self, q, stride: int, block: int, tau: float, protect_last: bool = True, layout: str = "blhd"):
+        import torch
+        lib = load_library()
+        self.layout = layout
+        self.prm = RrParams(stride, block, tau, 1 if protect_last else 0)
+        qv = tensor_view(q, layout)
+        nbytes = ctypes.c_size_t()
+        _check(lib.attn_rr_workspace_bytes(ctypes.byref(qv), ctypes.byref(self.prm), ctypes.byref(nbytes)))
+        self.workspace = torch.empty(max(256, nbytes.value), dtype=torch.uint8, device=q.device)
+        nb = -(-qv.L // block)
+        self.block_mask = torch.empty((qv.B, qv.H, nb, nb), dtype=torch.uint8, device=q.device)
+        self.block_score = torch.empty((qv.B, qv.H, nb, nb), dtype=torch.float32, device=q.device)
+
+    def __call__(self, q, k, stream=None, start_event=None, stop_event=None):
+        """Queue the search; returns (block_mask uint8 [B, H, Nb, Nb], block_score float32 [B, H, Nb, Nb])."""
+        lib = load_library()
+        qv, kv = tensor_view(q, self.layout), tensor_view(k, self.layout)
+        ln = Launch()
+        ln.stream = _stream_ptr(stream, q).value
+        ln.workspace = self.workspace.data_ptr()
+        ln.workspace_bytes = self.workspace.numel()
+        ln.start_event = None if start_event is None else start_event.cuda_event
+        ln.stop_event = None if stop_event is None else stop_event.cuda_event
+        _check(lib.attn_rr_search(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(self.prm),
+                                  ctypes.c_void_p(self.block_mask.data_ptr()),
+                                  ctypes.c_void_p(self.block_score.data_ptr()), ctypes.byref(ln)))
+        return self.block_mask, self.block_score
+
+
+def rr_search(q, k, stride: int, block: int, tau: float, protect_last: bool = True, layout: str = "blhd"):
+    """RRAttention's block-pattern search of bf16 CUDA tensors q, k (see include/bss_attn.h):
+    returns (block_mask uint8 [B, H, Nb, Nb], block_score float32 [B, H, Nb, Nb]) on the device."""
+    return RrSearch(q, stride, block, tau, protect_last, layout)(q, k)
 
 
 _prepared = {}

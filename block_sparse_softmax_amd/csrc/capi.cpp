@@ -344,6 +344,107 @@ attn_status attn_masked_fwd_group(int32_t n, const attn_plan* const* plans, cons
   }
 }
 
+namespace {
+
+constexpr int kRrTileQ = 128;    // sampled queries per work-group of the scores kernel
+constexpr int kRrMaxBlocks = 4096;
+
+// Validate a search request and fill the kernel parameters (pointers except the workspace).
+attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const attn_rr_params* prm, RrParams* out,
+                       size_t* ws_bytes) {
+  if (!q || !k || !prm) { set_error("q, k or prm is NULL"); return ATTN_E_INVAL; }
+  const int64_t B = q->B, L = q->L, H = q->H, D = q->D;
+  if (D != 64 && D != 80 && D != 128) {
+    set_error("head dim " + std::to_string(D) + " not supported (64, 80, 128)");
+    return ATTN_E_UNSUPPORTED;
+  }
+  if (B < 1 || B > 65535 || H < 1 || H > 65535 || L < 1 || L > INT32_MAX / 2) {
+    set_error("batch, heads or length out of range");
+    return ATTN_E_INVAL;
+  }
+  attn_status st;
+  if ((st = check_tensor(q, "q", B, L, H, D)) != ATTN_OK) return st;
+  if ((st = check_tensor(k, "k", B, L, H, D)) != ATTN_OK) return st;
+  const int64_t S = prm->stride, Bs = prm->block;
+  if (S < 1 || Bs < 1 || Bs % S != 0) { set_error("block must be a positive multiple of stride"); return ATTN_E_INVAL; }
+  const int64_t R = Bs / S;
+  if (R != 8 && R != 16 && R != 32) {
+    set_error("block / stride must be 8, 16 or 32 on the GPU path");
+    return ATTN_E_UNSUPPORTED;
+  }
+  if (!(prm->tau > 0.f && prm->tau <= 1.f)) { set_error("tau must be in (0, 1]"); return ATTN_E_INVAL; }
+  if (L < S) { set_error("the sequence is shorter than one stride"); return ATTN_E_INVAL; }
+  if (prm->protect_last != 0 && prm->protect_last != 1) { set_error("protect_last must be 0 or 1"); return ATTN_E_INVAL; }
+  const int64_t nb = (L + Bs - 1) / Bs;
+  if (nb > kRrMaxBlocks) {
+    set_error("more than " + std::to_string(kRrMaxBlocks) + " blocks per row");
+    return ATTN_E_UNSUPPORTED;
+  }
+  const int64_t ns = L / S;
+  const int64_t ns_pad = (ns + kRrTileQ - 1) / kRrTileQ * kRrTileQ;
+  RrParams p{};
+  p.q = static_cast<const uint16_t*>(q->data);
+  p.k = static_cast<const uint16_t*>(k->data);
+  p.q_sb = q->stride_b; p.q_sl = q->stride_l; p.q_sh = q->stride_h;
+  p.k_sb = k->stride_b; p.k_sl = k->stride_l; p.k_sh = k->stride_h;
+  p.scale_log2 = static_cast<float>(1.4426950408889634 / (double(S) * std::sqrt(double(D))));
+  p.tau = prm->tau;
+  p.B = static_cast<int32_t>(B); p.H = static_cast<int32_t>(H); p.L = static_cast<int32_t>(L);
+  p.D = static_cast<int32_t>(D); p.S = static_cast<int32_t>(S); p.Bs = static_cast<int32_t>(Bs);
+  p.ns = static_cast<int32_t>(ns);
+  p.ns_pad = static_cast<int32_t>(ns_pad);
+  p.nb = static_cast<int32_t>(nb);
+  int cap = 1;
+  while (cap < nb) cap <<= 1;
+  p.sel_cap = cap;
+  p.protect_last = prm->protect_last;
+  *out = p;
+  *ws_bytes = 2 * static_cast<size_t>(B) * H * ns_pad * D * sizeof(uint16_t);
+  return ATTN_OK;
+}
+
+}  // namespace
+
+attn_status attn_rr_workspace_bytes(const attn_tensor* q, const attn_rr_params* prm, size_t* bytes) {
+  try {
+    if (!bytes) { set_error("bytes is NULL"); return ATTN_E_INVAL; }
+    RrParams p;
+    return rr_prepare(q, q, prm, &p, bytes);
+  } catch (...) {
+    set_error("unexpected exception");
+    return ATTN_E_NOMEM;
+  }
+}
+
+attn_status attn_rr_search(const attn_tensor* q, const attn_tensor* k, const attn_rr_params* prm,
+                           void* block_mask, void* block_score, const attn_launch* launch) {
+  try {
+    if (!launch) { set_error("launch is NULL"); return ATTN_E_INVAL; }
+    RrParams p;
+    size_t need = 0;
+    attn_status st = rr_prepare(q, k, prm, &p, &need);
+    if (st != ATTN_OK) return st;
+    if (!block_mask || !block_score) { set_error("block_mask and block_score are required"); return ATTN_E_INVAL; }
+    if (!launch->workspace || launch->workspace_bytes < need) {
+      set_error("workspace smaller than attn_rr_workspace_bytes (" + std::to_string(need) + " bytes)");
+      return ATTN_E_WORKSPACE;
+    }
+    if (!aligned16(launch->workspace)) { set_error("workspace must be 16-byte aligned"); return ATTN_E_INVAL; }
+    p.qs = static_cast<uint16_t*>(launch->workspace);
+    p.ks = p.qs + static_cast<size_t>(p.B) * p.H * p.ns_pad * p.D;
+    p.score = static_cast<float*>(block_score);
+    p.bmask = static_cast<uint8_t*>(block_mask);
+    hipError_t e = launch_rr_search(p, static_cast<hipStream_t>(launch->stream),
+                                    static_cast<hipEvent_t>(launch->start_event),
+                                    static_cast<hipEvent_t>(launch->stop_event));
+    if (e != hipSuccess) return hip_fail(e, "search launch");
+    return ATTN_OK;
+  } catch (...) {
+    set_error("unexpected exception");
+    return ATTN_E_NOMEM;
+  }
+}
+
 void attn_plan_destroy(attn_plan* p) { delete p; }
 
 const char* attn_last_error(void) { return bss::g_last_error.c_str(); }

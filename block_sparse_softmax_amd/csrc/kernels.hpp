@@ -52,4 +52,24 @@ static_assert(sizeof(GroupParams) <= 4096, "kernel arguments are limited to 4 Ki
 hipError_t launch_fwd(const GroupParams& g, int D, int B, hipStream_t stream, hipEvent_t start,
                       hipEvent_t stop);
 
+// RRAttention block-pattern search (rr_search.hip).
+struct RrParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t q_sb, q_sl, q_sh;   // element strides
+  int64_t k_sb, k_sl, k_sh;
+  uint16_t* qs;               // workspace: sampled queries [B][H][ns_pad][D] bf16
+  uint16_t* ks;               // workspace: stride-summed keys [B][H][ns_pad][D] bf16
+  float* score;               // [B][H][nb][nb] block scores (Eq. 10)
+  uint8_t* bmask;             // [B][H][nb][nb] block matrix (Eq. 11-12)
+  float scale_log2;           // log2(e) / (S sqrt(D))
+  float tau;
+  int32_t B, H, L, D, S, Bs;
+  int32_t ns, ns_pad, nb, sel_cap, protect_last;
+};
+
+// Queue the three search kernels on `stream`; non-null events are recorded
+// before the first and after the last.
+hipError_t launch_rr_search(const RrParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
 }  // namespace bss

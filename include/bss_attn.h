@@ -205,6 +205,48 @@ attn_status attn_masked_fwd_group(int32_t n, const attn_plan* const* plans, cons
                                   attn_tensor* o, void* const* workspaces, const size_t* workspace_bytes,
                                   const attn_launch* launch);
 
+/*
+ * RRAttention block-pattern search ("RRAttention", section 3, Eq. 6-12): from
+ * Q and K to the block matrix B consumed by the BLOCK mask kind.
+ *   Eq. 6-7  head h samples query P(i,h) = iS + (S-1-(h mod S)) of every full
+ *            stride i = 0 .. floor(L/S)-1;
+ *   Eq. 8    I_ij = q_P(i,h) . (sum of the keys of stride j) / (S sqrt(D));
+ *   Eq. 9    softmax of each row over the causal key strides j <= i (the
+ *            attention it feeds is causal, Eq. 2 and 5);
+ *   Eq. 10   S_mn = sum of those probabilities over the strides of query
+ *            block m and key block n (stride i lies in block iS / block);
+ *   Eq. 11   per query block, the shortest prefix of S_m,n (n <= m) sorted
+ *            in descending order (ties: lower n first) whose mass reaches
+ *            tau times the row's mass;
+ *   Eq. 12   with protect_last, every causal block of the last query block.
+ * The stride importance runs on bf16 MFMA (stride sums of the keys rounded
+ * to bf16 once) with fp32 accumulation; the selection compares fp32 sums.
+ */
+typedef struct {
+  int64_t stride;             /* S >= 1                                                   */
+  int64_t block;              /* block size Bs: a multiple of S with Bs / S in {8, 16, 32} */
+  float tau;                  /* threshold in (0, 1]                                      */
+  int32_t protect_last;       /* 1: keep every causal block of the last query block      */
+} attn_rr_params;
+
+/* Workspace bytes attn_rr_search needs for q's shape (B, L, H, D) and prm. */
+attn_status attn_rr_workspace_bytes(const attn_tensor* q, const attn_rr_params* prm, size_t* bytes);
+
+/*
+ * Run the search on launch->stream (asynchronous; launch->workspace of at least
+ * attn_rr_workspace_bytes; optional events bracket the three kernels).
+ *   q, k         : bf16 [B, L, H, D] device views (same shape; D in {64, 80, 128}).
+ *   block_mask   : device uint8 [B][H][Nb][Nb], Nb = ceil(L / block): written
+ *                  entirely (1 = compute the block pair; zero above the diagonal).
+ *   block_score  : device float [B][H][Nb][Nb]: the block scores S_mn (zero
+ *                  above the diagonal).
+ * Errors: ATTN_E_INVAL (shapes, strides, NULL pointers, stride/block/tau out of
+ * range, L < stride), ATTN_E_UNSUPPORTED (D, block / stride not in {8, 16, 32},
+ * Nb > 4096), ATTN_E_WORKSPACE, ATTN_E_HIP.
+ */
+attn_status attn_rr_search(const attn_tensor* q, const attn_tensor* k, const attn_rr_params* prm,
+                           void* block_mask, void* block_score, const attn_launch* launch);
+
 /* Free a plan (NULL is allowed). */
 void attn_plan_destroy(attn_plan* plan);
 

@@ -32,6 +32,11 @@ notation, for one (batch, head) at a time:
 
 Returns the block scores S (float64) and the block matrix B (uint8), both
 [Nb, Nb] with Nb = ceil(L / Bs).
+
+ks_round="bf16" reproduces one rounding that a bf16 matrix-core
+implementation states: each stride sum of keys is formed in float32 (keys
+added in order k_jS, k_jS+1, ...) and rounded once to bfloat16
+(round-to-nearest-even).  Everything else stays float64.
 """
 
 from __future__ import annotations
@@ -92,8 +97,30 @@ def top_tau(scores_row: np.ndarray, tau: float) -> np.ndarray:
     return order[: min(k + 1, len(order))]
 
 
+def _round_bf16(x32: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bfloat16 (ties to even), returned as float64."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def stride_key_sums(kh: np.ndarray, S: int, ks_round=None) -> np.ndarray:
+    """sum_{k = jS}^{(j+1)S - 1} k_k for every full stride j (Eq. 8's key aggregate)."""
+    L, d = kh.shape
+    ns = L // S
+    blocks = kh[: ns * S].reshape(ns, S, d)
+    if ks_round is None:
+        return blocks.sum(axis=1)
+    if ks_round != "bf16":
+        raise ValueError(ks_round)
+    acc = np.zeros((ns, d), dtype=np.float32)
+    for s in range(S):                       # in order, float32
+        acc = acc + blocks[:, s].astype(np.float32)
+    return _round_bf16(acc)
+
+
 def rr_search(q, k, S: int, Bs: int, tau: float, protect_last: bool = True, b: int = 0, h: int = 0,
-              query_blocks=None):
+              query_blocks=None, ks_round=None):
     """Block scores and block matrix for (batch b, head h) of bf16 bit arrays (or floats) q, k of
     shape [B, H, L, d].
 
@@ -111,7 +138,7 @@ def rr_search(q, k, S: int, Bs: int, tau: float, protect_last: bool = True, b: i
     scores = np.zeros((nb, nb))
     bmat = np.zeros((nb, nb), dtype=np.uint8)
     pos = sample_positions(L, S, h)
-    ks = kh[: ns * S].reshape(ns, S, d).sum(axis=1)
+    ks = stride_key_sums(kh, S, ks_round)
     for m in blocks:
         rows = np.arange(m * R, min((m + 1) * R, ns))
         if rows.size:

@@ -1,0 +1,138 @@
+"""GPU parity of RRAttention's block-pattern search (attn_rr_search) against the float64 oracle.
+
+Block scores: compared with the oracle that rounds each stride sum of keys to bf16 as the kernel
+states (everything else float64), within a bound from the remaining fp32 arithmetic.  Block matrix:
+a floating-point decision (a sort and a threshold), so each row is checked to be a valid top-tau
+selection of the oracle's scores within that bound (the mass reaches tau, no selected block is
+superfluous, no unselected block is clearly larger), and must equal the oracle's row wherever no
+decision lies within the bound.  The last query block is protected exactly."""
+
+import numpy as np
+import pytest
+import torch
+
+from block_sparse_softmax_amd import inputs as gen
+from oracle.rr_search import rr_search as rr_oracle
+
+pytestmark = pytest.mark.gpu
+
+# |S_gpu - S_oracle| per unit of a row's mass scale (R = strides per block): the scores come from
+# bf16 products accumulated in fp32 and fp32 exponentials / sums, observed below 1e-7 R
+SCORE_TOL = 2e-6
+
+
+def _dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _random(seed, B, H, L, D):
+    rng = np.random.default_rng(seed)
+    return tuple(gen.f32_to_bf16_bits(rng.standard_normal((B, H, L, D), dtype=np.float32)) for _ in range(2))
+
+
+def _planted(seed, H, L, D, Bs):
+    """Queries share a direction u; the keys of a few chosen blocks per head point along it."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    q = rng.standard_normal((1, H, L, D)) + 3.0 * u
+    k = rng.standard_normal((1, H, L, D))
+    nb = -(-L // Bs)
+    for h in range(H):
+        for n in rng.choice(max(1, nb - 1), size=min(3, max(1, nb - 1)), replace=False):
+            k[0, h, n * Bs:(n + 1) * Bs] += 6.0 * u
+    return tuple(gen.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k))
+
+
+def _check_row(sel, s, tau, eps):
+    """sel: GPU row (0/1 over n <= m); s: oracle scores (n <= m).  Returns True if the decision is
+    clear (then sel must equal the oracle's own selection)."""
+    T = s.sum()
+    G = np.flatnonzero(sel)
+    if T <= 0:
+        assert G.size == 0
+        return True
+    mass = s[G].sum()
+    assert G.size > 0 and mass >= tau * T - eps, (mass, tau * T)
+    assert mass - s[G].min() < tau * T + eps, "a selected block is superfluous"
+    rest = np.setdiff1d(np.arange(s.size), G)
+    if rest.size:
+        assert s[rest].max() <= s[G].min() + eps, "a larger block was left out"
+    # clear decision: the sorted prefix sums stay away from the threshold and no near-ties cross it
+    order = np.argsort(-s, kind="stable")
+    cs = np.cumsum(s[order])
+    k = int(np.searchsorted(cs, tau * T))
+    k = min(k, s.size - 1)
+    clear = (cs[k] - tau * T > eps) and (k == 0 or tau * T - cs[k - 1] > eps)
+    if k + 1 < s.size:
+        clear = clear and (s[order[k]] - s[order[k + 1]] > eps)
+    return clear
+
+
+CASES = [
+    # (L, H, D, S, Bs, tau, kind)
+    (2048, 3, 128, 8, 128, 0.9, "random"),
+    (2000, 2, 64, 8, 128, 0.5, "random"),      # ragged last block
+    (1030, 2, 80, 4, 128, 0.9, "random"),      # ragged last stride, 32 strides per block
+    (1024, 2, 128, 16, 128, 0.95, "random"),   # 8 strides per block
+    (4096, 4, 128, 8, 128, 0.5, "planted"),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_rr_search_parity(ci):
+    from block_sparse_softmax_amd import rr_search
+    L, H, D, S, Bs, tau, kind = CASES[ci]
+    print(f"[case] rr search L={L} H={H} D={D} S={S} Bs={Bs} tau={tau} {kind}", flush=True)
+    q, k = _random(50 + ci, 1, H, L, D) if kind == "random" else _planted(60 + ci, H, L, D, Bs)
+    bm, sc = rr_search(_dev(q), _dev(k), S, Bs, tau, layout="bhld")
+    torch.cuda.synchronize()
+    bm, sc = bm.cpu().numpy(), sc.cpu().numpy().astype(np.float64)
+    nb = -(-L // Bs)
+    R = Bs // S
+    worst, clear_rows, rows = 0.0, 0, 0
+    for h in range(H):
+        s_ref, b_ref = rr_oracle(q, k, S, Bs, tau, h=h, ks_round="bf16")
+        err = np.abs(sc[0, h] - s_ref)
+        worst = max(worst, float(err.max()))
+        assert np.all(np.triu(sc[0, h], 1) == 0) and np.all(np.triu(bm[0, h], 1) == 0)
+        assert err.max() <= SCORE_TOL * R, (h, err.max())
+        eps = 4 * SCORE_TOL * R
+        for m in range(nb - 1):
+            clear = _check_row(bm[0, h, m, : m + 1], s_ref[m, : m + 1], tau, eps)
+            rows += 1
+            if clear:
+                clear_rows += 1
+                assert np.array_equal(bm[0, h, m], b_ref[m]), (h, m)
+        assert np.all(bm[0, h, nb - 1] == 1)
+    print(f"[rr] max |dS| = {worst:.2e}; {clear_rows}/{rows} rows with a clear decision, all equal", flush=True)
+    assert clear_rows >= 0.5 * rows
+
+
+def test_rr_search_128k_sampled_blocks():
+    """The 128K-token shape (32 heads, d = 128, stride 8, block 128, tau 0.9): GPU search over every
+    head; the oracle on 8 seeded query blocks of 4 heads."""
+    from block_sparse_softmax_amd import RrSearch
+    L, H, D, S, Bs, tau = 131072, 32, 128, 8, 128, 0.9
+    print("[case] rr search 128k: generating inputs", flush=True)
+    q = np.stack([gen.gaussian_bf16(0, 5, gen.Q_ID, h, (1, L, D)) for h in range(H)], axis=1)
+    k = np.stack([gen.gaussian_bf16(0, 5, gen.K_ID, h, (1, L, D)) for h in range(H)], axis=1)
+    qt, kt = _dev(q), _dev(k)
+    srch = RrSearch(qt, S, Bs, tau, layout="bhld")
+    bm, sc = srch(qt, kt)
+    torch.cuda.synchronize()
+    nb = L // Bs
+    rng = np.random.default_rng(7)
+    R = Bs // S
+    for h in (0, 9, 18, 31):
+        blocks = np.sort(rng.choice(nb - 1, size=8, replace=False))
+        s_ref, b_ref = rr_oracle(q, k, S, Bs, tau, h=h, query_blocks=blocks, ks_round="bf16")
+        s_gpu = sc[0, h].cpu().numpy().astype(np.float64)
+        b_gpu = bm[0, h].cpu().numpy()
+        for m in blocks:
+            err = np.abs(s_gpu[m] - s_ref[m]).max()
+            assert err <= SCORE_TOL * R, (h, m, err)
+            if _check_row(b_gpu[m, : m + 1], s_ref[m, : m + 1], tau, 4 * SCORE_TOL * R):
+                assert np.array_equal(b_gpu[m], b_ref[m]), (h, m)
+        assert np.all(b_gpu[nb - 1] == 1)
+    print(f"[rr] 128k: density of the selected blocks {bm.float().mean().item() * 2:.3f} of the causal half", flush=True)

@@ -136,3 +136,26 @@ def test_planted_pattern_is_found():
     for m in range(1, L // Bs):
         assert B[m, 1] == 1 and B[m].sum() == 1, (m, B[m])
         assert scores[m, 1] > 0.5 * scores[m].sum()
+
+
+def test_bf16_key_sums_option():
+    """ks_round='bf16': float32 sums in order, then round-to-nearest-even to bfloat16 (checked
+    against torch's conversion); the block scores stay within the rounding's effect of float64."""
+    import torch
+    from oracle.rr_search import stride_key_sums
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((64, 16)).astype(np.float32).astype(np.float64)
+    got = stride_key_sums(k, 8, "bf16")
+    acc = torch.zeros(8, 16, dtype=torch.float32)
+    kt = torch.from_numpy(k.astype(np.float32)).reshape(8, 8, 16)
+    for s in range(8):
+        acc = acc + kt[:, s]
+    want = acc.to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, want)
+    exact = stride_key_sums(k, 8)
+    assert np.max(np.abs(got - exact) / np.maximum(np.abs(exact), 1e-30)) <= 2.0 ** -8
+    q = _rand_bits((1, 1, 1024, 32), 11)
+    kk = _rand_bits((1, 1, 1024, 32), 12)
+    s0, _ = rr_search(q, kk, 8, 128, 0.9)
+    s1, _ = rr_search(q, kk, 8, 128, 0.9, ks_round="bf16")
+    assert 0 < np.max(np.abs(s1 - s0)) <= 1e-2
