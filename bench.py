@@ -18,7 +18,8 @@ Extra workloads (skipped with --quick): the 1792-px ViT layer (L = 16384, full
 and sliding window radius 512), causal LM prefill with per-head windows and
 sinks (L = 4096, d = 128) and 128K-token block-sparse causal prefill (32 heads,
 d = 128, block 128, about half of the causal blocks kept), timed the same way
-and reported under "extra".
+and reported under "extra", with RRAttention's block-pattern search on the
+128K-token Q and K (stride 8, block 128, tau 0.9).
 
 Prints ONE JSON line.
 """
@@ -210,6 +211,41 @@ def _cpu_baseline(setup, budget_s=20.0):
                        f"masks of the {setup['w']['L']}-token workload, float64 numpy, {done_s:.1f} s")
 
 
+def _bench_rr(q, k, steps, warmup, layout, stride=8, block=128, tau=0.9):
+    """RRAttention's block-pattern search on the 128K-token Q, K (all heads): events around its three
+    kernels.  Algorithmic work: the stride importance GEMM of Eq. 8 once over the causal stride pairs
+    (2 d flops per pair); bytes: Q's sampled rows and K read once, the block scores and block matrix
+    written once."""
+    import numpy as np
+    import torch
+    from block_sparse_softmax_amd import RrSearch
+    srch = RrSearch(q, stride, block, tau, layout=layout)
+    for _ in range(max(1, warmup)):
+        srch(q, k)
+    ev = _events(steps)
+    torch.cuda.synchronize()
+    for a, b in ev:
+        srch(q, k, start_event=a, stop_event=b)
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in ev]
+    B, H, L, D = (q.shape[0], q.shape[1], q.shape[2], q.shape[3]) if layout == "bhld" else \
+        (q.shape[0], q.shape[2], q.shape[1], q.shape[3])
+    ns = L // stride
+    nb = -(-L // block)
+    flops = 2.0 * D * B * H * ns * (ns + 1) / 2
+    nbytes = B * H * (ns * D * 2 + L * D * 2 + nb * nb * 5)
+    avg = float(np.mean(t))
+    density = float(srch.block_mask.float().mean().item() * 2)
+    return dict(workload=f"RRAttention block-pattern search (Eq. 6-12): L={L}, {H} heads, d={D}, stride {stride}, "
+                         f"block {block}, tau {tau}; synthetic Q, K of the 128K block-sparse workload",
+                avg_ms=avg, min_ms=float(np.min(t)), tflops=flops / (avg * 1e-3) / 1e12,
+                frac_bf16_peak=flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                alg_gbs=nbytes / (avg * 1e-3) / 1e9, kept_causal_fraction=density,
+                roofline=dict(bound="mfma", achieved=flops / (avg * 1e-3) / 1e12, peak=PEAK_BF16_TFLOPS,
+                              unit="TFLOP/s", frac=flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, traffic=None,
+                              kernel="rr_prep + rr_scores + rr_select", avg_launch_ms=avg))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,6 +302,9 @@ def main():
             extra[name] = dict(workload=WORKLOADS[name], ms_per_step=ms2, tflops=tf2 / (ms2 * 1e-3) / 1e12,
                                frac_bf16_peak=tf2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, masks=r2,
                                grouped_launch=g2, roofline=_roofline(setup, g2, tf2, name))
+            if name == "blocksparse128k":
+                q, k, _ = setup["dev"]
+                extra["rr_search128k"] = _bench_rr(q, k, 5, 1, args.layout)
 
     out = {
         "metric": "effective attention TFLOP/s (unmasked pairs) and % bf16 MFMA peak, 1 MI355X",
