@@ -51,7 +51,7 @@ class MaskDesc(ctypes.Structure):
                 ("chunk", ctypes.c_int64), ("left", ctypes.c_int64), ("right", ctypes.c_int64),
                 ("head_left", ctypes.POINTER(ctypes.c_int64)),
                 ("block", ctypes.c_int64), ("block_mask", ctypes.POINTER(ctypes.c_uint8)),
-                ("block_mask_heads", ctypes.c_int32)]
+                ("block_mask_heads", ctypes.c_int32), ("prefix", ctypes.c_int64)]
 
 
 class Launch(ctypes.Structure):
@@ -151,6 +151,7 @@ def build_desc(mask: dict, H: int):
         keep.append(arr)
         d.block_mask = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
         d.block_mask_heads = arr.shape[0]
+    d.prefix = int(mask.get("prefix", 0) or 0)
     return d, keep
 
 

@@ -201,7 +201,10 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D>
+// PREFIX: the launch may add prefix tokens to the rows' sets (a second
+// allowed interval [0, pend) checked on PARTIAL tiles); without it the mask
+// is the single interval [lo, hi).
+template <int D, bool PREFIX>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams g) {
   using S = Shape<D>;
   constexpr int64_t kSlotFloats = partial_slot_floats(D);
@@ -245,10 +248,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
 
   const unsigned char* qbase =
       reinterpret_cast<const unsigned char*>(p.q + b * p.q_sb + head * p.q_sh);
+  // grouped-query attention: runs of kv_group consecutive query heads share one K/V head
+  const int kv_head = head / p.kv_group;
   const unsigned char* kbase =
-      reinterpret_cast<const unsigned char*>(p.k + b * p.k_sb + head * p.k_sh);
+      reinterpret_cast<const unsigned char*>(p.k + b * p.k_sb + kv_head * p.k_sh);
   const unsigned char* vbase =
-      reinterpret_cast<const unsigned char*>(p.v + b * p.v_sb + head * p.v_sh);
+      reinterpret_cast<const unsigned char*>(p.v + b * p.v_sb + kv_head * p.v_sh);
   unsigned char* obase = reinterpret_cast<unsigned char*>(p.o + b * p.o_sb + head * p.o_sh);
   const int64_t q_row_bytes = p.q_sl * 2, k_row_bytes = p.k_sl * 2, v_row_bytes = p.v_sl * 2,
                 o_row_bytes = p.o_sl * 2;
@@ -288,6 +293,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
   if (p.causal || p.kind == kMaskBlock) hi = min(hi, qi + 1);
   hi = max(hi, lo);
   const unsigned width = static_cast<unsigned>(hi - lo);
+  // prefix tokens: keys [0, pend) are allowed as well
+  int pend = 0;
+  if constexpr (PREFIX) {
+    pend = min(p.prefix, p.L);
+    if (p.causal) pend = min(pend, qi + 1);
+  }
   // A tile flagged PARTIAL for the 128 rows of the item can still allow every
   // pair for this wave's 32 rows: the intervals' ends never decrease with the
   // row, so the wave's rows all allow keys [lo of its last row, hi of its
@@ -534,10 +545,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
     // mask (PARTIAL) and row max of tile j: step r (0..15)
     float x = 0.f;
     const unsigned mbase = static_cast<unsigned>((ent >> 1) * kBN + 4 * h2 - lo);
+    const int kbase_key = (ent >> 1) * kBN + 4 * h2;
     auto mask_step = [&](int r) __attribute__((always_inline)) {
       const unsigned u = mbase + 8 * (r >> 2) + (r & 3);
-      sn[0][r] = (u >= width) ? -INFINITY : sn[0][r];
-      sn[1][r] = (u + 32 >= width) ? -INFINITY : sn[1][r];
+      if constexpr (PREFIX) {
+        const int key = kbase_key + 8 * (r >> 2) + (r & 3);
+        sn[0][r] = (u >= width && key >= pend) ? -INFINITY : sn[0][r];
+        sn[1][r] = (u + 32 >= width && key + 32 >= pend) ? -INFINITY : sn[1][r];
+      } else {
+        sn[0][r] = (u >= width) ? -INFINITY : sn[0][r];
+        sn[1][r] = (u + 32 >= width) ? -INFINITY : sn[1][r];
+      }
     };
     auto max_step = [&](int r) __attribute__((always_inline)) {
       x = (r == 0) ? fmaxf(sn[0][0], sn[1][0]) : max3(x, sn[0][r], sn[1][r]);
@@ -670,11 +688,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
     }
     if constexpr (kMask) {
       const unsigned mbase = static_cast<unsigned>((ent >> 1) * kBN + 4 * h2 - lo);
+      const int kbase_key = (ent >> 1) * kBN + 4 * h2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const unsigned u = mbase + 8 * (r >> 2) + (r & 3);
-        sn[0][r] = (u >= width) ? -INFINITY : sn[0][r];
-        sn[1][r] = (u + 32 >= width) ? -INFINITY : sn[1][r];
+        if constexpr (PREFIX) {
+          const int key = kbase_key + 8 * (r >> 2) + (r & 3);
+          sn[0][r] = (u >= width && key >= pend) ? -INFINITY : sn[0][r];
+          sn[1][r] = (u + 32 >= width && key + 32 >= pend) ? -INFINITY : sn[1][r];
+        } else {
+          sn[0][r] = (u >= width) ? -INFINITY : sn[0][r];
+          sn[1][r] = (u + 32 >= width) ? -INFINITY : sn[1][r];
+        }
       }
     }
     if constexpr (kFirst) {
@@ -750,7 +775,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
 #pragma unroll 1
       for (int kk = 0; kk < kBN; ++kk) {
         const int key = kv0 + kk;
-        const bool allowed = key < p.L && ((ent & 1) || static_cast<unsigned>(key - lo) < width);
+        const bool allowed = key < p.L && ((ent & 1) || static_cast<unsigned>(key - lo) < width || key < pend);
         const int krow = key < p.L ? key : p.L - 1;
         const unsigned char* kr = kbase + static_cast<int64_t>(krow) * k_row_bytes + h2 * DH * 2;
         float part = 0.f;
@@ -815,7 +840,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
     for (int e = e_begin; e < e_end; ++e) {
       const int ent = p.kv[e];
       const int j0 = (ent >> 1) * kBN;
-      has = has || (ent & 1) || (j0 < hi_row && j0 + kBN > lo);
+      has = has || (ent & 1) || (j0 < hi_row && j0 + kBN > lo) || j0 < pend;
     }
     return has;
   };
@@ -987,8 +1012,11 @@ template <int D>
 hipError_t launch_d(const GroupParams& g, int blocks, int B, hipStream_t stream, hipEvent_t start,
                     hipEvent_t stop) {
   dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(B));
+  bool prefix = false;
+  for (int j = 0; j < g.n_jobs; ++j) prefix = prefix || g.job[j].prefix > 0;
   // the extended launch attaches the events to the kernel's own dispatch
-  hipExtLaunchKernelGGL(attn_fwd_kernel<D>, grid, dim3(kThreads), 0, stream, start, stop, 0, g);
+  if (prefix) hipExtLaunchKernelGGL((attn_fwd_kernel<D, true>), grid, dim3(kThreads), 0, stream, start, stop, 0, g);
+  else hipExtLaunchKernelGGL((attn_fwd_kernel<D, false>), grid, dim3(kThreads), 0, stream, start, stop, 0, g);
   return hipGetLastError();
 }
 

@@ -65,8 +65,15 @@ attn_status make_job(const attn_plan& p, const attn_tensor* q, const attn_tensor
   if (B < 1 || B > 65535) { set_error("batch must be in [1, 65535]"); return ATTN_E_INVAL; }
   attn_status st;
   if ((st = check_tensor(q, "q", B, p.L, p.H, p.D)) != ATTN_OK) return st;
-  if ((st = check_tensor(k, "k", B, p.L, p.H, p.D)) != ATTN_OK) return st;
-  if ((st = check_tensor(v, "v", B, p.L, p.H, p.D)) != ATTN_OK) return st;
+  // grouped-query attention: K and V may have fewer heads, a divisor of Q's
+  if (!k || !v) { set_error("k or v is NULL"); return ATTN_E_INVAL; }
+  const int64_t hkv = k->H;
+  if (hkv < 1 || p.H % hkv != 0 || v->H != hkv) {
+    set_error("k and v need the same number of heads, a divisor of q's (" + std::to_string(p.H) + ")");
+    return ATTN_E_INVAL;
+  }
+  if ((st = check_tensor(k, "k", B, p.L, hkv, p.D)) != ATTN_OK) return st;
+  if ((st = check_tensor(v, "v", B, p.L, hkv, p.D)) != ATTN_OK) return st;
   if ((st = check_tensor(o, "o", B, p.L, p.H, p.D)) != ATTN_OK) return st;
   if (o->data == q->data || o->data == k->data || o->data == v->data) {
     set_error("o must not alias q, k or v");
@@ -117,6 +124,8 @@ attn_status make_job(const attn_plan& p, const attn_tensor* q, const attn_tensor
   f.chunk = static_cast<int32_t>(std::min<int64_t>(p.chunk, p.L));
   if (f.chunk < 1) f.chunk = 1;
   f.right = static_cast<int32_t>(p.right);
+  f.prefix = static_cast<int32_t>(std::min<int64_t>(p.prefix, p.L));
+  f.kv_group = static_cast<int32_t>(p.H / hkv);
   *out = f;
   *queue_len = static_cast<int32_t>(n_items / 8);
   return ATTN_OK;
@@ -364,7 +373,11 @@ attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const attn_rr
   }
   attn_status st;
   if ((st = check_tensor(q, "q", B, L, H, D)) != ATTN_OK) return st;
-  if ((st = check_tensor(k, "k", B, L, H, D)) != ATTN_OK) return st;
+  if (k->H < 1 || H % k->H != 0) {
+    set_error("k needs a number of heads that divides q's (grouped-query attention)");
+    return ATTN_E_INVAL;
+  }
+  if ((st = check_tensor(k, "k", B, L, k->H, D)) != ATTN_OK) return st;
   const int64_t S = prm->stride, Bs = prm->block;
   if (S < 1 || Bs < 1 || Bs % S != 0) { set_error("block must be a positive multiple of stride"); return ATTN_E_INVAL; }
   const int64_t R = Bs / S;
@@ -398,6 +411,7 @@ attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const attn_rr
   while (cap < nb) cap <<= 1;
   p.sel_cap = cap;
   p.protect_last = prm->protect_last;
+  p.kv_group = static_cast<int32_t>(H / k->H);
   *out = p;
   *ws_bytes = 2 * static_cast<size_t>(B) * H * ns_pad * D * sizeof(uint16_t);
   return ATTN_OK;

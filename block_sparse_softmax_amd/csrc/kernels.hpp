@@ -34,6 +34,8 @@ struct FwdParams {
   int32_t L, H, n_items;
   int32_t kind, causal;
   int32_t chunk, right;
+  int32_t prefix;             // prefix tokens added to every row's set (0 = none)
+  int32_t kv_group;           // query heads per K/V head (grouped-query attention; 1 = MHA)
 };
 
 // Several launches (jobs) with the same head dim and batch run as one kernel.
@@ -66,6 +68,7 @@ struct RrParams {
   float tau;
   int32_t B, H, L, D, S, Bs;
   int32_t ns, ns_pad, nb, sel_cap, protect_last;
+  int32_t kv_group;           // query heads per K head (grouped-query attention)
 };
 
 // Queue the three search kernels on `stream`; non-null events are recorded

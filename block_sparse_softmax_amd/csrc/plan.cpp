@@ -6,6 +6,8 @@
 //   WINDOW  i - left_h <= j <= i + right           (inclusive; the serialisation
 //                                                   slide's 7..23 example)
 //   BLOCK   B_h[i/Bs][j/Bs] == 1 and j <= i         (RRAttention Eq. 2)
+//   prefix  keys 0 .. prefix-1 are added to every row's set (FULL, CHUNK,
+//           WINDOW; the StreamingLLM sink tokens kept beside a window).
 //   causal = 1 additionally requires j <= i.
 // For FULL, CHUNK and WINDOW the allowed keys of row i form one interval
 // [lo(i), hi(i)) whose ends never decrease as i grows; the compiler works on
@@ -60,6 +62,13 @@ inline void row_interval(const attn_plan& p, int64_t h, int64_t i, int64_t* lo, 
   *hi = b;
 }
 
+// Prefix part [0, pe) of row i's allowed set (empty without a prefix).
+inline int64_t row_prefix_end(const attn_plan& p, int64_t i) {
+  int64_t pe = std::min(p.prefix, p.L);
+  if (p.causal) pe = std::min(pe, i + 1);
+  return pe;
+}
+
 attn_status validate(const attn_mask_desc* m, int64_t L, int64_t H, int64_t D) {
   if (!m) { set_error("mask descriptor is NULL"); return ATTN_E_INVAL; }
   if (L < 1 || H < 1) { set_error("L and H must be >= 1"); return ATTN_E_INVAL; }
@@ -70,6 +79,11 @@ attn_status validate(const attn_mask_desc* m, int64_t L, int64_t H, int64_t D) {
     return ATTN_E_UNSUPPORTED;
   }
   if (m->causal != 0 && m->causal != 1) { set_error("causal must be 0 or 1"); return ATTN_E_INVAL; }
+  if (m->prefix < 0) { set_error("prefix must be >= 0"); return ATTN_E_INVAL; }
+  if (m->prefix > 0 && m->kind == ATTN_MASK_BLOCK) {
+    set_error("prefix tokens are not defined for BLOCK masks");
+    return ATTN_E_INVAL;
+  }
   switch (m->kind) {
     case ATTN_MASK_FULL:
       break;
@@ -126,8 +140,16 @@ void compile_intervals(attn_plan& p) {
         row_interval(p, h, i, &lo, &hi);
         max_lo = std::max(max_lo, lo);
         min_hi = std::min(min_hi, hi);
-        if (hi <= lo) continue;
-        p.pairs[h] += hi - lo;
+        const int64_t pe = row_prefix_end(p, i);
+        if (pe > 0) {
+          diff[0] += 1;
+          diff[(pe - 1) / bn + 1] -= 1;
+        }
+        if (hi <= lo) {
+          p.pairs[h] += pe;
+          continue;
+        }
+        p.pairs[h] += (hi - lo) + pe - std::max<int64_t>(0, std::min(pe, hi) - lo);
         diff[lo / bn] += 1;
         diff[(hi - 1) / bn + 1] -= 1;
       }
@@ -137,7 +159,20 @@ void compile_intervals(attn_plan& p) {
         run += diff[kt];
         if (run <= 0) continue;
         const int64_t j0 = kt * bn, j1 = j0 + bn;
-        const bool full = rows_full && j1 <= p.L && max_lo <= j0 && min_hi >= j1;
+        bool full = rows_full && j1 <= p.L && max_lo <= j0 && min_hi >= j1;
+        if (!full && p.prefix > 0 && rows_full && j1 <= p.L) {
+          // every row must cover [j0, j1) with its prefix, its window or both joined
+          full = true;
+          for (int64_t i = i0; full && i < i1; ++i) {
+            int64_t lo, hi;
+            row_interval(p, h, i, &lo, &hi);
+            const int64_t pe = row_prefix_end(p, i);
+            const bool joined = hi > lo && lo <= pe;
+            const bool covered = (j1 <= pe) || (hi > lo && j0 >= lo && j1 <= hi) ||
+                                 (joined && j1 <= std::max(hi, pe));
+            full = covered;
+          }
+        }
         p.kv_tile.push_back(static_cast<int32_t>(kt));
         p.flags.push_back(full ? 1 : 0);
       }
@@ -368,7 +403,7 @@ void build_image(attn_plan& p) {
 uint64_t fingerprint(const attn_mask_desc* m, int64_t L, int64_t H, int64_t D) {
   Hasher hs;
   hs.pod(L); hs.pod(H); hs.pod(D);
-  hs.pod(m->kind); hs.pod(m->causal);
+  hs.pod(m->kind); hs.pod(m->causal); hs.pod(m->prefix);
   switch (m->kind) {
     case ATTN_MASK_CHUNK: hs.pod(m->chunk); break;
     case ATTN_MASK_WINDOW:
@@ -396,6 +431,7 @@ attn_status compile_plan(const attn_mask_desc* m, int64_t L, int64_t H, int64_t 
     p = new attn_plan();
     p->kind = m->kind;
     p->causal = m->causal;
+    p->prefix = m->prefix;
     p->L = L; p->H = H; p->D = D;
     p->nq = ceil_div(L, p->bm);
     p->nk = ceil_div(L, p->bn);

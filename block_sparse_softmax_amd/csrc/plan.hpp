@@ -50,6 +50,7 @@ struct attn_plan {
   // descriptor (copied)
   int32_t kind = 0, causal = 0;
   int64_t chunk = 0, left = 0, right = 0, block = 0;
+  int64_t prefix = 0;                 // keys 0 .. prefix-1 added to every row (before the causal cut)
   int32_t block_heads = 0;
   std::vector<int64_t> head_left;     // [H] for WINDOW (left broadcast when no per-head array)
   std::vector<uint8_t> block_mask;    // [Hb][Nb][Nb] for BLOCK

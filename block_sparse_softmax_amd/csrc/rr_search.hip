@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256) void rr_prep_kernel(const RrParams p) {
     const int pos = j * p.S + (p.S - 1 - (h % p.S));
     qo = *reinterpret_cast<const bf16x8*>(p.q + b * p.q_sb + static_cast<int64_t>(pos) * p.q_sl + h * p.q_sh + 8 * c);
     float acc[8] = {};
-    const uint16_t* kr = p.k + b * p.k_sb + static_cast<int64_t>(j) * p.S * p.k_sl + h * p.k_sh + 8 * c;
+    const uint16_t* kr = p.k + b * p.k_sb + static_cast<int64_t>(j) * p.S * p.k_sl + (h / p.kv_group) * p.k_sh + 8 * c;
     for (int s = 0; s < p.S; ++s) {
       const bf16x8 x = *reinterpret_cast<const bf16x8*>(kr + static_cast<int64_t>(s) * p.k_sl);
 #pragma unroll

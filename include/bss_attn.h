@@ -69,6 +69,10 @@ typedef enum {
 } attn_mask_kind;
 
 /* A bf16 device tensor view of logical shape [B, L, H, D]. */
+/* K and V may have fewer heads than Q (grouped-query attention): Q's head count
+ * must be a multiple of theirs, and query head h reads K/V head h / (Hq / Hkv),
+ * so each run of Hq / Hkv consecutive query heads shares one ("sliding window
+ * vs linear attention" article: 32 query heads sharing 8 key-value heads). */
 typedef struct {
   void* data;                 /* device pointer to element [0,0,0,0]                  */
   int64_t B, L, H, D;         /* batch, tokens, heads, head dim                       */
@@ -85,6 +89,9 @@ typedef struct {
   int64_t block;              /* BLOCK: token block size Bs >= 1                       */
   const uint8_t* block_mask;  /* BLOCK: host [Hb][Nb][Nb] row-major 0/1, Nb = ceil(L/Bs) */
   int32_t block_mask_heads;   /* BLOCK: Hb = 1 (shared by all heads) or H             */
+  int64_t prefix;             /* FULL, CHUNK, WINDOW: keys 0 .. prefix-1 are added to every query's
+                                 set before the causal cut (the StreamingLLM sink tokens kept beside a
+                                 window, e.g. 572 + 4); 0 = none; must be 0 for BLOCK              */
 } attn_mask_desc;
 
 /* Launch context. */

@@ -27,6 +27,14 @@ Definition followed
 * Sink: a per-head logit s_aux added to the softmax denominator only, a key
   with no value; s_aux = -inf is plain softmax (SHS slides, the sink-bias
   slide, "Eq. 1").
+* Prefix tokens: mask["prefix"] = P adds keys 0..P-1 to every query's set
+  before the causal cut (the StreamingLLM sink tokens that the
+  sliding-window-vs-linear-attention article, sections "forget or compress"
+  and "comparison at equal memory", keeps beside a window: 572 + 4).
+* Grouped-query attention: K and V may have fewer heads Hk (H a multiple of
+  Hk); query head h uses K/V head h // (H / Hk), so each run of H/Hk
+  consecutive query heads shares one (the same article: 32 query heads
+  sharing 8 key-value heads).
 * Output: o_i = sum_j a_ij v_j ("Vision transformers ...", section 2).
 * Numerically stable form: subtract the row maximum before exponentiating
   (the same page's interactive softmax example).
@@ -73,6 +81,9 @@ def allowed_rows(mask: dict, h: int, rows: np.ndarray, L: int) -> np.ndarray:
         m = (bh[i // bs, j // bs] != 0) & (j <= i)
     else:
         raise ValueError(f"unknown mask kind {kind!r}")
+    prefix = int(mask.get("prefix", 0) or 0)
+    if prefix > 0:
+        m = m | (j < prefix)
     if mask.get("causal", False):
         m = m & (j <= i)
     return m
@@ -86,7 +97,8 @@ def dense_mask(mask: dict, h: int, L: int) -> np.ndarray:
 def attention(q, k, v, mask: dict, sink=None, rows=None, scale=None, row_chunk: int = 256) -> dict:
     """Masked softmax attention in float64.
 
-    q, k, v : [B, H, L, D] arrays (bf16 bit patterns as uint16, or any float dtype).
+    q       : [B, H, L, D] arrays (bf16 bit patterns as uint16, or any float dtype).
+    k, v    : [B, Hk, L, D] with H a multiple of Hk (grouped-query attention when Hk < H).
     mask    : mask dict (see module docstring).
     sink    : None or [H] per-head logits (on the scale of s_ij; -inf = no sink).
     rows    : None for every query row, or int [H, n] of query rows per head.
@@ -100,6 +112,10 @@ def attention(q, k, v, mask: dict, sink=None, rows=None, scale=None, row_chunk: 
       rows     [H, n] the evaluated rows.
     """
     B, H, L, D = np.shape(q)
+    Hk = np.shape(k)[1]
+    if H % Hk != 0 or np.shape(v)[1] != Hk:
+        raise ValueError("K and V need the same number of heads, a divisor of Q's")
+    group = H // Hk
     sigma = (1.0 / np.sqrt(D)) if scale is None else float(scale)
     if rows is None:
         rows = np.tile(np.arange(L, dtype=np.int64), (H, 1))
@@ -114,7 +130,7 @@ def attention(q, k, v, mask: dict, sink=None, rows=None, scale=None, row_chunk: 
     for h in range(H):
         sa = -np.inf if s_aux is None else s_aux[h]
         for b in range(B):
-            kf, vf = _as_f64(k[b, h]), _as_f64(v[b, h])
+            kf, vf = _as_f64(k[b, h // group]), _as_f64(v[b, h // group])
             for r0 in range(0, n, row_chunk):
                 rr = rows[h, r0:r0 + row_chunk]
                 allowed = allowed_rows(mask, h, rr, L)

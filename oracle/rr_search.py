@@ -129,7 +129,7 @@ def rr_search(q, k, S: int, Bs: int, tau: float, protect_last: bool = True, b: i
     if Bs % S != 0:
         raise ValueError("the block size must be a multiple of the stride")
     qh = _as_f64(q[b, h])
-    kh = _as_f64(k[b, h])
+    kh = _as_f64(k[b, h // (np.shape(q)[1] // np.shape(k)[1])])   # grouped-query: K head of query head h
     L, d = qh.shape
     nb = -(-L // Bs)
     ns = L // S

@@ -306,3 +306,29 @@ def test_grouped_launch_matches_single_launches():
             assert torch.equal(outs[j], single[j]), masks[j]
     ref = attention(*(x for x in _random_case(21, 1, H, L, D)), masks[1])["out"]
     _compare(outs[1].float().cpu().double().numpy(), ref, "group-chunk")
+
+
+GQA_PREFIX = [
+    # (mask, L, H, Hkv, D, sink, B)
+    (dict(kind="full", causal=True), 700, 8, 2, 128, False, 1),
+    (dict(kind="window", left=300, right=0, causal=True), 1000, 4, 1, 80, True, 2),
+    # the pages' SWA with 4 StreamingLLM sink tokens (572 + 4) and 32 query heads on 8 K/V heads, scaled down
+    (dict(kind="window", left=571, right=0, causal=True, prefix=4), 2048, 8, 2, 128, True, 1),
+    (dict(kind="chunk", chunk=256, prefix=16), 900, 4, 2, 64, False, 1),
+    (dict(kind="window", left=64, right=64, prefix=100), 1500, 2, 2, 80, False, 1),   # prefix over 2 tiles
+    (dict(kind="full", prefix=40), 333, 2, 1, 64, True, 2),                           # prefix inside full: no-op
+]
+
+
+@pytest.mark.parametrize("ci", range(len(GQA_PREFIX)))
+def test_grouped_query_heads_and_prefix_tokens(ci):
+    mask, L, H, Hkv, D, with_sink, B = GQA_PREFIX[ci]
+    print(f"[case] gqa/prefix {ci} {mask} L={L} H={H}/{Hkv} D={D} B={B}", flush=True)
+    rng = np.random.default_rng(500 + ci)
+    q = gen.f32_to_bf16_bits(rng.standard_normal((B, H, L, D), dtype=np.float32))
+    k = gen.f32_to_bf16_bits(rng.standard_normal((B, Hkv, L, D), dtype=np.float32))
+    v = gen.f32_to_bf16_bits(rng.standard_normal((B, Hkv, L, D), dtype=np.float32))
+    sink = rng.standard_normal(H).astype(np.float32) if with_sink else None
+    got = _run_gpu(q, k, v, mask, sink, layout="bhld")
+    ref = attention(q, k, v, mask, sink=sink)["out"]
+    _compare(got, ref, f"gqa-prefix{ci}")

@@ -136,3 +136,22 @@ def test_rr_search_128k_sampled_blocks():
                 assert np.array_equal(b_gpu[m], b_ref[m]), (h, m)
         assert np.all(b_gpu[nb - 1] == 1)
     print(f"[rr] 128k: density of the selected blocks {bm.float().mean().item() * 2:.3f} of the causal half", flush=True)
+
+
+def test_rr_search_grouped_keys():
+    """Grouped-query attention: 4 query heads on 2 key heads (query head h reads key head h // 2)."""
+    from block_sparse_softmax_amd import rr_search
+    L, H, Hk, D, S, Bs, tau = 2048, 4, 2, 128, 8, 128, 0.9
+    rng = np.random.default_rng(77)
+    q = gen.f32_to_bf16_bits(rng.standard_normal((1, H, L, D), dtype=np.float32))
+    k = gen.f32_to_bf16_bits(rng.standard_normal((1, Hk, L, D), dtype=np.float32))
+    bm, sc = rr_search(_dev(q), _dev(k), S, Bs, tau, layout="bhld")
+    torch.cuda.synchronize()
+    bm, sc = bm.cpu().numpy(), sc.cpu().numpy().astype(np.float64)
+    R = Bs // S
+    for h in range(H):
+        s_ref, b_ref = rr_oracle(q, k, S, Bs, tau, h=h, ks_round="bf16")
+        assert np.abs(sc[0, h] - s_ref).max() <= SCORE_TOL * R
+        for m in range(L // Bs - 1):
+            if _check_row(bm[0, h, m, : m + 1], s_ref[m, : m + 1], tau, 4 * SCORE_TOL * R):
+                assert np.array_equal(bm[0, h, m], b_ref[m]), (h, m)

@@ -45,25 +45,31 @@ def _keys_brute(mask, h, i, L):
             if bh[i // bs][n]:
                 ks.extend(j for j in range(n * bs, min(L, (n + 1) * bs)) if j <= i)
         ks.sort()
+    prefix = mask.get("prefix", 0) or 0
+    if prefix:
+        ks = sorted(set(ks) | set(range(min(prefix, L))))
     if mask.get("causal", False):
         ks = [j for j in ks if j <= i]
     return ks
 
 
 def _brute(q, k, v, mask, sink):
-    """q, k, v: [H, L, D] nested lists; returns [H, L, D]."""
+    """q: [H, L, D], k, v: [Hk, L, D] nested lists (query head h reads K/V head h // (H/Hk));
+    returns [H, L, D]."""
     H, L, D = len(q), len(q[0]), len(q[0][0])
+    g = H // len(k)
     out = []
     for h in range(H):
+        kh, vh = k[h // g], v[h // g]
         oh = []
         for i in range(L):
             ks = _keys_brute(mask, h, i, L)
-            w = [math.exp(sum(q[h][i][t] * k[h][j][t] for t in range(D)) / math.sqrt(D)) for j in ks]
+            w = [math.exp(sum(q[h][i][t] * kh[j][t] for t in range(D)) / math.sqrt(D)) for j in ks]
             z = sum(w) + (math.exp(sink[h]) if sink is not None else 0.0)
             if z == 0.0:
                 oh.append([0.0] * D)
                 continue
-            oh.append([sum(w[a] * v[h][ks[a]][t] for a in range(len(ks))) / z for t in range(D)])
+            oh.append([sum(w[a] * vh[ks[a]][t] for a in range(len(ks))) / z for t in range(D)])
         out.append(oh)
     return np.array(out)
 
@@ -76,6 +82,9 @@ BRUTE_MASKS = [
     dict(kind="window", left=3, right=3),
     dict(kind="window", left=5, right=2),
     dict(kind="window", left=0, right=0, causal=True, head_left=[2, 30]),
+    dict(kind="window", left=6, right=0, causal=True, prefix=3),   # StreamingLLM prefix + causal window
+    dict(kind="window", left=2, right=4, prefix=5),                # prefix + symmetric window
+    dict(kind="chunk", chunk=8, prefix=2),
     dict(kind="block", block=8, block_mask=np.array([np.tril(np.ones((4, 4), np.uint8)),
                                                      np.array([[1, 0, 0, 0], [1, 1, 0, 0],
                                                                [0, 1, 0, 0], [1, 0, 1, 1]], np.uint8)])),
@@ -99,6 +108,30 @@ def test_brute_force_tiny(mi, with_sink):
     got = attention(q, k, v, mask, sink=sink)["out"][0]
     ref = _brute(q[0].tolist(), k[0].tolist(), v[0].tolist(), mask, None if sink is None else sink.tolist())
     assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_grouped_query_heads():
+    """Grouped-query attention is multi-head attention with each K/V head repeated for its run of
+    consecutive query heads; brute force agrees on a tiny case."""
+    H, Hk, L, D = 6, 2, 24, 8
+    q = _rand((1, H, L, D), 31)
+    k, v = _rand((1, Hk, L, D), 32), _rand((1, Hk, L, D), 33)
+    for mask in (dict(kind="full", causal=True), dict(kind="window", left=4, right=1, prefix=2)):
+        got = attention(q, k, v, mask)["out"]
+        rep = attention(q, np.repeat(k, H // Hk, axis=1), np.repeat(v, H // Hk, axis=1), mask)["out"]
+        assert np.array_equal(got, rep)
+        ref = _brute(q[0].tolist(), k[0].tolist(), v[0].tolist(), mask, None)
+        assert np.max(np.abs(got[0] - ref)) <= 1e-12
+    with pytest.raises(ValueError):
+        attention(q, _rand((1, 4, L, D), 1), _rand((1, 4, L, D), 2), dict(kind="full"))
+
+
+def test_prefix_tokens_hand_example():
+    """Causal window of 3 keys plus 2 prefix tokens: row 6 sees {0, 1, 4, 5, 6}; row 1 sees {0, 1}."""
+    from oracle.attention import allowed_rows
+    m = allowed_rows(dict(kind="window", left=2, right=0, causal=True, prefix=2), 0, np.array([6, 1]), 10)
+    assert np.flatnonzero(m[0]).tolist() == [0, 1, 4, 5, 6]
+    assert np.flatnonzero(m[1]).tolist() == [0, 1]
 
 
 def test_brute_force_sampled_rows():
@@ -267,7 +300,7 @@ def test_neg_inf_sink_is_no_sink():
 
 def test_empty_rows_give_zero():
     """A block row with no kept block has no allowed key: o_i = 0, also with a sink."""
-    mask = BRUTE_MASKS[8]            # block row 3 is empty
+    mask = BRUTE_MASKS[-1]           # block row 3 is empty
     H, L, D = 1, 32, 8
     q, k, v = (_rand((1, H, L, D), s) for s in (37, 38, 39))
     for sink in (None, np.array([0.2])):

@@ -81,7 +81,7 @@ def test_tile_lists_match_oracle_block(lib, bs, nb, L):
 
 def test_random_descriptors_match_oracle(lib):
     rng = np.random.default_rng(11)
-    for _ in range(25):
+    for trial in range(40):
         L = int(rng.integers(1, 700))
         H = int(rng.integers(1, 3))
         kind = rng.choice(["full", "chunk", "window", "block"])
@@ -100,6 +100,8 @@ def test_random_descriptors_match_oracle(lib):
             nb = -(-L // bs)
             b = np.tril(rng.integers(0, 2, (H, nb, nb))).astype(np.uint8)
             mask = dict(kind="block", block=bs, block_mask=b)
+        if kind != "block" and trial % 2:
+            mask["prefix"] = int(rng.integers(1, 200))    # StreamingLLM prefix tokens
         plan = _lib.Plan(mask, L, H, 80)
         bm, bn, rp, kv, fl = plan.tiles()
         ref = tile_lists_dense(mask, H, L, bm, bn)
@@ -214,6 +216,10 @@ def test_descriptor_errors(lib):
     st, _ = _status(lib, dict(kind="block", block=16, block_mask=np.ones((3, 4, 4), np.uint8)), 64, 2, 64)
     assert st == _lib.ATTN_E_INVAL
     assert _status(lib, dict(kind="full"), 0, 1, 64)[0] == _lib.ATTN_E_INVAL
+    assert _status(lib, dict(kind="window", left=3, right=0, prefix=-1), 64, 1, 64)[0] == _lib.ATTN_E_INVAL
+    st, msg = _status(lib, dict(kind="block", block=16, block_mask=np.tril(np.ones((1, 4, 4), np.uint8)), prefix=4),
+                      64, 1, 64)
+    assert st == _lib.ATTN_E_INVAL and "prefix" in msg
     d = _lib.MaskDesc()
     d.kind = 9
     h = ctypes.c_void_p()
