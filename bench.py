@@ -246,6 +246,34 @@ def _bench_rr(q, k, steps, warmup, layout, stride=8, block=128, tau=0.9):
                               kernel="rr_prep + rr_scores + rr_select", avg_launch_ms=avg))
 
 
+def _bench_reorder(xs, gh, gw, steps, layout):
+    """Re-permute the layer's Q, K and V from the 2 x 2-block row-major to the column-major order
+    (Ariadne's switch between layer orders): algorithmic bytes = every token row read and written
+    once, per tensor."""
+    import numpy as np
+    import torch
+    from block_sparse_softmax_amd import reorder_tokens
+    outs = [torch.empty_like(x) for x in xs]
+    for x, o in zip(xs, outs):
+        reorder_tokens(x, "block_row", "block_col", gh, gw, out=o, layout=layout)
+    ev = _events(steps * len(xs))
+    torch.cuda.synchronize()
+    for s in range(steps):
+        for i, (x, o) in enumerate(zip(xs, outs)):
+            a, b = ev[s * len(xs) + i]
+            reorder_tokens(x, "block_row", "block_col", gh, gw, out=o, layout=layout, start_event=a, stop_event=b)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    avg = float(np.mean(per))
+    nbytes = 2 * xs[0].numel() * xs[0].element_size()
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    return dict(workload=f"token re-permutation 2x2-block row-major -> column-major, {gh}x{gw} grid, "
+                         f"tensor {tuple(xs[0].shape)} bf16 ({layout}), Q, K and V",
+                avg_ms=avg, min_ms=float(np.min(per)), alg_gbs=gbs,
+                roofline=dict(bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s", frac=gbs / PEAK_HBM_GBS,
+                              traffic=None, kernel="reorder_kernel", avg_launch_ms=avg))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -305,6 +333,8 @@ def main():
             if name == "blocksparse128k":
                 q, k, _ = setup["dev"]
                 extra["rr_search128k"] = _bench_rr(q, k, 5, 1, args.layout)
+            if name == "vit1792":
+                extra["reorder_vit1792"] = _bench_reorder(list(setup["dev"]), 128, 128, 5, args.layout)
 
     out = {
         "metric": "effective attention TFLOP/s (unmasked pairs) and % bf16 MFMA peak, 1 MI355X",

@@ -14,9 +14,10 @@ from ._lib import (  # noqa: F401
     masked_fwd,
     masked_fwd_oneshot,
     prepare,
+    reorder_tokens,
     rr_search,
     tensor_view,
 )
 
 __all__ = ["AttnError", "Plan", "PreparedMask", "RrSearch", "bind_group", "load_library", "masked_fwd",
-           "masked_fwd_oneshot", "prepare", "rr_search", "tensor_view"]
+           "masked_fwd_oneshot", "prepare", "reorder_tokens", "rr_search", "tensor_view"]

@@ -26,6 +26,7 @@ STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_E_INVAL", -2: "ATTN_E_UNSUPPORTED", -3: 
 EXPORTS = ("attn_masked_fwd", "attn_workspace_bytes", "attn_plan_create", "attn_plan_tiles",
            "attn_plan_pairs", "attn_plan_schedule", "attn_plan_workspace_bytes", "attn_plan_upload",
            "attn_masked_fwd_plan", "attn_masked_fwd_group", "attn_rr_workspace_bytes", "attn_rr_search",
+           "attn_reorder_tokens",
            "attn_plan_destroy", "attn_last_error", "attn_version")
 
 
@@ -91,6 +92,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       P(vp), P(sz), P(Launch)],
             "attn_rr_workspace_bytes": [P(AttnTensor), P(RrParams), P(sz)],
             "attn_rr_search": [P(AttnTensor), P(AttnTensor), P(RrParams), vp, vp, P(Launch)],
+            "attn_reorder_tokens": [P(AttnTensor), i32, P(AttnTensor), i32, i64, i64, P(Launch)],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -382,6 +384,27 @@ def rr_search(q, k, stride: int, block: int, tau: float, protect_last: bool = Tr
     """RRAttention's block-pattern search of bf16 CUDA tensors q, k (see include/bss_attn.h):
     returns (block_mask uint8 [B, H, Nb, Nb], block_score float32 [B, H, Nb, Nb]) on the device."""
     return RrSearch(q, stride, block, tau, protect_last, layout)(q, k)
+
+
+ORDERS = {"raster": 0, "block_row": 1, "block_col": 2}
+
+
+def reorder_tokens(x, src: str, dst: str, grid_h: int, grid_w: int, out=None, layout: str = "blhd", stream=None,
+                   start_event=None, stop_event=None):
+    """Re-permute the tokens of bf16 CUDA tensor x from serialisation order `src` to `dst`
+    (attn_reorder_tokens; orders 'raster', 'block_row', 'block_col')."""
+    import torch
+    lib = load_library()
+    if out is None:
+        out = torch.empty_like(x)
+    iv, ov = tensor_view(x, layout), tensor_view(out, layout)
+    ln = Launch()
+    ln.stream = _stream_ptr(stream, x).value
+    ln.start_event = None if start_event is None else start_event.cuda_event
+    ln.stop_event = None if stop_event is None else stop_event.cuda_event
+    _check(lib.attn_reorder_tokens(ctypes.byref(iv), ORDERS[src], ctypes.byref(ov), ORDERS[dst], grid_h, grid_w,
+                                   ctypes.byref(ln)))
+    return out
 
 
 _prepared = {}

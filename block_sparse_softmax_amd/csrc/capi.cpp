@@ -459,6 +459,47 @@ attn_status attn_rr_search(const attn_tensor* q, const attn_tensor* k, const att
   }
 }
 
+attn_status attn_reorder_tokens(const attn_tensor* in, int32_t from, attn_tensor* out, int32_t to,
+                                int64_t grid_h, int64_t grid_w, const attn_launch* launch) {
+  try {
+    if (!in || !out || !launch) { set_error("in, out or launch is NULL"); return ATTN_E_INVAL; }
+    if (from < 0 || from > 2 || to < 0 || to > 2) { set_error("unknown token order"); return ATTN_E_INVAL; }
+    if (grid_h < 1 || grid_w < 1 || grid_h * grid_w != in->L) {
+      set_error("grid_h * grid_w must equal the token count");
+      return ATTN_E_INVAL;
+    }
+    if ((from != ATTN_ORDER_RASTER || to != ATTN_ORDER_RASTER) && (grid_h % 2 || grid_w % 2)) {
+      set_error("2 x 2-block orders need even grid sides");
+      return ATTN_E_INVAL;
+    }
+    if (in->D < 8 || in->D % 8 || in->B < 1 || in->H < 1 || in->L > INT32_MAX / 2 || in->B > 65535) {
+      set_error("D must be a positive multiple of 8; B, H >= 1");
+      return ATTN_E_INVAL;
+    }
+    attn_status st;
+    if ((st = check_tensor(in, "in", in->B, in->L, in->H, in->D)) != ATTN_OK) return st;
+    if ((st = check_tensor(out, "out", in->B, in->L, in->H, in->D)) != ATTN_OK) return st;
+    if (in->data == out->data) { set_error("out must not alias in"); return ATTN_E_INVAL; }
+    ReorderParams p{};
+    p.in = static_cast<const uint16_t*>(in->data);
+    p.out = static_cast<uint16_t*>(out->data);
+    p.in_sb = in->stride_b; p.in_sl = in->stride_l; p.in_sh = in->stride_h;
+    p.out_sb = out->stride_b; p.out_sl = out->stride_l; p.out_sh = out->stride_h;
+    p.B = static_cast<int32_t>(in->B); p.L = static_cast<int32_t>(in->L);
+    p.H = static_cast<int32_t>(in->H); p.D = static_cast<int32_t>(in->D);
+    p.gh = static_cast<int32_t>(grid_h); p.gw = static_cast<int32_t>(grid_w);
+    p.from = from; p.to = to;
+    hipError_t e = launch_reorder(p, static_cast<hipStream_t>(launch->stream),
+                                  static_cast<hipEvent_t>(launch->start_event),
+                                  static_cast<hipEvent_t>(launch->stop_event));
+    if (e != hipSuccess) return hip_fail(e, "reorder launch");
+    return ATTN_OK;
+  } catch (...) {
+    set_error("unexpected exception");
+    return ATTN_E_NOMEM;
+  }
+}
+
 void attn_plan_destroy(attn_plan* p) { delete p; }
 
 const char* attn_last_error(void) { return bss::g_last_error.c_str(); }

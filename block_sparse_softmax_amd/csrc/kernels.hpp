@@ -75,4 +75,17 @@ struct RrParams {
 // before the first and after the last.
 hipError_t launch_rr_search(const RrParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
+// Token re-permutation between serialisation orders (reorder.hip).
+struct ReorderParams {
+  const uint16_t* in;
+  uint16_t* out;
+  int64_t in_sb, in_sl, in_sh;    // element strides
+  int64_t out_sb, out_sl, out_sh;
+  int32_t B, L, H, D;             // D a multiple of 8
+  int32_t gh, gw;                 // grid rows and columns (L = gh * gw)
+  int32_t from, to;               // 0 raster, 1 2x2-block row-major, 2 2x2-block column-major
+};
+
+hipError_t launch_reorder(const ReorderParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
 }  // namespace bss

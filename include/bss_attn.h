@@ -254,6 +254,32 @@ attn_status attn_rr_workspace_bytes(const attn_tensor* q, const attn_rr_params* 
 attn_status attn_rr_search(const attn_tensor* q, const attn_tensor* k, const attn_rr_params* prm,
                            void* block_mask, void* block_score, const attn_launch* launch);
 
+/*
+ * Token serialisation orders of a grid_h x grid_w patch grid ("Semantic Head
+ * Specialization ...", the Factor-2 slides and the Ariadne design):
+ *   RASTER      row by row, position r * grid_w + c;
+ *   BLOCK_ROW   (c) 2 x 2 blocks left to right, then top to bottom, the 4
+ *               patches of a block row by row;
+ *   BLOCK_COL   (d) the BLOCK_ROW order of the transposed grid: blocks top to
+ *               bottom, then left to right, a block's patches column by column.
+ * The block orders need even grid sides.
+ */
+typedef enum { ATTN_ORDER_RASTER = 0, ATTN_ORDER_BLOCK_ROW = 1, ATTN_ORDER_BLOCK_COL = 2 } attn_token_order;
+
+/*
+ * Re-permute the tokens of `in` (in order `from`) into `out` (order `to`):
+ * out[b, t, h, :] = in[b, s, h, :] where s is the position, in order `from`,
+ * of the patch that order `to` puts at t (Ariadne's re-permutation where the
+ * layer order changes).  in, out: bf16 [B, L, H, D] device views with
+ * L = grid_h * grid_w, any D that is a multiple of 8 (16-byte rows), same
+ * shape; they must not overlap.  Asynchronous on launch->stream; optional
+ * events mark the kernel; launch->workspace is not used.
+ * Errors: ATTN_E_INVAL (shapes, strides, orders, odd grid for a block order,
+ * out == in), ATTN_E_HIP.
+ */
+attn_status attn_reorder_tokens(const attn_tensor* in, int32_t from, attn_tensor* out, int32_t to,
+                                int64_t grid_h, int64_t grid_w, const attn_launch* launch);
+
 /* Free a plan (NULL is allowed). */
 void attn_plan_destroy(attn_plan* plan);
 

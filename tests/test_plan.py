@@ -294,3 +294,21 @@ def test_group_argument_errors_without_gpu(lib):
     # differing head dims
     assert call(2, [h, plan2.handle.value], [t(fake * 2), t(fake * 3)], [fake * 4, fake * 5]) == _lib.ATTN_E_INVAL
     assert "same head dim" in lib.attn_last_error().decode()
+
+
+def test_reorder_argument_errors_without_gpu(lib):
+    fake = 1 << 20
+
+    def t(L, data=fake):
+        a = _lib.AttnTensor()
+        a.data, a.B, a.L, a.H, a.D = data, 1, L, 2, 64
+        a.stride_b, a.stride_l, a.stride_h = L * 128, 128, 64
+        return a
+
+    ln = _lib.Launch()
+    i, o = t(48), t(48, fake * 2)
+    f = lib.attn_reorder_tokens
+    assert f(ctypes.byref(i), 0, ctypes.byref(o), 1, 6, 7, ctypes.byref(ln)) == _lib.ATTN_E_INVAL   # 6*7 != 48
+    assert f(ctypes.byref(i), 0, ctypes.byref(o), 1, 3, 16, ctypes.byref(ln)) == _lib.ATTN_E_INVAL  # odd side
+    assert f(ctypes.byref(i), 0, ctypes.byref(o), 3, 6, 8, ctypes.byref(ln)) == _lib.ATTN_E_INVAL   # bad order
+    assert f(ctypes.byref(i), 0, ctypes.byref(i), 1, 6, 8, ctypes.byref(ln)) == _lib.ATTN_E_INVAL   # aliasing
