@@ -17,6 +17,9 @@ counts.py     unmasked-pair counts by enumeration of the explicit mask.
 rr_search.py  RRAttention's block-pattern search (Eq. 6-12): sampled queries,
               stride-summed keys, stride softmax, block scores, top-tau, the
               last-row protection.
+backward.py   the gradients dQ, dK, dV and of the sink logit, and the row
+              log-sum-exp, by the chain rule through the masked softmax.
+serialize.py  token positions under raster and 2x2-block serialisation orders.
 
 Every function is pinned by ``tests/test_oracle*.py`` against brute force,
 closed forms, invariants and the worked numbers printed on the pages; see the
@@ -27,3 +30,4 @@ from .attention import attention, allowed_rows, bf16_to_f64, dense_mask  # noqa:
 from .tiles import tile_lists  # noqa: F401
 from .counts import pair_count  # noqa: F401
 from .rr_search import rr_search  # noqa: F401
+from .backward import attention_backward  # noqa: F401
