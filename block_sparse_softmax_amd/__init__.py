@@ -7,17 +7,22 @@ The compute path is the HIP library ``libbss_attn.so`` built from ``csrc/``
 from ._lib import (  # noqa: F401
     AttnError,
     Plan,
+    PreparedBackward,
     PreparedMask,
     RrSearch,
     bind_group,
     load_library,
+    masked_bwd,
     masked_fwd,
+    masked_fwd_lse,
     masked_fwd_oneshot,
     prepare,
+    prepare_backward,
     reorder_tokens,
     rr_search,
     tensor_view,
 )
 
-__all__ = ["AttnError", "Plan", "PreparedMask", "RrSearch", "bind_group", "load_library", "masked_fwd",
-           "masked_fwd_oneshot", "prepare", "reorder_tokens", "rr_search", "tensor_view"]
+__all__ = ["AttnError", "Plan", "PreparedBackward", "PreparedMask", "RrSearch", "bind_group", "load_library",
+           "masked_bwd", "masked_fwd", "masked_fwd_lse", "masked_fwd_oneshot", "prepare", "prepare_backward",
+           "reorder_tokens", "rr_search", "tensor_view"]

@@ -26,7 +26,9 @@ STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_E_INVAL", -2: "ATTN_E_UNSUPPORTED", -3: 
 EXPORTS = ("attn_masked_fwd", "attn_workspace_bytes", "attn_plan_create", "attn_plan_tiles",
            "attn_plan_pairs", "attn_plan_schedule", "attn_plan_workspace_bytes", "attn_plan_upload",
            "attn_masked_fwd_plan", "attn_masked_fwd_group", "attn_rr_workspace_bytes", "attn_rr_search",
-           "attn_reorder_tokens",
+           "attn_reorder_tokens", "attn_masked_fwd_lse", "attn_bwd_workspace_bytes", "attn_bwd_lists",
+           "attn_bwd_upload",
+           "attn_masked_bwd",
            "attn_plan_destroy", "attn_last_error", "attn_version")
 
 
@@ -93,6 +95,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "attn_rr_workspace_bytes": [P(AttnTensor), P(RrParams), P(sz)],
             "attn_rr_search": [P(AttnTensor), P(AttnTensor), P(RrParams), vp, vp, P(Launch)],
             "attn_reorder_tokens": [P(AttnTensor), i32, P(AttnTensor), i32, i64, i64, P(Launch)],
+            "attn_masked_fwd_lse": [plan_p, P(AttnTensor), P(AttnTensor), P(AttnTensor), vp, P(AttnTensor), vp,
+                                    P(Launch)],
+            "attn_bwd_workspace_bytes": [plan_p, i64, i64, P(sz)],
+            "attn_bwd_upload": [plan_p, i64, vp, sz, vp],
+            "attn_bwd_lists": [plan_p, i64, P(i64), P(P(i32)), P(i64), P(P(i32)), P(i64), P(P(i32))],
+            "attn_masked_bwd": [plan_p, P(AttnTensor), P(AttnTensor), P(AttnTensor), P(AttnTensor), P(AttnTensor),
+                                vp, vp, P(AttnTensor), P(AttnTensor), P(AttnTensor), vp, P(Launch)],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -207,6 +216,18 @@ class Plan:
         _check(lib.attn_plan_schedule(self._h, ctypes.byref(n), ctypes.byref(it)))
         return np.ctypeslib.as_array(it, shape=(n.value, 8)).copy() if n.value else np.zeros((0, 8), np.int32)
 
+    def bwd_lists(self, kv_heads: int):
+        """Transposed lists of the backward: (n_blocks, col_ptr, entries, items (n, 8))."""
+        lib = load_library()
+        nb, ne, ni = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        cp, en, it = (ctypes.POINTER(ctypes.c_int32)() for _ in range(3))
+        _check(lib.attn_bwd_lists(self._h, kv_heads, ctypes.byref(nb), ctypes.byref(cp), ctypes.byref(ne),
+                                  ctypes.byref(en), ctypes.byref(ni), ctypes.byref(it)))
+        col_ptr = np.ctypeslib.as_array(cp, shape=(kv_heads * nb.value + 1,)).copy()
+        entries = np.ctypeslib.as_array(en, shape=(ne.value,)).copy() if ne.value else np.zeros(0, np.int32)
+        items = np.ctypeslib.as_array(it, shape=(ni.value, 8)).copy() if ni.value else np.zeros((0, 8), np.int32)
+        return nb.value, col_ptr, entries, items
+
     def workspace_bytes(self) -> int:
         lib = load_library()
         b = ctypes.c_size_t()
@@ -312,6 +333,137 @@ class PreparedMask:
         _check(lib.attn_masked_fwd_plan(self.plan.handle, ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv),
                                         sp, ctypes.byref(ov), ctypes.byref(ln)))
         return o
+
+
+def _sink_ptr(sink, H):
+    if sink is None:
+        return None
+    import torch
+    if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() != H:
+        raise TypeError("sink must be a float32 CUDA tensor with one entry per head")
+    return ctypes.c_void_p(sink.data_ptr())
+
+
+def _f32_ptr(t, n, name):
+    import torch
+    if t.dtype != torch.float32 or not t.is_cuda or t.numel() != n or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous float32 CUDA tensor of {n} elements")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class PreparedBackward:
+    """A plan plus a workspace prepared by attn_bwd_upload for batch B and kv_heads K/V heads: it serves
+    the forward that also writes the row log-sum-exp (attn_masked_fwd_lse) and the backward
+    (attn_masked_bwd)."""
+
+    def __init__(self, mask: dict, L: int, H: int, D: int, B: int, kv_heads: int, device):
+        import torch
+        lib = load_library()
+        self.plan = Plan(mask, L, H, D)
+        self.B, self.kv_heads = B, kv_heads
+        nbytes = ctypes.c_size_t()
+        _check(lib.attn_bwd_workspace_bytes(self.plan.handle, B, kv_heads, ctypes.byref(nbytes)))
+        self.workspace = torch.empty(max(256, nbytes.value), dtype=torch.uint8, device=device)
+        _check(lib.attn_bwd_upload(self.plan.handle, kv_heads, ctypes.c_void_p(self.workspace.data_ptr()),
+                                   self.workspace.numel(), _stream_ptr(None, self.workspace)))
+        torch.cuda.synchronize(device)
+
+    def _launch(self, like, stream, softmax_scale):
+        ln = Launch()
+        ln.stream = _stream_ptr(stream, like).value
+        ln.workspace = self.workspace.data_ptr()
+        ln.workspace_bytes = self.workspace.numel()
+        ln.softmax_scale = softmax_scale
+        return ln
+
+    def bind_forward(self, q, k, v, o, lse, sink=None, layout="blhd", stream=None, softmax_scale: float = 0.0):
+        """Marshal attn_masked_fwd_lse once; the returned callable launches it (lse: float32 [B, H, L])."""
+        lib = load_library()
+        qv, kv, vv, ov = (tensor_view(x, layout) for x in (q, k, v, o))
+        lp = _f32_ptr(lse, qv.B * qv.H * qv.L, "lse")
+        sp = _sink_ptr(sink, self.plan.H)
+        ln = self._launch(q, stream, softmax_scale)
+        args = (self.plan.handle, ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), sp, ctypes.byref(ov), lp,
+                ctypes.byref(ln))
+        keep = (qv, kv, vv, ov, ln, q, k, v, o, lse, sink)
+        fn = lib.attn_masked_fwd_lse
+
+        def run(start_event=None, stop_event=None):
+            ln.start_event = None if start_event is None else start_event.cuda_event
+            ln.stop_event = None if stop_event is None else stop_event.cuda_event
+            _check(fn(*args))
+            return keep[8], keep[9]
+        return run
+
+    def bind_backward(self, q, k, v, o, dout, lse, dq, dk, dv, sink=None, dsink=None, layout="blhd", stream=None,
+                      softmax_scale: float = 0.0):
+        """Marshal attn_masked_bwd once; the returned callable launches it and returns (dq, dk, dv, dsink)."""
+        lib = load_library()
+        views = [tensor_view(x, layout) for x in (q, k, v, o, dout, dq, dk, dv)]
+        qv = views[0]
+        lp = _f32_ptr(lse, qv.B * qv.H * qv.L, "lse")
+        sp = _sink_ptr(sink, self.plan.H)
+        dsp = None if dsink is None else _f32_ptr(dsink, self.plan.H, "dsink")
+        ln = self._launch(q, stream, softmax_scale)
+        args = (self.plan.handle, *(ctypes.byref(x) for x in views[:5]), lp, sp,
+                *(ctypes.byref(x) for x in views[5:]), dsp, ctypes.byref(ln))
+        keep = (views, ln, q, k, v, o, dout, lse, sink, (dq, dk, dv, dsink))
+        fn = lib.attn_masked_bwd
+
+        def run(start_event=None, stop_event=None):
+            ln.start_event = None if start_event is None else start_event.cuda_event
+            ln.stop_event = None if stop_event is None else stop_event.cuda_event
+            _check(fn(*args))
+            return keep[9]
+        return run
+
+
+_prepared_bwd = {}
+
+
+def prepare_backward(mask: dict, L: int, H: int, D: int, B: int, kv_heads: int, device) -> PreparedBackward:
+    key = (mask_key(mask), L, H, D, B, kv_heads, str(device))
+    with _prepared_lock:
+        pb = _prepared_bwd.get(key)
+        if pb is None:
+            pb = PreparedBackward(mask, L, H, D, B, kv_heads, device)
+            _prepared_bwd[key] = pb
+        return pb
+
+
+def _shape(q, layout):
+    if layout == "blhd":
+        B, L, H, D = q.shape
+    else:
+        B, H, L, D = q.shape
+    return B, L, H, D
+
+
+def masked_fwd_lse(q, k, v, mask: dict, sink=None, layout: str = "blhd", stream=None, softmax_scale: float = 0.0):
+    """(O, lse) of masked softmax attention: lse float32 [B, H, L] is each row's log-sum-exp (natural log,
+    sink included), which masked_bwd needs."""
+    import torch
+    B, L, H, D = _shape(q, layout)
+    kvh = k.shape[2] if layout == "blhd" else k.shape[1]
+    pb = prepare_backward(mask, L, H, D, B, kvh, q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    return pb.bind_forward(q, k, v, out, lse, sink=sink, layout=layout, stream=stream,
+                           softmax_scale=softmax_scale)()
+
+
+def masked_bwd(q, k, v, o, dout, lse, mask: dict, sink=None, layout: str = "blhd", stream=None,
+               softmax_scale: float = 0.0):
+    """Gradients (dq, dk, dv, dsink) of masked softmax attention (see attn_masked_bwd in
+    include/bss_attn.h); dsink is None without a sink."""
+    import torch
+    B, L, H, D = _shape(q, layout)
+    kvh = k.shape[2] if layout == "blhd" else k.shape[1]
+    pb = prepare_backward(mask, L, H, D, B, kvh, q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dsink = None if sink is None else torch.empty(H, dtype=torch.float32, device=q.device)
+    return pb.bind_backward(q, k, v, o, dout, lse, dq, dk, dv, sink=sink, dsink=dsink, layout=layout,
+                            stream=stream, softmax_scale=softmax_scale)()
 
 
 def bind_group(prepared, qs, ks, vs, outs, sinks=None, layout="blhd", stream=None, softmax_scale: float = 0.0):

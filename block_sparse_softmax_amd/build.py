@@ -47,12 +47,13 @@ def build(verbose: bool = False) -> str:
     inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
     jobs = [
         [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "attn_fwd.hip"), "-o", os.path.join(BUILD, "attn_fwd.o")],
+        [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "attn_bwd.hip"), "-o", os.path.join(BUILD, "attn_bwd.o")],
         [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "rr_search.hip"), "-o", os.path.join(BUILD, "rr_search.o")],
         [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "reorder.hip"), "-o", os.path.join(BUILD, "reorder.o")],
         ["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "plan.cpp"), "-o", os.path.join(BUILD, "plan.o")],
         ["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "capi.cpp"), "-o", os.path.join(BUILD, "capi.o")],
     ]
-    with ThreadPoolExecutor(5) as ex:
+    with ThreadPoolExecutor(6) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:
         for o in outs:
@@ -60,7 +61,7 @@ def build(verbose: bool = False) -> str:
                 print(o)
     tmp = LIB + ".tmp"
     _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
-          os.path.join(BUILD, "attn_fwd.o"), os.path.join(BUILD, "rr_search.o"), os.path.join(BUILD, "reorder.o"),
+          os.path.join(BUILD, "attn_fwd.o"), os.path.join(BUILD, "attn_bwd.o"), os.path.join(BUILD, "rr_search.o"), os.path.join(BUILD, "reorder.o"),
           os.path.join(BUILD, "plan.o"),
           os.path.join(BUILD, "capi.o")])
     os.replace(tmp, LIB)

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <initializer_list>
 #include <memory>
 #include <mutex>
 #include <new>
@@ -347,6 +348,251 @@ attn_status attn_masked_fwd_group(int32_t n, const attn_plan* const* plans, cons
       }
     }
     return run_group(g, plans[0]->D, q[0].B, launch);
+  } catch (...) {
+    set_error("unexpected exception during launch");
+    return ATTN_E_NOMEM;
+  }
+}
+
+namespace {
+
+bool overlaps_any(const void* x, std::initializer_list<const void*> others) {
+  for (const void* o : others)
+    if (o == x) return true;
+  return false;
+}
+
+// Validate a backward launch and fill its kernel parameters.
+attn_status make_bwd(const attn_plan& p, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                     const attn_tensor* o, const attn_tensor* dout, const float* lse, const float* sink,
+                     attn_tensor* dq, attn_tensor* dk, attn_tensor* dv, float* dsink, const attn_launch* launch,
+                     BwdParams* out) {
+  if (!launch) { set_error("launch is NULL"); return ATTN_E_INVAL; }
+  if (!q || !k || !v || !o || !dout || !dq || !dk || !dv) {
+    set_error("q, k, v, o, dout, dq, dk and dv are required");
+    return ATTN_E_INVAL;
+  }
+  const int64_t B = q->B;
+  if (B < 1 || B > 65535) { set_error("batch must be in [1, 65535]"); return ATTN_E_INVAL; }
+  const int64_t hkv = k->H;
+  if (hkv < 1 || p.H % hkv != 0 || v->H != hkv) {
+    set_error("k and v need the same number of heads, a divisor of q's (" + std::to_string(p.H) + ")");
+    return ATTN_E_INVAL;
+  }
+  if (p.H / hkv > 127) { set_error("at most 127 query heads per K/V head"); return ATTN_E_UNSUPPORTED; }
+  attn_status st;
+  if ((st = check_tensor(q, "q", B, p.L, p.H, p.D)) != ATTN_OK) return st;
+  if ((st = check_tensor(k, "k", B, p.L, hkv, p.D)) != ATTN_OK) return st;
+  if ((st = check_tensor(v, "v", B, p.L, hkv, p.D)) != ATTN_OK) return st;
+  if ((st = check_tensor(o, "o", B, p.L, p.H, p.D)) != ATTN_OK) return st;
+  if ((st = check_tensor(dout, "dout", B, p.L, p.H, p.D)) != ATTN_OK) return st;
+  if ((st = check_tensor(dq, "dq", B, p.L, p.H, p.D)) != ATTN_OK) return st;
+  if ((st = check_tensor(dk, "dk", B, p.L, hkv, p.D)) != ATTN_OK) return st;
+  if ((st = check_tensor(dv, "dv", B, p.L, hkv, p.D)) != ATTN_OK) return st;
+  const std::initializer_list<const void*> ins = {q->data, k->data, v->data, o->data, dout->data};
+  if (overlaps_any(dq->data, ins) || overlaps_any(dk->data, ins) || overlaps_any(dv->data, ins) ||
+      dq->data == dk->data || dq->data == dv->data || dk->data == dv->data) {
+    set_error("dq, dk and dv must be distinct and must not alias the inputs");
+    return ATTN_E_INVAL;
+  }
+  if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u)) { set_error("lse is NULL or misaligned"); return ATTN_E_INVAL; }
+  if (p.kind == ATTN_MASK_BLOCK && !p.block_aligned) {
+    set_error("block size must be a multiple of 128 for the GPU kernel");
+    return ATTN_E_UNSUPPORTED;
+  }
+  const BwdImage& img = bwd_image(p, hkv);
+  const BwdLayout lay = bwd_layout(p, img, B);
+  if (!launch->workspace || launch->workspace_bytes < lay.total) {
+    set_error("workspace smaller than attn_bwd_workspace_bytes (" + std::to_string(lay.total) + " bytes)");
+    return ATTN_E_WORKSPACE;
+  }
+  if (!aligned16(launch->workspace)) { set_error("workspace must be 16-byte aligned"); return ATTN_E_INVAL; }
+  {
+    std::lock_guard<std::mutex> lk(p.bwd_mu);
+    auto it = p.bwd_uploads.find(launch->workspace);
+    if (it == p.bwd_uploads.end() || it->second != hkv) {
+      set_error("workspace was not prepared by attn_bwd_upload for this plan and " + std::to_string(hkv) +
+                " K/V heads");
+      return ATTN_E_INVAL;
+    }
+  }
+  const size_t nq_items = p.items_unsplit.size(), nkv_items = img.items.size();
+  if (nq_items % 8 || nkv_items % 8 || nq_items / 8 > static_cast<size_t>(INT32_MAX / 8) ||
+      nkv_items / 8 > static_cast<size_t>(INT32_MAX / 8) || p.nq * kBM > INT32_MAX) {
+    set_error("too many work items");
+    return ATTN_E_UNSUPPORTED;
+  }
+  uint8_t* ws = static_cast<uint8_t*>(launch->workspace);
+  BwdParams f{};
+  f.q = static_cast<const uint16_t*>(q->data);
+  f.k = static_cast<const uint16_t*>(k->data);
+  f.v = static_cast<const uint16_t*>(v->data);
+  f.o = static_cast<const uint16_t*>(o->data);
+  f.dout = static_cast<const uint16_t*>(dout->data);
+  f.dq = static_cast<uint16_t*>(dq->data);
+  f.dk = static_cast<uint16_t*>(dk->data);
+  f.dv = static_cast<uint16_t*>(dv->data);
+  f.q_sb = q->stride_b; f.q_sl = q->stride_l; f.q_sh = q->stride_h;
+  f.k_sb = k->stride_b; f.k_sl = k->stride_l; f.k_sh = k->stride_h;
+  f.v_sb = v->stride_b; f.v_sl = v->stride_l; f.v_sh = v->stride_h;
+  f.o_sb = o->stride_b; f.o_sl = o->stride_l; f.o_sh = o->stride_h;
+  f.do_sb = dout->stride_b; f.do_sl = dout->stride_l; f.do_sh = dout->stride_h;
+  f.dq_sb = dq->stride_b; f.dq_sl = dq->stride_l; f.dq_sh = dq->stride_h;
+  f.dk_sb = dk->stride_b; f.dk_sl = dk->stride_l; f.dk_sh = dk->stride_h;
+  f.dv_sb = dv->stride_b; f.dv_sl = dv->stride_l; f.dv_sh = dv->stride_h;
+  f.lse = lse;
+  f.sink = sink;
+  f.dsink = dsink;
+  f.stat = reinterpret_cast<float*>(ws + lay.off_stat);
+  f.sinkpart = reinterpret_cast<float*>(ws + lay.off_sinkpart);
+  f.qs = reinterpret_cast<uint16_t*>(ws + lay.off_qs);
+  f.q_items = reinterpret_cast<const int32_t*>(ws + p.layout.off_items_unsplit);
+  f.kv = reinterpret_cast<const int32_t*>(ws + p.layout.off_kv);
+  f.kv_items = reinterpret_cast<const int32_t*>(ws + lay.off_image + img.off_items);
+  f.col = reinterpret_cast<const int32_t*>(ws + lay.off_image + img.off_col);
+  f.head_left = reinterpret_cast<const int32_t*>(ws + p.layout.off_head_left);
+  const float scale = launch->softmax_scale > 0.f ? launch->softmax_scale
+                                                  : static_cast<float>(1.0 / std::sqrt(double(p.D)));
+  f.scale = scale;
+  f.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
+  f.L = static_cast<int32_t>(p.L);
+  f.H = static_cast<int32_t>(p.H);
+  f.Lpad = static_cast<int32_t>(p.nq * kBM);
+  f.nq = static_cast<int32_t>(p.nq);
+  f.kind = p.kind;
+  f.causal = p.causal;
+  f.chunk = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(p.chunk, p.L)));
+  f.right = static_cast<int32_t>(p.right);
+  f.prefix = static_cast<int32_t>(std::min<int64_t>(p.prefix, p.L));
+  f.kv_group = static_cast<int32_t>(p.H / hkv);
+  f.q_queue = static_cast<int32_t>(nq_items / 8);
+  f.kv_queue = static_cast<int32_t>(nkv_items / 8);
+  *out = f;
+  return ATTN_OK;
+}
+
+attn_status check_kv_heads(const attn_plan& p, int64_t kv_heads) {
+  if (kv_heads < 1 || p.H % kv_heads != 0) {
+    set_error("kv_heads must divide the plan's head count (" + std::to_string(p.H) + ")");
+    return ATTN_E_INVAL;
+  }
+  if (p.H / kv_heads > 127) { set_error("at most 127 query heads per K/V head"); return ATTN_E_UNSUPPORTED; }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+attn_status attn_masked_fwd_lse(const attn_plan* p, const attn_tensor* q, const attn_tensor* k,
+                                const attn_tensor* v, const float* sink, attn_tensor* o, float* lse,
+                                const attn_launch* launch) {
+  try {
+    if (!p) { set_error("plan is NULL"); return ATTN_E_INVAL; }
+    if (!launch) { set_error("launch is NULL"); return ATTN_E_INVAL; }
+    if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u)) { set_error("lse is NULL or misaligned"); return ATTN_E_INVAL; }
+    GroupParams g{};
+    g.n_jobs = 1;
+    attn_status st = make_job(*p, q, k, v, sink, o, launch->workspace, launch->workspace_bytes,
+                              launch->softmax_scale, &g.job[0], &g.queue_len[0]);
+    if (st != ATTN_OK) return st;
+    g.job[0].lse = lse;
+    return run_group(g, p->D, q->B, launch);
+  } catch (...) {
+    set_error("unexpected exception during launch");
+    return ATTN_E_NOMEM;
+  }
+}
+
+attn_status attn_bwd_workspace_bytes(const attn_plan* p, int64_t B, int64_t kv_heads, size_t* bytes) {
+  try {
+    if (!p || !bytes) { set_error("plan or bytes is NULL"); return ATTN_E_INVAL; }
+    if (B < 1 || B > 65535) { set_error("batch must be in [1, 65535]"); return ATTN_E_INVAL; }
+    attn_status st = check_kv_heads(*p, kv_heads);
+    if (st != ATTN_OK) return st;
+    *bytes = bwd_layout(*p, bwd_image(*p, kv_heads), B).total;
+    return ATTN_OK;
+  } catch (const std::bad_alloc&) {
+    set_error("host allocation failed while building the backward lists");
+    return ATTN_E_NOMEM;
+  } catch (...) {
+    set_error("unexpected exception");
+    return ATTN_E_NOMEM;
+  }
+}
+
+attn_status attn_bwd_lists(const attn_plan* p, int64_t kv_heads, int64_t* n_blocks, const int32_t** col_ptr,
+                           int64_t* n_entries, const int32_t** entries, int64_t* n_items, const int32_t** items) {
+  try {
+    if (!p) { set_error("plan is NULL"); return ATTN_E_INVAL; }
+    attn_status st = check_kv_heads(*p, kv_heads);
+    if (st != ATTN_OK) return st;
+    const BwdImage& img = bwd_image(*p, kv_heads);
+    if (n_blocks) *n_blocks = img.nkb;
+    if (col_ptr) *col_ptr = img.col_ptr.data();
+    if (n_entries) *n_entries = static_cast<int64_t>(img.col.size());
+    if (entries) *entries = img.col.data();
+    if (n_items) *n_items = static_cast<int64_t>(img.items.size());
+    if (items) *items = reinterpret_cast<const int32_t*>(img.items.data());
+    return ATTN_OK;
+  } catch (const std::bad_alloc&) {
+    set_error("host allocation failed while building the backward lists");
+    return ATTN_E_NOMEM;
+  } catch (...) {
+    set_error("unexpected exception");
+    return ATTN_E_NOMEM;
+  }
+}
+
+attn_status attn_bwd_upload(const attn_plan* p, int64_t kv_heads, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  try {
+    if (!p) { set_error("plan is NULL"); return ATTN_E_INVAL; }
+    attn_status st = check_kv_heads(*p, kv_heads);
+    if (st != ATTN_OK) return st;
+    const BwdImage& img = bwd_image(*p, kv_heads);
+    const BwdLayout lay = bwd_layout(*p, img, 1);
+    if (!workspace || workspace_bytes < lay.total) {
+      set_error("workspace smaller than attn_bwd_workspace_bytes (" + std::to_string(lay.total) + " bytes)");
+      return ATTN_E_WORKSPACE;
+    }
+    if (!aligned16(workspace)) { set_error("workspace must be 16-byte aligned"); return ATTN_E_INVAL; }
+    if ((st = upload(*p, workspace, workspace_bytes, stream)) != ATTN_OK) return st;
+    std::vector<uint8_t> buf(img.bytes);
+    write_bwd_image(img, buf.data());
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(static_cast<uint8_t*>(workspace) + lay.off_image, buf.data(), buf.size(),
+                                  hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (backward image)");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize (backward image)");
+    std::lock_guard<std::mutex> lk(p->bwd_mu);
+    p->bwd_uploads[workspace] = kv_heads;
+    return ATTN_OK;
+  } catch (const std::bad_alloc&) {
+    set_error("host allocation failed for the backward image");
+    return ATTN_E_NOMEM;
+  } catch (...) {
+    set_error("unexpected exception during upload");
+    return ATTN_E_NOMEM;
+  }
+}
+
+attn_status attn_masked_bwd(const attn_plan* p, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                            const attn_tensor* o, const attn_tensor* dout, const float* lse, const float* sink,
+                            attn_tensor* dq, attn_tensor* dk, attn_tensor* dv, float* dsink,
+                            const attn_launch* launch) {
+  try {
+    if (!p) { set_error("plan is NULL"); return ATTN_E_INVAL; }
+    BwdParams f;
+    attn_status st = make_bwd(*p, q, k, v, o, dout, lse, sink, dq, dk, dv, dsink, launch, &f);
+    if (st != ATTN_OK) return st;
+    hipError_t e = launch_bwd(f, static_cast<int>(p->D), static_cast<int>(q->B),
+                              static_cast<hipStream_t>(launch->stream), static_cast<hipEvent_t>(launch->start_event),
+                              static_cast<hipEvent_t>(launch->stop_event));
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return ATTN_OK;
+  } catch (const std::bad_alloc&) {
+    set_error("host allocation failed while building the backward lists");
+    return ATTN_E_NOMEM;
   } catch (...) {
     set_error("unexpected exception during launch");
     return ATTN_E_NOMEM;

@@ -36,6 +36,7 @@ struct FwdParams {
   int32_t chunk, right;
   int32_t prefix;             // prefix tokens added to every row's set (0 = none)
   int32_t kv_group;           // query heads per K/V head (grouped-query attention; 1 = MHA)
+  float* lse;                 // optional [B][H][L]: row log-sum-exp (natural log), -inf for empty rows
 };
 
 // Several launches (jobs) with the same head dim and batch run as one kernel.
@@ -53,6 +54,46 @@ static_assert(sizeof(GroupParams) <= 4096, "kernel arguments are limited to 4 Ki
 // (8 * sum of queue lengths, B); non-null events record the kernel's start and end.
 hipError_t launch_fwd(const GroupParams& g, int D, int B, hipStream_t stream, hipEvent_t start,
                       hipEvent_t stop);
+
+// Backward pass (attn_bwd.hip).
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int64_t q_sb, q_sl, q_sh;   // element strides
+  int64_t k_sb, k_sl, k_sh;
+  int64_t v_sb, v_sl, v_sh;
+  int64_t o_sb, o_sl, o_sh;
+  int64_t do_sb, do_sl, do_sh;
+  int64_t dq_sb, dq_sl, dq_sh;
+  int64_t dk_sb, dk_sl, dk_sh;
+  int64_t dv_sb, dv_sl, dv_sh;
+  const float* lse;           // [B][H][L] from the forward (natural log)
+  const float* sink;          // [H] or nullptr
+  float* dsink;               // [H] or nullptr
+  float* stat;                // workspace [B][H][2][Lpad]: lse in log2 units (+inf: no mass), then D
+  float* sinkpart;            // workspace [B][H][nq]: per query tile sums of exp(s_aux - lse_i) D_i
+  uint16_t* qs;               // workspace [B][H][L][D] bf16: Q * sigma * log2(e) rounded as the forward rounds it
+  const int32_t* q_items;     // dQ work items: the forward's unsplit schedule (8 queues)
+  const int32_t* kv;          // the forward's lists: (kv_tile << 1) | full
+  const int32_t* kv_items;    // dK/dV work items {kv head, key block, begin, end, ...} (8 queues)
+  const int32_t* col;         // per (kv head, key block): (group head << 24) | (query tile << 1) | full
+  const int32_t* head_left;   // [H] window left reach (WINDOW)
+  float scale;                // softmax scale sigma
+  float scale_log2;           // sigma * log2(e)
+  int32_t L, H, Lpad, nq;     // Lpad = nq * 128
+  int32_t kind, causal, chunk, right, prefix, kv_group;
+  int32_t q_queue, kv_queue;  // items per XCD queue
+};
+
+// Queue the backward kernels (prep, dQ, dK/dV, sink) on `stream`; non-null
+// events record the start of the first and the end of the last.
+hipError_t launch_bwd(const BwdParams& p, int D, int B, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 // RRAttention block-pattern search (rr_search.hip).
 struct RrParams {

@@ -472,6 +472,94 @@ attn_status compile_plan(const attn_mask_desc* m, int64_t L, int64_t H, int64_t 
   return ATTN_OK;
 }
 
+const BwdImage& bwd_image(const attn_plan& p, int64_t kv_heads) {
+  std::lock_guard<std::mutex> lk(p.bwd_mu);
+  auto it = p.bwd_images.find(kv_heads);
+  if (it != p.bwd_images.end()) return *it->second;
+  auto img = std::make_unique<BwdImage>();
+  const int64_t g = p.H / kv_heads;
+  const int64_t nkb = ceil_div(p.L, 2 * static_cast<int64_t>(kBN));
+  img->kv_heads = kv_heads;
+  img->nkb = nkb;
+  // per (query head, key block): query tiles listing tile 2kb or 2kb+1, and
+  // whether every pair of the block is allowed (both tiles FULL, or the
+  // block's second tile lies past the sequence end)
+  std::vector<std::vector<int32_t>> per(static_cast<size_t>(p.H * nkb));
+  for (int64_t h = 0; h < p.H; ++h) {
+    for (int64_t qt = 0; qt < p.nq; ++qt) {
+      const int64_t r = h * p.nq + qt;
+      int64_t last_kb = -1;
+      for (int32_t e = p.row_ptr[r]; e < p.row_ptr[r + 1]; ++e) {
+        const int64_t kt = p.kv_tile[e], kb = kt / 2;
+        const bool half_full = p.flags[e] != 0;
+        std::vector<int32_t>& v = per[static_cast<size_t>(h * nkb + kb)];
+        if (kb != last_kb) {
+          // first tile of this block in the row: FULL only if it is tile 2kb
+          // and tile 2kb+1 either follows FULL or does not exist
+          const bool second_exists = 2 * kb + 1 < p.nk;
+          bool full = half_full && (kt == 2 * kb);
+          if (full && second_exists) {
+            const bool next_listed = e + 1 < p.row_ptr[r + 1] && p.kv_tile[e + 1] == kt + 1;
+            full = next_listed && p.flags[e + 1] != 0;
+          }
+          v.push_back(static_cast<int32_t>((qt << 1) | (full ? 1 : 0)));
+          last_kb = kb;
+        }
+      }
+    }
+  }
+  // per (kv head, key block): the group's lists in head order; cost of an item
+  std::vector<Item> all;
+  std::vector<double> cost;
+  std::vector<double> head_cost(static_cast<size_t>(kv_heads), 0.0);
+  all.reserve(static_cast<size_t>(kv_heads * nkb));
+  img->col_ptr.assign(1, 0);
+  for (int64_t hk = 0; hk < kv_heads; ++hk) {
+    for (int64_t kb = 0; kb < nkb; ++kb) {
+      const int32_t begin = static_cast<int32_t>(img->col.size());
+      double c = 1.0;  // K, V fragment loads and the dK, dV stores
+      for (int64_t gi = 0; gi < g; ++gi) {
+        for (int32_t x : per[static_cast<size_t>((hk * g + gi) * nkb + kb)]) {
+          img->col.push_back(static_cast<int32_t>((gi << 24) | x));
+          c += (x & 1) ? 2.0 : 2.25;  // two 64-row steps; masking on PARTIAL entries
+        }
+      }
+      all.push_back(Item{static_cast<int32_t>(hk), static_cast<int32_t>(kb), begin,
+                         static_cast<int32_t>(img->col.size()), 0, 0, 1, 0});
+      img->col_ptr.push_back(static_cast<int32_t>(img->col.size()));
+      cost.push_back(c);
+      head_cost[static_cast<size_t>(hk)] += c;
+    }
+  }
+  std::vector<int64_t> heads(static_cast<size_t>(kv_heads));
+  std::iota(heads.begin(), heads.end(), 0);
+  std::stable_sort(heads.begin(), heads.end(), [&](int64_t a, int64_t b) { return head_cost[a] > head_cost[b]; });
+  img->items = layout_queues(heads, all, cost);
+  img->off_items = 0;
+  img->off_col = align_up(img->items.size() * sizeof(Item));
+  img->bytes = align_up(img->off_col + std::max<size_t>(1, img->col.size()) * sizeof(int32_t));
+  const BwdImage& ref = *img;
+  p.bwd_images.emplace(kv_heads, std::move(img));
+  return ref;
+}
+
+BwdLayout bwd_layout(const attn_plan& p, const BwdImage& img, int64_t B) {
+  BwdLayout l;
+  l.off_image = align_up(p.layout.total);
+  l.off_stat = align_up(l.off_image + img.bytes);
+  const size_t lpad = static_cast<size_t>(p.nq) * kBM;
+  l.off_sinkpart = align_up(l.off_stat + static_cast<size_t>(B) * p.H * 2 * lpad * sizeof(float));
+  l.off_qs = align_up(l.off_sinkpart + static_cast<size_t>(B) * p.H * p.nq * sizeof(float));
+  l.total = align_up(l.off_qs + static_cast<size_t>(B) * p.H * p.L * p.D * sizeof(uint16_t));
+  return l;
+}
+
+void write_bwd_image(const BwdImage& img, uint8_t* dst) {
+  std::memset(dst, 0, img.bytes);
+  std::memcpy(dst + img.off_items, img.items.data(), img.items.size() * sizeof(Item));
+  if (!img.col.empty()) std::memcpy(dst + img.off_col, img.col.data(), img.col.size() * sizeof(int32_t));
+}
+
 void write_image(const attn_plan& p, uint8_t* dst) {
   std::memset(dst, 0, p.layout.bytes);
   std::memcpy(dst + p.layout.off_items, p.items.data(), p.items.size() * sizeof(Item));

@@ -11,6 +11,9 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <map>
+#include <memory>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -40,6 +43,32 @@ struct ImageLayout {
   size_t off_items = 0, off_items_unsplit = 0, off_kv = 0, off_head_left = 0, off_bits = 0,
          off_counters = 0, bytes = 0;
   size_t off_partials = 0, total = 0;
+};
+
+// Backward image for one K/V head count (grouped-query attention changes
+// which query heads a dK/dV work item visits).  Key blocks are 2 key tiles
+// (128 keys, one work-group).  `col` lists, for every (kv head, key block),
+// the query tiles of each of the group's query heads whose forward list holds
+// one of the block's key tiles, as (group head << 24) | (query tile << 1) |
+// full, group heads in order and query tiles ascending; full = every pair of
+// the 128 x 128 rectangle is allowed.  `items` are the dK/dV work items
+// {kv head, key block, first col entry, one past the last, 0, 0, 1, 0} in
+// kXcds equal-length queues (kv head -1 pads).
+struct BwdImage {
+  int64_t kv_heads = 0, nkb = 0;
+  std::vector<Item> items;
+  std::vector<int32_t> col_ptr;  // [kv_heads * nkb + 1] (host only): (kv head, key block) row-major
+  std::vector<int32_t> col;
+  size_t off_items = 0, off_col = 0, bytes = 0;  // relative to the image start
+};
+
+// Workspace of a backward launch with batch B: the forward workspace
+// (image and partial states), the backward image, per-row statistics
+// (lse in log2 units and D, float [B][H][2][nq * kBM]), the per query tile
+// partial sums of the sink gradient (float [B][H][nq]) and the scaled
+// queries the scores are recomputed from (bf16 [B][H][L][D]).
+struct BwdLayout {
+  size_t off_image = 0, off_stat = 0, off_sinkpart = 0, off_qs = 0, total = 0;
 };
 
 void set_error(const std::string& msg);
@@ -79,6 +108,12 @@ struct attn_plan {
 
   // content fingerprint (cache key)
   uint64_t fingerprint = 0;
+
+  // backward images by K/V head count (built on first use) and the K/V head
+  // count each workspace was last uploaded for
+  mutable std::mutex bwd_mu;
+  mutable std::map<int64_t, std::unique_ptr<bss::BwdImage>> bwd_images;
+  mutable std::map<const void*, int64_t> bwd_uploads;
 };
 
 namespace bss {
@@ -93,5 +128,15 @@ uint64_t fingerprint(const attn_mask_desc* mask, int64_t L, int64_t H, int64_t D
 
 // Serialise the device image into `dst` (layout.bytes long).
 void write_image(const attn_plan& p, uint8_t* dst);
+
+// The backward image of plan p for kv_heads K/V heads (built once, cached in
+// the plan; thread-safe).  kv_heads must divide p.H.  Throws std::bad_alloc.
+const BwdImage& bwd_image(const attn_plan& p, int64_t kv_heads);
+
+// Byte layout of a backward workspace for batch B.
+BwdLayout bwd_layout(const attn_plan& p, const BwdImage& img, int64_t B);
+
+// Serialise the backward image into `dst` (img.bytes long).
+void write_bwd_image(const BwdImage& img, uint8_t* dst);
 
 }  // namespace bss

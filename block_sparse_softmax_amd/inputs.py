@@ -8,7 +8,7 @@ path can both be fed from it without sharing any part of the method.
 Every random stream is a numpy ``default_rng`` seeded with a list
 ``[seed, cfg, tensor_id, h]`` so that a single head of a 128K-token problem can
 be regenerated on its own.  Tensor ids: Q=0, K=1, V=2, sink=3, windows=4,
-block scores=5, sampled rows=6.
+block scores=5, sampled rows=6, upstream gradient dO=7.
 
 The workloads mirror the shapes on the pages: ViT token grids from 14-pixel
 patches (448/896/1792 px give 1,024/4,096/16,384 tokens; "Semantic Head
@@ -25,7 +25,7 @@ import math
 
 import numpy as np
 
-Q_ID, K_ID, V_ID, SINK_ID, WIN_ID, BLOCK_ID, ROWS_ID = 0, 1, 2, 3, 4, 5, 6
+Q_ID, K_ID, V_ID, SINK_ID, WIN_ID, BLOCK_ID, ROWS_ID, DO_ID = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 def child_rng(seed: int, cfg: int, tensor_id: int, h: int = 0) -> np.random.Generator:
@@ -63,6 +63,14 @@ def qkv_bf16(seed: int, cfg: int, B: int, H: int, L: int, D: int):
             t[:, h] = gaussian_bf16(seed, cfg, tid, h, (B, L, D))
         out.append(t)
     return tuple(out)
+
+
+def grad_out_bf16(seed: int, cfg: int, B: int, H: int, L: int, D: int) -> np.ndarray:
+    """Upstream gradient dO ~ N(0,1) as uint16 bf16 bits in [B, H, L, D] order."""
+    t = np.empty((B, H, L, D), dtype=np.uint16)
+    for h in range(H):
+        t[:, h] = gaussian_bf16(seed, cfg, DO_ID, h, (B, L, D))
+    return t
 
 
 def qkv_f32(seed: int, cfg: int, B: int, H: int, L: int, D: int):

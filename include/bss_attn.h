@@ -39,8 +39,8 @@
  *   - Functions return attn_status and never throw or abort.  On a non-OK status
  *     attn_last_error() returns a message (thread-local, valid until the next call
  *     on that thread).
- *   - Supported head dims: 64, 80, 128.  Batch B >= 1.  Lq == Lk.  GQA is not
- *     supported (K and V have as many heads as Q).
+ *   - Supported head dims: 64, 80, 128.  Batch B >= 1.  Lq == Lk.  K and V may
+ *     have fewer heads than Q (grouped-query attention, see attn_tensor).
  */
 #ifndef BSS_ATTN_H
 #define BSS_ATTN_H
@@ -211,6 +211,83 @@ attn_status attn_masked_fwd_group(int32_t n, const attn_plan* const* plans, cons
                                   const attn_tensor* k, const attn_tensor* v, const float* const* sinks,
                                   attn_tensor* o, void* const* workspaces, const size_t* workspace_bytes,
                                   const attn_launch* launch);
+
+/*
+ * Forward that also writes the log-sum-exp of every row, which the backward
+ * needs:  lse[b][h][i] = ln( sum over allowed j of exp(s_ij) + exp(s_aux[h]) )
+ * with s_ij = softmax_scale q_i.k_j; -inf for a row with neither an allowed
+ * key nor a sink.  lse: device float32 [B][H][L], contiguous, 4-byte aligned.
+ * Everything else as attn_masked_fwd_plan (a backward workspace prepared by
+ * attn_bwd_upload serves as the forward workspace too).
+ */
+attn_status attn_masked_fwd_lse(const attn_plan* plan, const attn_tensor* q, const attn_tensor* k,
+                                const attn_tensor* v, const float* sink, attn_tensor* o, float* lse,
+                                const attn_launch* launch);
+
+/*
+ * Backward pass.  For a loss with upstream gradient dO = dL/dO, the chain rule
+ * through O = P V and the masked row softmax P (the same definition as the
+ * forward; s_aux enters the denominator only) gives, per (batch, head), with
+ * sigma = softmax_scale and p_ij = exp(s_ij - lse_i) on allowed pairs (0 elsewhere):
+ *   D_i = dO_i . O_i,   dS_ij = p_ij (dO_i . v_j - D_i),
+ *   dQ_i = sigma sum_j dS_ij k_j,   dK_j = sigma sum_i dS_ij q_i,   dV_j = sum_i p_ij dO_i,
+ *   d s_aux[h] = - sum over b, i of exp(s_aux[h] - lse_i) D_i.
+ * With grouped-query heads, dK and dV of a K/V head sum over its query heads.
+ * The masks are those the pages train ("Semantic Head Specialization ...":
+ * the ViT variants with full / chunk / sliding-window heads; "Asymmetric
+ * Attention Heads": per-head causal windows); masked-out tiles are skipped,
+ * as in the forward.
+ *
+ * Workspace: attn_bwd_workspace_bytes(plan, B, kv_heads) bytes, prepared once
+ * by attn_bwd_upload(plan, kv_heads, ...) (it holds the plan's forward image,
+ * the transposed tile lists and dK/dV schedule for kv_heads K/V heads, then
+ * per-row statistics written by every backward launch).  Launches sharing a
+ * workspace must not overlap in time.
+ */
+attn_status attn_bwd_workspace_bytes(const attn_plan* plan, int64_t B, int64_t kv_heads, size_t* bytes);
+
+/*
+ * Transposed tile lists of the backward for kv_heads K/V heads (host views
+ * owned by the plan, valid until destroy).  Key blocks are 128 keys (two key
+ * tiles), n_blocks = ceil(L/128); rows are (K/V head, key block) in row-major
+ * order, col_ptr[kv_heads * n_blocks + 1].  An entry is
+ * (g << 24) | (query tile << 1) | full: query tile (of bm rows) of query head
+ * kv_head * (H / kv_heads) + g lists at least one of the block's key tiles;
+ * full = the whole 128-row x 128-key rectangle (clipped to the key tiles that
+ * exist) lies inside the sequence and is allowed.  Entries are ordered by g,
+ * then query tile.  items: the dK/dV work schedule, n_items records of 8 int32
+ * {kv head, key block, first entry, one past the last, 0, 0, 1, 0} in 8 equal
+ * queues like attn_plan_schedule (kv head -1 pads).
+ */
+attn_status attn_bwd_lists(const attn_plan* plan, int64_t kv_heads, int64_t* n_blocks, const int32_t** col_ptr,
+                           int64_t* n_entries, const int32_t** entries, int64_t* n_items, const int32_t** items);
+
+/* Copy the forward and backward images into `workspace` on `stream` (returns
+ * once copied); kv_heads must divide the plan's H (at most 127 query heads per
+ * K/V head). */
+attn_status attn_bwd_upload(const attn_plan* plan, int64_t kv_heads, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * Gradients of the forward with the same plan, inputs, sink and softmax_scale.
+ *   q, k, v, o : the forward's bf16 inputs and output ([B, L, H, D]; k, v with
+ *                kv_heads heads); dout: bf16 dL/dO [B, L, H, D].
+ *   lse        : device float32 [B][H][L] written by attn_masked_fwd_lse.
+ *   sink       : NULL or device float32 [H] (as in the forward).
+ *   dq         : bf16 [B, L, H, D] output; dk, dv: bf16 [B, L, kv_heads, D]
+ *                outputs (written entirely; distinct, not aliasing any input).
+ *   dsink      : NULL, or device float32 [H] output (zeros when sink is NULL).
+ *   launch     : stream, workspace (prepared by attn_bwd_upload for k->H K/V
+ *                heads), softmax_scale, optional events (start of the first
+ *                and end of the last of the backward kernels).
+ * Asynchronous.  Errors: ATTN_E_INVAL (shapes, strides, aliasing, NULL
+ * arguments, a workspace not prepared for this plan and K/V head count),
+ * ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP, ATTN_E_NOMEM.
+ */
+attn_status attn_masked_bwd(const attn_plan* plan, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                            const attn_tensor* o, const attn_tensor* dout, const float* lse, const float* sink,
+                            attn_tensor* dq, attn_tensor* dk, attn_tensor* dv, float* dsink,
+                            const attn_launch* launch);
 
 /*
  * RRAttention block-pattern search ("RRAttention", section 3, Eq. 6-12): from

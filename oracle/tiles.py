@@ -89,3 +89,32 @@ def tile_lists(mask: dict, H: int, L: int, bm: int, bn: int):
     if mask["kind"] == "block" and int(mask["block"]) % bm == 0 and int(mask["block"]) % bn == 0 and L > 16384:
         return tile_lists_block(mask, H, L, bm, bn)
     return tile_lists_dense(mask, H, L, bm, bn)
+
+
+def key_block_lists(mask: dict, H: int, Hk: int, L: int, bm: int, bn: int, kb_size: int = 128):
+    """Transposed lists for the backward, from the dense mask: for every (K/V head hk, key block of
+    kb_size keys), in that row-major order, the entries (g << 24) | (query tile << 1) | full for each
+    query head h = hk * (H / Hk) + g in turn and each query tile (of bm rows) whose rectangle with
+    the block holds an allowed pair; full = the rectangle (keys clipped to the bn-key tiles that
+    exist, i.e. to ceil(L / bn) * bn) lies inside the sequence and every pair is allowed.
+    Returns (col_ptr int32 [Hk * nkb + 1], entries int32)."""
+    g = H // Hk
+    nq, nk = math.ceil(L / bm), math.ceil(L / bn)
+    nkb = math.ceil(L / kb_size)
+    dense = [np.zeros((nq * bm, nkb * kb_size), dtype=bool) for _ in range(H)]
+    for h in range(H):
+        dense[h][:L, :L] = allowed_rows(mask, h, np.arange(L), L)
+    col_ptr, entries = [0], []
+    for hk in range(Hk):
+        for kb in range(nkb):
+            k0, k1 = kb * kb_size, min((kb + 1) * kb_size, nk * bn)
+            for gi in range(g):
+                m = dense[hk * g + gi]
+                for qt in range(nq):
+                    r0, r1 = qt * bm, (qt + 1) * bm
+                    rect = m[r0:r1, k0:k1]
+                    if rect.any():
+                        full = bool(rect.all()) and r1 <= L and k1 <= L
+                        entries.append((gi << 24) | (qt << 1) | int(full))
+            col_ptr.append(len(entries))
+    return np.array(col_ptr, dtype=np.int32), np.array(entries, dtype=np.int32)

@@ -145,3 +145,29 @@ def test_lse(mi):
             with np.errstate(divide="ignore"):
                 ref = logsumexp(s, axis=1)
             np.testing.assert_allclose(g["lse"][0, h], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mi", range(len(MASKS)))
+def test_sampled_rows_and_columns(mi):
+    """The row-sampled dQ and column-sampled dK/dV (for long sequences) equal the full gradients'
+    rows and columns, with and without a sink and with grouped heads."""
+    from oracle.backward import dkdv_cols, dq_rows, lse_rows
+    mask = MASKS[mi]
+    H, Hk, L, D = 2, 1, 16, 4
+    q, do = _rand((2, H, L, D), 71), _rand((2, H, L, D), 72)
+    for hk_n, sink in ((H, None), (Hk, np.array([0.3, -1.2]))):
+        k, v = _rand((2, hk_n, L, D), 73), _rand((2, hk_n, L, D), 74)
+        g = attention_backward(q, k, v, do, mask, sink=sink)
+        rows = np.array([[0, 5, 15], [3, 4, 9]])
+        np.testing.assert_allclose(dq_rows(q, k, v, do, mask, rows, sink=sink),
+                                   np.take_along_axis(g["dq"], rows[None, :, :, None], axis=2), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse_rows(q, k, mask, rows, sink=sink), np.take_along_axis(g["lse"], rows[None], axis=2),
+                                   rtol=0, atol=1e-12)
+        cols = np.array([[1, 8, 14], [0, 7, 15]])[:hk_n]
+        dk, dv = dkdv_cols(q, k, v, do, mask, cols, sink=sink, row_chunk=5)
+        np.testing.assert_allclose(dk, np.take_along_axis(g["dk"], cols[None, :, :, None], axis=2), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dv, np.take_along_axis(g["dv"], cols[None, :, :, None], axis=2), rtol=0, atol=1e-12)
+        if mask.get("causal"):   # rows before the first key cannot see it
+            dk2, dv2 = dkdv_cols(q, k, v, do, mask, cols, sink=sink, first_row=int(cols.min()))
+            np.testing.assert_allclose(dk2, dk, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(dv2, dv, rtol=0, atol=1e-12)
