@@ -19,7 +19,8 @@ and sliding window radius 512), causal LM prefill with per-head windows and
 sinks (L = 4096, d = 128) and 128K-token block-sparse causal prefill (32 heads,
 d = 128, block 128, about half of the causal blocks kept), timed the same way
 and reported under "extra", with RRAttention's block-pattern search on the
-128K-token Q and K (stride 8, block 128, tau 0.9).
+128K-token Q and K (stride 8, block 128, tau 0.9), and the backward pass of
+every mask of the 896-px layer and of the per-head-window LM.
 
 Prints ONE JSON line.
 """
@@ -274,6 +275,56 @@ def _bench_reorder(xs, gh, gw, steps, layout):
                               traffic=None, kernel="reorder_kernel", avg_launch_ms=avg))
 
 
+def _bench_bwd(name, device, steps, layout):
+    """Backward of every mask of a workload (the masks the pages train): attn_masked_fwd_lse once, then
+    attn_masked_bwd timed with events attached to its first and last kernel.  Algorithmic work per allowed
+    pair: 10 d flops (five products of 2 d: the scores, dP = dO V^T, dV, dK and dQ); the kernels
+    recompute the scores and dP once more each (14 d performed).  Bytes: Q, K, V, O, dO read and dQ,
+    dK, dV written once (bf16), the row statistics are negligible."""
+    import numpy as np
+    import torch
+    from block_sparse_softmax_amd import inputs as gen
+    from block_sparse_softmax_amd import prepare_backward
+    w = gen.workload(name)
+    B, H, L, D = w["B"], w["H"], w["L"], w["D"]
+    q, k, v = (_bits_to_dev(x, device, layout) for x in gen.qkv_bf16(0, w["cfg"], B, H, L, D))
+    g = torch.Generator(device="cpu").manual_seed(7)
+    dout = (torch.randn(q.shape, generator=g) * 0.05).to(torch.bfloat16).to(device)
+    sink = None if w["sink"] is None else torch.from_numpy(w["sink"]).to(device)
+    rows, tot_flops, tot_ms = [], 0.0, 0.0
+    for label, mask in w["masks"].items():
+        pb = prepare_backward(mask, L, H, D, B, H, device)
+        _, pairs = pb.plan.pairs()
+        o, lse = torch.empty_like(q), torch.empty((B, H, L), dtype=torch.float32, device=device)
+        pb.bind_forward(q, k, v, o, lse, sink=sink, layout=layout)()
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dsink = None if sink is None else torch.empty(H, dtype=torch.float32, device=device)
+        f = pb.bind_backward(q, k, v, o, dout, lse, dq, dk, dv, sink=sink, dsink=dsink, layout=layout)
+        f()
+        ev = _events(steps)
+        torch.cuda.synchronize()
+        for a, b in ev:
+            f(a, b)
+        torch.cuda.synchronize()
+        t = [a.elapsed_time(b) for a, b in ev]
+        avg = float(np.mean(t))
+        flops = 10.0 * D * float(pairs) * B
+        tot_flops += flops
+        tot_ms += avg
+        rows.append(dict(mask=label, pairs=int(pairs), avg_ms=avg, min_ms=float(np.min(t)),
+                         tflops=flops / (avg * 1e-3) / 1e12,
+                         frac_bf16_peak=flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         alg_gbs=(8 * B * H * L * D * 2) / (avg * 1e-3) / 1e9))
+        del pb, o, lse, dq, dk, dv
+    ach = tot_flops / (tot_ms * 1e-3) / 1e12
+    return dict(workload=WORKLOADS[name] + " -- backward (dQ, dK, dV, sink gradient), 10 d flops per allowed pair",
+                masks=rows, tflops=ach, frac_bf16_peak=ach / PEAK_BF16_TFLOPS,
+                roofline=dict(bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                              frac=ach / PEAK_BF16_TFLOPS, traffic=None,
+                              kernel=f"bwd_prep + bwd_dq + bwd_dkdv + bwd_sink, d = {D}, masks run one after another",
+                              avg_launch_ms=tot_ms / len(rows)))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,6 +386,10 @@ def main():
                 extra["rr_search128k"] = _bench_rr(q, k, 5, 1, args.layout)
             if name == "vit1792":
                 extra["reorder_vit1792"] = _bench_reorder(list(setup["dev"]), 128, 128, 5, args.layout)
+        del setup
+        torch.cuda.empty_cache()
+        for name in ("vit896", "lm_headwin"):
+            extra[f"backward_{name}"] = _bench_bwd(name, device, 5, args.layout)
 
     out = {
         "metric": "effective attention TFLOP/s (unmasked pairs) and % bf16 MFMA peak, 1 MI355X",

@@ -91,7 +91,8 @@ def _compare(got, ref, what):
 def _compare_lse(got, ref, what):
     both_inf = np.isneginf(got) & np.isneginf(ref)
     assert np.array_equal(np.isneginf(got), np.isneginf(ref)), what
-    err = float(np.abs(np.where(both_inf, 0.0, got - ref)).max()) if got.size else 0.0
+    diff = np.subtract(np.where(both_inf, 0.0, got), np.where(both_inf, 0.0, ref))
+    err = float(np.abs(diff).max()) if got.size else 0.0
     print(f"[parity] {what} lse: max_abs={err:.3e}", flush=True)
     assert err <= LSE_ABS, (what, err)
 
