@@ -20,7 +20,10 @@ sinks (L = 4096, d = 128) and 128K-token block-sparse causal prefill (32 heads,
 d = 128, block 128, about half of the causal blocks kept), timed the same way
 and reported under "extra", with RRAttention's block-pattern search on the
 128K-token Q and K (stride 8, block 128, tau 0.9), and the backward pass of
-every mask of the 896-px layer and of the per-head-window LM.
+every mask of the 896-px layer and of the per-head-window LM, and one-query
+decode steps over key/value caches (windows of 576 keys with a sink, 572 + 4
+prefix tokens, full attention at 128K; 32 query heads on 8 K/V heads at d = 128
+and 16 on 4 at d = 256), reported in GB/s against HBM.
 
 Prints ONE JSON line.
 """
@@ -325,6 +328,58 @@ def _bench_bwd(name, device, steps, layout):
                               avg_launch_ms=tot_ms / len(rows)))
 
 
+def _bench_decode(name, device, steps):
+    """One decode step (attn_decode_fwd) over the sequences of a decode workload: caches resident on the
+    device (every row outside the filled window / prefix holds NaN), events on the launch.  Algorithmic
+    bytes: the K and V rows of every allowed key of every sequence read once, the queries read and the
+    outputs written once (bf16)."""
+    import numpy as np
+    import torch
+    from block_sparse_softmax_amd import PreparedDecode
+    from block_sparse_softmax_amd import inputs as gen
+    w = gen.decode_workload(name)
+    B, H, Hkv, D, L, W, P = w["B"], w["H"], w["Hkv"], w["D"], w["Lmax"], w["window"], w["prefix"]
+    kc = torch.full((B, L, Hkv, D), float("nan"), dtype=torch.bfloat16, device=device)
+    vc = torch.full((B, L, Hkv, D), float("nan"), dtype=torch.bfloat16, device=device)
+    for b in range(B):
+        pos, kr, vr = gen.decode_cache_rows(0, w["cfg"], b, int(w["lens"][b]), Hkv, D, P, W if W > 0 else L)
+        idx = torch.as_tensor(pos, device=device)
+        kc[b].index_copy_(0, idx, _bits_to_dev(kr.transpose(1, 0, 2)[None], device, "bhld")[0])
+        vc[b].index_copy_(0, idx, _bits_to_dev(vr.transpose(1, 0, 2)[None], device, "bhld")[0])
+    q = _bits_to_dev(gen.decode_queries(0, w["cfg"], B, H, D)[None], device, "bhld")[0]
+    lens = torch.as_tensor(w["lens"], device=device)
+    sink = None if w["sink"] is None else torch.as_tensor(w["sink"], device=device)
+    out = torch.empty_like(q)
+    pd = PreparedDecode(q, kc, L, W, P)
+    f = pd.bind(q, kc, vc, lens, out, sink=sink)
+    for _ in range(3):
+        f()
+    ev = _events(steps)
+    torch.cuda.synchronize()
+    for a, b in ev:
+        f(a, b)
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in ev]
+    n = w["lens"].astype(np.int64)
+    lo = np.maximum(0, n - W) if W > 0 else np.zeros_like(n)
+    keys = np.minimum(np.minimum(P, n), lo) + (n - lo)            # window plus the prefix keys outside it
+    nbytes = float(keys.sum()) * Hkv * D * 2 * 2 + 2.0 * B * H * D * 2
+    avg = float(np.mean(t))
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    del kc, vc
+    torch.cuda.empty_cache()
+    win = f"window {W}" if W > 0 else "full causal"
+    return dict(workload=f"decode step: {B} sequences of {int(n.min())}..{int(n.max())} cached tokens, {H} query heads "
+                         f"on {Hkv} K/V heads, d={D}, {win}" + (f" + {P} prefix tokens" if P else "")
+                         + (", sink per head" if sink is not None else ""),
+                avg_ms=avg, min_ms=float(np.min(t)), alg_bytes=nbytes, alg_gbs=gbs,
+                sequences_per_s=B / (avg * 1e-3), splits=None if pd.workspace_bytes == 0 else "split keys + merge",
+                roofline=dict(bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s", frac=gbs / PEAK_HBM_GBS,
+                              traffic=None, kernel=f"decode_kernel<{D}>" + (" + decode_combine_kernel"
+                                                                           if pd.workspace_bytes else ""),
+                              avg_launch_ms=avg))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,6 +391,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="vit896")
     ap.add_argument("--only", default=None, help="time only this mask of the workload (profiling)")
+    ap.add_argument("--decode-only", action="store_true", help="run only the decode workloads (profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB mebibytes (counter calibration)")
     args = ap.parse_args()
@@ -357,6 +413,11 @@ def main():
         return
     from block_sparse_softmax_amd import load_library
     load_library()
+
+    if args.decode_only:
+        from block_sparse_softmax_amd.inputs import DECODE_WORKLOADS
+        print(json.dumps({name: _bench_decode(name, device, args.steps) for name in DECODE_WORKLOADS}))
+        return
 
     setup = _setup(args.workload, device, args.layout)
     if args.only:
@@ -390,6 +451,9 @@ def main():
         torch.cuda.empty_cache()
         for name in ("vit896", "lm_headwin"):
             extra[f"backward_{name}"] = _bench_bwd(name, device, 5, args.layout)
+        from block_sparse_softmax_amd.inputs import DECODE_WORKLOADS
+        for name in DECODE_WORKLOADS:
+            extra[name] = _bench_decode(name, device, 10)
 
     out = {
         "metric": "effective attention TFLOP/s (unmasked pairs) and % bf16 MFMA peak, 1 MI355X",

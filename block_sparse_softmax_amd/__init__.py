@@ -8,9 +8,11 @@ from ._lib import (  # noqa: F401
     AttnError,
     Plan,
     PreparedBackward,
+    PreparedDecode,
     PreparedMask,
     RrSearch,
     bind_group,
+    decode_fwd,
     load_library,
     masked_bwd,
     masked_fwd,
@@ -23,6 +25,6 @@ from ._lib import (  # noqa: F401
     tensor_view,
 )
 
-__all__ = ["AttnError", "Plan", "PreparedBackward", "PreparedMask", "RrSearch", "bind_group", "load_library",
+__all__ = ["AttnError", "Plan", "PreparedBackward", "PreparedDecode", "decode_fwd", "PreparedMask", "RrSearch", "bind_group", "load_library",
            "masked_bwd", "masked_fwd", "masked_fwd_lse", "masked_fwd_oneshot", "prepare", "prepare_backward",
            "reorder_tokens", "rr_search", "tensor_view"]

@@ -28,7 +28,7 @@ EXPORTS = ("attn_masked_fwd", "attn_workspace_bytes", "attn_plan_create", "attn_
            "attn_masked_fwd_plan", "attn_masked_fwd_group", "attn_rr_workspace_bytes", "attn_rr_search",
            "attn_reorder_tokens", "attn_masked_fwd_lse", "attn_bwd_workspace_bytes", "attn_bwd_lists",
            "attn_bwd_upload",
-           "attn_masked_bwd",
+           "attn_masked_bwd", "attn_decode_workspace_bytes", "attn_decode_fwd",
            "attn_plan_destroy", "attn_last_error", "attn_version")
 
 
@@ -55,6 +55,10 @@ class MaskDesc(ctypes.Structure):
                 ("head_left", ctypes.POINTER(ctypes.c_int64)),
                 ("block", ctypes.c_int64), ("block_mask", ctypes.POINTER(ctypes.c_uint8)),
                 ("block_mask_heads", ctypes.c_int32), ("prefix", ctypes.c_int64)]
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [("window", ctypes.c_int64), ("prefix", ctypes.c_int64)]
 
 
 class Launch(ctypes.Structure):
@@ -102,6 +106,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "attn_bwd_lists": [plan_p, i64, P(i64), P(P(i32)), P(i64), P(P(i32)), P(i64), P(P(i32))],
             "attn_masked_bwd": [plan_p, P(AttnTensor), P(AttnTensor), P(AttnTensor), P(AttnTensor), P(AttnTensor),
                                 vp, vp, P(AttnTensor), P(AttnTensor), P(AttnTensor), vp, P(Launch)],
+            "attn_decode_workspace_bytes": [P(AttnTensor), P(AttnTensor), i64, P(DecodeDesc), P(sz)],
+            "attn_decode_fwd": [P(AttnTensor), P(AttnTensor), P(AttnTensor), vp, i64, P(DecodeDesc), vp,
+                                P(AttnTensor), P(Launch)],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -536,6 +543,77 @@ def rr_search(q, k, stride: int, block: int, tau: float, protect_last: bool = Tr
     """RRAttention's block-pattern search of bf16 CUDA tensors q, k (see include/bss_attn.h):
     returns (block_mask uint8 [B, H, Nb, Nb], block_score float32 [B, H, Nb, Nb]) on the device."""
     return RrSearch(q, stride, block, tau, protect_last, layout)(q, k)
+
+
+def _token_view(t) -> AttnTensor:
+    """AttnTensor [B, 1, H, D] over a bf16 CUDA tensor [B, H, D] (one token per sequence)."""
+    import torch
+    if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 3 or t.stride(2) != 1:
+        raise TypeError("decode queries and outputs must be bf16 CUDA tensors [B, H, D] with contiguous D")
+    a = AttnTensor()
+    a.data = t.data_ptr()
+    a.B, a.L, a.H, a.D = t.shape[0], 1, t.shape[1], t.shape[2]
+    a.stride_b, a.stride_h = t.stride(0), t.stride(1)
+    a.stride_l = max(t.shape[2], t.stride(1) * t.shape[1])   # unused for one token; any valid value
+    return a
+
+
+class PreparedDecode:
+    """attn_decode_fwd for one shape (q [B, H, D], caches [B, Lmax, Hkv, D] in `layout`), window, prefix
+    and max_len, with its workspace allocated once."""
+
+    def __init__(self, q, k_cache, max_len: int, window: int = 0, prefix: int = 0, layout: str = "blhd"):
+        import torch
+        lib = load_library()
+        self.layout, self.max_len = layout, int(max_len)
+        self.desc = DecodeDesc(int(window), int(prefix))
+        qv, kv = _token_view(q), tensor_view(k_cache, layout)
+        nbytes = ctypes.c_size_t()
+        _check(lib.attn_decode_workspace_bytes(ctypes.byref(qv), ctypes.byref(kv), self.max_len,
+                                               ctypes.byref(self.desc), ctypes.byref(nbytes)))
+        self.workspace_bytes = nbytes.value
+        self.workspace = torch.empty(max(256, nbytes.value), dtype=torch.uint8, device=q.device)
+
+    def bind(self, q, k_cache, v_cache, seq_lens, o, sink=None, stream=None, softmax_scale: float = 0.0):
+        """Marshal once; the returned callable launches (optional events mark the kernels)."""
+        import torch
+        lib = load_library()
+        qv, ov = _token_view(q), _token_view(o)
+        kv, vv = tensor_view(k_cache, self.layout), tensor_view(v_cache, self.layout)
+        if seq_lens.dtype != torch.int32 or not seq_lens.is_cuda or seq_lens.numel() != qv.B \
+                or not seq_lens.is_contiguous():
+            raise TypeError("seq_lens must be a contiguous int32 CUDA tensor with one entry per sequence")
+        sp = _sink_ptr(sink, qv.H)
+        ln = Launch()
+        ln.stream = _stream_ptr(stream, q).value
+        ln.workspace = self.workspace.data_ptr()
+        ln.workspace_bytes = self.workspace.numel()
+        ln.softmax_scale = softmax_scale
+        args = (ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), ctypes.c_void_p(seq_lens.data_ptr()),
+                self.max_len, ctypes.byref(self.desc), sp, ctypes.byref(ov), ctypes.byref(ln))
+        keep = (qv, kv, vv, ov, ln, q, k_cache, v_cache, seq_lens, o, sink)
+        fn = lib.attn_decode_fwd
+
+        def run(start_event=None, stop_event=None):
+            ln.start_event = None if start_event is None else start_event.cuda_event
+            ln.stop_event = None if stop_event is None else stop_event.cuda_event
+            _check(fn(*args))
+            return keep[9]
+        return run
+
+
+def decode_fwd(q, k_cache, v_cache, seq_lens, max_len: int, window: int = 0, prefix: int = 0, sink=None, out=None,
+               layout: str = "blhd", stream=None, softmax_scale: float = 0.0):
+    """One decode step (attn_decode_fwd): q bf16 [B, H, D] (the newest token of each sequence), caches bf16
+    [B, Lmax, Hkv, D] ('blhd') or [B, Hkv, Lmax, D] ('bhld'), seq_lens int32 [B] on the device; returns
+    bf16 [B, H, D]."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q)
+    pd = PreparedDecode(q, k_cache, max_len, window, prefix, layout)
+    pd.bind(q, k_cache, v_cache, seq_lens, out, sink=sink, stream=stream, softmax_scale=softmax_scale)()
+    torch.cuda.current_stream(q.device).synchronize()   # the workspace lives until the kernels have run
+    return out
 
 
 ORDERS = {"raster": 0, "block_row": 1, "block_col": 2}

@@ -50,10 +50,11 @@ def build(verbose: bool = False) -> str:
         [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "attn_bwd.hip"), "-o", os.path.join(BUILD, "attn_bwd.o")],
         [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "rr_search.hip"), "-o", os.path.join(BUILD, "rr_search.o")],
         [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "reorder.hip"), "-o", os.path.join(BUILD, "reorder.o")],
+        [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "decode.hip"), "-o", os.path.join(BUILD, "decode.o")],
         ["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "plan.cpp"), "-o", os.path.join(BUILD, "plan.o")],
         ["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "capi.cpp"), "-o", os.path.join(BUILD, "capi.o")],
     ]
-    with ThreadPoolExecutor(6) as ex:
+    with ThreadPoolExecutor(7) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:
         for o in outs:
@@ -62,7 +63,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
           os.path.join(BUILD, "attn_fwd.o"), os.path.join(BUILD, "attn_bwd.o"), os.path.join(BUILD, "rr_search.o"), os.path.join(BUILD, "reorder.o"),
-          os.path.join(BUILD, "plan.o"),
+          os.path.join(BUILD, "decode.o"), os.path.join(BUILD, "plan.o"),
           os.path.join(BUILD, "capi.o")])
     os.replace(tmp, LIB)
     return LIB

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <initializer_list>
@@ -356,14 +357,14 @@ attn_status attn_masked_fwd_group(int32_t n, const attn_plan* const* plans, cons
 
 namespace {
 
-bool overlaps_any(const void* x, std::initializer_list<const void*> others) {
+static bool overlaps_any(const void* x, std::initializer_list<const void*> others) {
   for (const void* o : others)
     if (o == x) return true;
   return false;
 }
 
 // Validate a backward launch and fill its kernel parameters.
-attn_status make_bwd(const attn_plan& p, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+static attn_status make_bwd(const attn_plan& p, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
                      const attn_tensor* o, const attn_tensor* dout, const float* lse, const float* sink,
                      attn_tensor* dq, attn_tensor* dk, attn_tensor* dv, float* dsink, const attn_launch* launch,
                      BwdParams* out) {
@@ -471,7 +472,7 @@ attn_status make_bwd(const attn_plan& p, const attn_tensor* q, const attn_tensor
   return ATTN_OK;
 }
 
-attn_status check_kv_heads(const attn_plan& p, int64_t kv_heads) {
+static attn_status check_kv_heads(const attn_plan& p, int64_t kv_heads) {
   if (kv_heads < 1 || p.H % kv_heads != 0) {
     set_error("kv_heads must divide the plan's head count (" + std::to_string(p.H) + ")");
     return ATTN_E_INVAL;
@@ -605,7 +606,7 @@ constexpr int kRrTileQ = 128;    // sampled queries per work-group of the scores
 constexpr int kRrMaxBlocks = 4096;
 
 // Validate a search request and fill the kernel parameters (pointers except the workspace).
-attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const attn_rr_params* prm, RrParams* out,
+static attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const attn_rr_params* prm, RrParams* out,
                        size_t* ws_bytes) {
   if (!q || !k || !prm) { set_error("q, k or prm is NULL"); return ATTN_E_INVAL; }
   const int64_t B = q->B, L = q->L, H = q->H, D = q->D;
@@ -661,6 +662,95 @@ attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const attn_rr
   *out = p;
   *ws_bytes = 2 * static_cast<size_t>(B) * H * ns_pad * D * sizeof(uint16_t);
   return ATTN_OK;
+}
+
+// Key split of a decode launch: enough work-groups to fill the chip at the
+// kernel's occupancy (about 512), at least one 64-key tile per split.
+struct DecodeSplit {
+  int32_t nsplit, chunk;
+};
+static DecodeSplit decode_split(int64_t B, int64_t hkv, int64_t max_len, int64_t window, int64_t prefix) {
+  const int64_t max_keys = window > 0 ? std::min<int64_t>(max_len, window + prefix) : max_len;
+  const int64_t tiles = std::max<int64_t>(1, (max_keys + 63) / 64);
+  const int64_t want = std::max<int64_t>(1, (512 + B * hkv - 1) / (B * hkv));
+  const int64_t ns = std::min<int64_t>(std::min<int64_t>(want, tiles), 4096);
+  const int64_t per = (tiles + ns - 1) / ns;
+  return DecodeSplit{static_cast<int32_t>((tiles + per - 1) / per), static_cast<int32_t>(per * 64)};
+}
+
+// Window and prefix of a decode launch as the kernel takes them: a window of
+// at least max_len keys is every cached key (0).
+static void decode_reach(const attn_decode_desc* desc, int64_t max_len, int64_t* window, int64_t* prefix) {
+  *window = (desc->window <= 0 || desc->window >= max_len) ? 0 : desc->window;
+  *prefix = std::min<int64_t>(desc->prefix, max_len);
+}
+
+// Validate a decode launch and fill its parameters (workspace not checked).
+static attn_status make_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, const attn_tensor* o,
+                        int64_t max_len, const attn_decode_desc* desc, DecodeParams* out, int64_t* D_out) {
+  if (!q || !k || !v || !desc) { set_error("q, k_cache, v_cache or desc is NULL"); return ATTN_E_INVAL; }
+  const int64_t B = q->B, H = q->H, D = q->D;
+  if (D != 64 && D != 128 && D != 256) {
+    set_error("decode supports head dims 64, 128 and 256");
+    return ATTN_E_UNSUPPORTED;
+  }
+  if (B < 1 || B > 65535 || H < 1 || q->L != 1) {
+    set_error("q must be [B, 1, H, D] with 1 <= B <= 65535, H >= 1");
+    return ATTN_E_INVAL;
+  }
+  attn_status st;
+  if ((st = check_tensor(q, "q", B, 1, H, D)) != ATTN_OK) return st;
+  const int64_t hkv = k->H, lmax = k->L;
+  if (hkv < 1 || H % hkv != 0 || v->H != hkv) {
+    set_error("k_cache and v_cache need the same number of heads, a divisor of q's");
+    return ATTN_E_INVAL;
+  }
+  if (H / hkv > 16) { set_error("at most 16 query heads per cache head"); return ATTN_E_UNSUPPORTED; }
+  if (lmax < 1 || hkv > 65535) { set_error("the caches need 1 <= Lmax and Hkv <= 65535"); return ATTN_E_INVAL; }
+  if ((st = check_tensor(k, "k_cache", B, lmax, hkv, D)) != ATTN_OK) return st;
+  if ((st = check_tensor(v, "v_cache", B, lmax, hkv, D)) != ATTN_OK) return st;
+  if ((st = check_tensor(o, "o", B, 1, H, D)) != ATTN_OK) return st;
+  if (o->data == q->data || o->data == k->data || o->data == v->data) {
+    set_error("o must not alias q or the caches");
+    return ATTN_E_INVAL;
+  }
+  if (max_len < 0 || max_len > lmax || max_len > INT32_MAX / 2) {
+    set_error("max_len must be in [0, Lmax]");
+    return ATTN_E_INVAL;
+  }
+  if (desc->prefix < 0) { set_error("prefix must be >= 0"); return ATTN_E_INVAL; }
+  // row offsets inside one (sequence, head) are 32-bit
+  if (lmax * std::max(k->stride_l, v->stride_l) * 2 + D * 2 > static_cast<int64_t>(UINT32_MAX)) {
+    set_error("cache token stride * Lmax too large for 32-bit row offsets");
+    return ATTN_E_UNSUPPORTED;
+  }
+  int64_t window, prefix;
+  decode_reach(desc, max_len, &window, &prefix);
+  const DecodeSplit sp = decode_split(B, hkv, max_len, window, prefix);
+  DecodeParams p{};
+  p.q = static_cast<const uint16_t*>(q->data);
+  p.k = static_cast<const uint16_t*>(k->data);
+  p.v = static_cast<const uint16_t*>(v->data);
+  p.o = static_cast<uint16_t*>(o->data);
+  p.q_sb = q->stride_b; p.q_sh = q->stride_h;
+  p.k_sb = k->stride_b; p.k_sl = k->stride_l; p.k_sh = k->stride_h;
+  p.v_sb = v->stride_b; p.v_sl = v->stride_l; p.v_sh = v->stride_h;
+  p.o_sb = o->stride_b; p.o_sh = o->stride_h;
+  p.B = static_cast<int32_t>(B);
+  p.H = static_cast<int32_t>(H);
+  p.G = static_cast<int32_t>(H / hkv);
+  p.max_len = static_cast<int32_t>(max_len);
+  p.window = static_cast<int32_t>(window);
+  p.prefix = static_cast<int32_t>(prefix);
+  p.nsplit = sp.nsplit;
+  p.chunk = sp.chunk;
+  *out = p;
+  *D_out = D;
+  return ATTN_OK;
+}
+
+static size_t decode_ws_bytes(int64_t B, int64_t H, int64_t D, int32_t nsplit) {
+  return nsplit > 1 ? static_cast<size_t>(B) * H * nsplit * (D + 2) * sizeof(float) : 0;
 }
 
 }  // namespace
@@ -739,6 +829,66 @@ attn_status attn_reorder_tokens(const attn_tensor* in, int32_t from, attn_tensor
                                   static_cast<hipEvent_t>(launch->start_event),
                                   static_cast<hipEvent_t>(launch->stop_event));
     if (e != hipSuccess) return hip_fail(e, "reorder launch");
+    return ATTN_OK;
+  } catch (...) {
+    set_error("unexpected exception");
+    return ATTN_E_NOMEM;
+  }
+}
+
+attn_status attn_decode_workspace_bytes(const attn_tensor* q, const attn_tensor* k_cache, int64_t max_len,
+                                        const attn_decode_desc* desc, size_t* bytes) {
+  try {
+    if (!bytes) { set_error("bytes is NULL"); return ATTN_E_INVAL; }
+    if (!q || !k_cache || !desc) { set_error("q, k_cache or desc is NULL"); return ATTN_E_INVAL; }
+    if (q->D != 64 && q->D != 128 && q->D != 256) {
+      set_error("decode supports head dims 64, 128 and 256");
+      return ATTN_E_UNSUPPORTED;
+    }
+    if (q->B < 1 || q->H < 1 || k_cache->H < 1 || q->H % k_cache->H != 0 || max_len < 0 ||
+        max_len > k_cache->L || desc->prefix < 0) {
+      set_error("inconsistent q / k_cache shapes, max_len or prefix");
+      return ATTN_E_INVAL;
+    }
+    int64_t window, prefix;
+    decode_reach(desc, max_len, &window, &prefix);
+    const DecodeSplit sp = decode_split(q->B, k_cache->H, max_len, window, prefix);
+    *bytes = decode_ws_bytes(q->B, q->H, q->D, sp.nsplit);
+    return ATTN_OK;
+  } catch (...) {
+    set_error("unexpected exception");
+    return ATTN_E_NOMEM;
+  }
+}
+
+attn_status attn_decode_fwd(const attn_tensor* q, const attn_tensor* k_cache, const attn_tensor* v_cache,
+                            const int32_t* seq_lens, int64_t max_len, const attn_decode_desc* desc,
+                            const float* sink, attn_tensor* o, const attn_launch* launch) {
+  try {
+    if (!launch) { set_error("launch is NULL"); return ATTN_E_INVAL; }
+    if (!seq_lens) { set_error("seq_lens is NULL"); return ATTN_E_INVAL; }
+    DecodeParams p{};
+    int64_t D = 0;
+    attn_status st = make_decode(q, k_cache, v_cache, o, max_len, desc, &p, &D);
+    if (st != ATTN_OK) return st;
+    const size_t need = decode_ws_bytes(p.B, p.H, D, p.nsplit);
+    if (need > 0) {
+      if (!launch->workspace || launch->workspace_bytes < need) {
+        set_error("workspace smaller than attn_decode_workspace_bytes (" + std::to_string(need) + " bytes)");
+        return ATTN_E_WORKSPACE;
+      }
+      if (!aligned16(launch->workspace)) { set_error("workspace must be 16-byte aligned"); return ATTN_E_INVAL; }
+      p.partials = static_cast<float*>(launch->workspace);
+    }
+    p.seq_lens = seq_lens;
+    p.sink = sink;
+    const float scale = launch->softmax_scale > 0.f ? launch->softmax_scale
+                                                    : static_cast<float>(1.0 / std::sqrt(double(D)));
+    p.scale_log2 = static_cast<float>(scale * 1.4426950408889634);
+    hipError_t e = launch_decode(p, static_cast<int>(D), static_cast<hipStream_t>(launch->stream),
+                                 static_cast<hipEvent_t>(launch->start_event),
+                                 static_cast<hipEvent_t>(launch->stop_event));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ATTN_OK;
   } catch (...) {
     set_error("unexpected exception");

@@ -129,4 +129,28 @@ struct ReorderParams {
 
 hipError_t launch_reorder(const ReorderParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
+// One-query decode attention over a key/value cache (decode.hip).
+struct DecodeParams {
+  const uint16_t* q;          // [B, H, D] (one query token per sequence)
+  const uint16_t* k;          // cache [B, Lmax, Hkv, D]
+  const uint16_t* v;
+  uint16_t* o;                // [B, H, D]
+  int64_t q_sb, q_sh;         // element strides
+  int64_t k_sb, k_sl, k_sh;
+  int64_t v_sb, v_sl, v_sh;
+  int64_t o_sb, o_sh;
+  const int32_t* seq_lens;    // device [B]: cached tokens n_b (the query is token n_b - 1)
+  const float* sink;          // [H] or nullptr
+  float* partials;            // [B][H][nsplit][D + 2] when nsplit > 1: acc, reference, denominator
+  float scale_log2;           // softmax scale * log2(e)
+  int32_t B, H, G;            // G = query heads per K/V head (<= 16)
+  int32_t max_len;            // bound applied to seq_lens (<= Lmax)
+  int32_t window;             // keys [n - window, n); <= 0: every cached key
+  int32_t prefix;             // keys [0, prefix) as well
+  int32_t nsplit, chunk;      // key splits and keys per split (a multiple of 64)
+};
+
+// Queue the decode kernel (and, with nsplit > 1, the split merge) on `stream`.
+hipError_t launch_decode(const DecodeParams& p, int D, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
 }  // namespace bss

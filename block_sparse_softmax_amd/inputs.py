@@ -8,7 +8,9 @@ path can both be fed from it without sharing any part of the method.
 Every random stream is a numpy ``default_rng`` seeded with a list
 ``[seed, cfg, tensor_id, h]`` so that a single head of a 128K-token problem can
 be regenerated on its own.  Tensor ids: Q=0, K=1, V=2, sink=3, windows=4,
-block scores=5, sampled rows=6, upstream gradient dO=7.
+block scores=5, sampled rows=6, upstream gradient dO=7, decode sequence
+lengths=8 (K/V cache rows and decode queries reuse the K, V and Q ids with
+the sequence index in place of the head).
 
 The workloads mirror the shapes on the pages: ViT token grids from 14-pixel
 patches (448/896/1792 px give 1,024/4,096/16,384 tokens; "Semantic Head
@@ -25,7 +27,7 @@ import math
 
 import numpy as np
 
-Q_ID, K_ID, V_ID, SINK_ID, WIN_ID, BLOCK_ID, ROWS_ID, DO_ID = 0, 1, 2, 3, 4, 5, 6, 7
+Q_ID, K_ID, V_ID, SINK_ID, WIN_ID, BLOCK_ID, ROWS_ID, DO_ID, LEN_ID = 0, 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def child_rng(seed: int, cfg: int, tensor_id: int, h: int = 0) -> np.random.Generator:
@@ -166,3 +168,55 @@ def workload(name: str, seed: int = 0) -> dict:
 
 
 WORKLOADS = ("tiny_chunk", "vit896", "vit1792", "lm_headwin", "blocksparse128k")
+
+
+# ---------------------------------------------------------------------------
+# Decode: one new query per sequence against a key/value cache.
+# ---------------------------------------------------------------------------
+
+def decode_lengths(seed: int, cfg: int, B: int, lo: int, hi: int) -> np.ndarray:
+    """Cached-token counts of B sequences, uniform integers in [lo, hi]: int32 [B]."""
+    return child_rng(seed, cfg, LEN_ID).integers(lo, hi + 1, size=B).astype(np.int32)
+
+
+def decode_queries(seed: int, cfg: int, B: int, H: int, D: int) -> np.ndarray:
+    """The new query token of every sequence, N(0,1) rounded to bf16: uint16 [B, H, D]."""
+    return np.stack([gaussian_bf16(seed, cfg, Q_ID, b, (H, D)) for b in range(B)])
+
+
+def decode_cache_rows(seed: int, cfg: int, b: int, n: int, Hkv: int, D: int, head_rows: int, tail_rows: int):
+    """The cache rows of sequence b (n cached tokens) that a run fills with data: the first
+    head_rows and the last tail_rows positions (every position when they cover all n).
+    Returns (positions int64 [m] ascending, K uint16 [Hkv, m, D], V uint16 [Hkv, m, D])."""
+    pos = np.union1d(np.arange(min(head_rows, n)), np.arange(max(0, n - tail_rows), n)).astype(np.int64)
+    k = gaussian_bf16(seed, cfg, K_ID, b, (Hkv, len(pos), D))
+    v = gaussian_bf16(seed, cfg, V_ID, b, (Hkv, len(pos), D))
+    return pos, k, v
+
+
+def decode_workload(name: str, seed: int = 0) -> dict:
+    """Decode shapes of the sliding-window vs linear-attention article: attention of a Qwen3-4B-like
+    layer (32 query heads on 8 K/V heads, head dim 128) and the Qwen3.5-4B-like speed test
+    (16 on 4, head dim 256); windows of 576 keys with a learned sink, 572 + 4 prefix tokens, and
+    full attention at a 128K-token prompt.  Returns {"cfg", "B", "H", "Hkv", "D", "Lmax",
+    "lens" int32 [B], "window", "prefix", "sink" float32 [H] or None}."""
+    if name == "decode_swa576":
+        B, H, Hkv, D, L = 64, 32, 8, 128, 131072
+        return dict(cfg=10, B=B, H=H, Hkv=Hkv, D=D, Lmax=L, lens=decode_lengths(seed, 10, B, 1024, L),
+                    window=576, prefix=0, sink=head_sinks(seed, 10, H))
+    if name == "decode_swa572_prefix4":
+        B, H, Hkv, D, L = 64, 32, 8, 128, 131072
+        return dict(cfg=11, B=B, H=H, Hkv=Hkv, D=D, Lmax=L, lens=decode_lengths(seed, 11, B, 1024, L),
+                    window=572, prefix=4, sink=None)
+    if name == "decode_full128k":
+        B, H, Hkv, D, L = 1, 32, 8, 128, 131072
+        return dict(cfg=12, B=B, H=H, Hkv=Hkv, D=D, Lmax=L, lens=np.full(B, L, np.int32),
+                    window=0, prefix=0, sink=None)
+    if name == "decode_swa576_d256":
+        B, H, Hkv, D, L = 64, 16, 4, 256, 131072
+        return dict(cfg=13, B=B, H=H, Hkv=Hkv, D=D, Lmax=L, lens=decode_lengths(seed, 13, B, 1024, L),
+                    window=576, prefix=0, sink=head_sinks(seed, 13, H))
+    raise KeyError(name)
+
+
+DECODE_WORKLOADS = ("decode_swa576", "decode_swa572_prefix4", "decode_full128k", "decode_swa576_d256")

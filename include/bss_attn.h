@@ -357,6 +357,53 @@ typedef enum { ATTN_ORDER_RASTER = 0, ATTN_ORDER_BLOCK_ROW = 1, ATTN_ORDER_BLOCK
 attn_status attn_reorder_tokens(const attn_tensor* in, int32_t from, attn_tensor* out, int32_t to,
                                 int64_t grid_h, int64_t grid_w, const attn_launch* launch);
 
+/*
+ * One-query (decode) attention over a key/value cache.  The sliding-window
+ * vs linear attention article generates with a causal window of the last W
+ * cached tokens ("comparison at equal memory": 576 tokens with a learned
+ * per-head sink, or 572 plus 4 StreamingLLM sink tokens) on grouped-query
+ * heads (32 query heads on 8 key/value heads at head dim 128; its speed test
+ * 16 on 4 at head dim 256).  For sequence b with n = seq_lens[b] cached
+ * tokens the query is token n - 1, and its allowed keys are
+ *     the window  n - W <= j <= n - 1   (W <= 0: every cached key, j < n)
+ *     the prefix  j < P                 (P = 0: none),
+ * the same set that the WINDOW mask with causal = 1, left = W - 1 and
+ * prefix = P gives that row in the prefill.  Softmax, sink and empty rows as
+ * for attn_masked_fwd.
+ */
+typedef struct {
+  int64_t window;             /* W: window length in keys (query included); <= 0 = every cached key */
+  int64_t prefix;             /* P >= 0: leading keys always allowed                          */
+} attn_decode_desc;
+
+/* Workspace bytes attn_decode_fwd needs for these shapes (0 when the keys of
+ * a sequence are not split over several work-groups). */
+attn_status attn_decode_workspace_bytes(const attn_tensor* q, const attn_tensor* k_cache, int64_t max_len,
+                                        const attn_decode_desc* desc, size_t* bytes);
+
+/*
+ * Decode step on launch->stream (asynchronous; optional events bracket its
+ * one or two kernels).
+ *   q        : bf16 [B, 1, H, D] device view, one query token per sequence; D in {64, 128, 256}.
+ *   k_cache, v_cache : bf16 [B, Lmax, Hkv, D] device views; H a multiple of Hkv
+ *              with H / Hkv <= 16 (query head h reads cache head h / (H / Hkv)).
+ *   seq_lens : device int32 [B]: cached tokens of each sequence; values are
+ *              clamped to [0, max_len] (0: the output row is zero).
+ *   max_len  : host bound on seq_lens, 0 <= max_len <= Lmax; it sizes the
+ *              split of the keys over work-groups.
+ *   desc     : host descriptor (window, prefix).
+ *   sink     : NULL, or device float32 [H] sink logits.
+ *   o        : bf16 [B, 1, H, D] output (must not alias the inputs).
+ * Workspace: attn_decode_workspace_bytes bytes (may be NULL when that is 0);
+ * launches that share a workspace must not overlap in time.
+ * Errors: ATTN_E_INVAL (shapes, strides, alignment, NULL pointers, negative
+ * prefix, max_len out of range), ATTN_E_UNSUPPORTED (D, H / Hkv > 16, a cache
+ * too large for 32-bit row offsets), ATTN_E_WORKSPACE, ATTN_E_HIP.
+ */
+attn_status attn_decode_fwd(const attn_tensor* q, const attn_tensor* k_cache, const attn_tensor* v_cache,
+                            const int32_t* seq_lens, int64_t max_len, const attn_decode_desc* desc,
+                            const float* sink, attn_tensor* o, const attn_launch* launch);
+
 /* Free a plan (NULL is allowed). */
 void attn_plan_destroy(attn_plan* plan);
 

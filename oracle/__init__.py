@@ -20,6 +20,8 @@ rr_search.py  RRAttention's block-pattern search (Eq. 6-12): sampled queries,
 backward.py   the gradients dQ, dK, dV and of the sink logit, and the row
               log-sum-exp, by the chain rule through the masked softmax.
 serialize.py  token positions under raster and 2x2-block serialisation orders.
+decode.py     one-query decode over a key/value cache: the new token's row of
+              the causal window (+ prefix) mask, gathered keys, the same softmax.
 
 Every function is pinned by ``tests/test_oracle*.py`` against brute force,
 closed forms, invariants and the worked numbers printed on the pages; see the
@@ -31,3 +33,4 @@ from .tiles import tile_lists  # noqa: F401
 from .counts import pair_count  # noqa: F401
 from .rr_search import rr_search  # noqa: F401
 from .backward import attention_backward  # noqa: F401
+from .decode import decode_attention  # noqa: F401

@@ -312,3 +312,47 @@ def test_reorder_argument_errors_without_gpu(lib):
     assert f(ctypes.byref(i), 0, ctypes.byref(o), 1, 3, 16, ctypes.byref(ln)) == _lib.ATTN_E_INVAL  # odd side
     assert f(ctypes.byref(i), 0, ctypes.byref(o), 3, 6, 8, ctypes.byref(ln)) == _lib.ATTN_E_INVAL   # bad order
     assert f(ctypes.byref(i), 0, ctypes.byref(i), 1, 6, 8, ctypes.byref(ln)) == _lib.ATTN_E_INVAL   # aliasing
+
+
+def test_decode_argument_errors_without_gpu(lib):
+    """Decode validation runs on the host before any device call."""
+    import ctypes
+    from block_sparse_softmax_amd._lib import AttnTensor, DecodeDesc, Launch
+
+    def view(B, L, H, D, ptr=16):
+        t = AttnTensor()
+        t.data, t.B, t.L, t.H, t.D = ptr, B, L, H, D
+        t.stride_b, t.stride_l, t.stride_h = L * H * D, H * D, D
+        return t
+
+    desc = DecodeDesc(576, 0)
+    nbytes = ctypes.c_size_t()
+    q, k = view(64, 1, 32, 128), view(64, 131072, 8, 128, 4096)
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(q), ctypes.byref(k), 131072, ctypes.byref(desc),
+                                           ctypes.byref(nbytes)) == 0
+    assert nbytes.value == 0                      # 512 work-groups: one split per sequence and head
+    q1, k1 = view(1, 1, 32, 128), view(1, 131072, 8, 128, 4096)
+    full = DecodeDesc(0, 0)
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(q1), ctypes.byref(k1), 131072, ctypes.byref(full),
+                                           ctypes.byref(nbytes)) == 0
+    assert nbytes.value == 32 * 64 * 130 * 4      # 64 splits of 2048 keys, (D + 2) floats each
+    bad_d = view(1, 1, 32, 80)
+    assert lib.attn_decode_workspace_bytes(ctypes.byref(bad_d), ctypes.byref(k1), 10, ctypes.byref(desc),
+                                           ctypes.byref(nbytes)) == -2
+    ln = Launch()
+    o = view(1, 1, 32, 128, 8192)
+    v1 = view(1, 131072, 8, 128, 4096 + 1024)
+    seq = ctypes.c_void_p(64)
+    assert lib.attn_decode_fwd(ctypes.byref(q1), ctypes.byref(k1), ctypes.byref(v1), None, 10,
+                               ctypes.byref(desc), None, ctypes.byref(o), ctypes.byref(ln)) == -1   # no seq_lens
+    assert lib.attn_decode_fwd(ctypes.byref(q1), ctypes.byref(k1), ctypes.byref(v1), seq, 131073,
+                               ctypes.byref(desc), None, ctypes.byref(o), ctypes.byref(ln)) == -1   # max_len > Lmax
+    g17 = view(1, 1, 17 * 8, 128)
+    assert lib.attn_decode_fwd(ctypes.byref(g17), ctypes.byref(k1), ctypes.byref(v1), seq, 10,
+                               ctypes.byref(desc), None, ctypes.byref(view(1, 1, 17 * 8, 128, 8192)),
+                               ctypes.byref(ln)) == -2                                                # 17 heads per cache head
+    neg = DecodeDesc(576, -1)
+    assert lib.attn_decode_fwd(ctypes.byref(q1), ctypes.byref(k1), ctypes.byref(v1), seq, 10,
+                               ctypes.byref(neg), None, ctypes.byref(o), ctypes.byref(ln)) == -1    # negative prefix
+    assert lib.attn_decode_fwd(ctypes.byref(q1), ctypes.byref(k1), ctypes.byref(v1), seq, 131072,
+                               ctypes.byref(full), None, ctypes.byref(o), ctypes.byref(ln)) == -3   # no workspace
