@@ -328,7 +328,7 @@ def _bench_bwd(name, device, steps, layout):
                               avg_launch_ms=tot_ms / len(rows)))
 
 
-def _bench_decode(name, device, steps):
+def _bench_decode(name, device, steps, layout="blhd"):
     """One decode step (attn_decode_fwd) over the sequences of a decode workload: caches resident on the
     device (every row outside the filled window / prefix holds NaN), events on the launch.  Algorithmic
     bytes: the K and V rows of every allowed key of every sequence read once, the queries read and the
@@ -339,18 +339,24 @@ def _bench_decode(name, device, steps):
     from block_sparse_softmax_amd import inputs as gen
     w = gen.decode_workload(name)
     B, H, Hkv, D, L, W, P = w["B"], w["H"], w["Hkv"], w["D"], w["Lmax"], w["window"], w["prefix"]
-    kc = torch.full((B, L, Hkv, D), float("nan"), dtype=torch.bfloat16, device=device)
-    vc = torch.full((B, L, Hkv, D), float("nan"), dtype=torch.bfloat16, device=device)
+    # caches [B, Lmax, Hkv, D] ('blhd', a token's heads side by side) or [B, Hkv, Lmax, D] ('bhld')
+    shape = (B, L, Hkv, D) if layout == "blhd" else (B, Hkv, L, D)
+    kc = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=device)
+    vc = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=device)
     for b in range(B):
         pos, kr, vr = gen.decode_cache_rows(0, w["cfg"], b, int(w["lens"][b]), Hkv, D, P, W if W > 0 else L)
         idx = torch.as_tensor(pos, device=device)
-        kc[b].index_copy_(0, idx, _bits_to_dev(kr.transpose(1, 0, 2)[None], device, "bhld")[0])
-        vc[b].index_copy_(0, idx, _bits_to_dev(vr.transpose(1, 0, 2)[None], device, "bhld")[0])
+        if layout == "blhd":
+            kc[b].index_copy_(0, idx, _bits_to_dev(kr.transpose(1, 0, 2)[None], device, "bhld")[0])
+            vc[b].index_copy_(0, idx, _bits_to_dev(vr.transpose(1, 0, 2)[None], device, "bhld")[0])
+        else:
+            kc[b].index_copy_(1, idx, _bits_to_dev(kr[None], device, "bhld")[0])
+            vc[b].index_copy_(1, idx, _bits_to_dev(vr[None], device, "bhld")[0])
     q = _bits_to_dev(gen.decode_queries(0, w["cfg"], B, H, D)[None], device, "bhld")[0]
     lens = torch.as_tensor(w["lens"], device=device)
     sink = None if w["sink"] is None else torch.as_tensor(w["sink"], device=device)
     out = torch.empty_like(q)
-    pd = PreparedDecode(q, kc, L, W, P)
+    pd = PreparedDecode(q, kc, L, W, P, layout=layout)
     f = pd.bind(q, kc, vc, lens, out, sink=sink)
     for _ in range(3):
         f()
@@ -370,7 +376,7 @@ def _bench_decode(name, device, steps):
     torch.cuda.empty_cache()
     win = f"window {W}" if W > 0 else "full causal"
     return dict(workload=f"decode step: {B} sequences of {int(n.min())}..{int(n.max())} cached tokens, {H} query heads "
-                         f"on {Hkv} K/V heads, d={D}, {win}" + (f" + {P} prefix tokens" if P else "")
+                         f"on {Hkv} K/V heads, d={D}, {win}, cache {layout}" + (f" + {P} prefix tokens" if P else "")
                          + (", sink per head" if sink is not None else ""),
                 avg_ms=avg, min_ms=float(np.min(t)), alg_bytes=nbytes, alg_gbs=gbs,
                 sequences_per_s=B / (avg * 1e-3), splits=None if pd.workspace_bytes == 0 else "split keys + merge",
@@ -392,6 +398,8 @@ def main():
     ap.add_argument("--workload", default="vit896")
     ap.add_argument("--only", default=None, help="time only this mask of the workload (profiling)")
     ap.add_argument("--decode-only", action="store_true", help="run only the decode workloads (profiling)")
+    ap.add_argument("--decode-layout", default="blhd", choices=["blhd", "bhld"],
+                    help="K/V cache layout of the decode workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB mebibytes (counter calibration)")
     args = ap.parse_args()
@@ -416,7 +424,8 @@ def main():
 
     if args.decode_only:
         from block_sparse_softmax_amd.inputs import DECODE_WORKLOADS
-        print(json.dumps({name: _bench_decode(name, device, args.steps) for name in DECODE_WORKLOADS}))
+        print(json.dumps({name: _bench_decode(name, device, args.steps, args.decode_layout)
+                          for name in DECODE_WORKLOADS}))
         return
 
     setup = _setup(args.workload, device, args.layout)

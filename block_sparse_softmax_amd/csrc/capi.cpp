@@ -665,14 +665,16 @@ static attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const 
 }
 
 // Key split of a decode launch: enough work-groups to fill the chip at the
-// kernel's occupancy (about 512), at least one 64-key tile per split.
+// kernel's LDS-bound occupancy (4, 2, 1 work-groups per CU at head dim 64,
+// 128, 256), at least one 64-key tile per split.
 struct DecodeSplit {
   int32_t nsplit, chunk;
 };
-static DecodeSplit decode_split(int64_t B, int64_t hkv, int64_t max_len, int64_t window, int64_t prefix) {
+static DecodeSplit decode_split(int64_t B, int64_t hkv, int64_t D, int64_t max_len, int64_t window, int64_t prefix) {
   const int64_t max_keys = window > 0 ? std::min<int64_t>(max_len, window + prefix) : max_len;
   const int64_t tiles = std::max<int64_t>(1, (max_keys + 63) / 64);
-  const int64_t want = std::max<int64_t>(1, (512 + B * hkv - 1) / (B * hkv));
+  const int64_t target = 256 * (D <= 64 ? 4 : D <= 128 ? 2 : 1);
+  const int64_t want = std::max<int64_t>(1, (target + B * hkv - 1) / (B * hkv));
   const int64_t ns = std::min<int64_t>(std::min<int64_t>(want, tiles), 4096);
   const int64_t per = (tiles + ns - 1) / ns;
   return DecodeSplit{static_cast<int32_t>((tiles + per - 1) / per), static_cast<int32_t>(per * 64)};
@@ -726,7 +728,7 @@ static attn_status make_decode(const attn_tensor* q, const attn_tensor* k, const
   }
   int64_t window, prefix;
   decode_reach(desc, max_len, &window, &prefix);
-  const DecodeSplit sp = decode_split(B, hkv, max_len, window, prefix);
+  const DecodeSplit sp = decode_split(B, hkv, D, max_len, window, prefix);
   DecodeParams p{};
   p.q = static_cast<const uint16_t*>(q->data);
   p.k = static_cast<const uint16_t*>(k->data);
@@ -852,7 +854,7 @@ attn_status attn_decode_workspace_bytes(const attn_tensor* q, const attn_tensor*
     }
     int64_t window, prefix;
     decode_reach(desc, max_len, &window, &prefix);
-    const DecodeSplit sp = decode_split(q->B, k_cache->H, max_len, window, prefix);
+    const DecodeSplit sp = decode_split(q->B, k_cache->H, q->D, max_len, window, prefix);
     *bytes = decode_ws_bytes(q->B, q->H, q->D, sp.nsplit);
     return ATTN_OK;
   } catch (...) {

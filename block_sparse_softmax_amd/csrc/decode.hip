@@ -22,9 +22,11 @@
 //     (unnormalised output, reference, denominator) and decode_combine merges
 //     them in split order with the sink.
 //   * K and V tiles of 64 keys go global -> LDS with global_load_lds_dwordx4
-//     (per-lane row addresses follow the virtual list), double-buffered; LDS
-//     rows carry one 16-byte pad chunk so that the fragment reads below fall
-//     in distinct banks.
+//     (per-lane row addresses follow the virtual list) into two buffers, two
+//     tiles in flight: tile t+2 is issued as soon as every wave is done with
+//     tile t, so a work-group waits on one tile while the next is already on
+//     its way.  LDS rows carry one 16-byte pad chunk so that the fragment
+//     reads below fall in distinct banks.
 //   * wave w takes keys 16w .. 16w+15 of each tile.  S^T = K Q^T on
 //     v_mfma_f32_16x16x32_bf16: K rows from LDS (A operand), the group's
 //     query heads as the 16 columns of B (zero columns past the group), so
@@ -73,6 +75,15 @@ __device__ __forceinline__ float pair16_max(float x) {
 __device__ __forceinline__ float pair16_sum(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (N < 64: the gfx9 vmcnt field is bits 3:0 and 15:14; expcnt and lgkmcnt
+// are left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // exp2 of a difference where a -inf first argument gives 0 (and -inf - -inf is not formed).
@@ -150,11 +161,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
   const int k_off = (16 * wave + col) * S::LRB + 16 * g;
   const int v_off = (16 * wave + 4 * g + (col >> 2)) * S::LRB + 8 * (col & 3);
 
+  // DMA instructions this wave issues per tile (instructions i = wave, wave + 4, ... < 2 SPR)
+  constexpr int kLoadsHi = (2 * S::SPR + 3) / 4, kLoadsLo = (2 * S::SPR) / 4;
+  const bool loads_hi = (2 * S::SPR - wave + 3) / 4 == kLoadsHi;
   if (ntiles > 0) issue(0, 0);
+  if (ntiles > 1) issue(1, 1);
   for (int t = 0; t < ntiles; ++t) {
-    wait_vmcnt<0>();   // this wave's part of tile t
-    wg_barrier();      // every wave's part; every wave is done with tile t-1's buffer
-    if (t + 1 < ntiles) issue(t + 1, (t + 1) & 1);
+    // this wave's part of tile t (tile t+1's loads, issued later, may stay in flight)
+    if (t + 1 < ntiles) {
+      if (loads_hi) wait_vm<kLoadsHi>();
+      else wait_vm<kLoadsLo>();
+    } else {
+      wait_vm<0>();
+    }
+    wg_barrier();      // every wave's part of tile t has landed
     const unsigned char* kt = smem + (2 * (t & 1)) * S::TILE;
     const unsigned char* vt = kt + S::TILE;
 
@@ -189,6 +209,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
       acc[dt] *= alpha;
       const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vt + v_off + 32 * dt));
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[dt], 0, 0, 0);
+    }
+    if (t + 2 < ntiles) {
+      wg_barrier();    // every wave is done with buffer t & 1
+      issue(t + 2, t & 1);
     }
   }
 
@@ -246,27 +270,59 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeParams p) 
   }
 }
 
-// Merge the splits of one (sequence, query head) in split order, with the sink.
+// Merge the splits of one (sequence, query head) with the sink.  The split
+// references and denominators are staged in LDS with their weights
+// 2^(m_s - M); thread (d, r) of the 256 sums the weighted partial outputs of
+// element d over splits r, r + R, ... (R = 256 / D), and the R partial sums
+// are added in a fixed order, so the result does not depend on timing.
+constexpr int kMaxSplits = 4096;
 __global__ __launch_bounds__(256) void decode_combine_kernel(const DecodeParams p, int D) {
-  const int hq = blockIdx.x, b = blockIdx.y;
-  const float* part = p.partials + (static_cast<int64_t>(b) * p.H + hq) * p.nsplit * (D + 2);
+  __shared__ float wgt[kMaxSplits];
+  __shared__ float red[256];
+  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int ns = p.nsplit;
+  const float* part = p.partials + (static_cast<int64_t>(b) * p.H + hq) * ns * (D + 2);
   const float sl = p.sink ? p.sink[hq] * kLog2e : kNegInf;
-  float M = sl;
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float out = 0.f;
-    if (M != kNegInf) {
-      float A = 0.f, Lsum = exp2_rel(sl, M);
-      for (int s = 0; s < p.nsplit; ++s) {
-        const float ms = part[s * (D + 2) + D];
-        if (ms == kNegInf) continue;
-        const float f = __builtin_amdgcn_exp2f(ms - M);
-        A += f * part[s * (D + 2) + d];
-        Lsum += f * part[s * (D + 2) + D + 1];
-      }
-      out = Lsum > 0.f ? A / Lsum : 0.f;
-    }
-    p.o[b * p.o_sb + hq * p.o_sh + d] = __builtin_bit_cast(uint16_t, (__bf16)out);
+  float mx = sl;
+  for (int s = tid; s < ns; s += 256) {
+    const float m = part[s * (D + 2) + D];
+    wgt[s] = m;
+    mx = fmaxf(mx, m);
+  }
+  red[tid] = mx;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float lsum = 0.f;
+  for (int s = tid; s < ns; s += 256) {
+    const float f = (M == kNegInf) ? 0.f : exp2_rel(wgt[s], M);
+    wgt[s] = f;
+    lsum += f * part[s * (D + 2) + D + 1];
+  }
+  red[tid] = lsum;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  const float den = red[0] + ((M == kNegInf) ? 0.f : exp2_rel(sl, M));
+  __syncthreads();
+  const int R = 256 / D;                 // D in {64, 128, 256}
+  const int d = tid % D, r = tid / D;
+  float a = 0.f;
+#pragma unroll 8
+  for (int s = r; s < ns; s += R) a += wgt[s] * part[s * (D + 2) + d];
+  red[tid] = a;
+  __syncthreads();
+  if (tid < D) {
+    float acc = 0.f;
+    for (int j = 0; j < R; ++j) acc += red[j * D + tid];
+    const float out = den > 0.f ? acc / den : 0.f;
+    p.o[b * p.o_sb + hq * p.o_sh + tid] = __builtin_bit_cast(uint16_t, (__bf16)out);
   }
 }
 
@@ -281,7 +337,7 @@ hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream, hipEvent_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipExtLaunchKernelGGL(decode_combine_kernel, dim3(static_cast<unsigned>(p.H), static_cast<unsigned>(p.B)),
-                        dim3(D < 256 ? D : 256), 0, stream, nullptr, stop, 0, p, D);
+                        dim3(256), 0, stream, nullptr, stop, 0, p, D);
   return hipGetLastError();
 }
 
