@@ -332,3 +332,32 @@ def test_grouped_query_heads_and_prefix_tokens(ci):
     got = _run_gpu(q, k, v, mask, sink, layout="bhld")
     ref = attention(q, k, v, mask, sink=sink)["out"]
     _compare(got, ref, f"gqa-prefix{ci}")
+
+
+def _grouped_as_bench(w, q, k, v):
+    """Every mask of workload w in ONE grouped launch on [B, H, L, D] tensors: the launch bench.py times."""
+    from block_sparse_softmax_amd import bind_group, prepare
+    qt, kt, vt = (_bits_to_bf16(x) for x in (q, k, v))
+    sink = None if w["sink"] is None else torch.as_tensor(w["sink"]).cuda()
+    labels = list(w["masks"])
+    pms = [prepare(w["masks"][m], w["L"], w["H"], w["D"], qt.device) for m in labels]
+    outs = [torch.empty_like(qt) for _ in labels]
+    n = len(labels)
+    bind_group(pms, [qt] * n, [kt] * n, [vt] * n, outs, sinks=[sink] * n, layout="bhld")()
+    torch.cuda.synchronize()
+    return {m: o.float().cpu().double().numpy() for m, o in zip(labels, outs)}
+
+
+@pytest.mark.parametrize("name", ["vit896", "vit1792", "lm_headwin", "blocksparse128k"])
+def test_workloads_in_the_bench_launch(name):
+    """The grouped [B, H, L, D] launch of each workload against the oracle: all rows up to 4096 tokens,
+    512 seeded rows per head beyond."""
+    w = gen.workload(name)
+    print(f"[case] {name}: grouped launch as timed", flush=True)
+    q, k, v = gen.qkv_bf16(0, w["cfg"], w["B"], w["H"], w["L"], w["D"])
+    got = _grouped_as_bench(w, q, k, v)
+    rows = None if w["rows"] is None else gen.sampled_rows(0, w["cfg"], w["H"], w["L"], w["rows"])
+    for label, mask in w["masks"].items():
+        ref = attention(q, k, v, mask, sink=w["sink"], rows=rows)["out"]
+        g = got[label] if rows is None else np.stack([got[label][:, h, rows[h]] for h in range(w["H"])], axis=1)
+        _compare(g, ref, f"{name}-{label} grouped")
