@@ -379,11 +379,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const BwdParams p) 
         dsb[t][e] = (__bf16)(pr * (dp[t >> 1][r] - drow));
       }
     }
-    // dQ^T += K^T dS^T
+    // dQ^T += K^T dS^T.  At d < 128 two waves share a SIMD: the one feeding
+    // the matrix core issues first (raised priority), the other's VALU work
+    // fills the MFMA shadow (+5 % on the 896-px full backward; at d = 128 it
+    // cost 3 %).
+    if constexpr (D != 128) {
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt) acc[dt] = mfma32(tr_frag<D>(kt, toff[dt][0], toff[dt][1], t), dsb[t], acc[dt]);
+    }
+    if constexpr (D != 128) {
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     ent_cur = ent_nxt;
     ent_nxt = __builtin_amdgcn_readfirstlane(raw2);
@@ -560,7 +571,12 @@ __global__ __launch_bounds__(kThreads, DkdvShape<D>::OCC) void bwd_dkdv_kernel(c
         pb[r >> 3][r & 7] = (__bf16)pr;
         dsb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - dr));
       }
-      // dV^T += dO^T P, dK^T += Q^T dS (K dimension: 16-query steps 2c, 2c+1)
+      // dV^T += dO^T P, dK^T += Q^T dS (K dimension: 16-query steps 2c, 2c+1),
+      // at raised priority when two waves share a SIMD (as in the dQ kernel)
+      if constexpr (D != 128) {
+        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
@@ -568,6 +584,10 @@ __global__ __launch_bounds__(kThreads, DkdvShape<D>::OCC) void bwd_dkdv_kernel(c
           dv[dt] = mfma32(tr_frag<D>(gt, toff[dt][0], toff[dt][1], 2 * c + t2), pb[t2], dv[dt]);
           dk[dt] = mfma32(tr_frag<D>(qt, toff[dt][0], toff[dt][1], 2 * c + t2), dsb[t2], dk[dt]);
         }
+      }
+      if constexpr (D != 128) {
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (s == 1) {
