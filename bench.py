@@ -14,7 +14,8 @@ head, summed over the masks, divided by the step time (2d flops for the score
 and 2d for the value mix per allowed pair; padding, masked pairs inside
 partial tiles and the exponentials are not counted).
 
-Extra workloads (skipped with --quick): the 1792-px ViT layer (L = 16384, full
+Extra workloads (skipped with --quick; each warmed up for about 0.2 s of
+launches so the clocks settle, then timed): the 1792-px ViT layer (L = 16384, full
 and sliding window radius 512), causal LM prefill with per-head windows and
 sinks (L = 4096, d = 128) and 128K-token block-sparse causal prefill (32 heads,
 d = 128, block 128, about half of the causal blocks kept), timed the same way
@@ -121,7 +122,7 @@ def _events(n):
     return ev
 
 
-def _time(setup, steps, warmup, layout):
+def _time(setup, steps, warmup, layout, warm_s=0.0):
     """Time `steps` steps.  A step is ONE grouped launch (attn_masked_fwd_group) of every mask of
     the workload, each mask writing its own output.
 
@@ -141,6 +142,12 @@ def _time(setup, steps, warmup, layout):
                        sinks=[sink] * n, layout=layout, stream=stream)
     for _ in range(warmup):
         group()
+    if warm_s > 0:   # extra workloads: keep launching until the clocks have settled
+        torch.cuda.synchronize()
+        t_w = time.perf_counter()
+        while time.perf_counter() - t_w < warm_s:
+            group()
+            torch.cuda.synchronize()
     ev = _events(steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -446,7 +453,7 @@ def main():
             torch.cuda.empty_cache()
             setup = _setup(name, device, args.layout)
             nst = max(5, args.steps // 2)
-            wl, pg, pm = _time(setup, nst, args.warmup, args.layout)
+            wl, pg, pm = _time(setup, nst, args.warmup, args.layout, warm_s=0.2)
             r2, tf2, ms2, g2 = _summarise(setup, wl, pg, pm, nst)
             extra[name] = dict(workload=WORKLOADS[name], ms_per_step=ms2, tflops=tf2 / (ms2 * 1e-3) / 1e12,
                                frac_bf16_peak=tf2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, masks=r2,
