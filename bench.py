@@ -12,7 +12,9 @@ steps, for the per-mask table.
 Metric: effective attention TFLOP/s = 4 * d * (unmasked query-key pairs) per
 head, summed over the masks, divided by the step time (2d flops for the score
 and 2d for the value mix per allowed pair; padding, masked pairs inside
-partial tiles and the exponentials are not counted).
+partial tiles and the exponentials are not counted).  Each mask's row also
+gives the computed-tile efficiency (unmasked pairs / pairs inside the listed
+128 x 64 tiles) and the exponentials per second (one per pair of a listed tile).
 
 Extra workloads (skipped with --quick; each warmed up for about 0.2 s of
 launches so the clocks settle, then timed): the 1792-px ViT layer (L = 16384, full
@@ -109,7 +111,9 @@ def _setup(name, device, layout):
     for label, mask in w["masks"].items():
         pm = prepare(mask, w["L"], w["H"], w["D"], device)
         _, pairs = pm.plan.pairs()
-        masks.append(dict(label=label, mask=mask, pm=pm, pairs=int(pairs), o=torch.empty_like(dev[0])))
+        bm, bn, _, kv_tile, _ = pm.plan.tiles()
+        masks.append(dict(label=label, mask=mask, pm=pm, pairs=int(pairs), tiles=int(len(kv_tile)), tile_pairs=bm * bn,
+                          o=torch.empty_like(dev[0])))
     return dict(w=w, host=(q, k, v), dev=dev, sink=sink, masks=masks)
 
 
@@ -178,10 +182,13 @@ def _summarise(setup, wall, per_group, per_mask, steps):
     for m, t in zip(setup["masks"], per_mask):
         flops = 4.0 * D * m["pairs"] * w["B"]
         avg = float(np.mean(t))
+        computed = float(m["tiles"]) * m["tile_pairs"] * w["B"]   # pairs inside listed tiles: one exp each
         rows.append(dict(mask=m["label"], pairs=m["pairs"], avg_ms=avg, min_ms=float(np.min(t)),
                          tflops=flops / (avg * 1e-3) / 1e12,
                          frac_bf16_peak=flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                         alg_gbs=(4 * w["B"] * w["H"] * w["L"] * D * 2) / (avg * 1e-3) / 1e9))
+                         alg_gbs=(4 * w["B"] * w["H"] * w["L"] * D * 2) / (avg * 1e-3) / 1e9,
+                         listed_tiles=m["tiles"], tile_efficiency=m["pairs"] * w["B"] / computed,
+                         exp_per_s=computed / (avg * 1e-3)))
     total_flops = sum(4.0 * D * m["pairs"] * w["B"] for m in setup["masks"])
     ms_per_step = wall / steps * 1e3
     group = dict(avg_ms=float(np.mean(per_group)), min_ms=float(np.min(per_group)),
