@@ -38,6 +38,7 @@ import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -88,6 +89,43 @@ def _roofline(setup, group, total_flops, workload):
                 frac=achieved / PEAK_BF16_TFLOPS, traffic=_traffic_from_profile(workload, label),
                 kernel=f"attn_fwd_kernel<{w['D']}> grouped launch ({workload}: {', '.join(group['masks'])})",
                 avg_launch_ms=group["avg_ms"])
+
+
+def _clocks():
+    """GPU clocks from amd-smi (best effort): mean and range of the graphics-engine clocks and the memory
+    clock in MHz, or None when the tool is unavailable."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+        c = (d["gpu_data"] if isinstance(d, dict) else d)[0]["clock"]
+        gfx = [float(v["clk"]["value"]) for k, v in c.items() if k.startswith("gfx") and isinstance(v, dict)]
+        mem = [float(v["clk"]["value"]) for k, v in c.items() if k.startswith("mem") and isinstance(v, dict)]
+        return dict(gfx_mhz_mean=sum(gfx) / len(gfx) if gfx else None, gfx_mhz_min=min(gfx) if gfx else None,
+                    gfx_mhz_max=max(gfx) if gfx else None, mem_mhz=mem[0] if mem else None)
+    except Exception:  # noqa: BLE001 - informational only
+        return None
+
+
+def _clocks_under_load(setup, layout, seconds=1.0):
+    """Sample the clocks while about `seconds` of the workload's launches are queued on the GPU."""
+    import torch
+    from block_sparse_softmax_amd import bind_group
+    q, k, v = setup["dev"]
+    ms = setup["masks"]
+    n = len(ms)
+    group = bind_group([m["pm"] for m in ms], [q] * n, [k] * n, [v] * n, [m["o"] for m in ms],
+                       sinks=[setup["sink"]] * n, layout=layout)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    group()
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-4)
+    for _ in range(max(1, int(seconds / one))):
+        group()
+    time.sleep(min(0.3, seconds / 3))
+    c = _clocks()
+    torch.cuda.synchronize()
+    return c
 
 
 def _bits_to_dev(u16, device, layout):
@@ -412,6 +450,7 @@ def main():
     ap.add_argument("--workload", default="vit896")
     ap.add_argument("--only", default=None, help="time only this mask of the workload (profiling)")
     ap.add_argument("--decode-only", action="store_true", help="run only the decode workloads (profiling)")
+    ap.add_argument("--no-clocks", action="store_true", help="do not query amd-smi for the GPU clocks")
     ap.add_argument("--decode-layout", default="blhd", choices=["blhd", "bhld"],
                     help="K/V cache layout of the decode workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -424,6 +463,8 @@ def main():
 
     import torch
     device = torch.device("cuda:0")
+    clock = (lambda: None) if args.no_clocks else _clocks
+    clocks = dict(idle_before=clock())
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
@@ -466,6 +507,13 @@ def main():
                                frac_bf16_peak=tf2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, masks=r2,
                                grouped_launch=g2, roofline=_roofline(setup, g2, tf2, name))
             if name == "blocksparse128k":
+                if not args.no_clocks:
+                    c = clocks["under_load_blocksparse128k"] = _clocks_under_load(setup, args.layout)
+                    if c and c.get("gfx_mhz_mean"):
+                        # context only: the bf16 peak at the clock the chip sustains under this load
+                        pk = PEAK_BF16_TFLOPS * c["gfx_mhz_mean"] / 2400.0
+                        extra[name]["roofline"]["peak_at_load_clock"] = pk
+                        extra[name]["roofline"]["frac_at_load_clock"] = extra[name]["roofline"]["achieved"] / pk
                 q, k, _ = setup["dev"]
                 extra["rr_search128k"] = _bench_rr(q, k, 5, 1, args.layout)
             if name == "vit1792":
@@ -498,6 +546,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "extra": extra,
+        "gpu_clocks": dict(clocks, after=clock()),
     }
     print(json.dumps(out))
 
