@@ -93,7 +93,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
   const int slot0 = __builtin_amdgcn_readfirstlane(split.x);
   const int piece = __builtin_amdgcn_readfirstlane(split.y);
   const int npieces = __builtin_amdgcn_readfirstlane(split.z);
-  const int counter = __builtin_amdgcn_readfirstlane(split.w);
   const int b = blockIdx.y;
 
   const unsigned char* qbase =
@@ -752,58 +751,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
     }
   };
 
-  // ---- a piece of a split row: publish the partial state, the last piece merges ----
+  // ---- a piece of a split row leaves its partial state in its slot ----
   // Slot layout (per wave): acc as float4 [DT][4][64 lanes], then m and l per
-  // lane.  Every wave has written its part of this piece's slot (from its
-  // registers, or from the exact path) before the call.
+  // lane.  attn_merge_kernel, launched after this kernel on the same stream,
+  // merges the pieces of every split row (so no device-scope fence is needed
+  // here: the kernel boundary orders the writes before the merge's reads).
   float* slots = p.partials + static_cast<int64_t>(slot0) * kSlotFloats;
-  auto publish_and_merge = [&]() __attribute__((always_inline)) {
-    // Publication: every wave's stores are ordered before the barrier
-    // (work-group scope); thread 0 then releases them at device scope (one
-    // write-back of the XCD's L2) and counts the piece.  The piece that
-    // counts last acquires at device scope (one invalidation), so after the
-    // second barrier its waves read every piece's state.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int* cnt = p.counters + counter;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      const int done = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = done == npieces - 1;
-      if (last) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next launch
-      }
-      list_lds[0] = last ? 1 : 0;
-    }
-    __syncthreads();
-    if (list_lds[0] == 0) return;
-    // Merge in piece order (fixed, whichever piece finishes last).
-    float mmax = -INFINITY;
-    for (int i = 0; i < npieces; ++i) mmax = fmaxf(mmax, slots[static_cast<int64_t>(i) * kSlotFloats + kSlotM + wave * 64 + lane]);
-#pragma unroll
-    for (int dt = 0; dt < S::DT; ++dt) acc[dt] = f32x16{};
-    float lm = 0.f;
-    for (int i = 0; i < npieces; ++i) {
-      const float* sp = slots + static_cast<int64_t>(i) * kSlotFloats;
-      const float mi = sp[kSlotM + wave * 64 + lane];
-      const float w = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - mmax);
-      lm = __builtin_fmaf(w, sp[kSlotL + wave * 64 + lane], lm);
-#pragma unroll
-      for (int dt = 0; dt < S::DT; ++dt) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 a = *reinterpret_cast<const float4*>(sp + (((wave * S::DT + dt) * 4 + g) * 64 + lane) * 4);
-          acc[dt][4 * g + 0] = __builtin_fmaf(w, a.x, acc[dt][4 * g + 0]);
-          acc[dt][4 * g + 1] = __builtin_fmaf(w, a.y, acc[dt][4 * g + 1]);
-          acc[dt][4 * g + 2] = __builtin_fmaf(w, a.z, acc[dt][4 * g + 2]);
-          acc[dt][4 * g + 3] = __builtin_fmaf(w, a.w, acc[dt][4 * g + 3]);
-        }
-      }
-    }
-    store_o(lm > 0.f ? 1.f / lm : 0.f);
-    store_lse(mmax, lm);
-  };
 
   // After the pass (fast pass: the reference is fixed after the first tile,
   // so later tiles need no row max).  Probabilities relative to it stay far
@@ -858,7 +811,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
                                    : halves_sum(l_run);
   if (n > 0 && finish_or_redo(lrow)) {
     exact_rows();  // writes O, or this piece's partial state
-    if (npieces > 1) publish_and_merge();
     return;
   }
   const float ltot = lrow + sink_l;
@@ -880,7 +832,84 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
     sp[kSlotM + wave * 64 + lane] = ltot > 0.f ? ref_of() : -INFINITY;
     sp[kSlotL + wave * 64 + lane] = ltot;
   }
-  publish_and_merge();
+}
+
+// Merge of split rows (batch 1): one work-group per split row, its 4 waves
+// with the forward's register layout (wave w, lane (l31, h2) holds query row
+// 32 w + l31 of the 128-row tile, O^T elements d = 32 dt + 8 g + 4 h2 + e).
+// The pieces' states are merged in piece order (the result does not depend
+// on which piece finished first): m* = max of the pieces' references, then
+// acc = sum of 2^(m_i - m*) acc_i and l = sum of 2^(m_i - m*) l_i; the sink
+// term is already in piece 0's l.  Writes O = acc / l (0 for an empty row)
+// and, when requested, the row's log-sum-exp.
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_merge_kernel(const GroupParams g) {
+  using S = Shape<D>;
+  constexpr int64_t kSlotFloats = partial_slot_floats(D);
+  constexpr int kSlotM = 4 * S::DT * 16 * 64;
+  constexpr int kSlotL = kSlotM + 4 * 64;
+  int idx = static_cast<int>(blockIdx.x), jb = 0;
+  while (jb + 1 < g.n_jobs && idx >= g.job[jb].n_merge) idx -= g.job[jb++].n_merge;
+  const int job = __builtin_amdgcn_readfirstlane(jb);
+  idx = __builtin_amdgcn_readfirstlane(idx);
+  const FwdParams& p = g.job[job];
+  if (idx >= p.n_merge) return;
+  const int4 row = reinterpret_cast<const int4*>(p.merge_rows)[idx];
+  const int head = __builtin_amdgcn_readfirstlane(row.x);
+  const int qtile = __builtin_amdgcn_readfirstlane(row.y);
+  const int slot0 = __builtin_amdgcn_readfirstlane(row.z);
+  const int npieces = __builtin_amdgcn_readfirstlane(row.w);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h2 = lane >> 5, l31 = lane & 31;
+  const float* slots = p.partials + static_cast<int64_t>(slot0) * kSlotFloats;
+
+  float mmax = -INFINITY;
+  for (int i = 0; i < npieces; ++i)
+    mmax = fmaxf(mmax, slots[static_cast<int64_t>(i) * kSlotFloats + kSlotM + wave * 64 + lane]);
+  f32x16 acc[S::DT];
+#pragma unroll
+  for (int dt = 0; dt < S::DT; ++dt) acc[dt] = f32x16{};
+  float lm = 0.f;
+  for (int i = 0; i < npieces; ++i) {
+    const float* sp = slots + static_cast<int64_t>(i) * kSlotFloats;
+    const float mi = sp[kSlotM + wave * 64 + lane];
+    const float w = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - mmax);
+    lm = __builtin_fmaf(w, sp[kSlotL + wave * 64 + lane], lm);
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) {
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const float4 a = *reinterpret_cast<const float4*>(sp + (((wave * S::DT + dt) * 4 + gg) * 64 + lane) * 4);
+        acc[dt][4 * gg + 0] = __builtin_fmaf(w, a.x, acc[dt][4 * gg + 0]);
+        acc[dt][4 * gg + 1] = __builtin_fmaf(w, a.y, acc[dt][4 * gg + 1]);
+        acc[dt][4 * gg + 2] = __builtin_fmaf(w, a.z, acc[dt][4 * gg + 2]);
+        acc[dt][4 * gg + 3] = __builtin_fmaf(w, a.w, acc[dt][4 * gg + 3]);
+      }
+    }
+  }
+  const int b = blockIdx.y;
+  const int qi = qtile * kBM + wave * 32 + l31;
+  if (qi >= p.L) return;
+  const float inv = lm > 0.f ? 1.f / lm : 0.f;
+  unsigned char* dst = reinterpret_cast<unsigned char*>(p.o + b * p.o_sb + head * p.o_sh) + qi * p.o_sl * 2;
+#pragma unroll
+  for (int dt = 0; dt < S::DT; ++dt) {
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const int d = 32 * dt + 8 * gg + 4 * h2;
+      if (S::PAD_ROWSUM && 32 * dt + 8 * gg >= D) continue;
+      bf16x4 out;
+      out[0] = (__bf16)(acc[dt][4 * gg + 0] * inv);
+      out[1] = (__bf16)(acc[dt][4 * gg + 1] * inv);
+      out[2] = (__bf16)(acc[dt][4 * gg + 2] * inv);
+      out[3] = (__bf16)(acc[dt][4 * gg + 3] * inv);
+      *reinterpret_cast<bf16x4*>(dst + d * 2) = out;
+    }
+  }
+  if (p.lse != nullptr && h2 == 0)
+    p.lse[(static_cast<int64_t>(b) * p.H + head) * p.L + qi] =
+        lm > 0.f ? (mmax + __builtin_amdgcn_logf(lm)) * kLn2 : -INFINITY;
 }
 
 template <int D>
@@ -889,9 +918,16 @@ hipError_t launch_d(const GroupParams& g, int blocks, int B, hipStream_t stream,
   dim3 grid(static_cast<unsigned>(blocks), static_cast<unsigned>(B));
   bool prefix = false;
   for (int j = 0; j < g.n_jobs; ++j) prefix = prefix || g.job[j].prefix > 0;
+  int64_t merges = 0;
+  for (int j = 0; j < g.n_jobs; ++j) merges += g.job[j].n_merge;
   // the extended launch attaches the events to the kernel's own dispatch
-  if (prefix) hipExtLaunchKernelGGL((attn_fwd_kernel<D, true>), grid, dim3(kThreads), 0, stream, start, stop, 0, g);
-  else hipExtLaunchKernelGGL((attn_fwd_kernel<D, false>), grid, dim3(kThreads), 0, stream, start, stop, 0, g);
+  hipEvent_t stop1 = merges > 0 ? nullptr : stop;
+  if (prefix) hipExtLaunchKernelGGL((attn_fwd_kernel<D, true>), grid, dim3(kThreads), 0, stream, start, stop1, 0, g);
+  else hipExtLaunchKernelGGL((attn_fwd_kernel<D, false>), grid, dim3(kThreads), 0, stream, start, stop1, 0, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || merges == 0) return e;
+  hipExtLaunchKernelGGL(attn_merge_kernel<D>, dim3(static_cast<unsigned>(merges), static_cast<unsigned>(B)),
+                        dim3(kThreads), 0, stream, nullptr, stop, 0, g);
   return hipGetLastError();
 }
 

@@ -114,7 +114,8 @@ attn_status make_job(const attn_plan& p, const attn_tensor* q, const attn_tensor
   f.head_left = reinterpret_cast<const int32_t*>(ws + p.layout.off_head_left);
   f.block_bits = reinterpret_cast<const uint32_t*>(ws + p.layout.off_bits);
   f.partials = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) + p.layout.off_partials);
-  f.counters = reinterpret_cast<int32_t*>(const_cast<uint8_t*>(ws) + p.layout.off_counters);
+  f.merge_rows = reinterpret_cast<const int32_t*>(ws + p.layout.off_merge);
+  f.n_merge = split ? static_cast<int32_t>(p.merge_rows.size()) : 0;
   f.sink = sink;
   const float scale = softmax_scale > 0.f ? softmax_scale : static_cast<float>(1.0 / std::sqrt(double(p.D)));
   f.scale_log2 = static_cast<float>(scale * 1.4426950408889634);

@@ -29,7 +29,8 @@ struct FwdParams {
   const uint32_t* block_bits; // unaligned BLOCK masks (unused when aligned)
   const float* sink;          // [H] or nullptr
   float* partials;            // partial-state slots of split items
-  int32_t* counters;          // per split row: pieces finished in this launch (returns to 0)
+  const int32_t* merge_rows;  // n_merge x {head, qtile, first slot, pieces}: the split rows
+  int32_t n_merge;            // split rows of this launch (0 unless batch 1 with split rows)
   float scale_log2;           // softmax scale * log2(e)
   int32_t L, H, n_items;
   int32_t kind, causal;
@@ -51,7 +52,9 @@ struct GroupParams {
 static_assert(sizeof(GroupParams) <= 4096, "kernel arguments are limited to 4 KiB");
 
 // Launch the forward kernel for head dim D on `stream` with grid
-// (8 * sum of queue lengths, B); non-null events record the kernel's start and end.
+// (8 * sum of queue lengths, B), then, when some job has split rows, the merge
+// kernel (one work-group per split row); non-null events record the start of
+// the first and the end of the last.
 hipError_t launch_fwd(const GroupParams& g, int D, int B, hipStream_t stream, hipEvent_t start,
                       hipEvent_t stop);
 

@@ -361,11 +361,11 @@ void schedule(attn_plan& p) {
                          static_cast<int32_t>(groups)});
       icost.push_back(c);
     }
+    p.merge_rows.push_back(MergeRow{whole[r].head, whole[r].qtile, static_cast<int32_t>(slots), np});
     slots += np;
     groups += 1;
   }
   p.n_partial_slots = slots;
-  p.n_counters = groups;
   p.items = layout_queues(heads, all, icost);
 }
 
@@ -391,8 +391,8 @@ void build_image(attn_plan& p) {
   l.off_kv = align_up(l.off_items_unsplit + p.items_unsplit.size() * sizeof(Item));
   l.off_head_left = align_up(l.off_kv + std::max<size_t>(1, p.kv_entries.size()) * sizeof(int32_t));
   l.off_bits = align_up(l.off_head_left + p.head_left32.size() * sizeof(int32_t));
-  l.off_counters = align_up(l.off_bits + p.block_bits.size() * sizeof(uint32_t));
-  l.bytes = align_up(l.off_counters + p.n_counters * sizeof(int32_t));
+  l.off_merge = align_up(l.off_bits + p.block_bits.size() * sizeof(uint32_t));
+  l.bytes = align_up(l.off_merge + p.merge_rows.size() * sizeof(MergeRow));
   l.off_partials = l.bytes;
   l.total = align_up(l.off_partials + static_cast<size_t>(p.n_partial_slots) *
                                           static_cast<size_t>(partial_slot_floats(p.D)) * sizeof(float));
@@ -568,6 +568,8 @@ void write_image(const attn_plan& p, uint8_t* dst) {
   std::memcpy(dst + p.layout.off_head_left, p.head_left32.data(), p.head_left32.size() * sizeof(int32_t));
   if (!p.block_bits.empty())
     std::memcpy(dst + p.layout.off_bits, p.block_bits.data(), p.block_bits.size() * sizeof(uint32_t));
+  if (!p.merge_rows.empty())
+    std::memcpy(dst + p.layout.off_merge, p.merge_rows.data(), p.merge_rows.size() * sizeof(MergeRow));
 }
 
 }  // namespace bss

@@ -29,19 +29,26 @@ constexpr int kSlots = 512;  // resident work-groups: 256 CUs x 2
 // Device record of one work item (32 bytes).  A (head, query tile) row whose
 // list is long compared with the whole launch is cut into `npieces`
 // contiguous pieces of its list; each piece leaves its partial softmax state
-// in partial slot `slot + piece`, and the last piece to finish (counted on
-// counters[counter]) merges them.  Unsplit items have npieces = 1.  Items
-// with head = -1 pad the per-XCD queues to equal length and do nothing.
+// in partial slot `slot + piece`, and a second kernel merges the pieces of
+// split row `split` (entry `split` of the image's merge list) in piece order.
+// Unsplit items have npieces = 1.  Items with head = -1 pad the per-XCD
+// queues to equal length and do nothing.
 struct Item {
   int32_t head, qtile, begin, end;
-  int32_t slot, piece, npieces, counter;
+  int32_t slot, piece, npieces, split;
+};
+
+// Merge-list record of one split row (16 bytes): its head, query tile, first
+// partial slot and piece count.
+struct MergeRow {
+  int32_t head, qtile, slot, npieces;
 };
 
 // Layout of the plan's device image inside the caller's workspace, followed
 // by the partial-state slots of split items (not part of the image).
 struct ImageLayout {
   size_t off_items = 0, off_items_unsplit = 0, off_kv = 0, off_head_left = 0, off_bits = 0,
-         off_counters = 0, bytes = 0;
+         off_merge = 0, bytes = 0;
   size_t off_partials = 0, total = 0;
 };
 
@@ -100,7 +107,8 @@ struct attn_plan {
   // `items_unsplit` (batch > 1: every row one item), each laid out as
   // kXcds equal-length queues
   std::vector<bss::Item> items, items_unsplit;
-  int64_t n_partial_slots = 0, n_counters = 0;
+  int64_t n_partial_slots = 0;
+  std::vector<bss::MergeRow> merge_rows;  // split rows of `items`, merged after the launch
   std::vector<int32_t> kv_entries;    // (kv_tile << 1) | full, in canonical order
   std::vector<int32_t> head_left32;   // [H]
   std::vector<uint32_t> block_bits;   // [Hb][Nb][ceil(Nb/32)] when not block_aligned

@@ -154,13 +154,14 @@ attn_status attn_plan_pairs(const attn_plan* plan, int64_t* pairs_per_head, int6
 /*
  * Work schedule of a batch-1 launch: n_items records of 8 int32 {head, query
  * tile, first list entry, one past the last list entry, partial slot, piece,
- * pieces, counter}, laid out as 8 equal-length queues (queue x = records
+ * pieces, split row}, laid out as 8 equal-length queues (queue x = records
  * [x n_items/8, (x+1) n_items/8), run by the work-groups of XCD x in order).
  * Every (head, query tile) row is covered once: by one record (pieces = 1;
  * empty rows too: they write zeros) or, when its list is long compared with
  * the launch, by `pieces` records that cut the list into consecutive ranges;
  * each piece leaves its partial softmax state in partial slot (slot + piece)
- * of the workspace and the last piece to finish merges them in piece order.
+ * of the workspace, and a second kernel of the same launch merges the pieces
+ * of each split row in piece order.
  * Records with head = -1 pad the queues.  Launches with batch > 1 run an
  * unsplit schedule of the same layout.  Host view owned by the plan.
  */
@@ -168,11 +169,10 @@ attn_status attn_plan_schedule(const attn_plan* plan, int64_t* n_items, const in
 
 /*
  * Device bytes a launch needs in the workspace: the plan's image (tile lists,
- * schedules, per-row piece counters) followed, for batch-1 launches, by the
+ * schedules, the list of split rows) followed, for batch-1 launches, by the
  * partial states of split rows.  Launches that share a workspace must not
- * overlap in time (the counters and partial states are per launch; launches
- * on one stream are ordered); every completed launch leaves the counters at
- * zero, as the upload does.
+ * overlap in time (the partial states are per launch; launches on one stream
+ * are ordered).
  */
 attn_status attn_plan_workspace_bytes(const attn_plan* plan, size_t* bytes);
 

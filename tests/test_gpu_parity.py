@@ -252,7 +252,7 @@ def test_split_rows_merge(D, ci):
     got = _run_gpu(q, k, v, mask, sink)
     ref = attention(q, k, v, mask, sink=sink)["out"]
     _compare(got, ref, f"split-{ci}-d{D}")
-    got2 = _run_gpu(q, k, v, mask, sink)   # counters returned to zero: the same result again
+    got2 = _run_gpu(q, k, v, mask, sink)   # a second launch on the same workspace: the same result
     assert np.array_equal(got, got2)
 
 
@@ -297,7 +297,7 @@ def test_grouped_launch_matches_single_launches():
         single.append(o)
     outs = [torch.empty_like(q) for _ in masks]
     run = bind_group(pms, [q] * 4, [k] * 4, [v] * 4, outs, sinks=sinks, layout="bhld")
-    for _ in range(2):  # twice: the split rows' counters are back at zero after a launch
+    for _ in range(2):  # twice on the same workspaces: the same result
         for o in outs:
             o.zero_()
         run()

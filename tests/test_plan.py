@@ -150,7 +150,8 @@ def _schedule_cost(flags, b, e):
 def test_schedule_covers_every_row_once(lib):
     """The batch-1 schedule: 8 equal-length XCD queues (padding items have head -1); every (head, query
     tile) row's list is covered exactly once, by one item or by pieces that cut it into contiguous ranges
-    in piece order; split rows own distinct partial slots and counters; the queues carry equal cost."""
+    in piece order; split rows own distinct partial slots and split-row indices (their merge-list entry);
+    the queues carry equal cost."""
     split_seen = {}
     for name in ("vit896", "vit1792", "lm_headwin"):
         w = workload(name)
@@ -164,7 +165,7 @@ def test_schedule_covers_every_row_once(lib):
             assert np.all(items[items[:, 0] < 0][:, 3] == items[items[:, 0] < 0][:, 2])
             rows = real[:, 0] * nq + real[:, 1]
             assert np.array_equal(np.unique(rows), np.arange(w["H"] * nq))
-            slots, counters = [], []
+            slots, split_rows = [], []
             for r in np.unique(rows):
                 its = real[rows == r]
                 its = its[np.argsort(its[:, 5])]
@@ -175,11 +176,11 @@ def test_schedule_covers_every_row_once(lib):
                 if npc > 1:
                     assert np.all(its[:, 4] == its[0, 4]) and np.all(its[:, 7] == its[0, 7])
                     slots.extend(its[0, 4] + np.arange(npc))
-                    counters.append(its[0, 7])
-            assert len(set(slots)) == len(slots) and len(set(counters)) == len(counters)
+                    split_rows.append(its[0, 7])
+            assert len(set(slots)) == len(slots) and len(set(split_rows)) == len(split_rows)
             if slots:
-                assert sorted(slots) == list(range(len(slots))) and sorted(counters) == list(range(len(counters)))
-            split_seen[(name, label)] = len(counters)
+                assert sorted(slots) == list(range(len(slots))) and sorted(split_rows) == list(range(len(split_rows)))
+            split_seen[(name, label)] = len(split_rows)
             # per-XCD queues of equal total cost (within one item's cost)
             q = items.reshape(8, -1, 8)
             cost = np.array([[0.0 if it[0] < 0 else 0.5 + _schedule_cost(fl, it[2], it[3]) + (2.0 if it[6] > 1 else 0.0)
