@@ -265,11 +265,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const BwdParams p) 
   if (pos >= p.q_queue) return;
   const int item_idx = static_cast<int>(blockIdx.x % 8) * p.q_queue + pos;
   const int4 item = reinterpret_cast<const int4*>(p.q_items)[2 * item_idx];
+  const int4 split = reinterpret_cast<const int4*>(p.q_items)[2 * item_idx + 1];
   const int head = __builtin_amdgcn_readfirstlane(item.x);
   if (head < 0) return;
   const int qtile = __builtin_amdgcn_readfirstlane(item.y);
   const int e_begin = __builtin_amdgcn_readfirstlane(item.z);
   const int e_end = __builtin_amdgcn_readfirstlane(item.w);
+  // a piece of a split row (batch 1) sums dQ over its part of the row's list
+  const int slot = __builtin_amdgcn_readfirstlane(split.x + split.y);
+  const int npieces = __builtin_amdgcn_readfirstlane(split.z);
   const int b = blockIdx.y;
   const int kv_head = head / p.kv_group;
   const uint16_t* kb = p.k + b * p.k_sb + kv_head * p.k_sh;
@@ -399,9 +403,59 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(const BwdParams p) 
     ent_cur = ent_nxt;
     ent_nxt = __builtin_amdgcn_readfirstlane(raw2);
   }
+  if (npieces > 1) {  // this piece's dQ^T sum, in the forward's partial-slot layout (acc part)
+    float* sp = p.partials + static_cast<int64_t>(slot) * partial_slot_floats(D);
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 a = make_float4(acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]);
+        *reinterpret_cast<float4*>(sp + (((wave * S::DT + dt) * 4 + g) * 64 + lane) * 4) = a;
+      }
+    }
+    return;
+  }
   if (qi < p.L) {
     unsigned char* dst = reinterpret_cast<unsigned char*>(p.dq + b * p.dq_sb + head * p.dq_sh) +
                          static_cast<int64_t>(qi) * p.dq_sl * 2;
+    store_rows<D>(dst, acc, p.scale, h2);
+  }
+}
+
+// dQ of the split rows (batch 1): one work-group per split row adds its
+// pieces' sums in piece order (a fixed order: the result does not depend on
+// which piece finished first) and writes dQ = scale * sum.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dq_merge_kernel(const BwdParams p) {
+  using S = Shape<D>;
+  const int4 row = reinterpret_cast<const int4*>(p.merge_rows)[blockIdx.x];
+  const int head = __builtin_amdgcn_readfirstlane(row.x);
+  const int qtile = __builtin_amdgcn_readfirstlane(row.y);
+  const int slot0 = __builtin_amdgcn_readfirstlane(row.z);
+  const int npieces = __builtin_amdgcn_readfirstlane(row.w);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h2 = lane >> 5, l31 = lane & 31;
+  f32x16 acc[S::DT];
+#pragma unroll
+  for (int dt = 0; dt < S::DT; ++dt) acc[dt] = f32x16{};
+  for (int i = 0; i < npieces; ++i) {
+    const float* sp = p.partials + static_cast<int64_t>(slot0 + i) * partial_slot_floats(D);
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 a = *reinterpret_cast<const float4*>(sp + (((wave * S::DT + dt) * 4 + g) * 64 + lane) * 4);
+        acc[dt][4 * g + 0] += a.x;
+        acc[dt][4 * g + 1] += a.y;
+        acc[dt][4 * g + 2] += a.z;
+        acc[dt][4 * g + 3] += a.w;
+      }
+    }
+  }
+  const int qi = qtile * kBM + wave * 32 + l31;
+  if (qi < p.L) {
+    unsigned char* dst = reinterpret_cast<unsigned char*>(p.dq + head * p.dq_sh) + static_cast<int64_t>(qi) * p.dq_sl * 2;
     store_rows<D>(dst, acc, p.scale, h2);
   }
 }
@@ -617,6 +671,10 @@ hipError_t launch_bwd_d(const BwdParams& p, int B, hipStream_t stream, hipEvent_
   if (prefix) hipLaunchKernelGGL((bwd_dq_kernel<D, true>), gq, dim3(kThreads), 0, stream, p);
   else hipLaunchKernelGGL((bwd_dq_kernel<D, false>), gq, dim3(kThreads), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.n_merge > 0) {  // batch 1 only: the split rows' dQ
+    hipLaunchKernelGGL((bwd_dq_merge_kernel<D>), dim3(static_cast<unsigned>(p.n_merge)), dim3(kThreads), 0, stream, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const dim3 gk(static_cast<unsigned>(8 * p.kv_queue), static_cast<unsigned>(B));
   hipEvent_t last_stop = sink ? nullptr : stop;
   if (prefix) hipExtLaunchKernelGGL((bwd_dkdv_kernel<D, true>), gk, dim3(kThreads), 0, stream, nullptr, last_stop, 0, p);

@@ -418,7 +418,10 @@ static attn_status make_bwd(const attn_plan& p, const attn_tensor* q, const attn
       return ATTN_E_INVAL;
     }
   }
-  const size_t nq_items = p.items_unsplit.size(), nkv_items = img.items.size();
+  // batch 1 runs the forward's split schedule for dQ (pieces of long rows add their dQ sums into the
+  // forward's partial slots, merged after the dQ kernel); batch > 1 the unsplit one
+  const bool split = (B == 1) && !p.merge_rows.empty();
+  const size_t nq_items = split ? p.items.size() : p.items_unsplit.size(), nkv_items = img.items.size();
   if (nq_items % 8 || nkv_items % 8 || nq_items / 8 > static_cast<size_t>(INT32_MAX / 8) ||
       nkv_items / 8 > static_cast<size_t>(INT32_MAX / 8) || p.nq * kBM > INT32_MAX) {
     set_error("too many work items");
@@ -448,7 +451,10 @@ static attn_status make_bwd(const attn_plan& p, const attn_tensor* q, const attn
   f.stat = reinterpret_cast<float*>(ws + lay.off_stat);
   f.sinkpart = reinterpret_cast<float*>(ws + lay.off_sinkpart);
   f.qs = reinterpret_cast<uint16_t*>(ws + lay.off_qs);
-  f.q_items = reinterpret_cast<const int32_t*>(ws + p.layout.off_items_unsplit);
+  f.q_items = reinterpret_cast<const int32_t*>(ws + (split ? p.layout.off_items : p.layout.off_items_unsplit));
+  f.partials = reinterpret_cast<float*>(ws + p.layout.off_partials);
+  f.merge_rows = reinterpret_cast<const int32_t*>(ws + p.layout.off_merge);
+  f.n_merge = split ? static_cast<int32_t>(p.merge_rows.size()) : 0;
   f.kv = reinterpret_cast<const int32_t*>(ws + p.layout.off_kv);
   f.kv_items = reinterpret_cast<const int32_t*>(ws + lay.off_image + img.off_items);
   f.col = reinterpret_cast<const int32_t*>(ws + lay.off_image + img.off_col);

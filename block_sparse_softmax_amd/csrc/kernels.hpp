@@ -82,7 +82,10 @@ struct BwdParams {
   float* stat;                // workspace [B][H][2][Lpad]: lse in log2 units (+inf: no mass), then D
   float* sinkpart;            // workspace [B][H][nq]: per query tile sums of exp(s_aux - lse_i) D_i
   uint16_t* qs;               // workspace [B][H][L][D] bf16: Q * sigma * log2(e) rounded as the forward rounds it
-  const int32_t* q_items;     // dQ work items: the forward's unsplit schedule (8 queues)
+  const int32_t* q_items;     // dQ work items: the forward's schedule (8 queues; batch 1: long rows split)
+  float* partials;            // batch 1: the forward's partial slots, reused for the pieces' dQ sums
+  const int32_t* merge_rows;  // n_merge x {head, qtile, first slot, pieces}: the split rows
+  int32_t n_merge;
   const int32_t* kv;          // the forward's lists: (kv_tile << 1) | full
   const int32_t* kv_items;    // dK/dV work items {kv head, key block, begin, end, ...} (8 queues)
   const int32_t* col;         // per (kv head, key block): (group head << 24) | (query tile << 1) | full
