@@ -487,11 +487,15 @@ __global__ __launch_bounds__(kThreads, DkdvShape<D>::OCC) void bwd_dkdv_kernel(c
   if (pos >= p.kv_queue) return;
   const int item_idx = static_cast<int>(blockIdx.x % 8) * p.kv_queue + pos;
   const int4 item = reinterpret_cast<const int4*>(p.kv_items)[2 * item_idx];
+  const int4 split = reinterpret_cast<const int4*>(p.kv_items)[2 * item_idx + 1];
   const int hk = __builtin_amdgcn_readfirstlane(item.x);
   if (hk < 0) return;
   const int kblk = __builtin_amdgcn_readfirstlane(item.y);
   const int c_begin = __builtin_amdgcn_readfirstlane(item.z);
   const int c_end = __builtin_amdgcn_readfirstlane(item.w);
+  // a piece of a split key block (batch 1) sums dK and dV over its part of the block's list
+  const int slot = __builtin_amdgcn_readfirstlane(split.x + split.y);
+  const int npieces = __builtin_amdgcn_readfirstlane(split.z);
   const int b = blockIdx.y;
 
   // this lane's key (N index of every product) and its K, V fragments
@@ -650,6 +654,21 @@ __global__ __launch_bounds__(kThreads, DkdvShape<D>::OCC) void bwd_dkdv_kernel(c
       ent_nxt = (c_begin + next < c_end) ? p.col[c_begin + next] : 0;
     }
   }
+  if (npieces > 1) {  // this piece's dK^T and dV^T sums (dK then dV, float4 [wave][dt][4][lane])
+    float* sp = p.dkdv_partials + static_cast<int64_t>(slot) * dkdv_slot_floats(D);
+    constexpr int kHalf = 4 * S::DT * 16 * 64;
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int off = (((wave * S::DT + dt) * 4 + g) * 64 + lane) * 4;
+        *reinterpret_cast<float4*>(sp + off) = make_float4(dk[dt][4 * g], dk[dt][4 * g + 1], dk[dt][4 * g + 2], dk[dt][4 * g + 3]);
+        *reinterpret_cast<float4*>(sp + kHalf + off) =
+            make_float4(dv[dt][4 * g], dv[dt][4 * g + 1], dv[dt][4 * g + 2], dv[dt][4 * g + 3]);
+      }
+    }
+    return;
+  }
   if (kj < p.L) {
     unsigned char* dkr = reinterpret_cast<unsigned char*>(p.dk + b * p.dk_sb + hk * p.dk_sh) +
                          static_cast<int64_t>(kj) * p.dk_sl * 2;
@@ -657,6 +676,49 @@ __global__ __launch_bounds__(kThreads, DkdvShape<D>::OCC) void bwd_dkdv_kernel(c
                          static_cast<int64_t>(kj) * p.dv_sl * 2;
     store_rows<D>(dkr, dk, 1.f / kLog2e, h2);
     store_rows<D>(dvr, dv, 1.f, h2);
+  }
+}
+
+// dK and dV of the split key blocks (batch 1): one work-group per split block
+// adds its pieces' sums in piece order and writes dK = sum / log2(e) (the
+// scores were recomputed from Q scaled by sigma log2(e)) and dV = sum.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_merge_kernel(const BwdParams p) {
+  using S = Shape<D>;
+  constexpr int kHalf = 4 * S::DT * 16 * 64;
+  const int4 row = reinterpret_cast<const int4*>(p.kv_merge)[blockIdx.x];
+  const int hk = __builtin_amdgcn_readfirstlane(row.x);
+  const int kblk = __builtin_amdgcn_readfirstlane(row.y);
+  const int slot0 = __builtin_amdgcn_readfirstlane(row.z);
+  const int npieces = __builtin_amdgcn_readfirstlane(row.w);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h2 = lane >> 5, l31 = lane & 31;
+  for (int part = 0; part < 2; ++part) {  // dK, then dV
+    f32x16 acc[S::DT];
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt) acc[dt] = f32x16{};
+    for (int i = 0; i < npieces; ++i) {
+      const float* sp = p.dkdv_partials + static_cast<int64_t>(slot0 + i) * dkdv_slot_floats(D) + part * kHalf;
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 a = *reinterpret_cast<const float4*>(sp + (((wave * S::DT + dt) * 4 + g) * 64 + lane) * 4);
+          acc[dt][4 * g + 0] += a.x;
+          acc[dt][4 * g + 1] += a.y;
+          acc[dt][4 * g + 2] += a.z;
+          acc[dt][4 * g + 3] += a.w;
+        }
+      }
+    }
+    const int kj = kblk * 2 * kBN + wave * 32 + l31;
+    if (kj < p.L) {
+      uint16_t* base = part == 0 ? p.dk + hk * p.dk_sh : p.dv + hk * p.dv_sh;
+      const int64_t sl = part == 0 ? p.dk_sl : p.dv_sl;
+      unsigned char* dst = reinterpret_cast<unsigned char*>(base) + static_cast<int64_t>(kj) * sl * 2;
+      store_rows<D>(dst, acc, part == 0 ? 1.f / kLog2e : 1.f, h2);
+    }
   }
 }
 
@@ -676,10 +738,16 @@ hipError_t launch_bwd_d(const BwdParams& p, int B, hipStream_t stream, hipEvent_
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const dim3 gk(static_cast<unsigned>(8 * p.kv_queue), static_cast<unsigned>(B));
-  hipEvent_t last_stop = sink ? nullptr : stop;
+  const bool kv_merge = p.n_kv_merge > 0;
+  hipEvent_t last_stop = (sink || kv_merge) ? nullptr : stop;
   if (prefix) hipExtLaunchKernelGGL((bwd_dkdv_kernel<D, true>), gk, dim3(kThreads), 0, stream, nullptr, last_stop, 0, p);
   else hipExtLaunchKernelGGL((bwd_dkdv_kernel<D, false>), gk, dim3(kThreads), 0, stream, nullptr, last_stop, 0, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (kv_merge) {  // batch 1 only: the split key blocks' dK and dV
+    hipExtLaunchKernelGGL((bwd_dkdv_merge_kernel<D>), dim3(static_cast<unsigned>(p.n_kv_merge)), dim3(kThreads), 0,
+                          stream, nullptr, sink ? nullptr : stop, 0, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (sink) {
     hipExtLaunchKernelGGL(bwd_sink_kernel, dim3(p.H), dim3(256), 0, stream, nullptr, stop, 0, p, B);
     e = hipGetLastError();

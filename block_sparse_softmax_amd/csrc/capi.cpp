@@ -421,7 +421,9 @@ static attn_status make_bwd(const attn_plan& p, const attn_tensor* q, const attn
   // batch 1 runs the forward's split schedule for dQ (pieces of long rows add their dQ sums into the
   // forward's partial slots, merged after the dQ kernel); batch > 1 the unsplit one
   const bool split = (B == 1) && !p.merge_rows.empty();
-  const size_t nq_items = split ? p.items.size() : p.items_unsplit.size(), nkv_items = img.items.size();
+  const bool kv_split = (B == 1) && !img.merge.empty();
+  const size_t nq_items = split ? p.items.size() : p.items_unsplit.size();
+  const size_t nkv_items = kv_split ? img.items_split.size() : img.items.size();
   if (nq_items % 8 || nkv_items % 8 || nq_items / 8 > static_cast<size_t>(INT32_MAX / 8) ||
       nkv_items / 8 > static_cast<size_t>(INT32_MAX / 8) || p.nq * kBM > INT32_MAX) {
     set_error("too many work items");
@@ -456,7 +458,10 @@ static attn_status make_bwd(const attn_plan& p, const attn_tensor* q, const attn
   f.merge_rows = reinterpret_cast<const int32_t*>(ws + p.layout.off_merge);
   f.n_merge = split ? static_cast<int32_t>(p.merge_rows.size()) : 0;
   f.kv = reinterpret_cast<const int32_t*>(ws + p.layout.off_kv);
-  f.kv_items = reinterpret_cast<const int32_t*>(ws + lay.off_image + img.off_items);
+  f.kv_items = reinterpret_cast<const int32_t*>(ws + lay.off_image + (kv_split ? img.off_items_split : img.off_items));
+  f.dkdv_partials = reinterpret_cast<float*>(ws + lay.off_dkdv);
+  f.kv_merge = reinterpret_cast<const int32_t*>(ws + lay.off_image + img.off_merge);
+  f.n_kv_merge = kv_split ? static_cast<int32_t>(img.merge.size()) : 0;
   f.col = reinterpret_cast<const int32_t*>(ws + lay.off_image + img.off_col);
   f.head_left = reinterpret_cast<const int32_t*>(ws + p.layout.off_head_left);
   const float scale = launch->softmax_scale > 0.f ? launch->softmax_scale
@@ -557,9 +562,13 @@ attn_status attn_bwd_upload(const attn_plan* p, int64_t kv_heads, void* workspac
     attn_status st = check_kv_heads(*p, kv_heads);
     if (st != ATTN_OK) return st;
     const BwdImage& img = bwd_image(*p, kv_heads);
+    // the upload writes the forward and backward images (the statistics and
+    // partial sums behind them depend on the batch and are checked per launch)
     const BwdLayout lay = bwd_layout(*p, img, 1);
-    if (!workspace || workspace_bytes < lay.total) {
-      set_error("workspace smaller than attn_bwd_workspace_bytes (" + std::to_string(lay.total) + " bytes)");
+    const size_t images = lay.off_image + img.bytes;
+    if (!workspace || workspace_bytes < images) {
+      set_error("workspace smaller than the plan's forward and backward images (" + std::to_string(images) +
+                " bytes)");
       return ATTN_E_WORKSPACE;
     }
     if (!aligned16(workspace)) { set_error("workspace must be 16-byte aligned"); return ATTN_E_INVAL; }

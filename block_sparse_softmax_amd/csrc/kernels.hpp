@@ -14,6 +14,10 @@ namespace bss {
 // reference m and the denominator l of every lane.
 constexpr int64_t partial_slot_floats(int64_t D) { return 4 * (((D + 31) / 32) * 16 * 64 + 2 * 64); }
 
+// Floats of one dK/dV partial slot of a split key block (backward): dK then
+// dV, each as float4 [4 waves][D/32 tiles][4][64 lanes].
+constexpr int64_t dkdv_slot_floats(int64_t D) { return 2 * 4 * ((D + 31) / 32) * 16 * 64; }
+
 struct FwdParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -87,7 +91,11 @@ struct BwdParams {
   const int32_t* merge_rows;  // n_merge x {head, qtile, first slot, pieces}: the split rows
   int32_t n_merge;
   const int32_t* kv;          // the forward's lists: (kv_tile << 1) | full
-  const int32_t* kv_items;    // dK/dV work items {kv head, key block, begin, end, ...} (8 queues)
+  const int32_t* kv_items;    // dK/dV work items {kv head, key block, begin, end, slot, piece, pieces, split}
+                              // (8 queues; batch 1: long key blocks split)
+  float* dkdv_partials;       // batch 1: dK/dV partial slots of split key blocks
+  const int32_t* kv_merge;    // n_kv_merge x {kv head, key block, first slot, pieces}
+  int32_t n_kv_merge;
   const int32_t* col;         // per (kv head, key block): (group head << 24) | (query tile << 1) | full
   const int32_t* head_left;   // [H] window left reach (WINDOW)
   float scale;                // softmax scale sigma

@@ -535,8 +535,47 @@ const BwdImage& bwd_image(const attn_plan& p, int64_t kv_heads) {
   std::iota(heads.begin(), heads.end(), 0);
   std::stable_sort(heads.begin(), heads.end(), [&](int64_t a, int64_t b) { return head_cost[a] > head_cost[b]; });
   img->items = layout_queues(heads, all, cost);
+  // batch-1 schedule: items much longer than the fair share of the resident
+  // work-groups (one per CU at d = 128, two otherwise) cut into pieces of
+  // consecutive entries; each piece then pays for its partial sums
+  {
+    double total = 0.0;
+    for (double c : cost) total += c;
+    const double slots = (p.D >= 128 ? 1.0 : 2.0) * kSlots / 2;
+    const double share = std::max(total / slots, kMinPiece);
+    std::vector<Item> parts;
+    std::vector<double> pcost;
+    int64_t nslot = 0;
+    for (size_t i = 0; i < all.size(); ++i) {
+      const Item& it = all[i];
+      const int32_t n = it.end - it.begin;
+      int np = 1;
+      if (cost[i] > 1.25 * share)
+        np = static_cast<int>(std::min<double>({std::ceil(cost[i] / share), double(kMaxPieces), double(n)}));
+      if (np <= 1) {
+        parts.push_back(it);
+        pcost.push_back(cost[i]);
+        continue;
+      }
+      for (int k = 0; k < np; ++k) {
+        const int32_t pb = it.begin + static_cast<int32_t>(int64_t(n) * k / np);
+        const int32_t pe = it.begin + static_cast<int32_t>(int64_t(n) * (k + 1) / np);
+        double c = 1.0 + kPieceOverhead;
+        for (int32_t x = pb; x < pe; ++x) c += (img->col[x] & 1) ? 2.0 : 2.25;
+        parts.push_back(Item{it.head, it.qtile, pb, pe, static_cast<int32_t>(nslot), k, np,
+                             static_cast<int32_t>(img->merge.size())});
+        pcost.push_back(c);
+      }
+      img->merge.push_back(MergeRow{it.head, it.qtile, static_cast<int32_t>(nslot), np});
+      nslot += np;
+    }
+    img->n_slots = nslot;
+    img->items_split = img->merge.empty() ? img->items : layout_queues(heads, parts, pcost);
+  }
   img->off_items = 0;
-  img->off_col = align_up(img->items.size() * sizeof(Item));
+  img->off_items_split = align_up(img->items.size() * sizeof(Item));
+  img->off_merge = align_up(img->off_items_split + img->items_split.size() * sizeof(Item));
+  img->off_col = align_up(img->off_merge + img->merge.size() * sizeof(MergeRow));
   img->bytes = align_up(img->off_col + std::max<size_t>(1, img->col.size()) * sizeof(int32_t));
   const BwdImage& ref = *img;
   p.bwd_images.emplace(kv_heads, std::move(img));
@@ -550,13 +589,17 @@ BwdLayout bwd_layout(const attn_plan& p, const BwdImage& img, int64_t B) {
   const size_t lpad = static_cast<size_t>(p.nq) * kBM;
   l.off_sinkpart = align_up(l.off_stat + static_cast<size_t>(B) * p.H * 2 * lpad * sizeof(float));
   l.off_qs = align_up(l.off_sinkpart + static_cast<size_t>(B) * p.H * p.nq * sizeof(float));
-  l.total = align_up(l.off_qs + static_cast<size_t>(B) * p.H * p.L * p.D * sizeof(uint16_t));
+  l.off_dkdv = align_up(l.off_qs + static_cast<size_t>(B) * p.H * p.L * p.D * sizeof(uint16_t));
+  const size_t dkdv = B == 1 ? static_cast<size_t>(img.n_slots) * dkdv_slot_floats(p.D) * sizeof(float) : 0;
+  l.total = align_up(l.off_dkdv + dkdv);
   return l;
 }
 
 void write_bwd_image(const BwdImage& img, uint8_t* dst) {
   std::memset(dst, 0, img.bytes);
   std::memcpy(dst + img.off_items, img.items.data(), img.items.size() * sizeof(Item));
+  std::memcpy(dst + img.off_items_split, img.items_split.data(), img.items_split.size() * sizeof(Item));
+  if (!img.merge.empty()) std::memcpy(dst + img.off_merge, img.merge.data(), img.merge.size() * sizeof(MergeRow));
   if (!img.col.empty()) std::memcpy(dst + img.off_col, img.col.data(), img.col.size() * sizeof(int32_t));
 }
 

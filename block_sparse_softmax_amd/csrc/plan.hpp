@@ -61,21 +61,30 @@ struct ImageLayout {
 // the 128 x 128 rectangle is allowed.  `items` are the dK/dV work items
 // {kv head, key block, first col entry, one past the last, 0, 0, 1, 0} in
 // kXcds equal-length queues (kv head -1 pads).
+// `items_split` is the batch-1 schedule: an item whose list is long compared
+// with the launch is cut into pieces of consecutive entries, each adding its
+// dK and dV sums into partial slot `slot + piece` (n_slots slots of
+// dkdv_slot_floats floats after the statistics of a batch-1 workspace), and
+// `merge` lists the split items for the merge kernel (MergeRow with the kv
+// head in `head` and the key block in `qtile`).
 struct BwdImage {
   int64_t kv_heads = 0, nkb = 0;
-  std::vector<Item> items;
+  std::vector<Item> items, items_split;
+  std::vector<MergeRow> merge;
+  int64_t n_slots = 0;
   std::vector<int32_t> col_ptr;  // [kv_heads * nkb + 1] (host only): (kv head, key block) row-major
   std::vector<int32_t> col;
-  size_t off_items = 0, off_col = 0, bytes = 0;  // relative to the image start
+  size_t off_items = 0, off_items_split = 0, off_merge = 0, off_col = 0, bytes = 0;  // relative to the image start
 };
 
 // Workspace of a backward launch with batch B: the forward workspace
 // (image and partial states), the backward image, per-row statistics
 // (lse in log2 units and D, float [B][H][2][nq * kBM]), the per query tile
-// partial sums of the sink gradient (float [B][H][nq]) and the scaled
-// queries the scores are recomputed from (bf16 [B][H][L][D]).
+// partial sums of the sink gradient (float [B][H][nq]), the scaled queries
+// the scores are recomputed from (bf16 [B][H][L][D]) and, for B = 1, the
+// dK/dV partial slots of split key blocks.
 struct BwdLayout {
-  size_t off_image = 0, off_stat = 0, off_sinkpart = 0, off_qs = 0, total = 0;
+  size_t off_image = 0, off_stat = 0, off_sinkpart = 0, off_qs = 0, off_dkdv = 0, total = 0;
 };
 
 void set_error(const std::string& msg);

@@ -240,8 +240,10 @@ attn_status attn_masked_fwd_lse(const attn_plan* plan, const attn_tensor* q, con
  *
  * Workspace: attn_bwd_workspace_bytes(plan, B, kv_heads) bytes, prepared once
  * by attn_bwd_upload(plan, kv_heads, ...) (it holds the plan's forward image,
- * the transposed tile lists and dK/dV schedule for kv_heads K/V heads, then
- * per-row statistics written by every backward launch).  Launches sharing a
+ * the transposed tile lists and dK/dV schedules for kv_heads K/V heads, then
+ * per-row statistics written by every backward launch and, for batch 1, the
+ * partial sums of the long query rows and key blocks that the launch splits
+ * over several work-groups and merges in a fixed order).  Launches sharing a
  * workspace must not overlap in time.
  */
 attn_status attn_bwd_workspace_bytes(const attn_plan* plan, int64_t B, int64_t kv_heads, size_t* bytes);
