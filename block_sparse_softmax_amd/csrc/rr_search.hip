@@ -40,6 +40,32 @@ constexpr int kRrThreads = 256;
 constexpr int kRrQ = 128;     // sampled queries per work-group
 constexpr int kChunk = 32;    // key strides per chunk
 
+// Sum of v over the lanes l ^ x for every x < n (n = 8, 16 or 32: the lanes
+// of an aligned group of n), all holding the total: DPP quad and row-mirror
+// steps inside a 16-lane row, a row swap (v_permlane16_swap) for n = 32.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_mov<0x141>(v);   // row_half_mirror: the other quad of each 8 lanes
+  if constexpr (N >= 16) v += dpp_mov<0x140>(v);  // row_mirror: the other 8 lanes of the row
+  if constexpr (N >= 32) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return v;
+}
+
+// Sum of v over lanes l and l ^ 32.
+__device__ __forceinline__ float halves_sum32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------- prep ----
 // One thread per (batch, head, stride row of the padded table, 8-dim chunk).
 __global__ __launch_bounds__(256) void rr_prep_kernel(const RrParams p) {
@@ -146,7 +172,20 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p)
       const int buf = c & 1;
       if (c <= last_chunk) {
         const f32x16 acc = chunk_scores(buf);
-        if (pass == 0) {
+        // below the wave's diagonal sub-chunk every key stride precedes every
+        // query of the wave: no causal test (and no padded query: q0 + 31 < ns)
+        const bool open = c < last_chunk && q0 + 31 < p.ns;
+        if (pass == 0 && open) {
+          float mx = fmaxf(acc[0], acc[1]);
+#pragma unroll
+          for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(acc[r], acc[r + 1]));
+          const float m_new = fmaxf(m_run, mx * p.scale_log2);
+          float s = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], p.scale_log2, -m_new));
+          l_run = l_run * __builtin_amdgcn_exp2f(m_run - m_new) + s;
+          m_run = m_new;
+        } else if (pass == 0) {
           float mx = -INFINITY;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -170,19 +209,23 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p)
           float bs[KB];
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) bs[kb] = 0.f;
+          if (open) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = key_of(c, r);
-            const float pr = (q_valid && j <= qi) ? __builtin_amdgcn_exp2f(acc[r] * p.scale_log2 - m_row) * inv_l : 0.f;
-            bs[(8 * (r >> 2) + 4 * half + (r & 3)) / R] += pr;
+            for (int r = 0; r < 16; ++r)
+              bs[(8 * (r >> 2) + 4 * half + (r & 3)) / R] +=
+                  __builtin_amdgcn_exp2f(acc[r] * p.scale_log2 - m_row) * inv_l;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int j = key_of(c, r);
+              const float pr = (q_valid && j <= qi) ? __builtin_amdgcn_exp2f(acc[r] * p.scale_log2 - m_row) * inv_l : 0.f;
+              bs[(8 * (r >> 2) + 4 * half + (r & 3)) / R] += pr;
+            }
           }
           // sum over the lanes of each query block (R consecutive queries, both halves)
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
-            float v = bs[kb];
-#pragma unroll
-            for (int off = 1; off < (R < 32 ? R : 32); off <<= 1) v += __shfl_xor(v, off);
-            v += __shfl_xor(v, 32);
+            const float v = halves_sum32(group_sum<R>(bs[kb]));
             const int qb_first = q0 + (lane & 31);     // first query of a block when lane % R == 0
             if (half == 0 && (lane % R) == 0 && qb_first < p.ns_pad) {
               const int qb = (q0 + (lane & 31)) / R;
