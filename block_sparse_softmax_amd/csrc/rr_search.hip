@@ -308,17 +308,23 @@ __global__ __launch_bounds__(kRrThreads) void rr_select_kernel(const RrParams p)
   const int a0 = threadIdx.x * per, a1 = min(p2, a0 + per);
   float run = 0.f;
   for (int a = a0; a < a1; ++a) run += key[a] > 0.f ? key[a] : 0.f;
-  part[threadIdx.x] = run;
-  __syncthreads();
-  if (threadIdx.x == 0) {                      // exclusive scan of the run sums (256 values)
-    float acc = 0.f;
-    for (int t = 0; t < kRrThreads; ++t) {
-      const float v = part[t];
-      part[t] = acc;
-      acc += v;
+  {  // exclusive scan of the run sums in thread order (fixed association: per-wave
+     // inclusive scan, then the totals of the preceding waves)
+    __shared__ float wave_total[kRrThreads / 64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    float x = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(x, off);
+      if (lane >= off) x += y;
     }
+    if (lane == 63) wave_total[w] = x;
+    __syncthreads();
+    float base = 0.f;
+    for (int i = 0; i < w; ++i) base += wave_total[i];
+    part[threadIdx.x] = base + (x - run);
+    __syncthreads();
   }
-  __syncthreads();
   // keep sorted positions before and at the first one whose prefix reaches tau * total
   const float thr = p.tau * total;
   float c = part[threadIdx.x];
