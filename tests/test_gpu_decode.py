@@ -95,14 +95,14 @@ def test_small_cases(ci):
         _compare(got, ref, f"{CASES[ci]} {layout}")
 
 
-@pytest.mark.parametrize("window,prefix,B,Hkv,Lmax", [(0, 0, 1, 2, 20000), (5000, 4, 2, 1, 9000)])
-def test_split_path(window, prefix, B, Hkv, Lmax):
+@pytest.mark.parametrize("window,prefix,B,Hkv,Lmax,D,G", [(0, 0, 1, 2, 20000, 128, 4), (5000, 4, 2, 1, 9000, 128, 4),
+                                                       (0, 0, 1, 1, 12000, 256, 8), (3000, 2, 1, 2, 7000, 64, 2)])
+def test_split_path(window, prefix, B, Hkv, Lmax, D, G):
     """Few sequences x heads: one sequence's keys spread over many work-groups, merged in split order."""
-    D, G = 128, 4
     H = Hkv * G
-    cfg = 120 + Hkv
+    cfg = 120 + Hkv + D
     lens = np.array([Lmax - 17, Lmax][:B], np.int32)
-    print(f"[decode] split path window={window} prefix={prefix} B={B} Lmax={Lmax}", flush=True)
+    print(f"[decode] split path window={window} prefix={prefix} B={B} Lmax={Lmax} D={D} G={G}", flush=True)
     q = gen.decode_queries(0, cfg, B, H, D)
     k, v = _host_caches(cfg, B, Hkv, Lmax, D, lens, prefix, window if window > 0 else Lmax)
     sink = gen.head_sinks(0, cfg, H)
