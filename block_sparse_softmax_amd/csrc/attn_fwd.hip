@@ -24,7 +24,9 @@
 //     of the bf16 probabilities at no extra VALU cost.
 //   * K and V tiles go global -> LDS with global_load_lds_dwordx4 (no VGPR
 //     staging), double-buffered: the next listed tile streams in while the
-//     current one is multiplied.  LDS rows are XOR-swizzled by 16-byte chunk.
+//     current one is multiplied.  LDS rows are XOR-swizzled by 16-byte chunk
+//     (d = 64, 80) or padded (d = 128) so that fragment reads are
+//     conflict-free.
 //   * Masking code runs only on tiles flagged PARTIAL: every allowed key set
 //     of the interval masks is one interval [lo, hi) per query, and a block
 //     matrix whose block size is a multiple of the tile sizes adds only j <= i.
@@ -51,6 +53,28 @@ constexpr float kRescaleThreshold = 8.0f;
 constexpr int kListCap = 1024;  // KV-list entries staged in LDS at a time
 constexpr float kLn2 = 0.6931471805599453f;
 
+// LDS tiles.  d = 64 and 80: row-major rows of LRB bytes, 16-byte chunks
+// XOR-swizzled by row (the swizzle of tile_common.hpp).  d = 128: rows
+// padded so that every fragment address is one per-lane base plus a constant.
+// DMA wave-instruction i (0..15) of a tile carries rows i, i+16, i+32 and
+// i+48 into 1024 consecutive bytes (row i + 16k at +256k, unswizzled), and
+// consecutive instructions sit kKBlk (K) or kVBlk (V) bytes apart.  A K
+// fragment read (16 lanes, 16 consecutive rows, one chunk) then sees row
+// offsets 16 bytes apart modulo the 256-byte bank width, and a transposed V
+// read (32 lanes, 4 consecutive rows x 64 bytes) sees rows 64 bytes apart:
+// both conflict-free.
+template <int D>
+struct Lds {
+  static constexpr bool PADDED = (D == 128);
+  static constexpr int kKBlk = 1024 + 16;
+  static constexpr int kVBlk = 1024 + 64;
+  static constexpr int KT = PADDED ? 16 * kKBlk : Shape<D>::TILE;  // bytes of a K tile
+  static constexpr int VT = PADDED ? 16 * kVBlk : Shape<D>::TILE;  // bytes of a V tile
+  static constexpr int BYTES = 2 * KT + 2 * VT;
+  // buffers 0-1 hold K tiles, 2-3 V tiles
+  __device__ static constexpr int buf_off(int buf) { return buf < 2 ? buf * KT : 2 * KT + (buf - 2) * VT; }
+};
+
 // PREFIX: the launch may add prefix tokens to the rows' sets (a second
 // allowed interval [0, pend) checked on PARTIAL tiles); without it the mask
 // is the single interval [lo, hi).
@@ -61,8 +85,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
   constexpr int kSlotM = 4 * S::DT * 16 * 64;  // m of every lane of the 4 waves
   constexpr int kSlotL = kSlotM + 4 * 64;       // l of every lane
   static_assert(kSlotL + 4 * 64 == kSlotFloats, "partial slot layout");
-  // LDS: K tiles in buffers 0-1, V tiles in buffers 2-3 (row pitch LRB).
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * S::TILE];
+  using L = Lds<D>;
+  // LDS: K tiles in buffers 0-1, V tiles in buffers 2-3.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[L::BYTES];
   __shared__ int list_lds[kListCap];
 
   const int lane = threadIdx.x & 63;
@@ -181,9 +206,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
 
   // ---- LDS addressing ----
   // K fragment for k-step ks: row l31 (and l31 + 32: same swizzle), logical chunk 2*ks + h2.
-  // d = 128 keeps one base per table and rebuilds the others with an XOR per
-  // use (its swizzle XORs k-step / O^T-tile bits into address bits that are
-  // otherwise lane-only), which saves 14 registers.
+  // d = 128 (padded rows) needs one base per table and immediate offsets.
   int koff[S::KS];
 #pragma unroll
   for (int ks = 0; ks < S::KS; ++ks) koff[ks] = l31 * S::LRB + phys_chunk<D>(l31, 2 * ks + h2) * 16;
@@ -203,6 +226,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
     }
   }
   int vbase_off = voff[0][0];
+  if constexpr (L::PADDED) {
+    // row l31 (+32 per key half), chunk 2*ks + h2 / row 8*u + 4*h2 + tr_j (+16 per k-step)
+    kbase_off = (l31 & 15) * L::kKBlk + (l31 >> 4) * 256 + 16 * h2;
+    vbase_off = (4 * h2 + tr_j) * L::kVBlk + 32 * dhalf + 8 * tr_c;
+  }
   if constexpr (S::PAD_ROWSUM) {
     // Constant pad chunks 10-11 of every V row in both V buffers: element 80 = 1, the rest 0.
     for (int i = threadIdx.x; i < 2 * kBN * 4; i += kThreads) {  // 2 buffers x 64 rows x 4 x 8 bytes
@@ -210,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
       const int c = 10 + (q4 >> 1);
       uint2 v = make_uint2(0u, 0u);
       if (q4 == 0) v.x = 0x3F80u;  // bf16 1.0 in element 80
-      *reinterpret_cast<uint2*>(smem + (2 + buf) * S::TILE + row * S::LRB +
+      *reinterpret_cast<uint2*>(smem + L::buf_off(2 + buf) + row * S::LRB +
                                 phys_chunk<D>(row, c) * 16 + (q4 & 1) * 8) = v;
     }
   }
@@ -238,12 +266,34 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
     gskip[i] = (S::PAD_ROWSUM && dma_tensor == 1) ? __builtin_amdgcn_ballot_w64(pad) : 0;
   }
   const uint32_t smem_lds = lds_addr(smem);
+  // d = 128: lane (k, c) of every wave-instruction copies chunk c of row
+  // (instruction) + 16 k; the instruction's row is added to the uniform base.
+  const uint32_t goff_pad = static_cast<uint32_t>(16 * (lane >> 4)) * dma_row_bytes + 16 * (lane & 15);
+  const uint32_t blk_bytes = dma_tensor ? L::kVBlk : L::kKBlk;
   // Issue this wave's share of tile kt into LDS buffer buf (0-1 K, 2-3 V).
   auto issue_tile = [&](int kt, int buf) __attribute__((always_inline)) {
     const uint32_t kv0 = static_cast<uint32_t>(kt * kBN);
     const uint64_t tb = uniform_u64(reinterpret_cast<uint64_t>(dma_base) + static_cast<uint64_t>(kv0) * dma_row_bytes);
+    if constexpr (L::PADDED) {
+      constexpr int kPer = 8;  // instructions per wave: two waves per tensor, 16 per tile
+      const int i0 = (wave & 1) * kPer;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(smem_lds + L::buf_off(buf) + i0 * blk_bytes);
+      if (static_cast<int>(kv0) + kBN <= p.L) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+          dma16(tb + static_cast<uint64_t>(i0 + i) * dma_row_bytes, goff_pad, dst + i * blk_bytes);
+      } else {  // ragged last tile: clamp rows past the end of the sequence (their keys are masked)
+        const int last = p.L - 1 - static_cast<int>(kv0);
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const int row = i0 + i + 16 * (lane >> 4);
+          dma16(tb, min(row, last) * dma_row_bytes + 16 * (lane & 15), dst + i * blk_bytes);
+        }
+      }
+      return;
+    }
     const uint32_t dst =
-        __builtin_amdgcn_readfirstlane(smem_lds + buf * S::TILE + (wave & 1) * S::LOADS * 1024);
+        __builtin_amdgcn_readfirstlane(smem_lds + L::buf_off(buf) + (wave & 1) * S::LOADS * 1024);
     if (static_cast<int>(kv0) + kBN <= p.L) {
 #pragma unroll
       for (int i = 0; i < S::LOADS; ++i) {
@@ -270,23 +320,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
   // only touches the two low chunk bits, so addresses are one of two bases
   // plus an immediate (32 bytes per k-step, 64 bytes per O^T tile).
   auto k_addr = [&](int ks) __attribute__((always_inline)) {
-    if constexpr (D == 128) return kbase_off ^ (ks << 5);
+    if constexpr (L::PADDED) return kbase_off + 32 * ks;
     else if constexpr (D == 80) return koff[ks & 1] + 32 * (ks & ~1);
     else return koff[ks];
   };
   auto v_addr = [&](int dt, int u) __attribute__((always_inline)) {
-    if constexpr (D == 128) return vbase_off ^ (dt << 6) ^ (u ? 0x820 : 0);
+    if constexpr (L::PADDED) return vbase_off + 64 * dt + 8 * u * L::kVBlk;
     else if constexpr (D == 80) return voff[0][u] + 64 * dt;
     else return voff[dt][u];
   };
   // K fragment (A operand of S^T = K Q^T) for k-step ks, keys 32*half .. +31.
   auto kfrag = [&](int kbuf, int ks, int half) __attribute__((always_inline)) {
-    return *reinterpret_cast<const bf16x8*>(smem + kbuf * S::TILE + k_addr(ks) + half * 32 * S::LRB);
+    constexpr int kHalf = L::PADDED ? 2 * 256 : 32 * S::LRB;  // keys 32 .. 63
+    return *reinterpret_cast<const bf16x8*>(smem + L::buf_off(kbuf) + k_addr(ks) + half * kHalf);
   };
   // V^T fragment for PV step p = t * DT + dt (keys 16t .. 16t+15, O^T tile dt).
   auto vfrag = [&](int vbuf, int p) __attribute__((always_inline)) {
     const int t = p / S::DT, dt = p % S::DT;
-    const unsigned char* src = smem + vbuf * S::TILE + 16 * t * S::LRB;
+    const unsigned char* src = smem + L::buf_off(vbuf) + t * (L::PADDED ? 256 : 16 * S::LRB);
     const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + v_addr(dt, 0)));
     const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + v_addr(dt, 1)));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
