@@ -22,8 +22,11 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
-    # NaNs need no IEEE quieting in min/max (infinities are still honoured: masks use -inf)
-    "-fno-honor-nans", "-mno-amdgpu-ieee",
+    # NaNs need no IEEE quieting in min/max (infinities are still honoured: masks use -inf).
+    # The kernels keep the default IEEE mode: -mno-amdgpu-ieee would stop the device library's
+    # work-item and work-group id functions from being inlined (they become calls returning the
+    # ids in vector registers), and -fno-honor-nans already drops the quieting of min/max inputs.
+    "-fno-honor-nans",
     # m0 is written only by the LDS-DMA helper, which declares it clobbered
     "-Wno-inline-asm",
     # no packed-FP32 instructions are generated
