@@ -676,7 +676,8 @@ static attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const 
   p.protect_last = prm->protect_last;
   p.kv_group = static_cast<int32_t>(H / k->H);
   *out = p;
-  *ws_bytes = 2 * static_cast<size_t>(B) * H * ns_pad * D * sizeof(uint16_t);
+  // sampled queries (rows of D bf16), then stride-summed keys (rows of D bf16 + 16 pad bytes)
+  *ws_bytes = static_cast<size_t>(B) * H * ns_pad * (2 * D + (2 * D + 16));
   return ATTN_OK;
 }
 

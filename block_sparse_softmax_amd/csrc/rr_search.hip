@@ -18,10 +18,11 @@
 //
 // Layout of the scores kernel: a work-group of 4 waves takes 128 consecutive
 // sampled queries of one (batch, head); wave w owns queries 32w..32w+31 of
-// them.  Chunks of 32 stride-summed keys are staged in LDS (double-buffered,
-// shared by the 4 waves).  I^T = Ksum Q^T: the key chunk is the A operand
-// (from LDS), the sampled queries the B operand (in registers), so lane l
-// holds query l mod 32 and 16 of the chunk's 32 key strides.
+// them.  The stride-summed keys are staged in LDS 64 at a time, three stages
+// in flight, shared by the 4 waves, and used in chunks of 32.  I^T = Ksum
+// Q^T: the key chunk is the A operand (from LDS), the sampled queries the B
+// operand (in registers), so lane l holds query l mod 32 and 16 of the
+// chunk's 32 key strides.
 
 #include <hip/hip_runtime.h>
 
@@ -29,6 +30,7 @@
 #include <cstdint>
 
 #include "kernels.hpp"
+#include "tile_common.hpp"
 
 namespace bss {
 namespace {
@@ -68,6 +70,9 @@ __device__ __forceinline__ float halves_sum32(float v) {
 
 // ---------------------------------------------------------------- prep ----
 // One thread per (batch, head, stride row of the padded table, 8-dim chunk).
+// The stride-summed key rows are 2 D + 16 bytes apart (the last 16 bytes are
+// never written or read): a run of rows is then byte for byte the padded LDS
+// layout of the scores kernel and is copied with LDS-DMA as it is.
 __global__ __launch_bounds__(256) void rr_prep_kernel(const RrParams p) {
   const int cpr = p.D / 8;
   const int64_t n = static_cast<int64_t>(p.B) * p.H * p.ns_pad * cpr;
@@ -93,7 +98,7 @@ __global__ __launch_bounds__(256) void rr_prep_kernel(const RrParams p) {
     for (int e = 0; e < 8; ++e) ko[e] = static_cast<__bf16>(acc[e]);
   }
   *reinterpret_cast<bf16x8*>(p.qs + row * p.D + 8 * c) = qo;
-  *reinterpret_cast<bf16x8*>(p.ks + row * p.D + 8 * c) = ko;
+  *reinterpret_cast<bf16x8*>(p.ks + row * (p.D + 8) + 8 * c) = ko;  // rows of 2 D + 16 bytes
 }
 
 // -------------------------------------------------------------- scores ----
@@ -101,12 +106,17 @@ __global__ __launch_bounds__(256) void rr_prep_kernel(const RrParams p) {
 template <int D, int R>
 __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p) {
   constexpr int KS = D / 16;                 // k-steps of the 32x32x16 product
-  constexpr int PITCH = 2 * D + 16;          // LDS row pitch: 16 rows of a fragment read hit distinct banks
+  constexpr int PITCH = 2 * D + 16;          // row pitch (table and LDS): 16 rows of a fragment read hit distinct banks
   constexpr int CPR = D / 8;                 // 16-byte pieces per key row
-  constexpr int PIECES = kChunk * CPR;       // per chunk
-  constexpr int PER_THREAD = (PIECES + kRrThreads - 1) / kRrThreads;
+  constexpr int STAGE = 2 * kChunk;          // key strides per copy stage
+  constexpr int SBYTES = STAGE * PITCH;      // bytes of one stage
+  constexpr int NI = SBYTES / 1024;          // LDS-DMA wave-instructions per stage (wave w takes w, w + 4, ...)
+  constexpr int NW_HI = (NI + 3) / 4, NW_LO = NI / 4;
+  constexpr int NBUF = 3;
+  static_assert(SBYTES % 1024 == 0, "a stage is whole 1 KiB copies");
+  static_assert(NW_HI < 16, "vmcnt immediate");
   static_assert(R == 8 || R == 16 || R == 32, "strides per block");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kChunk * PITCH];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * SBYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -115,7 +125,7 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p)
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t bh_row = (static_cast<int64_t>(b) * p.H + h) * p.ns_pad;
   const bf16x8* qs = reinterpret_cast<const bf16x8*>(p.qs) + bh_row * CPR;
-  const bf16x8* ks = reinterpret_cast<const bf16x8*>(p.ks) + bh_row * CPR;
+  const unsigned char* ksb = reinterpret_cast<const unsigned char*>(p.ks) + bh_row * PITCH;
 
   const int q0 = tile * kRrQ + 32 * wave;    // this wave's first sampled query
   const int qi = q0 + (lane & 31);           // this lane's query (column of I^T)
@@ -126,29 +136,36 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p)
 
   const int last_chunk_wg = (tile * kRrQ + kRrQ - 1) / kChunk;  // chunks the work-group stages
   const int last_chunk = q0 / kChunk;                            // chunks this wave computes
-  const int n_chunks = last_chunk_wg + 1;
+  const int n_chunks = last_chunk_wg + 1;                        // a multiple of 4
+  const int n_stage = n_chunks / 2;
 
-  // staging: piece t of a chunk = row t / CPR, 16 bytes at column t % CPR
-  bf16x8 stage[PER_THREAD];
-  auto load_chunk = [&](int c) __attribute__((always_inline)) {
+  // Stage s (key strides 64 s .. 64 s + 63, contiguous in the table) into
+  // buffer s mod 3: wave w issues 1 KiB copies w, w + 4, ... of it.
+  const uint32_t smem_lds = dev::lds_addr(smem);
+  const int nw = (NI - wave + 3) / 4;        // copies per stage issued by this wave
+  auto issue_stage = [&](int st) __attribute__((always_inline)) {
+    const uint64_t src = dev::uniform_u64(reinterpret_cast<uint64_t>(ksb) + static_cast<uint64_t>(st) * SBYTES);
+    const uint32_t dst = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+        static_cast<int>(smem_lds + (st % NBUF) * SBYTES)));
 #pragma unroll
-    for (int u = 0; u < PER_THREAD; ++u) {
-      const int t = threadIdx.x + u * kRrThreads;
-      if (t < PIECES) stage[u] = ks[static_cast<int64_t>(c * kChunk + t / CPR) * CPR + t % CPR];
+    for (int i = 0; i < NW_HI; ++i) {
+      const int ins = wave + 4 * i;
+      if (ins < NI) dev::dma16(src + static_cast<uint64_t>(ins) * 1024, 16 * lane, dst + ins * 1024);
     }
   };
-  auto store_chunk = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < PER_THREAD; ++u) {
-      const int t = threadIdx.x + u * kRrThreads;
-      if (t < PIECES)
-        *reinterpret_cast<bf16x8*>(smem + buf * kChunk * PITCH + (t / CPR) * PITCH + (t % CPR) * 16) = stage[u];
-    }
+  // Wait for this wave's copies of stage st when the copies of stage st + 1
+  // (issued after them) may stay in flight; global stores issued in between
+  // only make the wait longer, never shorter.
+  auto wait_stage = [&](bool next_in_flight) __attribute__((always_inline)) {
+    if (!next_in_flight) dev::wait_vmcnt<0>();
+    else if (nw == NW_HI) dev::wait_vmcnt<NW_HI>();
+    else dev::wait_vmcnt<NW_LO>();
   };
-  // I^T tile of chunk c (in buffer buf): lane holds key strides c*32 + 8g + 4*half + e (register 4g + e)
-  auto chunk_scores = [&](int buf) __attribute__((always_inline)) {
+  // I^T tile of chunk c (half `sub` of the stage in buffer buf): lane holds
+  // key strides c*32 + 8g + 4*half + e (register 4g + e)
+  auto chunk_scores = [&](int buf, int sub) __attribute__((always_inline)) {
     f32x16 acc = {};
-    const unsigned char* base = smem + buf * kChunk * PITCH + (lane & 31) * PITCH + half * 16;
+    const unsigned char* base = smem + buf * SBYTES + (sub * kChunk + (lane & 31)) * PITCH + half * 16;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(base + 32 * s);
@@ -164,85 +181,91 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p)
   // ---- pass 2 state: this lane's query's max and sum (both halves combined) ----
   float m_row = 0.f, inv_l = 0.f;
   for (int pass = 0; pass < 2; ++pass) {
-    load_chunk(0);
-    store_chunk(0);
-    if (n_chunks > 1) load_chunk(1);
-    __syncthreads();
-    for (int c = 0; c < n_chunks; ++c) {
-      const int buf = c & 1;
-      if (c <= last_chunk) {
-        const f32x16 acc = chunk_scores(buf);
-        // below the wave's diagonal sub-chunk every key stride precedes every
-        // query of the wave: no causal test (and no padded query: q0 + 31 < ns)
-        const bool open = c < last_chunk && q0 + 31 < p.ns;
-        if (pass == 0 && open) {
-          float mx = fmaxf(acc[0], acc[1]);
+    issue_stage(0);
+    if (n_stage > 1) issue_stage(1);
+    for (int st = 0; st < n_stage; ++st) {
+      wait_stage(st + 1 < n_stage);
+      __syncthreads();                         // stage st everywhere; stage st - 1 no longer read
+      if (st + 2 < n_stage) issue_stage(st + 2);  // into the buffer of stage st - 1
+      const int buf = st % NBUF;
+      // both chunks' products first: the softmax work of the first runs
+      // beside the MFMAs of the second
+      f32x16 accs[2];
 #pragma unroll
-          for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(acc[r], acc[r + 1]));
-          const float m_new = fmaxf(m_run, mx * p.scale_log2);
-          float s = 0.f;
+      for (int sub = 0; sub < 2; ++sub)
+        if (2 * st + sub <= last_chunk) accs[sub] = chunk_scores(buf, sub);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], p.scale_log2, -m_new));
-          l_run = l_run * __builtin_amdgcn_exp2f(m_run - m_new) + s;
-          m_run = m_new;
-        } else if (pass == 0) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = key_of(c, r);
-            if (q_valid && j <= qi) mx = fmaxf(mx, acc[r] * p.scale_log2);
-          }
-          const float m_new = fmaxf(m_run, mx);
-          if (m_new > -INFINITY) {
+      for (int sub = 0; sub < 2; ++sub) {
+        const int c = 2 * st + sub;
+        if (c <= last_chunk) {
+          const f32x16& acc = accs[sub];
+          // below the wave's diagonal sub-chunk every key stride precedes every
+          // query of the wave: no causal test (and no padded query: q0 + 31 < ns)
+          const bool open = c < last_chunk && q0 + 31 < p.ns;
+          if (pass == 0 && open) {
+            float mx = fmaxf(acc[0], acc[1]);
+  #pragma unroll
+            for (int r = 2; r < 16; r += 2) mx = fmaxf(mx, fmaxf(acc[r], acc[r + 1]));
+            const float m_new = fmaxf(m_run, mx * p.scale_log2);
             float s = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int j = key_of(c, r);
-              if (q_valid && j <= qi) s += __builtin_amdgcn_exp2f(acc[r] * p.scale_log2 - m_new);
-            }
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) s += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], p.scale_log2, -m_new));
             l_run = l_run * __builtin_amdgcn_exp2f(m_run - m_new) + s;
             m_run = m_new;
-          }
-        } else {
-          // probabilities of this lane's 16 key strides, summed per key block
-          constexpr int KB = kChunk / R;     // key blocks in a chunk
-          float bs[KB];
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) bs[kb] = 0.f;
-          if (open) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              bs[(8 * (r >> 2) + 4 * half + (r & 3)) / R] +=
-                  __builtin_amdgcn_exp2f(acc[r] * p.scale_log2 - m_row) * inv_l;
-          } else {
-#pragma unroll
+          } else if (pass == 0) {
+            float mx = -INFINITY;
+  #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int j = key_of(c, r);
-              const float pr = (q_valid && j <= qi) ? __builtin_amdgcn_exp2f(acc[r] * p.scale_log2 - m_row) * inv_l : 0.f;
-              bs[(8 * (r >> 2) + 4 * half + (r & 3)) / R] += pr;
+              if (q_valid && j <= qi) mx = fmaxf(mx, acc[r] * p.scale_log2);
             }
-          }
-          // sum over the lanes of each query block (R consecutive queries, both halves)
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            const float v = halves_sum32(group_sum<R>(bs[kb]));
-            const int qb_first = q0 + (lane & 31);     // first query of a block when lane % R == 0
-            if (half == 0 && (lane % R) == 0 && qb_first < p.ns_pad) {
-              const int qb = (q0 + (lane & 31)) / R;
-              const int kblk = (c * kChunk) / R + kb;
-              if (qb < p.nb && kblk < p.nb)
-                p.score[(static_cast<int64_t>(b) * p.H + h) * p.nb * p.nb + static_cast<int64_t>(qb) * p.nb + kblk] = v;
+            const float m_new = fmaxf(m_run, mx);
+            if (m_new > -INFINITY) {
+              float s = 0.f;
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int j = key_of(c, r);
+                if (q_valid && j <= qi) s += __builtin_amdgcn_exp2f(acc[r] * p.scale_log2 - m_new);
+              }
+              l_run = l_run * __builtin_amdgcn_exp2f(m_run - m_new) + s;
+              m_run = m_new;
+            }
+          } else {
+            // probabilities of this lane's 16 key strides, summed per key block
+            constexpr int KB = kChunk / R;     // key blocks in a chunk
+            float bs[KB];
+  #pragma unroll
+            for (int kb = 0; kb < KB; ++kb) bs[kb] = 0.f;
+            if (open) {
+  #pragma unroll
+              for (int r = 0; r < 16; ++r)
+                bs[(8 * (r >> 2) + 4 * half + (r & 3)) / R] +=
+                    __builtin_amdgcn_exp2f(acc[r] * p.scale_log2 - m_row) * inv_l;
+            } else {
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int j = key_of(c, r);
+                const float pr = (q_valid && j <= qi) ? __builtin_amdgcn_exp2f(acc[r] * p.scale_log2 - m_row) * inv_l : 0.f;
+                bs[(8 * (r >> 2) + 4 * half + (r & 3)) / R] += pr;
+              }
+            }
+            // sum over the lanes of each query block (R consecutive queries, both halves)
+  #pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              const float v = halves_sum32(group_sum<R>(bs[kb]));
+              const int qb_first = q0 + (lane & 31);     // first query of a block when lane % R == 0
+              if (half == 0 && (lane % R) == 0 && qb_first < p.ns_pad) {
+                const int qb = (q0 + (lane & 31)) / R;
+                const int kblk = (c * kChunk) / R + kb;
+                if (qb < p.nb && kblk < p.nb)
+                  p.score[(static_cast<int64_t>(b) * p.H + h) * p.nb * p.nb + static_cast<int64_t>(qb) * p.nb + kblk] = v;
+              }
             }
           }
         }
       }
-      if (c + 1 < n_chunks) {
-        __syncthreads();                       // everyone is done with buffer buf ^ 1 (chunk c-1)
-        store_chunk(buf ^ 1);
-        if (c + 2 < n_chunks) load_chunk(c + 2);
-        __syncthreads();
-      }
     }
+    __syncthreads();                           // the next pass restages buffers 0 and 1
     if (pass == 0) {
       // combine the two halves of each query: max and sum over all its key strides
       const float mo = __shfl_xor(m_run, 32), lo = __shfl_xor(l_run, 32);
@@ -251,7 +274,6 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p)
                                        : l_run * __builtin_amdgcn_exp2f(m_run - m) + lo * __builtin_amdgcn_exp2f(mo - m);
       m_row = (m == -INFINITY) ? 0.f : m;
       inv_l = l > 0.f ? 1.f / l : 0.f;
-      __syncthreads();                         // pass 2 restages from chunk 0
     }
   }
 }
