@@ -619,7 +619,6 @@ attn_status attn_masked_bwd(const attn_plan* p, const attn_tensor* q, const attn
 namespace {
 
 constexpr int kRrTileQ = 128;    // sampled queries per work-group of the scores kernel
-constexpr int kRrMaxBlocks = 4096;
 
 // Validate a search request and fill the kernel parameters (pointers except the workspace).
 static attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const attn_rr_params* prm, RrParams* out,
@@ -670,9 +669,6 @@ static attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const 
   p.ns = static_cast<int32_t>(ns);
   p.ns_pad = static_cast<int32_t>(ns_pad);
   p.nb = static_cast<int32_t>(nb);
-  int cap = 1;
-  while (cap < nb) cap <<= 1;
-  p.sel_cap = cap;
   p.protect_last = prm->protect_last;
   p.kv_group = static_cast<int32_t>(H / k->H);
   *out = p;

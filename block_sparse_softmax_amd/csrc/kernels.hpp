@@ -110,6 +110,7 @@ struct BwdParams {
 hipError_t launch_bwd(const BwdParams& p, int D, int B, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
 // RRAttention block-pattern search (rr_search.hip).
+constexpr int kRrMaxBlocks = 4096;  // key blocks per row of the pattern search
 struct RrParams {
   const uint16_t* q;
   const uint16_t* k;
@@ -122,7 +123,7 @@ struct RrParams {
   float scale_log2;           // log2(e) / (S sqrt(D))
   float tau;
   int32_t B, H, L, D, S, Bs;
-  int32_t ns, ns_pad, nb, sel_cap, protect_last;
+  int32_t ns, ns_pad, nb, protect_last;
   int32_t kv_group;           // query heads per K head (grouped-query attention)
 };
 

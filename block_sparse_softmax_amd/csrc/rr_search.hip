@@ -11,10 +11,11 @@
 //           (Eq. 9's softmax denominator), pass 2 recomputes I, normalises
 //           and sums the probabilities straight into block scores S_mn
 //           (Eq. 10).  The stride-level matrix is never stored.
-//   select  per query block m: sort S_m,n (n <= m) descending (ties to the
-//           lower n), keep the shortest prefix whose mass reaches tau times
-//           the row's mass (Eq. 11), and every causal block of the last query
-//           block (Eq. 12).
+//   select  per query block m: of S_m,n (n <= m) ordered descending (ties to
+//           the lower n), keep the shortest prefix whose mass reaches tau
+//           times the row's mass (Eq. 11), found by a threshold search rather
+//           than a sort, and every causal block of the last query block
+//           (Eq. 12).
 //
 // Layout of the scores kernel: a work-group of 4 waves takes 128 consecutive
 // sampled queries of one (batch, head); wave w owns queries 32w..32w+31 of
@@ -279,96 +280,100 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p)
 }
 
 // -------------------------------------------------------------- select ----
-// One work-group per (query block m, head, batch).
+// One work-group per (query block m, head, batch).  Eq. 11 keeps the shortest
+// prefix of the row's causal blocks, ordered by descending score (ties: lower
+// n first), whose mass reaches tau times the row's mass.  That prefix is
+// found without sorting.  With F(x) = mass of the scores >= x, the last kept
+// score is theta = the largest x with F(x) >= tau * total; every block above
+// theta is kept and, of the blocks scoring exactly theta, the lowest-n ones
+// until the mass is reached.  Scores are >= 0, so their bit patterns order
+// like their values and theta is a binary search over bit patterns (31
+// steps).  Each F is summed in one fixed order (thread t over its contiguous
+// run of n, then a fixed tree), so F is monotone in x and reproducible.
 __global__ __launch_bounds__(kRrThreads) void rr_select_kernel(const RrParams p) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+  constexpr int kPerMax = kRrMaxBlocks / kRrThreads;
+  __shared__ float red_f[kRrThreads / 64];
+  __shared__ int red_i[kRrThreads / 64];
   const int m = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nv = m + 1;                       // causal key blocks n <= m
-  int p2 = 1;
-  while (p2 < nv) p2 <<= 1;
-  float* key = reinterpret_cast<float*>(dyn);
-  int* idx = reinterpret_cast<int*>(dyn + static_cast<size_t>(p.sel_cap) * 4);
-  float* part = reinterpret_cast<float*>(dyn + static_cast<size_t>(p.sel_cap) * 8);  // kRrThreads partial sums
   const int64_t row = (static_cast<int64_t>(b) * p.H + h) * p.nb * p.nb + static_cast<int64_t>(m) * p.nb;
   float* srow = p.score + row;
   uint8_t* brow = p.bmask + row;
-  for (int n = threadIdx.x; n < p2; n += kRrThreads) {
-    key[n] = n < nv ? srow[n] : -1.f;         // scores are >= 0: padding sorts last
-    idx[n] = n;
-  }
-  __syncthreads();
-  // total mass of the row, in a fixed order (thread t sums n = t, t + 256, ...)
-  float s = 0.f;
-  for (int n = threadIdx.x; n < nv; n += kRrThreads) s += key[n];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  for (int w = kRrThreads / 2; w > 0; w >>= 1) {
-    if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
-    __syncthreads();
-  }
-  const float total = part[0];
-  __syncthreads();
-  // bitonic sort: descending score, ascending index on ties
-  for (int k = 2; k <= p2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int t = threadIdx.x; t < p2; t += kRrThreads) {
-        const int u = t ^ j;
-        if (u > t) {
-          const bool first_before = (key[t] > key[u]) || (key[t] == key[u] && idx[t] < idx[u]);
-          const bool up = (t & k) == 0;        // this run is sorted "first before" ascending in t
-          if (first_before != up) {
-            const float kt = key[t]; key[t] = key[u]; key[u] = kt;
-            const int it = idx[t]; idx[t] = idx[u]; idx[u] = it;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  // prefix sums of the sorted scores: thread t owns a contiguous run of positions
-  const int per = (p2 + kRrThreads - 1) / kRrThreads;
-  const int a0 = threadIdx.x * per, a1 = min(p2, a0 + per);
-  float run = 0.f;
-  for (int a = a0; a < a1; ++a) run += key[a] > 0.f ? key[a] : 0.f;
-  {  // exclusive scan of the run sums in thread order (fixed association: per-wave
-     // inclusive scan, then the totals of the preceding waves)
-    __shared__ float wave_total[kRrThreads / 64];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    float x = run;
+  // thread t owns blocks t * per .. t * per + per - 1
+  const int per = (nv + kRrThreads - 1) / kRrThreads;
+  const int a0 = threadIdx.x * per;
+  float v[kPerMax];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(x, off);
-      if (lane >= off) x += y;
-    }
-    if (lane == 63) wave_total[w] = x;
-    __syncthreads();
-    float base = 0.f;
-    for (int i = 0; i < w; ++i) base += wave_total[i];
-    part[threadIdx.x] = base + (x - run);
-    __syncthreads();
+  for (int i = 0; i < kPerMax; ++i) {
+    const int n = a0 + i;
+    v[i] = (i < per && n < nv) ? fmaxf(srow[n], 0.f) : 0.f;
   }
-  // keep sorted positions before and at the first one whose prefix reaches tau * total
+  // work-group sums in a fixed order; every thread gets the result
+  auto block_sum = [&](float x) __attribute__((always_inline)) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    if (lane == 0) red_f[w] = x;
+    __syncthreads();
+    const float t = (red_f[0] + red_f[1]) + (red_f[2] + red_f[3]);
+    __syncthreads();
+    return t;
+  };
+  auto mass_from = [&](uint32_t xb) __attribute__((always_inline)) {  // F(x), x given by its bits
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPerMax; ++i)
+      if (i < per && __float_as_uint(v[i]) >= xb) s += v[i];
+    return block_sum(s);
+  };
+  static_assert(kRrThreads == 256, "four waves in the fixed reduction tree");
+  const float total = mass_from(0u);
   const float thr = p.tau * total;
-  float c = part[threadIdx.x];
-  int cut = -1;                                // first position (in this run) reaching the threshold
-  for (int a = a0; a < a1; ++a) {
-    c += key[a] > 0.f ? key[a] : 0.f;
-    if (cut < 0 && c >= thr && total > 0.f) cut = a;
+  uint32_t theta = 0xFFFFFFFFu;               // no block kept (a row without mass)
+  int need = 0;                               // blocks scoring exactly theta to keep
+  if (total > 0.f) {
+    uint32_t lo = 0u, hi = 0x7F800000u;       // F(lo) >= thr > F(hi) (thr > 0 = F(+inf))
+    while (hi - lo > 1u) {
+      const uint32_t mid = lo + (hi - lo) / 2u;
+      if (mass_from(mid) >= thr) lo = mid;
+      else hi = mid;
+    }
+    theta = lo;
+    const float above = mass_from(lo + 1u);   // mass of the scores above theta (< thr)
+    const float tv = __uint_as_float(lo);
+    const float q = tv > 0.f ? ceilf((thr - above) / tv) : static_cast<float>(nv);
+    need = q >= static_cast<float>(nv) ? nv : max(1, static_cast<int>(q));
   }
+  // rank (in n order) of this thread's first block scoring exactly theta
+  int ties = 0;
+#pragma unroll
+  for (int i = 0; i < kPerMax; ++i)
+    if (i < per && a0 + i < nv && __float_as_uint(v[i]) == theta) ++ties;
+  int x = ties;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) red_i[w] = x;
   __syncthreads();
-  int* first = reinterpret_cast<int*>(part);   // reuse: the earliest cut over all threads
-  if (threadIdx.x == 0) first[0] = 0x7fffffff;
-  __syncthreads();
-  if (cut >= 0) atomicMin(first, cut);         // LDS atomic
-  __syncthreads();
-  const int kcut = total > 0.f ? min(first[0], nv - 1) : -1;
-  for (int n = threadIdx.x; n < p.nb; n += kRrThreads) brow[n] = 0;
-  __syncthreads();
-  for (int a = threadIdx.x; a <= kcut; a += kRrThreads)
-    if (idx[a] < nv) brow[idx[a]] = 1;        // (padding sorts last unless a score is NaN)
-  if (p.protect_last && m == p.nb - 1)
-    for (int n = threadIdx.x; n < nv; n += kRrThreads) brow[n] = 1;
-  for (int n = nv + threadIdx.x; n < p.nb; n += kRrThreads) srow[n] = 0.f;
+  int rank = x - ties;
+  for (int i = 0; i < w; ++i) rank += red_i[i];
+  const bool protect = p.protect_last && m == p.nb - 1;
+#pragma unroll
+  for (int i = 0; i < kPerMax; ++i) {
+    const int n = a0 + i;
+    if (i < per && n < nv) {
+      const uint32_t vb = __float_as_uint(v[i]);
+      bool keep = theta != 0xFFFFFFFFu && vb > theta;
+      if (theta != 0xFFFFFFFFu && vb == theta) keep = rank++ < need;
+      brow[n] = (keep || protect) ? 1 : 0;
+    }
+  }
+  for (int n = nv + threadIdx.x; n < p.nb; n += kRrThreads) {
+    brow[n] = 0;
+    srow[n] = 0.f;
+  }
 }
 
 template <int D>
@@ -398,10 +403,9 @@ hipError_t launch_rr_search(const RrParams& p, hipStream_t stream, hipEvent_t st
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  const size_t lds = static_cast<size_t>(p.sel_cap) * 8 + kRrThreads * 4;
   hipLaunchKernelGGL(rr_select_kernel, dim3(static_cast<unsigned>(p.nb), static_cast<unsigned>(p.H),
                                             static_cast<unsigned>(p.B)),
-                     dim3(kRrThreads), lds, stream, p);
+                     dim3(kRrThreads), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (stop != nullptr && (e = hipEventRecord(stop, stream)) != hipSuccess) return e;
   return hipSuccess;
