@@ -76,6 +76,7 @@ CASES = [
     (1030, 2, 80, 4, 128, 0.9, "random"),      # ragged last stride, 32 strides per block
     (1024, 2, 128, 16, 128, 0.95, "random"),   # 8 strides per block
     (4096, 4, 128, 8, 128, 0.5, "planted"),
+    (2048, 2, 64, 8, 128, 1.0, "random"),      # tau = 1: every block with mass
 ]
 
 

@@ -357,3 +357,34 @@ def test_decode_argument_errors_without_gpu(lib):
                                ctypes.byref(neg), None, ctypes.byref(o), ctypes.byref(ln)) == -1    # negative prefix
     assert lib.attn_decode_fwd(ctypes.byref(q1), ctypes.byref(k1), ctypes.byref(v1), seq, 131072,
                                ctypes.byref(full), None, ctypes.byref(o), ctypes.byref(ln)) == -3   # no workspace
+
+
+def test_rr_workspace_and_argument_errors_without_gpu(lib):
+    """Pattern-search validation and workspace size on the host.  The workspace holds the sampled queries
+    (rows of d bf16) and then the stride-summed keys (rows of d bf16 plus 16 pad bytes), floor(L / S) rows
+    each, padded to a multiple of 128 rows."""
+    import ctypes
+    from block_sparse_softmax_amd._lib import AttnTensor, RrParams
+
+    def view(B, L, H, D, ptr=16):
+        t = AttnTensor()
+        t.data, t.B, t.L, t.H, t.D = ptr, B, L, H, D
+        t.stride_b, t.stride_l, t.stride_h = L * H * D, H * D, D
+        return t
+
+    def ws(q, prm):
+        n = ctypes.c_size_t()
+        st = lib.attn_rr_workspace_bytes(ctypes.byref(q), ctypes.byref(prm), ctypes.byref(n))
+        return st, n.value
+
+    assert ws(view(1, 131072, 32, 128), RrParams(8, 128, 0.9, 1)) == (0, 32 * 16384 * (256 + 256 + 16))
+    # 1030 // 4 = 257 strides -> 384 rows
+    assert ws(view(2, 1030, 3, 80), RrParams(4, 128, 0.5, 0)) == (0, 2 * 3 * 384 * (160 + 160 + 16))
+    assert ws(view(1, 4096, 2, 96), RrParams(8, 128, 0.9, 1))[0] == _lib.ATTN_E_UNSUPPORTED   # head dim
+    assert ws(view(1, 4096, 2, 64), RrParams(8, 100, 0.9, 1))[0] == _lib.ATTN_E_INVAL         # Bs % S != 0
+    assert ws(view(1, 4096, 2, 64), RrParams(8, 512, 0.9, 1))[0] == _lib.ATTN_E_UNSUPPORTED   # Bs / S = 64
+    assert ws(view(1, 4096, 2, 64), RrParams(8, 128, 0.0, 1))[0] == _lib.ATTN_E_INVAL         # tau
+    assert ws(view(1, 4096, 2, 64), RrParams(8, 128, 1.5, 1))[0] == _lib.ATTN_E_INVAL
+    assert ws(view(1, 4096, 2, 64), RrParams(8, 128, 0.9, 2))[0] == _lib.ATTN_E_INVAL         # protect_last
+    assert ws(view(1, 4, 2, 64), RrParams(8, 64, 0.9, 1))[0] == _lib.ATTN_E_INVAL              # L < S
+    assert ws(view(1, 4096 * 64 + 64, 1, 64), RrParams(8, 64, 0.9, 1))[0] == _lib.ATTN_E_UNSUPPORTED  # > 4096 blocks
