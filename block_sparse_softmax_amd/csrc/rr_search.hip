@@ -280,53 +280,45 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p)
 }
 
 // -------------------------------------------------------------- select ----
-// One work-group per (query block m, head, batch).  Eq. 11 keeps the shortest
-// prefix of the row's causal blocks, ordered by descending score (ties: lower
-// n first), whose mass reaches tau times the row's mass.  That prefix is
-// found without sorting.  With F(x) = mass of the scores >= x, the last kept
-// score is theta = the largest x with F(x) >= tau * total; every block above
-// theta is kept and, of the blocks scoring exactly theta, the lowest-n ones
-// until the mass is reached.  Scores are >= 0, so their bit patterns order
-// like their values and theta is a binary search over bit patterns (31
-// steps).  Each F is summed in one fixed order (thread t over its contiguous
-// run of n, then a fixed tree), so F is monotone in x and reproducible.
+// One wave per (query block m, head, batch), four block rows per work-group.
+// Eq. 11 keeps the shortest prefix of the row's causal blocks, ordered by
+// descending score (ties: lower n first), whose mass reaches tau times the
+// row's mass.  That prefix is found without sorting.  With F(x) = mass of the
+// scores >= x, the last kept score is theta = the largest x with
+// F(x) >= tau * total; every block above theta is kept and, of the blocks
+// scoring exactly theta, the lowest-n ones until the mass is reached.  Scores
+// are >= 0, so their bit patterns order like their values and theta is a
+// binary search over bit patterns (31 steps).  Lane l holds the scores of
+// n = l, l + 64, ...; each F is summed in one fixed order (the lane's own
+// scores in n order, then a butterfly over the wave that leaves every lane
+// the same total), so F is monotone in x and reproducible.
+constexpr int kSelRows = kRrThreads / 64;
+// PER: scores per lane (16 for rows of up to 1024 blocks, 64 up to 4096).
+template <int PER>
 __global__ __launch_bounds__(kRrThreads) void rr_select_kernel(const RrParams p) {
-  constexpr int kPerMax = kRrMaxBlocks / kRrThreads;
-  __shared__ float red_f[kRrThreads / 64];
-  __shared__ int red_i[kRrThreads / 64];
-  const int m = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int kPerMax = PER;
+  const int lane = threadIdx.x & 63;
+  const int m = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * kSelRows + (threadIdx.x >> 6));
+  const int h = blockIdx.y, b = blockIdx.z;
+  if (m >= p.nb) return;                      // the whole wave: no work-group barrier in this kernel
   const int nv = m + 1;                       // causal key blocks n <= m
+  const int per = (nv + 63) / 64;
   const int64_t row = (static_cast<int64_t>(b) * p.H + h) * p.nb * p.nb + static_cast<int64_t>(m) * p.nb;
   float* srow = p.score + row;
   uint8_t* brow = p.bmask + row;
-  // thread t owns blocks t * per .. t * per + per - 1
-  const int per = (nv + kRrThreads - 1) / kRrThreads;
-  const int a0 = threadIdx.x * per;
   float v[kPerMax];
 #pragma unroll
   for (int i = 0; i < kPerMax; ++i) {
-    const int n = a0 + i;
+    const int n = lane + 64 * i;
     v[i] = (i < per && n < nv) ? fmaxf(srow[n], 0.f) : 0.f;
   }
-  // work-group sums in a fixed order; every thread gets the result
-  auto block_sum = [&](float x) __attribute__((always_inline)) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    if (lane == 0) red_f[w] = x;
-    __syncthreads();
-    const float t = (red_f[0] + red_f[1]) + (red_f[2] + red_f[3]);
-    __syncthreads();
-    return t;
-  };
   auto mass_from = [&](uint32_t xb) __attribute__((always_inline)) {  // F(x), x given by its bits
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < kPerMax; ++i)
       if (i < per && __float_as_uint(v[i]) >= xb) s += v[i];
-    return block_sum(s);
+    return halves_sum32(group_sum<32>(s));
   };
-  static_assert(kRrThreads == 256, "four waves in the fixed reduction tree");
   const float total = mass_from(0u);
   const float thr = p.tau * total;
   uint32_t theta = 0xFFFFFFFFu;               // no block kept (a row without mass)
@@ -344,33 +336,22 @@ __global__ __launch_bounds__(kRrThreads) void rr_select_kernel(const RrParams p)
     const float q = tv > 0.f ? ceilf((thr - above) / tv) : static_cast<float>(nv);
     need = q >= static_cast<float>(nv) ? nv : max(1, static_cast<int>(q));
   }
-  // rank (in n order) of this thread's first block scoring exactly theta
-  int ties = 0;
-#pragma unroll
-  for (int i = 0; i < kPerMax; ++i)
-    if (i < per && a0 + i < nv && __float_as_uint(v[i]) == theta) ++ties;
-  int x = ties;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) red_i[w] = x;
-  __syncthreads();
-  int rank = x - ties;
-  for (int i = 0; i < w; ++i) rank += red_i[i];
   const bool protect = p.protect_last && m == p.nb - 1;
+  int ties_before = 0;                        // blocks scoring theta at lower n (earlier rounds)
 #pragma unroll
   for (int i = 0; i < kPerMax; ++i) {
-    const int n = a0 + i;
-    if (i < per && n < nv) {
-      const uint32_t vb = __float_as_uint(v[i]);
-      bool keep = theta != 0xFFFFFFFFu && vb > theta;
-      if (theta != 0xFFFFFFFFu && vb == theta) keep = rank++ < need;
-      brow[n] = (keep || protect) ? 1 : 0;
-    }
+    const int n = lane + 64 * i;
+    const uint32_t vb = __float_as_uint(v[i]);
+    const bool tie = theta != 0xFFFFFFFFu && i < per && n < nv && vb == theta;
+    const uint64_t tmask = __builtin_amdgcn_ballot_w64(tie);
+    const int rank = ties_before + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                       static_cast<uint32_t>(tmask >> 32),
+                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(tmask), 0u)));
+    ties_before += __builtin_popcountll(tmask);
+    const bool keep = (theta != 0xFFFFFFFFu && vb > theta) || (tie && rank < need);
+    if (i < per && n < nv) brow[n] = (keep || protect) ? 1 : 0;
   }
-  for (int n = nv + threadIdx.x; n < p.nb; n += kRrThreads) {
+  for (int n = nv + lane; n < p.nb; n += 64) {
     brow[n] = 0;
     srow[n] = 0.f;
   }
@@ -403,9 +384,11 @@ hipError_t launch_rr_search(const RrParams& p, hipStream_t stream, hipEvent_t st
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rr_select_kernel, dim3(static_cast<unsigned>(p.nb), static_cast<unsigned>(p.H),
-                                            static_cast<unsigned>(p.B)),
-                     dim3(kRrThreads), 0, stream, p);
+  const dim3 sgrid(static_cast<unsigned>((p.nb + kSelRows - 1) / kSelRows), static_cast<unsigned>(p.H),
+                   static_cast<unsigned>(p.B));
+  static_assert(kRrMaxBlocks == 64 * 64, "select variants cover up to 4096 blocks");
+  if (p.nb <= 1024) hipLaunchKernelGGL(rr_select_kernel<16>, sgrid, dim3(kRrThreads), 0, stream, p);
+  else hipLaunchKernelGGL(rr_select_kernel<64>, sgrid, dim3(kRrThreads), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (stop != nullptr && (e = hipEventRecord(stop, stream)) != hipSuccess) return e;
   return hipSuccess;
