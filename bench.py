@@ -1,32 +1,43 @@
 """Benchmark of the structured-mask attention forward on one MI355X.
 
-One step = one pass of the whole hot path over the ViT layer at 896 px
-(64 x 64 patch grid flattened row-major: L = 4096 tokens, batch 1, 16 heads,
-head dim 80, bf16): the three masks of that layer -- full attention, 1D chunks
-of 256 tokens and a symmetric sliding window of radius 128 -- on the same
-resident Q, K, V, run as one grouped launch of the HIP kernel (each mask writes
-its own output).  Mask plans are compiled and uploaded before the timed region
-(they are cached per mask).  Each mask is also timed alone, after the timed
-steps, for the per-mask table.
+One step = one pass of the hot path over the 128K-token block-sparse causal
+prefill (L = 131072, batch 1, 32 heads, head dim 128, bf16, block 128; every
+block row keeps the diagonal block, the first block and the top half of the
+remaining causal blocks by a seeded score): one launch of the HIP kernel over
+the plan compiled from the block matrix, on resident Q, K, V.  The plan is
+compiled and uploaded before the timed region.  `--workload` selects another
+workload of the catalogue for the headline (its masks then run as one grouped
+launch per step).
 
 Metric: effective attention TFLOP/s = 4 * d * (unmasked query-key pairs) per
-head, summed over the masks, divided by the step time (2d flops for the score
-and 2d for the value mix per allowed pair; padding, masked pairs inside
-partial tiles and the exponentials are not counted).  Each mask's row also
-gives the computed-tile efficiency (unmasked pairs / pairs inside the listed
-128 x 64 tiles) and the exponentials per second (one per pair of a listed tile).
+head divided by the step time (2d flops for the score and 2d for the value mix
+per allowed pair; padding, masked pairs inside partial tiles and the
+exponentials are not counted), and the same as a fraction of the bf16 dense
+MFMA peak.  Launch durations come from HIP events attached to the kernel's own
+dispatch; the median and minimum of the launches are reported beside the mean.
 
-Extra workloads (skipped with --quick; each warmed up for about 0.2 s of
-launches so the clocks settle, then timed): the 1792-px ViT layer (L = 16384, full
-and sliding window radius 512), causal LM prefill with per-head windows and
-sinks (L = 4096, d = 128) and 128K-token block-sparse causal prefill (32 heads,
-d = 128, block 128, about half of the causal blocks kept), timed the same way
-and reported under "extra", with RRAttention's block-pattern search on the
-128K-token Q and K (stride 8, block 128, tau 0.9), and the backward pass of
-every mask of the 896-px layer and of the per-head-window LM, and one-query
-decode steps over key/value caches (windows of 576 keys with a sink, 572 + 4
-prefix tokens, full attention at 128K; 32 query heads on 8 K/V heads at d = 128
-and 16 on 4 at d = 256), reported in GB/s against HBM.
+Timing protocol of the per-mask figures (headline workload and `extra`): 3
+warm-up launches, then every launch timed alone by its events, with a 512 MiB
+scratch buffer rewritten between launches for every workload whose inputs and
+outputs fit in the 256 MB last-level cache (so no launch starts from a warm
+cache); median and minimum reported.  The 128K-token inputs (4.3 GB) exceed
+that cache by far and run back to back.
+
+CPU baseline: the float64 oracle on 512 seeded query rows per head of the same
+workload (the sampled-row protocol of the largest configs), on as many heads
+as fit in about 20 s of host time, with the BLAS thread count; the full-config
+oracle time is extrapolated from the per-row time and labelled so.
+
+Extra workloads (skipped with --quick): the 896-px ViT layer (L = 4096, d = 80:
+full, chunk 256, window radius 128, one grouped launch), the 1792-px layer
+(L = 16384: full and window radius 512), causal LM prefill with per-head
+windows and sinks (L = 4096, d = 128), RRAttention's block-pattern search on
+the 128K-token Q and K, the token re-permutation, the backward pass of the
+896-px and per-head-window masks, and one-query decode steps over key/value
+caches, reported in GB/s against HBM.
+
+GPU clocks: sampled with amd-smi by a helper process started before this
+process touches the GPU (the helper never does), skipped under a profiler.
 
 Prints ONE JSON line.
 """
@@ -47,7 +58,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+LLC_BYTES = 256 * 2**20       # MI355X last-level (Infinity) cache
+FLUSH_BYTES = 512 * 2**20     # scratch rewritten between launches to evict it
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_softmax_amd", "csrc", "attn_fwd.hip")
+DEFAULT_WORKLOAD = "blocksparse128k"
 
 
 def _kernel_hash() -> str:
@@ -80,33 +94,79 @@ WORKLOADS = {
 }
 
 
-def _roofline(setup, group, total_flops, workload):
-    """Roofline object for the step's kernel: the grouped launch of all masks of the workload."""
-    w = setup["w"]
-    achieved = total_flops / (group["avg_ms"] * 1e-3) / 1e12
-    label = "+".join(group["masks"])
-    return dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                frac=achieved / PEAK_BF16_TFLOPS, traffic=_traffic_from_profile(workload, label),
-                kernel=f"attn_fwd_kernel<{w['D']}> grouped launch ({workload}: {', '.join(group['masks'])})",
-                avg_launch_ms=group["avg_ms"])
+def under_profiler() -> bool:
+    """True when a profiler's tool library is loaded into this process (rocprofv3 exports its settings
+    as ROCPROF* variables): a child started now would inherit it."""
+    return any(k.startswith("ROCPROF") for k in os.environ)
 
 
-def _clocks():
-    """GPU clocks from amd-smi (best effort): mean and range of the graphics-engine clocks and the memory
-    clock in MHz, or None when the tool is unavailable."""
+# The clock sampler: a helper process started before this process touches the GPU.  It never
+# initialises the GPU itself; on each request line it runs amd-smi (its own child) and answers with
+# one JSON line.  So no process that holds the GPU ever starts another program.
+_SAMPLER = r"""
+import json, subprocess, sys
+for line in sys.stdin:
     try:
         r = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True, timeout=20)
         d = json.loads(r.stdout)
         c = (d["gpu_data"] if isinstance(d, dict) else d)[0]["clock"]
         gfx = [float(v["clk"]["value"]) for k, v in c.items() if k.startswith("gfx") and isinstance(v, dict)]
         mem = [float(v["clk"]["value"]) for k, v in c.items() if k.startswith("mem") and isinstance(v, dict)]
-        return dict(gfx_mhz_mean=sum(gfx) / len(gfx) if gfx else None, gfx_mhz_min=min(gfx) if gfx else None,
-                    gfx_mhz_max=max(gfx) if gfx else None, mem_mhz=mem[0] if mem else None)
-    except Exception:  # noqa: BLE001 - informational only
-        return None
+        out = dict(gfx_mhz_mean=sum(gfx) / len(gfx) if gfx else None, gfx_mhz_min=min(gfx) if gfx else None,
+                   gfx_mhz_max=max(gfx) if gfx else None, mem_mhz=mem[0] if mem else None)
+    except Exception:
+        out = None
+    sys.stdout.write(json.dumps(out) + "\n")
+    sys.stdout.flush()
+"""
 
 
-def _clocks_under_load(setup, layout, seconds=1.0):
+class ClockSampler:
+    """GPU clocks from amd-smi through the helper process (best effort; None when unavailable)."""
+
+    def __init__(self, enabled: bool):
+        self.proc = None
+        if enabled and not under_profiler():
+            try:
+                self.proc = subprocess.Popen([sys.executable, "-c", _SAMPLER], stdin=subprocess.PIPE,
+                                             stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+            except OSError:
+                self.proc = None
+
+    def __call__(self):
+        if self.proc is None:
+            return None
+        try:
+            self.proc.stdin.write("sample\n")
+            self.proc.stdin.flush()
+            return json.loads(self.proc.stdout.readline() or "null")
+        except (OSError, ValueError):
+            return None
+
+    def close(self):
+        if self.proc is not None:
+            try:
+                self.proc.stdin.close()
+                self.proc.wait(timeout=30)
+            except Exception:  # noqa: BLE001 - shutting down a best-effort helper
+                self.proc.kill()
+            self.proc = None
+
+
+def calibrate_copy(mib: int, steps: int, device: str) -> dict:
+    """A plain device copy of `mib` MiB, `steps` times: the reference the HBM counters are scaled by."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    if src.is_cuda:
+        torch.cuda.synchronize()
+    return {"calibrate_copy_bytes": n, "copies": steps}
+
+
+def _clocks_under_load(setup, layout, sampler, seconds=1.0):
     """Sample the clocks while about `seconds` of the workload's launches are queued on the GPU."""
     import torch
     from block_sparse_softmax_amd import bind_group
@@ -123,7 +183,7 @@ def _clocks_under_load(setup, layout, seconds=1.0):
     for _ in range(max(1, int(seconds / one))):
         group()
     time.sleep(min(0.3, seconds / 3))
-    c = _clocks()
+    c = sampler()
     torch.cuda.synchronize()
     return c
 
@@ -152,7 +212,10 @@ def _setup(name, device, layout):
         bm, bn, _, kv_tile, _ = pm.plan.tiles()
         masks.append(dict(label=label, mask=mask, pm=pm, pairs=int(pairs), tiles=int(len(kv_tile)), tile_pairs=bm * bn,
                           o=torch.empty_like(dev[0])))
-    return dict(w=w, host=(q, k, v), dev=dev, sink=sink, masks=masks)
+    # bytes a launch of one mask touches: Q, K, V read and O written (bf16)
+    ws_bytes = 4 * w["B"] * w["H"] * w["L"] * w["D"] * 2
+    return dict(w=w, host=(q, k, v), dev=dev, sink=sink, masks=masks, name=name,
+                flush=ws_bytes * len(masks) < LLC_BYTES)
 
 
 def _events(n):
@@ -164,15 +227,33 @@ def _events(n):
     return ev
 
 
-def _time(setup, steps, warmup, layout, warm_s=0.0):
-    """Time `steps` steps.  A step is ONE grouped launch (attn_masked_fwd_group) of every mask of
-    the workload, each mask writing its own output.
+class _Flusher:
+    """Rewrites a 512 MiB scratch buffer (read and write of every byte), evicting the last-level cache
+    and the L2s before the next launch."""
 
-    Launch durations come from HIP events that the launch attaches to the kernel's own dispatch
-    (hipExtLaunchKernel), so nothing is recorded between the kernels of the timed steps; the step
-    time is the host wall clock between two device synchronisations.  After the timed steps each
-    mask is also launched alone (same events) for the per-mask table.
-    """
+    def __init__(self, device):
+        import torch
+        self.buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=device)
+
+    def __call__(self):
+        self.buf.add_(1)
+
+
+def _stats(t):
+    import numpy as np
+    t = np.asarray(t, dtype=np.float64)
+    return dict(avg_ms=float(t.mean()), median_ms=float(np.median(t)), min_ms=float(t.min()), n=int(t.size))
+
+
+def _time(setup, steps, warmup, layout, flusher=None, warm_s=0.0, reps=20):
+    """Time `steps` steps back to back.  A step is ONE grouped launch (attn_masked_fwd_group) of every
+    mask of the workload, each mask writing its own output; the step time is the host wall clock
+    between two device synchronisations, and the launch durations come from HIP events that the
+    launch attaches to its own dispatch (nothing is recorded between the kernels).
+
+    Then the per-launch protocol: each mask alone, `reps` launches each timed by its events; with a
+    flusher (workloads that fit in the last-level cache) the scratch buffer is rewritten before every
+    launch, so every launch starts from cold caches."""
     import torch
     from block_sparse_softmax_amd import bind_group
     q, k, v = setup["dev"]
@@ -184,7 +265,7 @@ def _time(setup, steps, warmup, layout, warm_s=0.0):
                        sinks=[sink] * n, layout=layout, stream=stream)
     for _ in range(warmup):
         group()
-    if warm_s > 0:   # extra workloads: keep launching until the clocks have settled
+    if warm_s > 0:   # keep launching until the clocks have settled
         torch.cuda.synchronize()
         t_w = time.perf_counter()
         while time.perf_counter() - t_w < warm_s:
@@ -198,73 +279,109 @@ def _time(setup, steps, warmup, layout, warm_s=0.0):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_group = [a.elapsed_time(b) for a, b in ev]  # ms
-    # each mask alone (not part of the timed steps)
-    per_mask = []
-    reps = max(3, min(steps, 10))
-    for m in ms:
-        f = m["pm"].bind(q, k, v, m["o"], sink=sink, layout=layout, stream=stream)
-        f()
+
+    def protocol(f):
+        for _ in range(3):
+            f()
         e1 = _events(reps)
         for a, b in e1:
+            if flusher is not None:
+                flusher()
             f(a, b)
         torch.cuda.synchronize()
-        per_mask.append([a.elapsed_time(b) for a, b in e1])
-    return wall, per_group, per_mask
+        return [a.elapsed_time(b) for a, b in e1]
+
+    per_mask = [protocol(m["pm"].bind(q, k, v, m["o"], sink=sink, layout=layout, stream=stream)) for m in ms]
+    grouped_cold = protocol(group) if (flusher is not None and n > 1) else None
+    return wall, per_group, per_mask, grouped_cold
 
 
-def _summarise(setup, wall, per_group, per_mask, steps):
-    import numpy as np
+def _summarise(setup, wall, per_group, per_mask, steps, grouped_cold=None):
     w = setup["w"]
     D = w["D"]
     rows = []
     for m, t in zip(setup["masks"], per_mask):
         flops = 4.0 * D * m["pairs"] * w["B"]
-        avg = float(np.mean(t))
+        st = _stats(t)
+        med = st["median_ms"] * 1e-3
         computed = float(m["tiles"]) * m["tile_pairs"] * w["B"]   # pairs inside listed tiles: one exp each
-        rows.append(dict(mask=m["label"], pairs=m["pairs"], avg_ms=avg, min_ms=float(np.min(t)),
-                         tflops=flops / (avg * 1e-3) / 1e12,
-                         frac_bf16_peak=flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                         alg_gbs=(4 * w["B"] * w["H"] * w["L"] * D * 2) / (avg * 1e-3) / 1e9,
+        rows.append(dict(mask=m["label"], pairs=m["pairs"], **st, cold_caches=setup["flush"],
+                         tflops=flops / med / 1e12, frac_bf16_peak=flops / med / 1e12 / PEAK_BF16_TFLOPS,
+                         alg_gbs=(4 * w["B"] * w["H"] * w["L"] * D * 2) / med / 1e9,
+                         frac_hbm=(4 * w["B"] * w["H"] * w["L"] * D * 2) / med / 1e9 / PEAK_HBM_GBS,
                          listed_tiles=m["tiles"], tile_efficiency=m["pairs"] * w["B"] / computed,
-                         exp_per_s=computed / (avg * 1e-3)))
+                         exp_per_s=computed / med))
     total_flops = sum(4.0 * D * m["pairs"] * w["B"] for m in setup["masks"])
     ms_per_step = wall / steps * 1e3
-    group = dict(avg_ms=float(np.mean(per_group)), min_ms=float(np.min(per_group)),
-                 masks=[m["label"] for m in setup["masks"]])
+    group = dict(**_stats(per_group), masks=[m["label"] for m in setup["masks"]], back_to_back=True)
+    if grouped_cold is not None:
+        group["cold_caches"] = _stats(grouped_cold)
     return rows, total_flops, ms_per_step, group
 
 
-def _cpu_baseline(setup, budget_s=20.0):
-    """The float64 oracle on a bounded sample of query rows of the same workload, on the host cores."""
-    import numpy as np
-    from oracle.attention import attention
+def _roofline(setup, group, total_flops, workload):
+    """Roofline object for the step's kernel (the launch of all masks of the workload): achieved =
+    algorithmic flops / the mean event duration of the timed launches."""
+    w = setup["w"]
+    achieved = total_flops / (group["avg_ms"] * 1e-3) / 1e12
+    label = "+".join(group["masks"])
+    return dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                frac=achieved / PEAK_BF16_TFLOPS, traffic=_traffic_from_profile(workload, label),
+                kernel=f"attn_fwd_kernel<{w['D']}> ({workload}: {', '.join(group['masks'])})",
+                avg_launch_ms=group["avg_ms"], median_launch_ms=group["median_ms"],
+                frac_at_median=total_flops / (group["median_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS)
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
+
+
+def _cpu_baseline(setup, budget_s=20.0, rows_per_head=512):
+    """The float64 oracle on `rows_per_head` seeded query rows per head (the sampled rows of the
+    largest configs), head after head until about `budget_s` of host time, through every mask of the
+    workload.  Reports the useful rate (4 d flops per allowed pair in the evaluated rows), the
+    performed rate (the oracle is dense-then-mask: 4 d L flops per row), the cores, and the
+    full-config time extrapolated from the per-row time."""
+    import numpy as np
+    from block_sparse_softmax_amd import inputs as gen
+    from oracle.attention import attention
     w = setup["w"]
     q, k, v = setup["host"]
-    D, H, L = w["D"], w["H"], w["L"]
-    rng = np.random.default_rng(1234)
-    done_flops, done_s, rows_done = 0.0, 0.0, 0
-    n_per_head = 16
-    while done_s < budget_s * 0.5 and n_per_head <= L:
-        rows = np.sort(np.stack([rng.choice(L, n_per_head, replace=False) for _ in range(H)]), axis=1)
+    D, H, L, B = w["D"], w["H"], w["L"], w["B"]
+    n = min(rows_per_head, L)
+    rows_all = gen.sampled_rows(0, w["cfg"], H, L, n)
+    useful = performed = 0.0
+    done_s, heads = 0.0, 0
+    for h in range(H):
         t0 = time.perf_counter()
-        flops = 0.0
         for m in setup["masks"]:
-            r = attention(q, k, v, m["mask"], sink=w["sink"], rows=rows)
-            flops += 4.0 * D * float(r["pairs"].sum())
-        dt = time.perf_counter() - t0
-        done_flops += flops
-        done_s += dt
-        rows_done += n_per_head * H
-        n_per_head *= 2
-    return dict(value=done_flops / done_s / 1e12, unit="TFLOP/s (effective, unmasked pairs)",
-                cores=int(threads), kind="oracle",
-                sample=f"{rows_done} query rows (random, all {H} heads) through all {len(setup['masks'])} "
-                       f"masks of the {setup['w']['L']}-token workload, float64 numpy, {done_s:.1f} s")
+            mask = dict(m["mask"])
+            if mask.get("kind") == "block":
+                mask["block_mask"] = np.asarray(mask["block_mask"])[h:h + 1]
+            if mask.get("head_left") is not None:
+                mask["head_left"] = np.asarray(mask["head_left"])[h:h + 1]
+            r = attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], mask,
+                          sink=None if w["sink"] is None else w["sink"][h:h + 1], rows=rows_all[h:h + 1],
+                          row_chunk=64)
+            useful += 4.0 * D * float(r["pairs"].sum()) * B
+            performed += 4.0 * D * L * n * B
+        done_s += time.perf_counter() - t0
+        heads += 1
+        if done_s >= budget_s:
+            break
+    rows_done = heads * n
+    full_s = done_s / rows_done * (H * L)
+    return dict(value=useful / done_s / 1e12, unit="TFLOP/s (effective, unmasked pairs)",
+                cores=int(_blas_threads()), kind="oracle",
+                sample=f"{n} seeded query rows per head on {heads} of {H} heads ({rows_done} rows) through "
+                       f"{'every mask' if len(setup['masks']) > 1 else 'the mask'} of the {L}-token workload, "
+                       f"float64 numpy, {done_s:.1f} s",
+                performed_gflops=performed / done_s / 1e9, seconds=done_s,
+                full_config_seconds_extrapolated=full_s)
 
 
 def _bench_rr(q, k, steps, warmup, layout, stride=8, block=128, tau=0.9):
@@ -438,42 +555,54 @@ def _bench_decode(name, device, steps, layout="blhd"):
                               avg_launch_ms=avg))
 
 
-def main():
+def _workload_block(name, device, layout, steps, warmup, flusher, warm_s):
+    """Time one workload of the catalogue (back-to-back steps and the per-launch protocol)."""
+    setup = _setup(name, device, layout)
+    wall, pg, pm, gc = _time(setup, steps, warmup, layout, flusher=flusher if setup["flush"] else None,
+                             warm_s=warm_s)
+    rows, flops, ms, group = _summarise(setup, wall, pg, pm, steps, gc)
+    return setup, rows, flops, ms, group
+
+
+def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layout", default="bhld", choices=["blhd", "bhld"],
                     help="bhld = [B, H, L, D] (each head contiguous), blhd = [B, L, H, D]")
-    ap.add_argument("--quick", action="store_true", help="skip the 16K and 128K extra workloads")
+    ap.add_argument("--quick", action="store_true", help="skip the extra workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", default="vit896")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--only", default=None, help="time only this mask of the workload (profiling)")
     ap.add_argument("--decode-only", action="store_true", help="run only the decode workloads (profiling)")
-    ap.add_argument("--no-clocks", action="store_true", help="do not query amd-smi for the GPU clocks")
+    ap.add_argument("--no-clocks", action="store_true", help="do not sample the GPU clocks")
     ap.add_argument("--decode-layout", default="blhd", choices=["blhd", "bhld"],
                     help="K/V cache layout of the decode workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB mebibytes (counter calibration)")
-    args = ap.parse_args()
+    ap.add_argument("--device", default="cuda:0", help=argparse.SUPPRESS)
+    args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
               "(the kernel shards by head with no exchange; see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
-
-    import torch
-    device = torch.device("cuda:0")
-    clock = (lambda: None) if args.no_clocks else _clocks
-    clocks = dict(idle_before=clock())
     if args.calibrate_copy:
-        n = args.calibrate_copy * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(args.steps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n, "copies": args.steps}))
+        # counter calibration under a profiler: nothing else runs and no other process is started
+        print(json.dumps(calibrate_copy(args.calibrate_copy, args.steps, args.device)))
         return
+
+    sampler = ClockSampler(enabled=not args.no_clocks)   # before anything touches the GPU
+    try:
+        _run(args, sampler)
+    finally:
+        sampler.close()
+
+
+def _run(args, sampler):
+    import torch
+    device = torch.device(args.device)
+    clocks = dict(idle_before=sampler())
     from block_sparse_softmax_amd import load_library
     load_library()
 
@@ -483,43 +612,45 @@ def main():
                           for name in DECODE_WORKLOADS}))
         return
 
+    flusher = _Flusher(device)
     setup = _setup(args.workload, device, args.layout)
     if args.only:
         setup["masks"] = [m for m in setup["masks"] if m["label"] == args.only]
-    wall, per_group, per_mask = _time(setup, args.steps, args.warmup, args.layout)
-    rows, total_flops, ms_per_step, group = _summarise(setup, wall, per_group, per_mask, args.steps)
+    wall, per_group, per_mask, gc = _time(setup, args.steps, args.warmup, args.layout,
+                                          flusher=flusher if setup["flush"] else None)
+    rows, total_flops, ms_per_step, group = _summarise(setup, wall, per_group, per_mask, args.steps, gc)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
-
     roof = _roofline(setup, group, total_flops, args.workload)
+    if args.workload == "blocksparse128k" and not args.no_clocks:
+        c = clocks["under_load_blocksparse128k"] = _clocks_under_load(setup, args.layout, sampler)
+        if c and c.get("gfx_mhz_mean"):
+            # context only: the bf16 peak at the clock the chip sustains under this load
+            pk = PEAK_BF16_TFLOPS * c["gfx_mhz_mean"] / 2400.0
+            roof["peak_at_load_clock"] = pk
+            roof["frac_at_load_clock"] = roof["achieved"] / pk
 
     cpu = None if args.no_cpu_baseline else _cpu_baseline(setup)
 
     extra = {}
     if not args.quick:
-        for name in ("vit1792", "lm_headwin", "blocksparse128k"):
-            del setup
-            torch.cuda.empty_cache()
-            setup = _setup(name, device, args.layout)
-            nst = max(5, args.steps // 2)
-            wl, pg, pm = _time(setup, nst, args.warmup, args.layout, warm_s=0.2)
-            r2, tf2, ms2, g2 = _summarise(setup, wl, pg, pm, nst)
-            extra[name] = dict(workload=WORKLOADS[name], ms_per_step=ms2, tflops=tf2 / (ms2 * 1e-3) / 1e12,
-                               frac_bf16_peak=tf2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, masks=r2,
-                               grouped_launch=g2, roofline=_roofline(setup, g2, tf2, name))
-            if name == "blocksparse128k":
-                if not args.no_clocks:
-                    c = clocks["under_load_blocksparse128k"] = _clocks_under_load(setup, args.layout)
-                    if c and c.get("gfx_mhz_mean"):
-                        # context only: the bf16 peak at the clock the chip sustains under this load
-                        pk = PEAK_BF16_TFLOPS * c["gfx_mhz_mean"] / 2400.0
-                        extra[name]["roofline"]["peak_at_load_clock"] = pk
-                        extra[name]["roofline"]["frac_at_load_clock"] = extra[name]["roofline"]["achieved"] / pk
-                q, k, _ = setup["dev"]
-                extra["rr_search128k"] = _bench_rr(q, k, 5, 1, args.layout)
-            if name == "vit1792":
-                extra["reorder_vit1792"] = _bench_reorder(list(setup["dev"]), 128, 128, 5, args.layout)
+        if args.workload == "blocksparse128k":
+            q, k, _ = setup["dev"]
+            extra["rr_search128k"] = _bench_rr(q, k, 5, 1, args.layout)
+            del q, k
         del setup
         torch.cuda.empty_cache()
+        for name in ("vit896", "vit1792", "lm_headwin", "blocksparse128k"):
+            if name == args.workload:
+                continue
+            s2, r2, tf2, ms2, g2 = _workload_block(name, device, args.layout, max(5, args.steps // 2),
+                                                   args.warmup, flusher, warm_s=0.2)
+            extra[name] = dict(workload=WORKLOADS[name], ms_per_step=ms2, tflops=tf2 / (ms2 * 1e-3) / 1e12,
+                               frac_bf16_peak=tf2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, masks=r2,
+                               grouped_launch=g2, roofline=_roofline(s2, g2, tf2, name))
+            if name == "vit1792":
+                extra["reorder_vit1792"] = _bench_reorder(list(s2["dev"]), 128, 128, 5, args.layout)
+            del s2
+            torch.cuda.empty_cache()
         for name in ("vit896", "lm_headwin"):
             extra[f"backward_{name}"] = _bench_bwd(name, device, 5, args.layout)
         from block_sparse_softmax_amd.inputs import DECODE_WORKLOADS
@@ -546,7 +677,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "extra": extra,
-        "gpu_clocks": dict(clocks, after=clock()),
+        "gpu_clocks": dict(clocks, after=sampler()),
     }
     print(json.dumps(out))
 

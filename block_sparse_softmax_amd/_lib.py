@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_E_INVAL", -2: "ATTN_E_UNSUPPORTED", -3: 
                 -4: "ATTN_E_HIP", -5: "ATTN_E_NOMEM"}
 
 # every symbol the header declares
-EXPORTS = ("attn_masked_fwd", "attn_workspace_bytes", "attn_plan_create", "attn_plan_tiles",
+EXPORTS = ("attn_masked_fwd", "attn_workspace_bytes", "attn_workspace_release", "attn_plan_create", "attn_plan_tiles",
            "attn_plan_pairs", "attn_plan_schedule", "attn_plan_workspace_bytes", "attn_plan_upload",
            "attn_masked_fwd_plan", "attn_masked_fwd_group", "attn_rr_workspace_bytes", "attn_rr_search",
            "attn_reorder_tokens", "attn_masked_fwd_lse", "attn_bwd_workspace_bytes", "attn_bwd_lists",
@@ -87,6 +87,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         sig = {
             "attn_masked_fwd": [P(AttnTensor), P(AttnTensor), P(AttnTensor), P(MaskDesc), vp, P(AttnTensor), P(Launch)],
             "attn_workspace_bytes": [P(MaskDesc), i64, i64, i64, P(sz)],
+            "attn_workspace_release": [vp],
             "attn_plan_create": [P(MaskDesc), i64, i64, i64, P(plan_p)],
             "attn_plan_tiles": [plan_p, P(i32), P(i32), P(i64), P(i64), P(P(i32)), P(P(i32)), P(P(ctypes.c_uint8))],
             "attn_plan_pairs": [plan_p, P(i64), P(i64)],
@@ -281,15 +282,27 @@ def tensor_view(t, layout: str = "blhd") -> AttnTensor:
     return a
 
 
-class PreparedMask:
-    """A plan plus a device workspace holding its uploaded image."""
+def _release(workspace):
+    """Tell the library that a workspace it has seen is about to be freed (its upload record goes)."""
+    if workspace is not None and _lib is not None:
+        _lib.attn_workspace_release(ctypes.c_void_p(workspace.data_ptr()))
 
-    def __init__(self, mask: dict, L: int, H: int, D: int, device):
+
+class PreparedMask:
+    """A plan plus a device workspace holding its uploaded image.  The workspace belongs to the stream
+    it was created for (its partial states are per launch, so launches on other streams need their
+    own PreparedMask)."""
+
+    def __init__(self, mask: dict, L: int, H: int, D: int, device, stream=None):
         import torch
         self.plan = Plan(mask, L, H, D)
-        self.workspace = torch.empty(max(256, self.plan.workspace_bytes()), dtype=torch.uint8, device=device)
-        self.plan.upload(self.workspace)
-        torch.cuda.synchronize(device)
+        stream = torch.cuda.current_stream(device) if stream is None else stream
+        with torch.cuda.stream(stream):
+            self.workspace = torch.empty(max(256, self.plan.workspace_bytes()), dtype=torch.uint8, device=device)
+        self.plan.upload(self.workspace, stream)
+
+    def __del__(self):
+        _release(getattr(self, "workspace", None))
 
     def bind(self, q, k, v, o, sink=None, layout="blhd", stream=None, softmax_scale: float = 0.0):
         """Marshal the arguments once; the returned callable launches with a single C call.
@@ -303,12 +316,7 @@ class PreparedMask:
         ln.workspace = self.workspace.data_ptr()
         ln.workspace_bytes = self.workspace.numel()
         ln.softmax_scale = softmax_scale
-        sp = None
-        if sink is not None:
-            import torch
-            if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() != self.plan.H:
-                raise TypeError("sink must be a float32 CUDA tensor with one entry per head")
-            sp = ctypes.c_void_p(sink.data_ptr())
+        sp = _sink_ptr(sink, self.plan.H)
         args = (self.plan.handle, ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), sp,
                 ctypes.byref(ov), ctypes.byref(ln))
         keep = (qv, kv, vv, ov, ln, q, k, v, o, sink)
@@ -331,12 +339,7 @@ class PreparedMask:
         ln.workspace = self.workspace.data_ptr()
         ln.workspace_bytes = self.workspace.numel()
         ln.softmax_scale = softmax_scale
-        sp = None
-        if sink is not None:
-            import torch
-            if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() != self.plan.H:
-                raise TypeError("sink must be a float32 CUDA tensor with one entry per head")
-            sp = ctypes.c_void_p(sink.data_ptr())
+        sp = _sink_ptr(sink, self.plan.H)
         _check(lib.attn_masked_fwd_plan(self.plan.handle, ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv),
                                         sp, ctypes.byref(ov), ctypes.byref(ln)))
         return o
@@ -346,8 +349,8 @@ def _sink_ptr(sink, H):
     if sink is None:
         return None
     import torch
-    if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() != H:
-        raise TypeError("sink must be a float32 CUDA tensor with one entry per head")
+    if sink.dtype != torch.float32 or not sink.is_cuda or sink.numel() != H or not sink.is_contiguous():
+        raise TypeError("sink must be a contiguous float32 CUDA tensor with one entry per head")
     return ctypes.c_void_p(sink.data_ptr())
 
 
@@ -363,17 +366,21 @@ class PreparedBackward:
     the forward that also writes the row log-sum-exp (attn_masked_fwd_lse) and the backward
     (attn_masked_bwd)."""
 
-    def __init__(self, mask: dict, L: int, H: int, D: int, B: int, kv_heads: int, device):
+    def __init__(self, mask: dict, L: int, H: int, D: int, B: int, kv_heads: int, device, stream=None):
         import torch
         lib = load_library()
         self.plan = Plan(mask, L, H, D)
         self.B, self.kv_heads = B, kv_heads
         nbytes = ctypes.c_size_t()
         _check(lib.attn_bwd_workspace_bytes(self.plan.handle, B, kv_heads, ctypes.byref(nbytes)))
-        self.workspace = torch.empty(max(256, nbytes.value), dtype=torch.uint8, device=device)
+        stream = torch.cuda.current_stream(device) if stream is None else stream
+        with torch.cuda.stream(stream):
+            self.workspace = torch.empty(max(256, nbytes.value), dtype=torch.uint8, device=device)
         _check(lib.attn_bwd_upload(self.plan.handle, kv_heads, ctypes.c_void_p(self.workspace.data_ptr()),
-                                   self.workspace.numel(), _stream_ptr(None, self.workspace)))
-        torch.cuda.synchronize(device)
+                                   self.workspace.numel(), ctypes.c_void_p(stream.cuda_stream)))
+
+    def __del__(self):
+        _release(getattr(self, "workspace", None))
 
     def _launch(self, like, stream, softmax_scale):
         ln = Launch()
@@ -428,12 +435,17 @@ class PreparedBackward:
 _prepared_bwd = {}
 
 
-def prepare_backward(mask: dict, L: int, H: int, D: int, B: int, kv_heads: int, device) -> PreparedBackward:
-    key = (mask_key(mask), L, H, D, B, kv_heads, str(device))
+def prepare_backward(mask: dict, L: int, H: int, D: int, B: int, kv_heads: int, device,
+                     stream=None) -> PreparedBackward:
+    """The PreparedBackward of (mask, L, H, D, B, kv_heads) for `stream` (default: the current stream),
+    cached (its workspace holds per-launch statistics and partial sums, so each stream has its own)."""
+    import torch
+    stream = torch.cuda.current_stream(device) if stream is None else stream
+    key = (mask_key(mask), L, H, D, B, kv_heads, str(device), stream.cuda_stream)
     with _prepared_lock:
         pb = _prepared_bwd.get(key)
         if pb is None:
-            pb = PreparedBackward(mask, L, H, D, B, kv_heads, device)
+            pb = PreparedBackward(mask, L, H, D, B, kv_heads, device, stream)
             _prepared_bwd[key] = pb
         return pb
 
@@ -452,7 +464,8 @@ def masked_fwd_lse(q, k, v, mask: dict, sink=None, layout: str = "blhd", stream=
     import torch
     B, L, H, D = _shape(q, layout)
     kvh = k.shape[2] if layout == "blhd" else k.shape[1]
-    pb = prepare_backward(mask, L, H, D, B, kvh, q.device)
+    stream = torch.cuda.current_stream(q.device) if stream is None else stream
+    pb = prepare_backward(mask, L, H, D, B, kvh, q.device, stream)
     out = torch.empty_like(q)
     lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
     return pb.bind_forward(q, k, v, out, lse, sink=sink, layout=layout, stream=stream,
@@ -466,7 +479,8 @@ def masked_bwd(q, k, v, o, dout, lse, mask: dict, sink=None, layout: str = "blhd
     import torch
     B, L, H, D = _shape(q, layout)
     kvh = k.shape[2] if layout == "blhd" else k.shape[1]
-    pb = prepare_backward(mask, L, H, D, B, kvh, q.device)
+    stream = torch.cuda.current_stream(q.device) if stream is None else stream
+    pb = prepare_backward(mask, L, H, D, B, kvh, q.device, stream)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dsink = None if sink is None else torch.empty(H, dtype=torch.float32, device=q.device)
     return pb.bind_backward(q, k, v, o, dout, lse, dq, dk, dv, sink=sink, dsink=dsink, layout=layout,
@@ -641,12 +655,15 @@ _prepared = {}
 _prepared_lock = threading.Lock()
 
 
-def prepare(mask: dict, L: int, H: int, D: int, device) -> PreparedMask:
-    key = (mask_key(mask), L, H, D, str(device))
+def prepare(mask: dict, L: int, H: int, D: int, device, stream=None) -> PreparedMask:
+    """The PreparedMask of (mask, L, H, D) for `stream` (default: the device's current stream), cached."""
+    import torch
+    stream = torch.cuda.current_stream(device) if stream is None else stream
+    key = (mask_key(mask), L, H, D, str(device), stream.cuda_stream)
     with _prepared_lock:
         pm = _prepared.get(key)
         if pm is None:
-            pm = PreparedMask(mask, L, H, D, device)
+            pm = PreparedMask(mask, L, H, D, device, stream)
             _prepared[key] = pm
         return pm
 
@@ -656,22 +673,43 @@ def masked_fwd(q, k, v, mask: dict, sink=None, out=None, layout: str = "blhd", s
     """O = masked softmax attention of bf16 CUDA tensors q, k, v (see include/bss_attn.h).
 
     layout 'blhd' = [B, L, H, D] (the default) or 'bhld' = [B, H, L, D].
-    The compiled plan and its uploaded workspace are cached per (mask, L, H, D, device).
+    The compiled plan and its uploaded workspace are cached per (mask, L, H, D, device, stream).
     """
     import torch
     if layout == "blhd":
         B, L, H, D = q.shape
     else:
         B, H, L, D = q.shape
-    pm = prepare(mask, L, H, D, q.device)
+    stream = torch.cuda.current_stream(q.device) if stream is None else stream
+    pm = prepare(mask, L, H, D, q.device, stream)
     if out is None:
         out = torch.empty_like(q)
     return pm.launch(q, k, v, out, sink=sink, layout=layout, stream=stream, softmax_scale=softmax_scale)
 
 
+# Workspaces of the one-shot entry point, one per (device, stream), kept for the life of the process:
+# the library records the plan image each holds, so repeated calls with one mask copy nothing.
+_oneshot_ws = {}
+_oneshot_lock = threading.Lock()
+
+
+def _oneshot_workspace(device, stream, nbytes: int):
+    import torch
+    key = (str(device), stream.cuda_stream)
+    with _oneshot_lock:
+        ws = _oneshot_ws.get(key)
+        if ws is None or ws.numel() < nbytes:
+            _release(ws)                  # the old buffer goes back to the allocator (stream-ordered)
+            with torch.cuda.stream(stream):
+                ws = torch.empty(max(256, nbytes), dtype=torch.uint8, device=device)
+            _oneshot_ws[key] = ws
+        return ws
+
+
 def masked_fwd_oneshot(q, k, v, mask: dict, sink=None, out=None, layout: str = "blhd", stream=None,
                        softmax_scale: float = 0.0):
-    """The one-shot C entry point attn_masked_fwd (compile-or-cache, upload, launch per call)."""
+    """The one-shot C entry point attn_masked_fwd (plan from the library's cache; the image is copied
+    into the stream's workspace only when it does not hold it already).  Asynchronous."""
     import torch
     lib = load_library()
     qv, kv, vv = (tensor_view(x, layout) for x in (q, k, v))
@@ -681,15 +719,14 @@ def masked_fwd_oneshot(q, k, v, mask: dict, sink=None, out=None, layout: str = "
     desc, keep = build_desc(mask, qv.H)
     nbytes = ctypes.c_size_t()
     _check(lib.attn_workspace_bytes(ctypes.byref(desc), qv.L, qv.H, qv.D, ctypes.byref(nbytes)))
-    ws = torch.empty(max(256, nbytes.value), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device) if stream is None else stream
+    ws = _oneshot_workspace(q.device, stream, nbytes.value)
     ln = Launch()
-    ln.stream = _stream_ptr(stream, q).value
+    ln.stream = stream.cuda_stream
     ln.workspace = ws.data_ptr()
     ln.workspace_bytes = ws.numel()
     ln.softmax_scale = softmax_scale
-    sp = None if sink is None else ctypes.c_void_p(sink.data_ptr())
-    _check(lib.attn_masked_fwd(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), ctypes.byref(desc), sp,
-                               ctypes.byref(ov), ctypes.byref(ln)))
-    torch.cuda.current_stream(q.device).synchronize()  # keep ws alive until the kernel has run
+    _check(lib.attn_masked_fwd(ctypes.byref(qv), ctypes.byref(kv), ctypes.byref(vv), ctypes.byref(desc),
+                               _sink_ptr(sink, qv.H), ctypes.byref(ov), ctypes.byref(ln)))
     del keep
     return out

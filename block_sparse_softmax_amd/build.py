@@ -56,8 +56,9 @@ def build(verbose: bool = False) -> str:
         [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "decode.hip"), "-o", os.path.join(BUILD, "decode.o")],
         ["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "plan.cpp"), "-o", os.path.join(BUILD, "plan.o")],
         ["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "capi.cpp"), "-o", os.path.join(BUILD, "capi.o")],
+        ["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "plan_cache.cpp"), "-o", os.path.join(BUILD, "plan_cache.o")],
     ]
-    with ThreadPoolExecutor(7) as ex:
+    with ThreadPoolExecutor(8) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:
         for o in outs:
@@ -67,7 +68,7 @@ def build(verbose: bool = False) -> str:
     _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
           os.path.join(BUILD, "attn_fwd.o"), os.path.join(BUILD, "attn_bwd.o"), os.path.join(BUILD, "rr_search.o"), os.path.join(BUILD, "reorder.o"),
           os.path.join(BUILD, "decode.o"), os.path.join(BUILD, "plan.o"),
-          os.path.join(BUILD, "capi.o")])
+          os.path.join(BUILD, "capi.o"), os.path.join(BUILD, "plan_cache.o")])
     os.replace(tmp, LIB)
     return LIB
 

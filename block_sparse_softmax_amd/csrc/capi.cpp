@@ -17,15 +17,18 @@
 #include "bss_attn.h"
 #include "kernels.hpp"
 #include "plan.hpp"
+#include "plan_cache.hpp"
 
 namespace bss {
 
 namespace {
 thread_local std::string g_last_error;
 
-// Compiled plans keyed by descriptor content; entries live until process exit.
-std::mutex g_cache_mu;
-std::unordered_map<uint64_t, std::unique_ptr<attn_plan>> g_cache;
+// Compiled plans of the one-shot entry point, by descriptor content: at most
+// 16 plans and about 2 GiB of host memory, least recently used evicted first.
+PlanCache g_cache(16, size_t(2) << 30);
+// Which plan image each caller workspace holds.
+UploadTags g_tags;
 
 attn_status hip_fail(hipError_t e, const char* what) {
   set_error(std::string(what) + ": " + hipGetErrorString(e));
@@ -178,34 +181,21 @@ attn_status upload(const attn_plan& p, void* workspace, size_t bytes, void* stre
 }
 
 attn_status cached_plan(const attn_mask_desc* mask, int64_t L, int64_t H, int64_t D,
-                        const attn_plan** out) {
+                        std::shared_ptr<const attn_plan>* out) {
   if (!mask) { set_error("mask descriptor is NULL"); return ATTN_E_INVAL; }
-  // Validate pointers needed by the fingerprint before hashing them.
+  // the arrays the content is read from must be there before the cache reads them
   if (mask->kind == ATTN_MASK_BLOCK && (!mask->block_mask || mask->block < 1 ||
                                         (mask->block_mask_heads != 1 && mask->block_mask_heads != H))) {
     set_error("BLOCK descriptor needs block >= 1, block_mask and block_mask_heads in {1, H}");
     return ATTN_E_INVAL;
   }
   if (H < 1 || L < 1) { set_error("L and H must be >= 1"); return ATTN_E_INVAL; }
-  const uint64_t key = fingerprint(mask, L, H, D);
-  std::lock_guard<std::mutex> g(g_cache_mu);
-  auto it = g_cache.find(key);
-  if (it != g_cache.end()) {
-    *out = it->second.get();
-    return ATTN_OK;
-  }
-  attn_plan* p = nullptr;
-  attn_status st = compile_plan(mask, L, H, D, &p);
-  if (st != ATTN_OK) return st;
   try {
-    g_cache.emplace(key, std::unique_ptr<attn_plan>(p));
+    return g_cache.get(mask, L, H, D, out);
   } catch (const std::bad_alloc&) {
-    delete p;
     set_error("host allocation failed for the plan cache");
     return ATTN_E_NOMEM;
   }
-  *out = p;
-  return ATTN_OK;
 }
 
 }  // namespace
@@ -264,7 +254,10 @@ attn_status attn_plan_workspace_bytes(const attn_plan* p, size_t* bytes) {
 attn_status attn_plan_upload(const attn_plan* p, void* workspace, size_t workspace_bytes, void* stream) {
   if (!p) { set_error("plan is NULL"); return ATTN_E_INVAL; }
   try {
-    return upload(*p, workspace, workspace_bytes, stream);
+    g_tags.forget(workspace);
+    attn_status st = upload(*p, workspace, workspace_bytes, stream);
+    if (st == ATTN_OK) g_tags.note(workspace, p->serial, 0);
+    return st;
   } catch (...) {
     set_error("unexpected exception during upload");
     return ATTN_E_NOMEM;
@@ -287,7 +280,7 @@ attn_status attn_workspace_bytes(const attn_mask_desc* mask, int64_t L, int64_t 
                                  size_t* bytes) {
   if (!bytes) { set_error("bytes is NULL"); return ATTN_E_INVAL; }
   try {
-    const attn_plan* p = nullptr;
+    std::shared_ptr<const attn_plan> p;
     attn_status st = cached_plan(mask, L, H, D, &p);
     if (st != ATTN_OK) return st;
     *bytes = p->layout.total;
@@ -304,13 +297,28 @@ attn_status attn_masked_fwd(const attn_tensor* q, const attn_tensor* k, const at
   try {
     if (!q) { set_error("q is NULL"); return ATTN_E_INVAL; }
     if (!launch) { set_error("launch is NULL"); return ATTN_E_INVAL; }
-    const attn_plan* p = nullptr;
+    std::shared_ptr<const attn_plan> p;
     attn_status st = cached_plan(mask, q->L, q->H, q->D, &p);
     if (st != ATTN_OK) return st;
     if ((st = check_tensor(q, "q", q->B, p->L, p->H, p->D)) != ATTN_OK) return st;
-    st = upload(*p, launch->workspace, launch->workspace_bytes, launch->stream);
-    if (st != ATTN_OK) return st;
+    // the image is copied only when the workspace does not hold this plan's already
+    if (!g_tags.holds_forward(launch->workspace, p->serial)) {
+      g_tags.forget(launch->workspace);
+      st = upload(*p, launch->workspace, launch->workspace_bytes, launch->stream);
+      if (st != ATTN_OK) return st;
+      g_tags.note(launch->workspace, p->serial, 0);
+    }
     return launch_with_plan(*p, q, k, v, sink, o, launch);
+  } catch (...) {
+    set_error("unexpected exception");
+    return ATTN_E_NOMEM;
+  }
+}
+
+attn_status attn_workspace_release(const void* workspace) {
+  try {
+    g_tags.forget(workspace);
+    return ATTN_OK;
   } catch (...) {
     set_error("unexpected exception");
     return ATTN_E_NOMEM;
@@ -409,14 +417,10 @@ static attn_status make_bwd(const attn_plan& p, const attn_tensor* q, const attn
     return ATTN_E_WORKSPACE;
   }
   if (!aligned16(launch->workspace)) { set_error("workspace must be 16-byte aligned"); return ATTN_E_INVAL; }
-  {
-    std::lock_guard<std::mutex> lk(p.bwd_mu);
-    auto it = p.bwd_uploads.find(launch->workspace);
-    if (it == p.bwd_uploads.end() || it->second != hkv) {
-      set_error("workspace was not prepared by attn_bwd_upload for this plan and " + std::to_string(hkv) +
-                " K/V heads");
-      return ATTN_E_INVAL;
-    }
+  if (!g_tags.holds_backward(launch->workspace, p.serial, hkv)) {
+    set_error("workspace was not prepared by attn_bwd_upload for this plan and " + std::to_string(hkv) +
+              " K/V heads");
+    return ATTN_E_INVAL;
   }
   // batch 1 runs the forward's split schedule for dQ (pieces of long rows add their dQ sums into the
   // forward's partial slots, merged after the dQ kernel); batch > 1 the unsplit one
@@ -572,6 +576,7 @@ attn_status attn_bwd_upload(const attn_plan* p, int64_t kv_heads, void* workspac
       return ATTN_E_WORKSPACE;
     }
     if (!aligned16(workspace)) { set_error("workspace must be 16-byte aligned"); return ATTN_E_INVAL; }
+    g_tags.forget(workspace);
     if ((st = upload(*p, workspace, workspace_bytes, stream)) != ATTN_OK) return st;
     std::vector<uint8_t> buf(img.bytes);
     write_bwd_image(img, buf.data());
@@ -581,8 +586,7 @@ attn_status attn_bwd_upload(const attn_plan* p, int64_t kv_heads, void* workspac
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (backward image)");
     e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize (backward image)");
-    std::lock_guard<std::mutex> lk(p->bwd_mu);
-    p->bwd_uploads[workspace] = kv_heads;
+    g_tags.note(workspace, p->serial, kv_heads);
     return ATTN_OK;
   } catch (const std::bad_alloc&) {
     set_error("host allocation failed for the backward image");
@@ -673,7 +677,7 @@ static attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const 
   p.kv_group = static_cast<int32_t>(H / k->H);
   *out = p;
   // sampled queries (rows of D bf16), then stride-summed keys (rows of D bf16 + 16 pad bytes)
-  *ws_bytes = static_cast<size_t>(B) * H * ns_pad * (2 * D + (2 * D + 16));
+  *ws_bytes = static_cast<size_t>(B) * H * ns_pad * (2 * D + (4 * D + 16));  // queries, then hi/lo key sums
   return ATTN_OK;
 }
 

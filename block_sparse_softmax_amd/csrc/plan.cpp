@@ -18,6 +18,7 @@
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -32,20 +33,6 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// FNV-1a over bytes.
-struct Hasher {
-  uint64_t h = 1469598103934665603ull;
-  void bytes(const void* p, size_t n) {
-    const uint8_t* b = static_cast<const uint8_t*>(p);
-    for (size_t i = 0; i < n; ++i) {
-      h ^= b[i];
-      h *= 1099511628211ull;
-    }
-  }
-  template <class T>
-  void pod(const T& v) { bytes(&v, sizeof(T)); }
-};
 
 // Allowed interval [lo, hi) of row i for the interval kinds.
 inline void row_interval(const attn_plan& p, int64_t h, int64_t i, int64_t* lo, int64_t* hi) {
@@ -400,28 +387,6 @@ void build_image(attn_plan& p) {
 
 }  // namespace
 
-uint64_t fingerprint(const attn_mask_desc* m, int64_t L, int64_t H, int64_t D) {
-  Hasher hs;
-  hs.pod(L); hs.pod(H); hs.pod(D);
-  hs.pod(m->kind); hs.pod(m->causal); hs.pod(m->prefix);
-  switch (m->kind) {
-    case ATTN_MASK_CHUNK: hs.pod(m->chunk); break;
-    case ATTN_MASK_WINDOW:
-      hs.pod(m->left); hs.pod(m->right);
-      if (m->head_left) hs.bytes(m->head_left, sizeof(int64_t) * H);
-      else hs.pod(int64_t(-1));
-      break;
-    case ATTN_MASK_BLOCK: {
-      hs.pod(m->block); hs.pod(m->block_mask_heads);
-      const int64_t nb = ceil_div(L, m->block);
-      if (m->block_mask) hs.bytes(m->block_mask, static_cast<size_t>(m->block_mask_heads) * nb * nb);
-      break;
-    }
-    default: break;
-  }
-  return hs.h;
-}
-
 attn_status compile_plan(const attn_mask_desc* m, int64_t L, int64_t H, int64_t D, attn_plan** out) {
   if (!out) { set_error("output pointer is NULL"); return ATTN_E_INVAL; }
   attn_status st = validate(m, L, H, D);
@@ -462,7 +427,8 @@ attn_status compile_plan(const attn_mask_desc* m, int64_t L, int64_t H, int64_t 
     }
     schedule(*p);
     build_image(*p);
-    p->fingerprint = fingerprint(m, L, H, D);
+    static std::atomic<uint64_t> next_serial{1};
+    p->serial = next_serial.fetch_add(1);
   } catch (const std::bad_alloc&) {
     delete p;
     set_error("host allocation failed while compiling the plan");

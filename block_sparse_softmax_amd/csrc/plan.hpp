@@ -123,14 +123,13 @@ struct attn_plan {
   std::vector<uint32_t> block_bits;   // [Hb][Nb][ceil(Nb/32)] when not block_aligned
   bss::ImageLayout layout;
 
-  // content fingerprint (cache key)
-  uint64_t fingerprint = 0;
+  // process-wide serial number: names this compilation in the record of
+  // which plan image a workspace holds
+  uint64_t serial = 0;
 
-  // backward images by K/V head count (built on first use) and the K/V head
-  // count each workspace was last uploaded for
+  // backward images by K/V head count (built on first use)
   mutable std::mutex bwd_mu;
   mutable std::map<int64_t, std::unique_ptr<bss::BwdImage>> bwd_images;
-  mutable std::map<const void*, int64_t> bwd_uploads;
 };
 
 namespace bss {
@@ -139,9 +138,6 @@ namespace bss {
 // with the message set.
 attn_status compile_plan(const attn_mask_desc* mask, int64_t L, int64_t H, int64_t D,
                          attn_plan** out);
-
-// Hash of the descriptor content together with (L, H, D).
-uint64_t fingerprint(const attn_mask_desc* mask, int64_t L, int64_t H, int64_t D);
 
 // Serialise the device image into `dst` (layout.bytes long).
 void write_image(const attn_plan& p, uint8_t* dst);

@@ -4,7 +4,12 @@
 //
 //   prep    sampled queries q_P(i,h), P(i,h) = iS + (S - 1 - (h mod S)) (Eq. 6-7),
 //           and stride-summed keys sum_{k=jS}^{(j+1)S-1} k_k (Eq. 8), into
-//           contiguous bf16 rows of the workspace (sums in fp32, rounded once).
+//           contiguous bf16 rows of the workspace.  A stride sum is formed in
+//           fp32 and kept as two bf16 halves, hi = bf16(sum) and
+//           lo = bf16(sum - hi), whose sum is the fp32 sum to about 2^-16
+//           relative: the importance GEMM then runs on the matrix cores with
+//           the key aggregate at fp32 accuracy (hi and lo are two k-ranges of
+//           one product against the same query fragments).
 //   scores  the stride importance I = q . ksum / (S sqrt(d)) (Eq. 8) on
 //           v_mfma_f32_32x32x16_bf16, in two passes over the causal key
 //           strides j <= i: pass 1 keeps each row's running max and sum
@@ -71,9 +76,10 @@ __device__ __forceinline__ float halves_sum32(float v) {
 
 // ---------------------------------------------------------------- prep ----
 // One thread per (batch, head, stride row of the padded table, 8-dim chunk).
-// The stride-summed key rows are 2 D + 16 bytes apart (the last 16 bytes are
-// never written or read): a run of rows is then byte for byte the padded LDS
-// layout of the scores kernel and is copied with LDS-DMA as it is.
+// A stride-summed key row holds hi (D bf16) then lo (D bf16); rows are
+// 4 D + 16 bytes apart (the last 16 bytes are never written or read): a run
+// of rows is then byte for byte the padded LDS layout of the scores kernel
+// and is copied with LDS-DMA as it is.
 __global__ __launch_bounds__(256) void rr_prep_kernel(const RrParams p) {
   const int cpr = p.D / 8;
   const int64_t n = static_cast<int64_t>(p.B) * p.H * p.ns_pad * cpr;
@@ -84,7 +90,7 @@ __global__ __launch_bounds__(256) void rr_prep_kernel(const RrParams p) {
   const int j = static_cast<int>(row % p.ns_pad);
   const int bh = static_cast<int>(row / p.ns_pad);
   const int h = bh % p.H, b = bh / p.H;
-  bf16x8 qo = {}, ko = {};
+  bf16x8 qo = {}, ko = {}, kl = {};
   if (j < p.ns) {
     const int pos = j * p.S + (p.S - 1 - (h % p.S));
     qo = *reinterpret_cast<const bf16x8*>(p.q + b * p.q_sb + static_cast<int64_t>(pos) * p.q_sl + h * p.q_sh + 8 * c);
@@ -96,24 +102,32 @@ __global__ __launch_bounds__(256) void rr_prep_kernel(const RrParams p) {
       for (int e = 0; e < 8; ++e) acc[e] += static_cast<float>(x[e]);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ko[e] = static_cast<__bf16>(acc[e]);
+    for (int e = 0; e < 8; ++e) {
+      ko[e] = static_cast<__bf16>(acc[e]);
+      kl[e] = static_cast<__bf16>(acc[e] - static_cast<float>(ko[e]));  // the difference is exact in fp32
+    }
   }
   *reinterpret_cast<bf16x8*>(p.qs + row * p.D + 8 * c) = qo;
-  *reinterpret_cast<bf16x8*>(p.ks + row * (p.D + 8) + 8 * c) = ko;  // rows of 2 D + 16 bytes
+  uint16_t* kdst = p.ks + row * (2 * p.D + 8);                       // rows of 4 D + 16 bytes
+  *reinterpret_cast<bf16x8*>(kdst + 8 * c) = ko;
+  *reinterpret_cast<bf16x8*>(kdst + p.D + 8 * c) = kl;
 }
 
 // -------------------------------------------------------------- scores ----
 // R = block size / stride (strides per block): 8, 16 or 32.
 template <int D, int R>
 __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p) {
-  constexpr int KS = D / 16;                 // k-steps of the 32x32x16 product
-  constexpr int PITCH = 2 * D + 16;          // row pitch (table and LDS): 16 rows of a fragment read hit distinct banks
-  constexpr int CPR = D / 8;                 // 16-byte pieces per key row
+  constexpr int KS = D / 16;                 // k-steps of the 32x32x16 product per key half (hi, lo)
+  constexpr int PITCH = 4 * D + 16;          // row pitch (table and LDS): 16 rows of a fragment read hit distinct banks
+  constexpr int CPR = D / 8;                 // 16-byte pieces per query row
   constexpr int STAGE = 2 * kChunk;          // key strides per copy stage
   constexpr int SBYTES = STAGE * PITCH;      // bytes of one stage
   constexpr int NI = SBYTES / 1024;          // LDS-DMA wave-instructions per stage (wave w takes w, w + 4, ...)
   constexpr int NW_HI = (NI + 3) / 4, NW_LO = NI / 4;
-  constexpr int NBUF = 3;
+  // stages in LDS: three (two in flight during compute) where two work-groups
+  // still fit per CU, else two (one in flight)
+  constexpr int NBUF = (3 * SBYTES <= 80 * 1024) ? 3 : 2;
+  constexpr int AHEAD = NBUF - 1;            // stages issued ahead of the one computed
   static_assert(SBYTES % 1024 == 0, "a stage is whole 1 KiB copies");
   static_assert(NW_HI < 16, "vmcnt immediate");
   static_assert(R == 8 || R == 16 || R == 32, "strides per block");
@@ -155,22 +169,24 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p)
     }
   };
   // Wait for this wave's copies of stage st when the copies of stage st + 1
-  // (issued after them) may stay in flight; global stores issued in between
-  // only make the wait longer, never shorter.
+  // (issued after them) may stay in flight (three buffers only); global
+  // stores issued in between only make the wait longer, never shorter.
   auto wait_stage = [&](bool next_in_flight) __attribute__((always_inline)) {
     if (!next_in_flight) dev::wait_vmcnt<0>();
     else if (nw == NW_HI) dev::wait_vmcnt<NW_HI>();
     else dev::wait_vmcnt<NW_LO>();
   };
   // I^T tile of chunk c (half `sub` of the stage in buffer buf): lane holds
-  // key strides c*32 + 8g + 4*half + e (register 4g + e)
+  // key strides c*32 + 8g + 4*half + e (register 4g + e).  k-steps 0..KS-1
+  // take the hi halves of the key rows, KS..2KS-1 the lo halves, both against
+  // the same query fragments.
   auto chunk_scores = [&](int buf, int sub) __attribute__((always_inline)) {
     f32x16 acc = {};
     const unsigned char* base = smem + buf * SBYTES + (sub * kChunk + (lane & 31)) * PITCH + half * 16;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int s = 0; s < 2 * KS; ++s) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(base + 32 * s);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s % KS], acc, 0, 0, 0);
     }
     return acc;
   };
@@ -183,11 +199,11 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p)
   float m_row = 0.f, inv_l = 0.f;
   for (int pass = 0; pass < 2; ++pass) {
     issue_stage(0);
-    if (n_stage > 1) issue_stage(1);
+    if (AHEAD > 1 && n_stage > 1) issue_stage(1);
     for (int st = 0; st < n_stage; ++st) {
-      wait_stage(st + 1 < n_stage);
+      wait_stage(AHEAD > 1 && st + 1 < n_stage);
       __syncthreads();                         // stage st everywhere; stage st - 1 no longer read
-      if (st + 2 < n_stage) issue_stage(st + 2);  // into the buffer of stage st - 1
+      if (st + AHEAD < n_stage) issue_stage(st + AHEAD);  // into the buffer of stage st - 1
       const int buf = st % NBUF;
       // both chunks' products first: the softmax work of the first runs
       // beside the MFMAs of the second

@@ -34,8 +34,9 @@
  *   - Launches are asynchronous on the given HIP stream: they enqueue the
  *     kernel and return.  A kernel fault surfaces at the caller's next
  *     synchronisation as a HIP error.  Copying a plan's device image
- *     (attn_plan_upload, and attn_masked_fwd which uploads on every call)
- *     stages it in pageable host memory and synchronises the stream once.
+ *     (attn_plan_upload, attn_bwd_upload, and attn_masked_fwd when the
+ *     workspace does not hold that plan's image yet) stages it in pageable
+ *     host memory and synchronises the stream once.
  *   - Functions return attn_status and never throw or abort.  On a non-OK status
  *     attn_last_error() returns a message (thread-local, valid until the next call
  *     on that thread).
@@ -109,16 +110,28 @@ typedef struct {
 typedef struct attn_plan attn_plan;
 
 /*
- * One-shot forward.  Compiles (or finds in an internal cache keyed by the
- * descriptor's content, L, H and D) the plan for `mask`, copies its device
- * image into launch->workspace and launches the kernel on launch->stream.
+ * One-shot forward.  Finds the plan for `mask` in an internal cache, or
+ * compiles and caches it, makes sure launch->workspace holds its device image
+ * and launches the kernel on launch->stream.
  *   q, k, v : bf16 [B, L, H, D] inputs (same B, L, H, D).
  *   mask    : host descriptor.
  *   sink    : NULL, or device float32 [H] sink logits.
  *   o       : bf16 [B, L, H, D] output (may not alias q, k or v).
- * Required workspace: attn_plan_workspace_bytes of the same plan (query it with
- * attn_workspace_bytes below).  Errors: ATTN_E_INVAL, ATTN_E_UNSUPPORTED,
- * ATTN_E_WORKSPACE, ATTN_E_HIP, ATTN_E_NOMEM.
+ * Plan cache: a lookup hashes the descriptor's content (its fields, the
+ * per-head left reaches and the block matrix, with L, H, D) a machine word at
+ * a time, and a hit also compares that content with the cached entry's copy,
+ * so descriptors that merely share a hash never share a plan.  At most 16
+ * plans and about 2 GiB of host memory are kept, least recently used evicted
+ * first.
+ * Workspace: the library records which plan image each workspace holds (this
+ * call, attn_plan_upload and attn_bwd_upload record their uploads) and copies
+ * the image only when the workspace does not hold this plan's: repeated calls
+ * with the same mask and workspace neither copy nor synchronise.  A caller
+ * that frees the workspace or uses its memory for anything else must call
+ * attn_workspace_release first (or upload another image into it through this
+ * library).  Required size: attn_plan_workspace_bytes of the same plan (query
+ * it with attn_workspace_bytes below).  Errors: ATTN_E_INVAL,
+ * ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP, ATTN_E_NOMEM.
  */
 attn_status attn_masked_fwd(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
                             const attn_mask_desc* mask, const float* sink, attn_tensor* o,
@@ -127,6 +140,15 @@ attn_status attn_masked_fwd(const attn_tensor* q, const attn_tensor* k, const at
 /* Workspace bytes attn_masked_fwd needs for this descriptor and shape. */
 attn_status attn_workspace_bytes(const attn_mask_desc* mask, int64_t L, int64_t H, int64_t D,
                                  size_t* bytes);
+
+/*
+ * Forget whatever plan image `workspace` (a device address passed earlier as
+ * a workspace) holds: the next attn_masked_fwd with it copies the image again,
+ * and attn_masked_bwd refuses it until attn_bwd_upload.  Call it before
+ * freeing that memory or reusing it for other data.  Never fails (an unknown
+ * address is ignored); returns ATTN_OK.
+ */
+attn_status attn_workspace_release(const void* workspace);
 
 /*
  * Mask-descriptor compiler.  Validates `mask` against (L, H, D) and builds, for
@@ -305,8 +327,10 @@ attn_status attn_masked_bwd(const attn_plan* plan, const attn_tensor* q, const a
  *            in descending order (ties: lower n first) whose mass reaches
  *            tau times the row's mass;
  *   Eq. 12   with protect_last, every causal block of the last query block.
- * The stride importance runs on bf16 MFMA (stride sums of the keys rounded
- * to bf16 once) with fp32 accumulation; the selection compares fp32 sums.
+ * The stride importance runs on bf16 MFMA with fp32 accumulation; each stride
+ * sum of the keys is formed in fp32 and carried as a pair of bf16 values
+ * (hi + lo, the fp32 sum to about 2^-16 relative), so the products see the
+ * key aggregate at fp32 accuracy.  The selection compares fp32 sums.
  */
 typedef struct {
   int64_t stride;             /* S >= 1                                                   */

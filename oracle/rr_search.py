@@ -33,10 +33,12 @@ notation, for one (batch, head) at a time:
 Returns the block scores S (float64) and the block matrix B (uint8), both
 [Nb, Nb] with Nb = ceil(L / Bs).
 
-ks_round="bf16" reproduces one rounding that a bf16 matrix-core
-implementation states: each stride sum of keys is formed in float32 (keys
-added in order k_jS, k_jS+1, ...) and rounded once to bfloat16
-(round-to-nearest-even).  Everything else stays float64.
+softmax_range="all" follows Eq. 9 as printed instead: each row's softmax runs
+over every key stride j' = 0 .. floor(L/S) - 1, the block scores of Eq. 10 then
+fill whole rows (key blocks above the diagonal too) and Eq. 11 ranks all of a
+row's blocks.  Kept as an option so the two readings can be compared; the
+block matrix it yields can select blocks above the diagonal, which Eq. 5 rules
+out for the causal attention the search feeds.
 """
 
 from __future__ import annotations
@@ -61,14 +63,23 @@ def stride_importance(q: np.ndarray, k: np.ndarray, S: int, h: int) -> np.ndarra
     return (qs @ ks.T) / (S * np.sqrt(d))
 
 
-def stride_softmax(I: np.ndarray) -> np.ndarray:
-    """Eq. 9 over the causal key strides j <= i (max-subtracted)."""
+def stride_softmax(I: np.ndarray, softmax_range: str = "causal") -> np.ndarray:
+    """Eq. 9 over the causal key strides j <= i (max-subtracted); softmax_range="all": over every j'."""
     ns = I.shape[0]
-    causal = np.tril(np.ones((ns, ns), dtype=bool))
+    causal = _range_mask(ns, ns, np.arange(ns), softmax_range)
     z = np.where(causal, I, -np.inf)
     z = z - z.max(axis=1, keepdims=True)
     e = np.where(causal, np.exp(z), 0.0)
     return e / e.sum(axis=1, keepdims=True)
+
+
+def _range_mask(ns_q: int, ns_k: int, rows, softmax_range: str) -> np.ndarray:
+    """Key strides each row's softmax runs over: j <= i ("causal", the adopted reading) or all."""
+    if softmax_range == "causal":
+        return np.arange(ns_k)[None, :] <= np.asarray(rows)[:, None]
+    if softmax_range == "all":
+        return np.ones((len(rows), ns_k), dtype=bool)
+    raise ValueError(softmax_range)
 
 
 def block_scores(P: np.ndarray, S: int, Bs: int, nb: int, rows=None) -> np.ndarray:
@@ -97,35 +108,22 @@ def top_tau(scores_row: np.ndarray, tau: float) -> np.ndarray:
     return order[: min(k + 1, len(order))]
 
 
-def _round_bf16(x32: np.ndarray) -> np.ndarray:
-    """float32 -> nearest bfloat16 (ties to even), returned as float64."""
-    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32).astype(np.float64)
-
-
-def stride_key_sums(kh: np.ndarray, S: int, ks_round=None) -> np.ndarray:
+def stride_key_sums(kh: np.ndarray, S: int) -> np.ndarray:
     """sum_{k = jS}^{(j+1)S - 1} k_k for every full stride j (Eq. 8's key aggregate)."""
     L, d = kh.shape
     ns = L // S
-    blocks = kh[: ns * S].reshape(ns, S, d)
-    if ks_round is None:
-        return blocks.sum(axis=1)
-    if ks_round != "bf16":
-        raise ValueError(ks_round)
-    acc = np.zeros((ns, d), dtype=np.float32)
-    for s in range(S):                       # in order, float32
-        acc = acc + blocks[:, s].astype(np.float32)
-    return _round_bf16(acc)
+    return kh[: ns * S].reshape(ns, S, d).sum(axis=1)
 
 
 def rr_search(q, k, S: int, Bs: int, tau: float, protect_last: bool = True, b: int = 0, h: int = 0,
-              query_blocks=None, ks_round=None):
+              query_blocks=None, softmax_range: str = "causal"):
     """Block scores and block matrix for (batch b, head h) of bf16 bit arrays (or floats) q, k of
     shape [B, H, L, d].
 
     query_blocks: evaluate only these query blocks (the rows of S and B for other blocks are left
-    zero), for long sequences."""
+    zero), for long sequences.
+    softmax_range: "causal" (Eq. 9 over j' <= i, the adopted reading) or "all" (Eq. 9 as printed,
+    with Eq. 10-11 over the whole row)."""
     if Bs % S != 0:
         raise ValueError("the block size must be a multiple of the stride")
     qh = _as_f64(q[b, h])
@@ -138,18 +136,21 @@ def rr_search(q, k, S: int, Bs: int, tau: float, protect_last: bool = True, b: i
     scores = np.zeros((nb, nb))
     bmat = np.zeros((nb, nb), dtype=np.uint8)
     pos = sample_positions(L, S, h)
-    ks = stride_key_sums(kh, S, ks_round)
+    ks = stride_key_sums(kh, S)
+    causal_rows = softmax_range == "causal"
+    _range_mask(1, 1, [0], softmax_range)                                      # validates the option
     for m in blocks:
         rows = np.arange(m * R, min((m + 1) * R, ns))
         if rows.size:
             I = (qh[pos[rows]] @ ks.T) / (S * np.sqrt(d))                      # Eq. 8
-            causal = np.arange(ns)[None, :] <= rows[:, None]
+            causal = _range_mask(len(rows), ns, rows, softmax_range)
             z = np.where(causal, I, -np.inf)
             z = z - z.max(axis=1, keepdims=True)
             e = np.where(causal, np.exp(z), 0.0)
             P = e / e.sum(axis=1, keepdims=True)                                # Eq. 9
             scores[m] = block_scores(P, S, Bs, nb, rows=rows)[m]                # Eq. 10
-        sel = top_tau(scores[m, : m + 1], tau)                                  # Eq. 11
+        width = m + 1 if causal_rows else nb
+        sel = top_tau(scores[m, :width], tau)                                   # Eq. 11
         bmat[m, sel] = 1
     if protect_last and (nb - 1) in set(blocks.tolist()):
         bmat[nb - 1, :nb] = 1                                                   # Eq. 12

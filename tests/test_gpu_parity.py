@@ -361,3 +361,37 @@ def test_workloads_in_the_bench_launch(name):
         ref = attention(q, k, v, mask, sink=w["sink"], rows=rows)["out"]
         g = got[label] if rows is None else np.stack([got[label][:, h, rows[h]] for h in range(w["H"])], axis=1)
         _compare(g, ref, f"{name}-{label} grouped")
+
+
+def _spread_case(seed, H, L, D, spread_log2):
+    """Q = N(0,1) + 8u and K = N(0,1) + b_j u with b_j uniform, so that a row's logits differ across
+    its keys by about `spread_log2` log2 units (peaky heads), bf16."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    c = np.log2(np.e) / np.sqrt(D)
+    alpha = 8.0
+    b = spread_log2 / (2 * c * alpha)
+    q = rng.standard_normal((1, H, L, D)) + alpha * u
+    k = rng.standard_normal((1, H, L, D)) + rng.uniform(-b, b, (1, H, L, 1)) * u
+    v = rng.standard_normal((1, H, L, D))
+    return tuple(gen.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+
+
+@pytest.mark.parametrize("D", [64, 80, 128])
+@pytest.mark.parametrize("spread", [14.0, 32.0])
+def test_large_logit_spread(D, spread):
+    """Logits of a row spread over 20-40 log2 units across its keys (the key term b_j u gives
+    `spread`, the Gaussian parts about 7 more): the softmax concentrates on a few keys and the
+    kernel's score precision (bf16 operands, fp32 scores) decides the result."""
+    from oracle.attention import bf16_to_f64
+    L, H = 640, 2
+    q, k, v = _spread_case(int(spread) + D, H, L, D, spread)
+    s2 = (bf16_to_f64(q[0, 0]) @ bf16_to_f64(k[0, 0]).T) * (np.log2(np.e) / np.sqrt(D))
+    observed = float(np.median(s2.max(axis=1) - s2.min(axis=1)))
+    assert 18.0 <= observed <= 42.0, observed
+    for mask in (dict(kind="full"), dict(kind="window", left=200, right=0, causal=True)):
+        print(f"[case] spread {spread} D={D} {mask['kind']}", flush=True)
+        got = _run_gpu(q, k, v, mask, layout="bhld")
+        ref = attention(q, k, v, mask)["out"]
+        _compare(got, ref, f"spread{spread:.0f}-D{D}-{mask['kind']}")

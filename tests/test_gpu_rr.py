@@ -1,11 +1,13 @@
 """GPU parity of RRAttention's block-pattern search (attn_rr_search) against the float64 oracle.
 
-Block scores: compared with the oracle that rounds each stride sum of keys to bf16 as the kernel
-states (everything else float64), within a bound from the remaining fp32 arithmetic.  Block matrix:
-a floating-point decision (a sort and a threshold), so each row is checked to be a valid top-tau
-selection of the oracle's scores within that bound (the mass reaches tau, no selected block is
-superfluous, no unselected block is clearly larger), and must equal the oracle's row wherever no
-decision lies within the bound.  The last query block is protected exactly."""
+Block scores: compared with the plain float64 oracle of Eq. 6-10 (stride sums of the keys in
+float64), each within the bound that tests/rr_tolerance.py derives from the kernel's stated
+precision (fp32 stride sums carried as a bf16 hi + lo pair, bf16 products, fp32 accumulation and
+softmax).  Block matrix: a floating-point decision (a sort and a threshold), so each row is checked
+to be a valid top-tau selection of the oracle's scores within the row's summed bound (the mass
+reaches tau, no selected block is superfluous, no unselected block is clearly larger), and must
+equal the oracle's row wherever no decision lies within the bound.  The last query block is
+protected exactly."""
 
 import numpy as np
 import pytest
@@ -14,11 +16,9 @@ import torch
 from block_sparse_softmax_amd import inputs as gen
 from oracle.rr_search import rr_search as rr_oracle
 
-pytestmark = pytest.mark.gpu
+from rr_tolerance import score_tolerance
 
-# |S_gpu - S_oracle| per unit of a row's mass scale (R = strides per block): the scores come from
-# bf16 products accumulated in fp32 and fp32 exponentials / sums, observed below 1e-7 R
-SCORE_TOL = 2e-6
+pytestmark = pytest.mark.gpu
 
 
 def _dev(bits):
@@ -91,16 +91,16 @@ def test_rr_search_parity(ci):
     torch.cuda.synchronize()
     bm, sc = bm.cpu().numpy(), sc.cpu().numpy().astype(np.float64)
     nb = -(-L // Bs)
-    R = Bs // S
     worst, clear_rows, rows = 0.0, 0, 0
     for h in range(H):
-        s_ref, b_ref = rr_oracle(q, k, S, Bs, tau, h=h, ks_round="bf16")
+        s_ref, b_ref = rr_oracle(q, k, S, Bs, tau, h=h)
+        tol = score_tolerance(q, k, S, Bs, h)
         err = np.abs(sc[0, h] - s_ref)
-        worst = max(worst, float(err.max()))
+        worst = max(worst, float((err / np.maximum(tol, 1e-300)).max()))
         assert np.all(np.triu(sc[0, h], 1) == 0) and np.all(np.triu(bm[0, h], 1) == 0)
-        assert err.max() <= SCORE_TOL * R, (h, err.max())
-        eps = 4 * SCORE_TOL * R
+        assert np.all(err <= tol), (h, float((err - tol).max()))
         for m in range(nb - 1):
+            eps = float(tol[m].sum())
             if tau == 1.0:
                 # the whole mass: exactly the blocks with a positive score (here every causal block);
                 # no row has a clear decision in the sense of _check_row, whose band is the threshold
@@ -112,7 +112,8 @@ def test_rr_search_parity(ci):
                 clear_rows += 1
                 assert np.array_equal(bm[0, h, m], b_ref[m]), (h, m)
         assert np.all(bm[0, h, nb - 1] == 1)
-    print(f"[rr] max |dS| = {worst:.2e}; {clear_rows}/{rows} rows with a clear decision, all equal", flush=True)
+    print(f"[rr] max |dS| / bound = {worst:.2e}; {clear_rows}/{rows} rows with a clear decision, all equal",
+          flush=True)
     # every row passed the validity checks; rows of about a thousand blocks hold many scores within the
     # decision band of each other, so fewer of them are clear (about a fifth here, against 95 % at nb <= 64)
     assert clear_rows >= (0.5 if nb <= 64 else 0.15) * rows
@@ -132,16 +133,16 @@ def test_rr_search_128k_sampled_blocks():
     torch.cuda.synchronize()
     nb = L // Bs
     rng = np.random.default_rng(7)
-    R = Bs // S
     for h in (0, 9, 18, 31):
         blocks = np.sort(rng.choice(nb - 1, size=8, replace=False))
-        s_ref, b_ref = rr_oracle(q, k, S, Bs, tau, h=h, query_blocks=blocks, ks_round="bf16")
+        s_ref, b_ref = rr_oracle(q, k, S, Bs, tau, h=h, query_blocks=blocks)
+        tol = score_tolerance(q, k, S, Bs, h, query_blocks=blocks)
         s_gpu = sc[0, h].cpu().numpy().astype(np.float64)
         b_gpu = bm[0, h].cpu().numpy()
         for m in blocks:
-            err = np.abs(s_gpu[m] - s_ref[m]).max()
-            assert err <= SCORE_TOL * R, (h, m, err)
-            if _check_row(b_gpu[m, : m + 1], s_ref[m, : m + 1], tau, 4 * SCORE_TOL * R):
+            err = np.abs(s_gpu[m] - s_ref[m])
+            assert np.all(err <= tol[m]), (h, m, float((err - tol[m]).max()))
+            if _check_row(b_gpu[m, : m + 1], s_ref[m, : m + 1], tau, float(tol[m].sum())):
                 assert np.array_equal(b_gpu[m], b_ref[m]), (h, m)
         assert np.all(b_gpu[nb - 1] == 1)
     print(f"[rr] 128k: density of the selected blocks {bm.float().mean().item() * 2:.3f} of the causal half", flush=True)
@@ -157,10 +158,10 @@ def test_rr_search_grouped_keys():
     bm, sc = rr_search(_dev(q), _dev(k), S, Bs, tau, layout="bhld")
     torch.cuda.synchronize()
     bm, sc = bm.cpu().numpy(), sc.cpu().numpy().astype(np.float64)
-    R = Bs // S
     for h in range(H):
-        s_ref, b_ref = rr_oracle(q, k, S, Bs, tau, h=h, ks_round="bf16")
-        assert np.abs(sc[0, h] - s_ref).max() <= SCORE_TOL * R
+        s_ref, b_ref = rr_oracle(q, k, S, Bs, tau, h=h)
+        tol = score_tolerance(q, k, S, Bs, h)
+        assert np.all(np.abs(sc[0, h] - s_ref) <= tol)
         for m in range(L // Bs - 1):
-            if _check_row(bm[0, h, m, : m + 1], s_ref[m, : m + 1], tau, 4 * SCORE_TOL * R):
+            if _check_row(bm[0, h, m, : m + 1], s_ref[m, : m + 1], tau, float(tol[m].sum())):
                 assert np.array_equal(bm[0, h, m], b_ref[m]), (h, m)

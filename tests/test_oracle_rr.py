@@ -28,8 +28,8 @@ def test_sampling_is_round_robin(S):
     assert seen.tolist() == list(range((L // S) * S))
 
 
-def _brute_pipeline(q, k, S, Bs, h):
-    """Eq. 8-10 with explicit loops (tiny inputs only)."""
+def _brute_pipeline(q, k, S, Bs, h, all_strides=False):
+    """Eq. 8-10 with explicit loops (tiny inputs only); all_strides: Eq. 9 over every key stride."""
     L, d = len(q), len(q[0])
     ns = L // S
     I = [[0.0] * ns for _ in range(ns)]
@@ -43,9 +43,10 @@ def _brute_pipeline(q, k, S, Bs, h):
             I[i][j] = acc / (S * math.sqrt(d))
     P = [[0.0] * ns for _ in range(ns)]
     for i in range(ns):
-        mx = max(I[i][j] for j in range(i + 1))
-        z = sum(math.exp(I[i][j] - mx) for j in range(i + 1))
-        for j in range(i + 1):
+        keys = range(ns) if all_strides else range(i + 1)
+        mx = max(I[i][j] for j in keys)
+        z = sum(math.exp(I[i][j] - mx) for j in keys)
+        for j in keys:
             P[i][j] = math.exp(I[i][j] - mx) / z
     nb = -(-L // Bs)
     B = [[0.0] * nb for _ in range(nb)]
@@ -138,24 +139,60 @@ def test_planted_pattern_is_found():
         assert scores[m, 1] > 0.5 * scores[m].sum()
 
 
-def test_bf16_key_sums_option():
-    """ks_round='bf16': float32 sums in order, then round-to-nearest-even to bfloat16 (checked
-    against torch's conversion); the block scores stay within the rounding's effect of float64."""
-    import torch
-    from oracle.rr_search import stride_key_sums
-    rng = np.random.default_rng(9)
-    k = rng.standard_normal((64, 16)).astype(np.float32).astype(np.float64)
-    got = stride_key_sums(k, 8, "bf16")
-    acc = torch.zeros(8, 16, dtype=torch.float32)
-    kt = torch.from_numpy(k.astype(np.float32)).reshape(8, 8, 16)
-    for s in range(8):
-        acc = acc + kt[:, s]
-    want = acc.to(torch.bfloat16).to(torch.float64).numpy()
-    assert np.array_equal(got, want)
-    exact = stride_key_sums(k, 8)
-    assert np.max(np.abs(got - exact) / np.maximum(np.abs(exact), 1e-30)) <= 2.0 ** -8
-    q = _rand_bits((1, 1, 1024, 32), 11)
-    kk = _rand_bits((1, 1, 1024, 32), 12)
-    s0, _ = rr_search(q, kk, 8, 128, 0.9)
-    s1, _ = rr_search(q, kk, 8, 128, 0.9, ks_round="bf16")
-    assert 0 < np.max(np.abs(s1 - s0)) <= 1e-2
+@pytest.mark.parametrize("L,S,Bs,d,h", [(32, 4, 8, 3, 0), (37, 4, 16, 5, 2), (24, 8, 8, 2, 1)])
+def test_literal_range_against_brute_force(L, S, Bs, d, h):
+    """softmax_range="all" (Eq. 9 as printed: every key stride) against the same loops."""
+    rng = np.random.default_rng(3 * L + S + d)
+    q = rng.standard_normal((L, d))
+    k = rng.standard_normal((L, d))
+    I0, P0, B0 = _brute_pipeline(q.tolist(), k.tolist(), S, Bs, h, all_strides=True)
+    P = stride_softmax(stride_importance(q, k, S, h), "all")
+    np.testing.assert_allclose(P, P0, rtol=0, atol=1e-12)
+    qh = np.zeros((1, h + 1, L, d))
+    kh = np.zeros((1, h + 1, L, d))
+    qh[0, h], kh[0, h] = q, k
+    scores, B = rr_search(qh, kh, S, Bs, 1.0, h=h, protect_last=False, softmax_range="all")
+    np.testing.assert_allclose(scores, B0, rtol=0, atol=1e-12)
+    # tau = 1 over whole rows: every block with mass, above the diagonal too
+    assert np.array_equal(B, (B0 > 0).astype(np.uint8))
+
+
+def test_readings_agree_on_the_last_stride_and_differ_before():
+    """The last sampled stride sees every key stride under both readings, so its row of P is the
+    same; earlier rows differ (the causal reading gives future strides no mass); both readings give
+    each row a total of 1, so block rows hold the number of their sampled strides."""
+    rng = np.random.default_rng(21)
+    L, S, Bs, d = 256, 8, 64, 16
+    q = rng.standard_normal((L, d))
+    k = rng.standard_normal((L, d))
+    I = stride_importance(q, k, S, 0)
+    Pc, Pa = stride_softmax(I), stride_softmax(I, "all")
+    np.testing.assert_allclose(Pc[-1], Pa[-1], rtol=0, atol=1e-15)
+    upper = np.triu_indices(Pc.shape[0], 1)
+    assert np.all(Pc[upper] == 0) and np.all(Pa[upper] > 0)
+    assert np.max(np.abs(Pc[:-1] - Pa[:-1])) > 1e-3
+    np.testing.assert_allclose(Pa.sum(axis=1), 1.0, rtol=1e-13)
+    nb = L // Bs
+    for rng_name in ("causal", "all"):
+        sc, _ = rr_search(q[None, None], k[None, None], S, Bs, 0.9, softmax_range=rng_name)
+        np.testing.assert_allclose(sc.sum(axis=1), Bs // S, rtol=1e-12)
+    with pytest.raises(ValueError):
+        rr_search(q[None, None], k[None, None], S, Bs, 0.9, softmax_range="future")
+
+
+def test_literal_range_selects_a_future_block():
+    """Keys of the last block point along the queries' direction: as printed, Eq. 9 gives every
+    earlier query block its mass there (a block above the diagonal, excluded by Eq. 5 for causal
+    attention); the causal reading cannot."""
+    L, S, Bs, d = 1024, 8, 128, 32
+    rng = np.random.default_rng(6)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = rng.standard_normal((L, d)) + 3.0 * u
+    k = rng.standard_normal((L, d))
+    k[896:1024] += 6.0 * u                                  # key block 7 (the last)
+    _, Ba = rr_search(q[None, None], k[None, None], S, Bs, 0.5, protect_last=False, softmax_range="all")
+    _, Bc = rr_search(q[None, None], k[None, None], S, Bs, 0.5, protect_last=False)
+    for m in range(L // Bs - 1):
+        assert Ba[m, 7] == 1 and Ba[m].sum() == 1, (m, Ba[m])
+        assert Bc[m, 7] == 0 and np.all(np.triu(Bc, 1) == 0)

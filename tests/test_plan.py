@@ -361,7 +361,8 @@ def test_decode_argument_errors_without_gpu(lib):
 
 def test_rr_workspace_and_argument_errors_without_gpu(lib):
     """Pattern-search validation and workspace size on the host.  The workspace holds the sampled queries
-    (rows of d bf16) and then the stride-summed keys (rows of d bf16 plus 16 pad bytes), floor(L / S) rows
+    (rows of d bf16) and then the stride-summed keys (rows of 2 d bf16, the hi and lo halves, plus 16 pad
+    bytes), floor(L / S) rows
     each, padded to a multiple of 128 rows."""
     import ctypes
     from block_sparse_softmax_amd._lib import AttnTensor, RrParams
@@ -377,9 +378,9 @@ def test_rr_workspace_and_argument_errors_without_gpu(lib):
         st = lib.attn_rr_workspace_bytes(ctypes.byref(q), ctypes.byref(prm), ctypes.byref(n))
         return st, n.value
 
-    assert ws(view(1, 131072, 32, 128), RrParams(8, 128, 0.9, 1)) == (0, 32 * 16384 * (256 + 256 + 16))
+    assert ws(view(1, 131072, 32, 128), RrParams(8, 128, 0.9, 1)) == (0, 32 * 16384 * (256 + 512 + 16))
     # 1030 // 4 = 257 strides -> 384 rows
-    assert ws(view(2, 1030, 3, 80), RrParams(4, 128, 0.5, 0)) == (0, 2 * 3 * 384 * (160 + 160 + 16))
+    assert ws(view(2, 1030, 3, 80), RrParams(4, 128, 0.5, 0)) == (0, 2 * 3 * 384 * (160 + 320 + 16))
     assert ws(view(1, 4096, 2, 96), RrParams(8, 128, 0.9, 1))[0] == _lib.ATTN_E_UNSUPPORTED   # head dim
     assert ws(view(1, 4096, 2, 64), RrParams(8, 100, 0.9, 1))[0] == _lib.ATTN_E_INVAL         # Bs % S != 0
     assert ws(view(1, 4096, 2, 64), RrParams(8, 512, 0.9, 1))[0] == _lib.ATTN_E_UNSUPPORTED   # Bs / S = 64
