@@ -14,11 +14,15 @@ the oracle (ks = stride sums, Q = sampled queries, I = Eq. 8, P = Eq. 9):
 * softmax:        with eps_i = max_j E_ij over the row's key strides, every probability moves by a
                   factor in [exp(-2 eps_i), exp(2 eps_i)], so
                   |dS_mn| <= T_mn = sum_{i in m, j in n} P_ij (exp(2 eps_i) - 1)
-* fp32 sums:      the row's denominator and the block sums add at most n_row fp32 terms in sequence:
-                  relative error <= (n_row + 64) u, with n_row = the row's key strides; plus an
-                  absolute 1e-30 R for probabilities that flush to zero.
+* fp32 sums:      the kernel sums a row's probabilities per lane over chunks of 32 key strides (16
+                  terms of a chunk first, then one running addition per chunk) and combines lanes in
+                  a tree, so the longest chain of fp32 additions behind a denominator or a block
+                  score is about n_row / 32 + 40 (n_row = the row's key strides); with the
+                  exponential's and the normalisation's own rounding the relative error is at most
+                  (ceil(n_row / 32) + 64) u; plus an absolute 1e-30 R for probabilities that flush
+                  to zero.
 
-tol_mn = T_mn + (n_row + 64) u S_mn + 1e-30 R.
+tol_mn = T_mn + (ceil(n_row / 32) + 64) u S_mn + 1e-30 R.
 """
 
 from __future__ import annotations
@@ -57,8 +61,8 @@ def score_tolerance(q, k, S: int, Bs: int, h: int, b: int = 0, query_blocks=None
         e = np.where(causal, np.exp(z), 0.0)
         P = e / e.sum(axis=1, keepdims=True)
         eps = np.where(causal, E, 0.0).max(axis=1)
-        n_row = rows + 1
-        W = P * (np.expm1(2 * eps) + (n_row + 64) * U32)[:, None]
+        chain = -(-(rows + 1) // 32) + 64
+        W = P * (np.expm1(2 * eps) + chain * U32)[:, None]
         kb = (np.arange(ns) * S) // Bs
         tol[m] = np.bincount(kb, weights=W.sum(axis=0), minlength=nb)[:nb] + 1e-30 * R
     return tol
