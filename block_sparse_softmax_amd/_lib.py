@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_E_INVAL", -2: "ATTN_E_UNSUPPORTED", -3: 
                 -4: "ATTN_E_HIP", -5: "ATTN_E_NOMEM"}
 
 # every symbol the header declares
-EXPORTS = ("attn_masked_fwd", "attn_workspace_bytes", "attn_workspace_release", "attn_plan_create", "attn_plan_tiles",
+EXPORTS = ("attn_masked_fwd", "attn_masked_fwd_noalloc", "attn_workspace_bytes", "attn_workspace_release", "attn_plan_create", "attn_plan_tiles",
            "attn_plan_pairs", "attn_plan_schedule", "attn_plan_workspace_bytes", "attn_plan_upload",
            "attn_masked_fwd_plan", "attn_masked_fwd_group", "attn_rr_workspace_bytes", "attn_rr_search",
            "attn_reorder_tokens", "attn_masked_fwd_lse", "attn_bwd_workspace_bytes", "attn_bwd_lists",
@@ -88,6 +88,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "attn_masked_fwd": [P(AttnTensor), P(AttnTensor), P(AttnTensor), P(MaskDesc), vp, P(AttnTensor), P(Launch)],
             "attn_workspace_bytes": [P(MaskDesc), i64, i64, i64, P(sz)],
             "attn_workspace_release": [vp],
+            "attn_masked_fwd_noalloc": [P(AttnTensor), P(AttnTensor), P(AttnTensor), P(MaskDesc), vp, P(AttnTensor),
+                                        P(Launch)],
             "attn_plan_create": [P(MaskDesc), i64, i64, i64, P(plan_p)],
             "attn_plan_tiles": [plan_p, P(i32), P(i32), P(i64), P(i64), P(P(i32)), P(P(i32)), P(P(ctypes.c_uint8))],
             "attn_plan_pairs": [plan_p, P(i64), P(i64)],

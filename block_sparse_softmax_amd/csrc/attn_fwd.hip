@@ -39,6 +39,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -982,7 +983,34 @@ hipError_t launch_d(const GroupParams& g, int blocks, int B, hipStream_t stream,
   return hipGetLastError();
 }
 
+// Scratch of the allocation-free forward: the plan image and the partial
+// states of split rows, for callers that cannot allocate device memory.  In
+// host code `scratch` names a host-side stand-in, never the device memory:
+// only the address hipGetSymbolAddress returns (per device) is passed on.
+static __device__ __align__(256) unsigned char scratch[kFwdScratchBytes];
+
 }  // namespace
+
+hipError_t fwd_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with device `dev` current
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = kFwdScratchBytes;
+  return hipSuccess;
+}
 
 hipError_t launch_fwd(const GroupParams& g, int D, int B, hipStream_t stream, hipEvent_t start,
                       hipEvent_t stop) {

@@ -30,6 +30,12 @@ PlanCache g_cache(16, size_t(2) << 30);
 // Which plan image each caller workspace holds.
 UploadTags g_tags;
 
+// Per device: the plan whose image the allocation-free scratch holds (kept
+// alive, so its serial is not reused while it is recorded here).
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+std::shared_ptr<const attn_plan> g_scratch_plan[kScratchDevices];
+
 attn_status hip_fail(hipError_t e, const char* what) {
   set_error(std::string(what) + ": " + hipGetErrorString(e));
   return ATTN_E_HIP;
@@ -309,6 +315,53 @@ attn_status attn_masked_fwd(const attn_tensor* q, const attn_tensor* k, const at
       g_tags.note(launch->workspace, p->serial, 0);
     }
     return launch_with_plan(*p, q, k, v, sink, o, launch);
+  } catch (...) {
+    set_error("unexpected exception");
+    return ATTN_E_NOMEM;
+  }
+}
+
+attn_status attn_masked_fwd_noalloc(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                    const attn_mask_desc* mask, const float* sink, attn_tensor* o,
+                                    const attn_launch* launch) {
+  try {
+    if (!q) { set_error("q is NULL"); return ATTN_E_INVAL; }
+    if (!launch) { set_error("launch is NULL"); return ATTN_E_INVAL; }
+    if (launch->workspace != nullptr || launch->workspace_bytes != 0) {
+      set_error("attn_masked_fwd_noalloc takes no workspace: launch->workspace must be NULL and workspace_bytes 0");
+      return ATTN_E_INVAL;
+    }
+    std::shared_ptr<const attn_plan> p;
+    attn_status st = cached_plan(mask, q->L, q->H, q->D, &p);
+    if (st != ATTN_OK) return st;
+    if ((st = check_tensor(q, "q", q->B, p->L, p->H, p->D)) != ATTN_OK) return st;
+    void* scr = nullptr;
+    size_t scr_bytes = 0;
+    hipError_t e = fwd_scratch(&scr, &scr_bytes);
+    if (e != hipSuccess) return hip_fail(e, "scratch address (hipGetSymbolAddress)");
+    const size_t need = q->B == 1 ? p->layout.total : p->layout.bytes;
+    if (need > scr_bytes) {
+      set_error("this launch needs " + std::to_string(need) + " bytes of scratch (plan image and split-row states); "
+                "attn_masked_fwd_noalloc has " + std::to_string(scr_bytes) +
+                " per GPU: use attn_masked_fwd with a workspace");
+      return ATTN_E_WORKSPACE;
+    }
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kScratchDevices) { set_error("device index out of range"); return ATTN_E_UNSUPPORTED; }
+    {
+      // the image is copied only when this GPU's scratch does not hold it already
+      std::lock_guard<std::mutex> lk(g_scratch_mu);
+      if (!g_scratch_plan[dev] || g_scratch_plan[dev]->serial != p->serial) {
+        g_scratch_plan[dev].reset();
+        if ((st = upload(*p, scr, scr_bytes, launch->stream)) != ATTN_OK) return st;
+        g_scratch_plan[dev] = p;
+      }
+    }
+    attn_launch ln = *launch;
+    ln.workspace = scr;
+    ln.workspace_bytes = scr_bytes;
+    return launch_with_plan(*p, q, k, v, sink, o, &ln);
   } catch (...) {
     set_error("unexpected exception");
     return ATTN_E_NOMEM;

@@ -62,6 +62,13 @@ static_assert(sizeof(GroupParams) <= 4096, "kernel arguments are limited to 4 Ki
 hipError_t launch_fwd(const GroupParams& g, int D, int B, hipStream_t stream, hipEvent_t start,
                       hipEvent_t stop);
 
+// Device scratch of the allocation-free forward (attn_fwd.hip): a file-scope
+// device array of kFwdScratchBytes, one per GPU, alive until the process
+// ends.  Returns its device address on the current device (looked up once per
+// device with hipGetSymbolAddress) and its size.
+constexpr size_t kFwdScratchBytes = size_t(32) << 20;
+hipError_t fwd_scratch(void** ptr, size_t* bytes);
+
 // Backward pass (attn_bwd.hip).
 struct BwdParams {
   const uint16_t* q;

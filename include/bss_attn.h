@@ -142,6 +142,26 @@ attn_status attn_workspace_bytes(const attn_mask_desc* mask, int64_t L, int64_t 
                                  size_t* bytes);
 
 /*
+ * Allocation-free one-shot forward, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same computation, tensors and plan cache as
+ * attn_masked_fwd, but the plan image and the split rows' partial states live
+ * in a static device array of the library (32 MiB, one per GPU, held until
+ * the process ends) instead of a caller workspace: launch->workspace must be
+ * NULL and launch->workspace_bytes 0.  The call allocates no device memory
+ * and calls no allocating library routine.  The image is copied (and the
+ * stream synchronised once) only when the GPU's array does not hold this
+ * plan's image already.  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents: calls that overlap in time on one GPU race
+ * (serialise them, e.g. on one stream).  Errors: as attn_masked_fwd, plus
+ * ATTN_E_WORKSPACE when the launch needs more than the 32 MiB (the message
+ * gives the bytes needed) and ATTN_E_INVAL when a workspace is passed.
+ */
+attn_status attn_masked_fwd_noalloc(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                    const attn_mask_desc* mask, const float* sink, attn_tensor* o,
+                                    const attn_launch* launch);
+
+/*
  * Forget whatever plan image `workspace` (a device address passed earlier as
  * a workspace) holds: the next attn_masked_fwd with it copies the image again,
  * and attn_masked_bwd refuses it until attn_bwd_upload.  Call it before

@@ -180,6 +180,35 @@ void test_oneshot_uploads() {
   attn_workspace_release(ln2.workspace);
 }
 
+void test_noalloc() {
+  const int64_t B = 1, L = 1000, H = 2, D = 128;
+  const attn_mask_desc a = chunk_desc(100), b = chunk_desc(40);
+  attn_tensor q = fake_tensor(0x10000000, B, L, H, D), k = fake_tensor(0x20000000, B, L, H, D),
+              v = fake_tensor(0x30000000, B, L, H, D), o = fake_tensor(0x40000000, B, L, H, D);
+  attn_launch ln{};
+  const size_t m0 = mock::counters.memcpy_calls;
+  CHECK(attn_masked_fwd_noalloc(&q, &k, &v, &a, nullptr, &o, &ln) == ATTN_OK);
+  CHECK(mock::counters.memcpy_calls == m0 + 1);
+  CHECK(reinterpret_cast<uintptr_t>(mock::fwd_launches.back().kv) >= mock::kScratchAddr &&
+        reinterpret_cast<uintptr_t>(mock::fwd_launches.back().kv) < mock::kScratchAddr + bss::kFwdScratchBytes);
+  CHECK(attn_masked_fwd_noalloc(&q, &k, &v, &a, nullptr, &o, &ln) == ATTN_OK);   // the scratch holds it
+  CHECK(mock::counters.memcpy_calls == m0 + 1);
+  CHECK(attn_masked_fwd_noalloc(&q, &k, &v, &b, nullptr, &o, &ln) == ATTN_OK);
+  CHECK(mock::counters.memcpy_calls == m0 + 2);
+  attn_launch with_ws = ln;
+  with_ws.workspace = reinterpret_cast<void*>(0x50000000);
+  with_ws.workspace_bytes = 1 << 20;
+  CHECK(attn_masked_fwd_noalloc(&q, &k, &v, &a, nullptr, &o, &with_ws) == ATTN_E_INVAL);
+  // a plan larger than the scratch is refused before anything is copied
+  const int64_t L2 = 65536, H2 = 16;
+  attn_mask_desc full{};
+  attn_tensor q2 = fake_tensor(0x10000000, 1, L2, H2, 64), k2 = fake_tensor(0x20000000, 1, L2, H2, 64),
+              v2 = fake_tensor(0x30000000, 1, L2, H2, 64), o2 = fake_tensor(0x40000000, 1, L2, H2, 64);
+  CHECK(attn_masked_fwd_noalloc(&q2, &k2, &v2, &full, nullptr, &o2, &ln) == ATTN_E_WORKSPACE);
+  CHECK(std::string(attn_last_error()).find("bytes of scratch") != std::string::npos);
+  CHECK(mock::counters.memcpy_calls == m0 + 2);
+}
+
 void test_backward_records() {
   const int64_t B = 1, L = 640, H = 2, D = 64;
   attn_mask_desc m{};
@@ -274,6 +303,7 @@ int main() {
   test_cache_lru_and_content();
   test_oneshot_uploads();
   test_backward_records();
+  test_noalloc();
   test_images_in_bounds();
   if (g_failures) {
     std::printf("%d check(s) failed\n", g_failures);

@@ -28,6 +28,11 @@ hipError_t hipStreamSynchronize(hipStream_t) {
 
 const char* hipGetErrorString(hipError_t) { return "mock HIP error"; }
 
+hipError_t hipGetDevice(int* dev) {
+  *dev = 0;
+  return hipSuccess;
+}
+
 namespace bss {
 
 hipError_t launch_fwd(const GroupParams& g, int, int, hipStream_t, hipEvent_t, hipEvent_t) {
@@ -42,5 +47,12 @@ hipError_t launch_bwd(const BwdParams&, int, int, hipStream_t, hipEvent_t, hipEv
 hipError_t launch_rr_search(const RrParams&, hipStream_t, hipEvent_t, hipEvent_t) { return hipSuccess; }
 hipError_t launch_reorder(const ReorderParams&, hipStream_t, hipEvent_t, hipEvent_t) { return hipSuccess; }
 hipError_t launch_decode(const DecodeParams&, int, hipStream_t, hipEvent_t, hipEvent_t) { return hipSuccess; }
+
+// the library's static scratch, at a fixed fake device address
+hipError_t fwd_scratch(void** ptr, size_t* bytes) {
+  *ptr = reinterpret_cast<void*>(mock::kScratchAddr);
+  *bytes = kFwdScratchBytes;
+  return hipSuccess;
+}
 
 }  // namespace bss
