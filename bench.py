@@ -327,7 +327,8 @@ def _roofline(setup, group, total_flops, workload):
     label = "+".join(group["masks"])
     return dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                 frac=achieved / PEAK_BF16_TFLOPS, traffic=_traffic_from_profile(workload, label),
-                kernel=f"attn_fwd_kernel<{w['D']}> ({workload}: {', '.join(group['masks'])})",
+                kernel=(("attn_fwd_pp_kernel" if w["D"] == 128 else f"attn_fwd_kernel<{w['D']}>") +
+                        f" ({workload}: {', '.join(group['masks'])})"),
                 avg_launch_ms=group["avg_ms"], median_launch_ms=group["median_ms"],
                 frac_at_median=total_flops / (group["median_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS)
 

@@ -285,9 +285,13 @@ def tensor_view(t, layout: str = "blhd") -> AttnTensor:
 
 
 def _release(workspace):
-    """Tell the library that a workspace it has seen is about to be freed (its upload record goes)."""
-    if workspace is not None and _lib is not None:
-        _lib.attn_workspace_release(ctypes.c_void_p(workspace.data_ptr()))
+    """Tell the library that a workspace it has seen is about to be freed (its upload record goes).
+    Quiet at interpreter exit, when the module's globals may already be gone."""
+    try:
+        if workspace is not None and _lib is not None:
+            _lib.attn_workspace_release(ctypes.c_void_p(workspace.data_ptr()))
+    except (TypeError, AttributeError):
+        pass
 
 
 class PreparedMask:
