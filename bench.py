@@ -582,6 +582,7 @@ def main(argv=None):
                     help="K/V cache layout of the decode workloads")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB mebibytes (counter calibration)")
+    ap.add_argument("--reps", type=int, default=20, help="launches per mask in the per-launch protocol")
     ap.add_argument("--device", default="cuda:0", help=argparse.SUPPRESS)
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -618,7 +619,7 @@ def _run(args, sampler):
     if args.only:
         setup["masks"] = [m for m in setup["masks"] if m["label"] == args.only]
     wall, per_group, per_mask, gc = _time(setup, args.steps, args.warmup, args.layout,
-                                          flusher=flusher if setup["flush"] else None)
+                                          flusher=flusher if setup["flush"] else None, reps=args.reps)
     rows, total_flops, ms_per_step, group = _summarise(setup, wall, per_group, per_mask, args.steps, gc)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
     roof = _roofline(setup, group, total_flops, args.workload)
