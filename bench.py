@@ -60,15 +60,22 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 LLC_BYTES = 256 * 2**20       # MI355X last-level (Infinity) cache
 FLUSH_BYTES = 512 * 2**20     # scratch rewritten between launches to evict it
-KERNEL_SRC = os.path.join(ROOT, "block_sparse_softmax_amd", "csrc", "attn_fwd.hip")
+CSRC = os.path.join(ROOT, "block_sparse_softmax_amd", "csrc")
+# source of each head dim's forward kernel, and the headers every forward kernel includes
+KERNEL_SRC = {64: "attn_fwd.hip", 80: "attn_fwd.hip", 128: "attn_fwd_pp.hip", 256: "attn_fwd_d256.hip"}
+KERNEL_HEADERS = ("fwd_common.hpp", "tile_common.hpp", "kernels.hpp")
 DEFAULT_WORKLOAD = "blocksparse128k"
 
 
-def _kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def _kernel_hash(D: int) -> str:
+    """Hash of the forward kernel's source at head dim D (its file and the shared headers)."""
+    h = hashlib.sha256()
+    for f in (KERNEL_SRC[D], *KERNEL_HEADERS):
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
-def _traffic_from_profile(workload: str, mask: str):
+def _traffic_from_profile(workload: str, mask: str, D: int):
     """HBM bytes per launch from the committed counter summary, if it was taken on this kernel source."""
     path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_{mask}_traffic.txt")
     if not os.path.exists(path):
@@ -76,7 +83,7 @@ def _traffic_from_profile(workload: str, mask: str):
     txt = open(path).read()
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
     b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m or not b or m.group(1) != _kernel_hash():
+    if not m or not b or m.group(1) != _kernel_hash(D):
         return None
     return float(b.group(1))
 
@@ -326,7 +333,7 @@ def _roofline(setup, group, total_flops, workload):
     achieved = total_flops / (group["avg_ms"] * 1e-3) / 1e12
     label = "+".join(group["masks"])
     return dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                frac=achieved / PEAK_BF16_TFLOPS, traffic=_traffic_from_profile(workload, label),
+                frac=achieved / PEAK_BF16_TFLOPS, traffic=_traffic_from_profile(workload, label, w["D"]),
                 kernel=(("attn_fwd_pp_kernel" if w["D"] == 128 else f"attn_fwd_kernel<{w['D']}>") +
                         f" ({workload}: {', '.join(group['masks'])})"),
                 avg_launch_ms=group["avg_ms"], median_launch_ms=group["median_ms"],

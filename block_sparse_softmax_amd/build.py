@@ -32,6 +32,11 @@ HIP_FLAGS = [
     # no packed-FP32 instructions are generated
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# forward kernels: d = 64/80 (attn_fwd.hip, also the split-row merge and the
+# dispatch), d = 128 (attn_fwd_pp.hip), d = 256 (attn_fwd_d256.hip)
+HIP_SOURCES = ["attn_fwd.hip", "attn_fwd_pp.hip", "attn_fwd_d256.hip", "attn_bwd.hip", "rr_search.hip",
+               "reorder.hip", "decode.hip"]
+HOST_SOURCES = ["plan.cpp", "capi.cpp", "plan_cache.cpp"]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
               f"-I{ROCM}/include"]
 
@@ -48,16 +53,10 @@ def build(verbose: bool = False) -> str:
     hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
     os.makedirs(BUILD, exist_ok=True)
     inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
-    jobs = [
-        [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "attn_fwd.hip"), "-o", os.path.join(BUILD, "attn_fwd.o")],
-        [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "attn_bwd.hip"), "-o", os.path.join(BUILD, "attn_bwd.o")],
-        [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "rr_search.hip"), "-o", os.path.join(BUILD, "rr_search.o")],
-        [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "reorder.hip"), "-o", os.path.join(BUILD, "reorder.o")],
-        [hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, "decode.hip"), "-o", os.path.join(BUILD, "decode.o")],
-        ["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "plan.cpp"), "-o", os.path.join(BUILD, "plan.o")],
-        ["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "capi.cpp"), "-o", os.path.join(BUILD, "capi.o")],
-        ["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, "plan_cache.cpp"), "-o", os.path.join(BUILD, "plan_cache.o")],
-    ]
+    objs = [os.path.join(BUILD, os.path.splitext(f)[0] + ".o") for f in HIP_SOURCES + HOST_SOURCES]
+    jobs = [[hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, f), "-o", o] for f, o in zip(HIP_SOURCES, objs)]
+    jobs += [["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, f), "-o", o]
+             for f, o in zip(HOST_SOURCES, objs[len(HIP_SOURCES):])]
     with ThreadPoolExecutor(8) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:
@@ -65,10 +64,7 @@ def build(verbose: bool = False) -> str:
             if o.strip():
                 print(o)
     tmp = LIB + ".tmp"
-    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
-          os.path.join(BUILD, "attn_fwd.o"), os.path.join(BUILD, "attn_bwd.o"), os.path.join(BUILD, "rr_search.o"), os.path.join(BUILD, "reorder.o"),
-          os.path.join(BUILD, "decode.o"), os.path.join(BUILD, "plan.o"),
-          os.path.join(BUILD, "capi.o"), os.path.join(BUILD, "plan_cache.o")])
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
     return LIB
 

@@ -425,6 +425,20 @@ static bool overlaps_any(const void* x, std::initializer_list<const void*> other
   return false;
 }
 
+// Backward requests: the kernels cover head dims 64, 80 and 128.
+static attn_status check_kv_heads(const attn_plan& p, int64_t kv_heads) {
+  if (p.D > 128) {
+    set_error("the backward supports head dims 64, 80 and 128 (plan has " + std::to_string(p.D) + ")");
+    return ATTN_E_UNSUPPORTED;
+  }
+  if (kv_heads < 1 || p.H % kv_heads != 0) {
+    set_error("kv_heads must divide the plan's head count (" + std::to_string(p.H) + ")");
+    return ATTN_E_INVAL;
+  }
+  if (p.H / kv_heads > 127) { set_error("at most 127 query heads per K/V head"); return ATTN_E_UNSUPPORTED; }
+  return ATTN_OK;
+}
+
 // Validate a backward launch and fill its kernel parameters.
 static attn_status make_bwd(const attn_plan& p, const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
                      const attn_tensor* o, const attn_tensor* dout, const float* lse, const float* sink,
@@ -443,7 +457,8 @@ static attn_status make_bwd(const attn_plan& p, const attn_tensor* q, const attn
     return ATTN_E_INVAL;
   }
   if (p.H / hkv > 127) { set_error("at most 127 query heads per K/V head"); return ATTN_E_UNSUPPORTED; }
-  attn_status st;
+  attn_status st = check_kv_heads(p, hkv);
+  if (st != ATTN_OK) return st;
   if ((st = check_tensor(q, "q", B, p.L, p.H, p.D)) != ATTN_OK) return st;
   if ((st = check_tensor(k, "k", B, p.L, hkv, p.D)) != ATTN_OK) return st;
   if ((st = check_tensor(v, "v", B, p.L, hkv, p.D)) != ATTN_OK) return st;
@@ -538,15 +553,6 @@ static attn_status make_bwd(const attn_plan& p, const attn_tensor* q, const attn
   f.q_queue = static_cast<int32_t>(nq_items / 8);
   f.kv_queue = static_cast<int32_t>(nkv_items / 8);
   *out = f;
-  return ATTN_OK;
-}
-
-static attn_status check_kv_heads(const attn_plan& p, int64_t kv_heads) {
-  if (kv_heads < 1 || p.H % kv_heads != 0) {
-    set_error("kv_heads must divide the plan's head count (" + std::to_string(p.H) + ")");
-    return ATTN_E_INVAL;
-  }
-  if (p.H / kv_heads > 127) { set_error("at most 127 query heads per K/V head"); return ATTN_E_UNSUPPORTED; }
   return ATTN_OK;
 }
 

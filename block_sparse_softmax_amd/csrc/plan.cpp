@@ -61,8 +61,8 @@ attn_status validate(const attn_mask_desc* m, int64_t L, int64_t H, int64_t D) {
   if (L < 1 || H < 1) { set_error("L and H must be >= 1"); return ATTN_E_INVAL; }
   if (L > (int64_t(1) << 30)) { set_error("L above 2^30 is not supported"); return ATTN_E_UNSUPPORTED; }
   if (H > 65535) { set_error("H above 65535 is not supported"); return ATTN_E_UNSUPPORTED; }
-  if (D != 64 && D != 80 && D != 128) {
-    set_error("head dim " + std::to_string(D) + " is not supported (64, 80, 128)");
+  if (D != 64 && D != 80 && D != 128 && D != 256) {
+    set_error("head dim " + std::to_string(D) + " is not supported (64, 80, 128, 256)");
     return ATTN_E_UNSUPPORTED;
   }
   if (m->causal != 0 && m->causal != 1) { set_error("causal must be 0 or 1"); return ATTN_E_INVAL; }

@@ -55,10 +55,9 @@ struct Shape {
   // k-step), so the scores come out of the MFMA already shifted.
   static constexpr bool SEEDED = true;
   // d = 64 and 80 software-pipeline the tiles (the VALU work of one tile
-  // runs beside the MFMAs of the next); at d = 128 the second score block
-  // that needs does not fit in 256 VGPRs, so each tile runs QK, softmax, PV
-  // in turn and the second wave on the SIMD provides the overlap.
-  static constexpr bool PIPELINED = D != 128;
+  // runs beside the MFMAs of the next); at d >= 128 the second score block
+  // that needs does not fit the registers, and other kernels take over.
+  static constexpr bool PIPELINED = D < 128;
 };
 
 // Physical 16-byte chunk of logical chunk c in LDS row `row` (an XOR, so its

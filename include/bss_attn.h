@@ -40,7 +40,8 @@
  *   - Functions return attn_status and never throw or abort.  On a non-OK status
  *     attn_last_error() returns a message (thread-local, valid until the next call
  *     on that thread).
- *   - Supported head dims: 64, 80, 128.  Batch B >= 1.  Lq == Lk.  K and V may
+ *   - Supported head dims: 64, 80, 128 and 256 for the forward entry points;
+ *     64, 80, 128 for the backward and the pattern search.  Batch B >= 1.  Lq == Lk.  K and V may
  *     have fewer heads than Q (grouped-query attention, see attn_tensor).
  */
 #ifndef BSS_ATTN_H
@@ -175,7 +176,7 @@ attn_status attn_workspace_release(const void* workspace);
  * every (head, query tile), the ascending list of key tiles that hold at least
  * one allowed pair, each flagged FULL or PARTIAL, plus the work schedule.
  * Errors: ATTN_E_INVAL (bad descriptor; B violating Eq. 5), ATTN_E_UNSUPPORTED
- * (D not in {64, 80, 128}), ATTN_E_NOMEM.  *out is set only on ATTN_OK.
+ * (D not in {64, 80, 128, 256}), ATTN_E_NOMEM.  *out is set only on ATTN_OK.
  */
 attn_status attn_plan_create(const attn_mask_desc* mask, int64_t L, int64_t H, int64_t D,
                              attn_plan** out);
@@ -286,7 +287,8 @@ attn_status attn_masked_fwd_lse(const attn_plan* plan, const attn_tensor* q, con
  * per-row statistics written by every backward launch and, for batch 1, the
  * partial sums of the long query rows and key blocks that the launch splits
  * over several work-groups and merges in a fixed order).  Launches sharing a
- * workspace must not overlap in time.
+ * workspace must not overlap in time.  Plans of head dim 256 are refused with
+ * ATTN_E_UNSUPPORTED by every backward entry point.
  */
 attn_status attn_bwd_workspace_bytes(const attn_plan* plan, int64_t B, int64_t kv_heads, size_t* bytes);
 

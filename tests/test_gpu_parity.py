@@ -70,6 +70,8 @@ SMALL = [
     (dict(kind="window", left=40, right=7), 333, 3, 128, True),
     (dict(kind="window", left=0, right=0, causal=True, head_left=[0, 63, 200, 2000]), 777, 4, 128, True),
     (dict(kind="window", left=0, right=0), 200, 1, 64, False),
+    (dict(kind="full"), 300, 2, 256, True),
+    (dict(kind="chunk", chunk=100), 450, 2, 256, False),
 ]
 
 
@@ -185,7 +187,7 @@ def _offset_case(seed, H, L, D, first_sign):
     return tuple(gen.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
 
 
-@pytest.mark.parametrize("D", [64, 80, 128])
+@pytest.mark.parametrize("D", [64, 80, 128, 256])
 @pytest.mark.parametrize("first_sign", [-1, 1])
 def test_wide_logit_range(D, first_sign):
     """Scores of later tiles far above (-1) or below (+1) those of the first listed tile: the first case
@@ -214,7 +216,7 @@ def _far_below_case(seed, H, L, D):
     return tuple(gen.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
 
 
-@pytest.mark.parametrize("D", [64, 80, 128])
+@pytest.mark.parametrize("D", [64, 80, 128, 256])
 def test_scores_far_below_placeholder_reference(D):
     """Rows whose first listed tile holds none of their keys start from the placeholder reference 0;
     with every score about 2^-200 relative to it the probabilities underflow, and the work-group must
@@ -237,7 +239,7 @@ SPLIT = [
 ]
 
 
-@pytest.mark.parametrize("D", [64, 80, 128])
+@pytest.mark.parametrize("D", [64, 80, 128, 256])
 @pytest.mark.parametrize("ci", range(len(SPLIT)))
 def test_split_rows_merge(D, ci):
     """Long rows split into pieces whose partial states the last piece merges (batch 1)."""
@@ -317,6 +319,11 @@ GQA_PREFIX = [
     (dict(kind="chunk", chunk=256, prefix=16), 900, 4, 2, 64, False, 1),
     (dict(kind="window", left=64, right=64, prefix=100), 1500, 2, 2, 80, False, 1),   # prefix over 2 tiles
     (dict(kind="full", prefix=40), 333, 2, 1, 64, True, 2),                           # prefix inside full: no-op
+    # head dim 256 with 16 query heads on 4 K/V heads (the SWA-vs-linear-attention article's speed-test
+    # layer): its sliding window of 576 keys with a learned sink, and 572 window keys + 4 prefix tokens
+    (dict(kind="window", left=575, right=0, causal=True), 1500, 16, 4, 256, True, 1),
+    (dict(kind="window", left=571, right=0, causal=True, prefix=4), 1500, 16, 4, 256, True, 1),
+    (dict(kind="full", causal=True), 777, 16, 4, 256, False, 2),
 ]
 
 
@@ -332,6 +339,27 @@ def test_grouped_query_heads_and_prefix_tokens(ci):
     got = _run_gpu(q, k, v, mask, sink, layout="bhld")
     ref = attention(q, k, v, mask, sink=sink)["out"]
     _compare(got, ref, f"gqa-prefix{ci}")
+
+
+@pytest.mark.parametrize("mask", [dict(kind="window", left=575, right=0, causal=True),
+                                  dict(kind="window", left=571, right=0, causal=True, prefix=4)],
+                         ids=["swa576-sink", "swa572-prefix4"])
+def test_d256_grouped_query_sampled_rows(mask):
+    """Head dim 256, 16 query heads on 4 K/V heads over 16384 tokens (batch 1): the windows of the
+    SWA-vs-linear-attention article's speed test, with a learned sink; 512 seeded rows per head."""
+    B, H, Hkv, L, D = 1, 16, 4, 16384, 256
+    print(f"[case] d256 gqa sampled {mask}", flush=True)
+    rng = np.random.default_rng(900 + mask.get("prefix", 0))
+    q = gen.f32_to_bf16_bits(rng.standard_normal((B, H, L, D), dtype=np.float32))
+    k = gen.f32_to_bf16_bits(rng.standard_normal((B, Hkv, L, D), dtype=np.float32))
+    v = gen.f32_to_bf16_bits(rng.standard_normal((B, Hkv, L, D), dtype=np.float32))
+    sink = rng.standard_normal(H).astype(np.float32)
+    got = _run_gpu(q, k, v, mask, sink, layout="bhld")
+    rows = np.sort(rng.choice(L, size=(H, 512), replace=True), axis=1)
+    rows[:, :4] = [0, 575, 576, L - 1]          # the first row, both sides of the window edge, the last
+    ref = attention(q, k, v, mask, sink=sink, rows=rows)["out"]
+    sel = np.stack([got[:, h, rows[h]] for h in range(H)], axis=1)
+    _compare(sel, ref, f"d256-sampled-{mask.get('prefix', 0)}")
 
 
 def _grouped_as_bench(w, q, k, v):
@@ -378,7 +406,7 @@ def _spread_case(seed, H, L, D, spread_log2):
     return tuple(gen.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
 
 
-@pytest.mark.parametrize("D", [64, 80, 128])
+@pytest.mark.parametrize("D", [64, 80, 128, 256])
 @pytest.mark.parametrize("spread", [14.0, 32.0])
 def test_large_logit_spread(D, spread):
     """Logits of a row spread over 20-40 log2 units across its keys (the key term b_j u gives

@@ -207,6 +207,8 @@ def test_descriptor_errors(lib):
     assert ok == _lib.ATTN_OK
     st, msg = _status(lib, dict(kind="full"), 64, 1, 96)
     assert st == _lib.ATTN_E_UNSUPPORTED and "96" in msg
+    assert _status(lib, dict(kind="window", left=575, right=0, causal=True, prefix=4), 4096, 16, 256)[0] == \
+        _lib.ATTN_OK
     assert _status(lib, dict(kind="chunk", chunk=0), 64, 1, 64)[0] == _lib.ATTN_E_INVAL
     assert _status(lib, dict(kind="window", left=-1, right=0), 64, 1, 64)[0] == _lib.ATTN_E_INVAL
     assert _status(lib, dict(kind="window", left=0, right=0, head_left=[3, -2]), 64, 2, 64)[0] == _lib.ATTN_E_INVAL
@@ -389,3 +391,17 @@ def test_rr_workspace_and_argument_errors_without_gpu(lib):
     assert ws(view(1, 4096, 2, 64), RrParams(8, 128, 0.9, 2))[0] == _lib.ATTN_E_INVAL         # protect_last
     assert ws(view(1, 4, 2, 64), RrParams(8, 64, 0.9, 1))[0] == _lib.ATTN_E_INVAL              # L < S
     assert ws(view(1, 4096 * 64 + 64, 1, 64), RrParams(8, 64, 0.9, 1))[0] == _lib.ATTN_E_UNSUPPORTED  # > 4096 blocks
+
+
+def test_head_dim_256_is_forward_only(lib):
+    """Plans of head dim 256 compile (the forward runs them); every backward entry point refuses them."""
+    plan = _lib.Plan(dict(kind="window", left=575, right=0, causal=True), 2048, 16, 256)
+    assert plan.workspace_bytes() > 0
+    nbytes = ctypes.c_size_t(0)
+    st = lib.attn_bwd_workspace_bytes(plan.handle, 1, 4, ctypes.byref(nbytes))
+    assert st == _lib.ATTN_E_UNSUPPORTED and "256" in lib.attn_last_error().decode()
+    nb, ne, ni = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    cp, en, it = (ctypes.POINTER(ctypes.c_int32)(), ctypes.POINTER(ctypes.c_int32)(), ctypes.POINTER(ctypes.c_int32)())
+    assert lib.attn_bwd_lists(plan.handle, 4, ctypes.byref(nb), ctypes.byref(cp), ctypes.byref(ne), ctypes.byref(en),
+                              ctypes.byref(ni), ctypes.byref(it)) == _lib.ATTN_E_UNSUPPORTED
+    assert lib.attn_bwd_upload(plan.handle, 4, None, 0, None) == _lib.ATTN_E_UNSUPPORTED
