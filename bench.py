@@ -98,6 +98,8 @@ WORKLOADS = {
                   "{512, 1024, 2048, 4096} and a sink logit per head",
     "blocksparse128k": "Block-sparse causal prefill: L=131072, batch 1, 32 heads, head dim 128; block 128, "
                        "diagonal + first block + top half of the remaining causal blocks per block row",
+    "swa576_d256": "Sliding-window causal prefill: L=131072, batch 1, 16 query heads on 4 K/V heads, head dim "
+                   "256; window of 576 keys and a sink logit per head",
 }
 
 
@@ -173,6 +175,137 @@ def calibrate_copy(mib: int, steps: int, device: str) -> dict:
     return {"calibrate_copy_bytes": n, "copies": steps}
 
 
+def _kernel_name(D: int) -> str:
+    return {128: "attn_fwd_pp_kernel", 256: "attn_fwd_d256_kernel"}.get(D, f"attn_fwd_kernel<{D}")
+
+
+def _counter_values(run_dir: str, counter: str, kernel: str):
+    """Per-dispatch values of `counter` for kernels whose name contains `kernel`, from the
+    counter_collection.csv files rocprofv3 wrote under run_dir."""
+    import csv
+    import glob
+    vals = []
+    for path in sorted(glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]:
+                    vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} values for {kernel} under {run_dir}")
+    return vals
+
+
+def traffic_summary(workload: str, pmc_dir: str, copy_mib: int = 1024, out_dir: str | None = None) -> str:
+    """Write profiles/attn_fwd_<workload>_<mask>_traffic.txt from four rocprofv3 counter passes under
+    pmc_dir (FETCH_SIZE and WRITE_SIZE of the workload's launches and of a plain copy of copy_mib MiB,
+    each scaled so that the copy reads as its known size).  Single-mask workloads only."""
+    import statistics
+    from block_sparse_softmax_amd import inputs as gen
+    w = gen.workload(workload)
+    if len(w["masks"]) != 1:
+        raise SystemExit("traffic summaries cover single-mask workloads")
+    label = next(iter(w["masks"]))
+    kern = _kernel_name(w["D"])
+    run = (f"python3 bench.py --workload {workload} --quick --no-cpu-baseline --no-clocks --steps 3 --warmup 1 "
+           "--reps 3")
+    copy = f"python3 bench.py --calibrate-copy {copy_mib} --steps 3"
+    kib = copy_mib * 1024.0
+    fc = statistics.median(_counter_values(os.path.join(pmc_dir, "FETCH_SIZE_copy"), "FETCH_SIZE", "copyBuffer"))
+    wc = statistics.median(_counter_values(os.path.join(pmc_dir, "WRITE_SIZE_copy"), "WRITE_SIZE", "copyBuffer"))
+    fs, ws = kib / fc, kib / wc
+    fv = _counter_values(os.path.join(pmc_dir, f"FETCH_SIZE_{workload}"), "FETCH_SIZE", kern)
+    wv = _counter_values(os.path.join(pmc_dir, f"WRITE_SIZE_{workload}"), "WRITE_SIZE", kern)
+    f, wr = statistics.median(fv), statistics.median(wv)
+    hbm = (f * fs + wr * ws) * 1024
+    alg = _io_bytes(w)
+    cmds = "\n".join(
+        f"rocprofv3 --pmc {c} --output-format csv -d {pmc_dir}/{c}_{tag} -o run -- {cmd}"
+        for tag, cmd in ((workload, run), ("copy", copy)) for c in ("FETCH_SIZE", "WRITE_SIZE"))
+    txt = f"""# {kern}, {workload} launch ({label}) — HBM traffic per launch
+
+Commands (from the repository root, one MI355X; each counter in its own pass), then
+`python3 bench.py --traffic-summary {pmc_dir} --workload {workload}`:
+
+```
+{cmds}
+```
+
+kernel_source_sha256_16: {_kernel_hash(w["D"])}
+
+Calibration with a plain {copy_mib} MiB device copy ({kib:,.0f} KiB read and written):
+
+- FETCH_SIZE reads {fc:.1f} KiB per copy -> scale {fs:.4f}
+- WRITE_SIZE reads {wc:.1f} KiB per copy -> scale {ws:.4f}
+
+Launches of the run (median of {len(fv)}):
+
+- FETCH_SIZE {f:.1f} KiB raw -> {f * 1024 * fs / 1e6:.2f} MB
+- WRITE_SIZE {wr:.1f} KiB raw -> {wr * 1024 * ws / 1e6:.2f} MB
+
+hbm_bytes_per_launch: {hbm:.0f}
+algorithmic_bytes_per_launch: {alg}  (Q, K, V read once and O written once, bf16)
+ratio: {hbm / alg:.3f}
+"""
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"attn_fwd_{workload}_{label}_traffic.txt")
+    with open(path, "w") as fh:
+        fh.write(txt)
+    return path
+
+
+def trace_summary(workload: str, trace_dir: str, out_dir: str | None = None) -> str:
+    """Write profiles/<kernel>_<workload>_stats.md from a rocprofv3 --kernel-trace --stats run of
+    this workload under trace_dir (the command below): the forward kernel's calls and durations,
+    and the throughput at the average duration."""
+    import csv
+    import glob
+    import statistics
+    from block_sparse_softmax_amd import inputs as gen
+    from block_sparse_softmax_amd._lib import Plan
+    w = gen.workload(workload)
+    kern = _kernel_name(w["D"])
+    durs, name = [], None
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if kern in r["Kernel_Name"]:
+                    name = name or r["Kernel_Name"]
+                    durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+    if not durs:
+        raise SystemExit(f"no {kern} dispatches under {trace_dir}")
+    pairs = sum(int(Plan(m, w["L"], w["H"], w["D"]).pairs()[1]) for m in w["masks"].values())
+    flops = 4.0 * w["D"] * pairs * w["B"]
+    avg, med = statistics.mean(durs), statistics.median(durs)
+    tf = flops / (avg * 1e-3) / 1e12
+    cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o run -- python3 bench.py "
+           f"--workload {workload} --quick --no-cpu-baseline --no-clocks --steps 10 --warmup 2 --reps 10")
+    txt = f"""# {kern}, {workload} — kernel trace
+
+{WORKLOADS[workload]}.
+
+Command (from the repository root, one MI355X), then
+`python3 bench.py --trace-summary {trace_dir} --workload {workload}`:
+
+```
+{cmd}
+```
+
+kernel_source_sha256_16: {_kernel_hash(w["D"])}
+
+| kernel | calls | average | median | min | max |
+|---|---|---|---|---|---|
+| {name} | {len(durs)} | {avg:.3f} ms | {med:.3f} ms | {min(durs):.3f} ms | {max(durs):.3f} ms |
+
+Effective throughput at the average duration: {flops / 1e12:.3f} TFLOP (4 d per allowed pair) / {avg:.3f} ms =
+{tf:.1f} TFLOP/s = {tf / PEAK_BF16_TFLOPS:.3f} of the {PEAK_BF16_TFLOPS} TFLOP/s bf16 peak.  The calls are the
+warm-up, timed and per-launch-protocol launches of the command (the last with a cache flush between
+launches when the working set fits the last-level cache).
+"""
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"{kern}_{workload}_stats.md")
+    with open(path, "w") as fh:
+        fh.write(txt)
+    return path
+
+
 def _clocks_under_load(setup, layout, sampler, seconds=1.0):
     """Sample the clocks while about `seconds` of the workload's launches are queued on the GPU."""
     import torch
@@ -209,7 +342,7 @@ def _setup(name, device, layout):
     from block_sparse_softmax_amd import inputs as gen
     from block_sparse_softmax_amd import prepare
     w = gen.workload(name)
-    q, k, v = gen.qkv_bf16(0, w["cfg"], w["B"], w["H"], w["L"], w["D"])
+    q, k, v = gen.qkv_bf16(0, w["cfg"], w["B"], w["H"], w["L"], w["D"], w["Hkv"])
     dev = [_bits_to_dev(x, device, layout) for x in (q, k, v)]
     sink = None if w["sink"] is None else torch.from_numpy(w["sink"]).to(device)
     masks = []
@@ -220,9 +353,14 @@ def _setup(name, device, layout):
         masks.append(dict(label=label, mask=mask, pm=pm, pairs=int(pairs), tiles=int(len(kv_tile)), tile_pairs=bm * bn,
                           o=torch.empty_like(dev[0])))
     # bytes a launch of one mask touches: Q, K, V read and O written (bf16)
-    ws_bytes = 4 * w["B"] * w["H"] * w["L"] * w["D"] * 2
+    ws_bytes = _io_bytes(w)
     return dict(w=w, host=(q, k, v), dev=dev, sink=sink, masks=masks, name=name,
                 flush=ws_bytes * len(masks) < LLC_BYTES)
+
+
+def _io_bytes(w) -> int:
+    """Algorithmic bytes of one launch: Q, K, V read once and O written once (bf16)."""
+    return 2 * w["B"] * w["L"] * w["D"] * (2 * w["H"] + 2 * w["Hkv"])
 
 
 def _events(n):
@@ -314,8 +452,8 @@ def _summarise(setup, wall, per_group, per_mask, steps, grouped_cold=None):
         computed = float(m["tiles"]) * m["tile_pairs"] * w["B"]   # pairs inside listed tiles: one exp each
         rows.append(dict(mask=m["label"], pairs=m["pairs"], **st, cold_caches=setup["flush"],
                          tflops=flops / med / 1e12, frac_bf16_peak=flops / med / 1e12 / PEAK_BF16_TFLOPS,
-                         alg_gbs=(4 * w["B"] * w["H"] * w["L"] * D * 2) / med / 1e9,
-                         frac_hbm=(4 * w["B"] * w["H"] * w["L"] * D * 2) / med / 1e9 / PEAK_HBM_GBS,
+                         alg_gbs=_io_bytes(w) / med / 1e9,
+                         frac_hbm=_io_bytes(w) / med / 1e9 / PEAK_HBM_GBS,
                          listed_tiles=m["tiles"], tile_efficiency=m["pairs"] * w["B"] / computed,
                          exp_per_s=computed / med))
     total_flops = sum(4.0 * D * m["pairs"] * w["B"] for m in setup["masks"])
@@ -334,7 +472,7 @@ def _roofline(setup, group, total_flops, workload):
     label = "+".join(group["masks"])
     return dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                 frac=achieved / PEAK_BF16_TFLOPS, traffic=_traffic_from_profile(workload, label, w["D"]),
-                kernel=(("attn_fwd_pp_kernel" if w["D"] == 128 else f"attn_fwd_kernel<{w['D']}>") +
+                kernel=(_kernel_name(w["D"]) + (">" if w["D"] < 128 else "") +
                         f" ({workload}: {', '.join(group['masks'])})"),
                 avg_launch_ms=group["avg_ms"], median_launch_ms=group["median_ms"],
                 frac_at_median=total_flops / (group["median_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS)
@@ -372,7 +510,8 @@ def _cpu_baseline(setup, budget_s=20.0, rows_per_head=512):
                 mask["block_mask"] = np.asarray(mask["block_mask"])[h:h + 1]
             if mask.get("head_left") is not None:
                 mask["head_left"] = np.asarray(mask["head_left"])[h:h + 1]
-            r = attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], mask,
+            hk = h // (H // w["Hkv"])          # the K/V head of query head h
+            r = attention(q[:, h:h + 1], k[:, hk:hk + 1], v[:, hk:hk + 1], mask,
                           sink=None if w["sink"] is None else w["sink"][h:h + 1], rows=rows_all[h:h + 1],
                           row_chunk=64)
             useful += 4.0 * D * float(r["pairs"].sum()) * B
@@ -590,12 +729,22 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB mebibytes (counter calibration)")
     ap.add_argument("--reps", type=int, default=20, help="launches per mask in the per-launch protocol")
+    ap.add_argument("--trace-summary", default=None, metavar="DIR",
+                    help="summarise a rocprofv3 kernel trace of the workload under DIR into profiles/ (no GPU)")
+    ap.add_argument("--traffic-summary", default=None, metavar="DIR",
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE passes under DIR into profiles/ (no GPU)")
     ap.add_argument("--device", default="cuda:0", help=argparse.SUPPRESS)
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
               "(the kernel shards by head with no exchange; see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+    if args.trace_summary:
+        print(trace_summary(args.workload, args.trace_summary))
+        return
+    if args.traffic_summary:
+        print(traffic_summary(args.workload, args.traffic_summary))
+        return
     if args.calibrate_copy:
         # counter calibration under a profiler: nothing else runs and no other process is started
         print(json.dumps(calibrate_copy(args.calibrate_copy, args.steps, args.device)))

@@ -56,12 +56,14 @@ def gaussian_bf16(seed: int, cfg: int, tensor_id: int, h: int, shape) -> np.ndar
     return f32_to_bf16_bits(x)
 
 
-def qkv_bf16(seed: int, cfg: int, B: int, H: int, L: int, D: int):
-    """Q, K, V as uint16 bf16 bits in [B, H, L, D] order (one stream per tensor and head)."""
+def qkv_bf16(seed: int, cfg: int, B: int, H: int, L: int, D: int, Hkv: int | None = None):
+    """Q [B, H, L, D] and K, V [B, Hkv, L, D] (Hkv defaults to H) as uint16 bf16 bits, one stream per
+    tensor and head."""
     out = []
     for tid in (Q_ID, K_ID, V_ID):
-        t = np.empty((B, H, L, D), dtype=np.uint16)
-        for h in range(H):
+        nh = H if (tid == Q_ID or Hkv is None) else Hkv
+        t = np.empty((B, nh, L, D), dtype=np.uint16)
+        for h in range(nh):
             t[:, h] = gaussian_bf16(seed, cfg, tid, h, (B, L, D))
         out.append(t)
     return tuple(out)
@@ -138,7 +140,14 @@ def sampled_rows(seed: int, cfg: int, H: int, L: int, n: int) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def workload(name: str, seed: int = 0) -> dict:
-    """Return {"cfg", "B", "H", "L", "D", "masks": {label: mask}, "sink": array|None, "rows": int|None}."""
+    """Return {"cfg", "B", "H", "Hkv", "L", "D", "masks": {label: mask}, "sink": array|None,
+    "rows": int|None}; Hkv is the number of K/V heads (H unless the workload groups query heads)."""
+    w = _workload(name, seed)
+    w.setdefault("Hkv", w["H"])
+    return w
+
+
+def _workload(name: str, seed: int) -> dict:
     if name == "tiny_chunk":
         return dict(cfg=1, B=1, H=2, L=256, D=64, sink=None, rows=None,
                     masks={"chunk64": dict(kind="chunk", chunk=64)})
@@ -164,10 +173,16 @@ def workload(name: str, seed: int = 0) -> dict:
         return dict(cfg=5, B=1, H=H, L=L, D=128, sink=None, rows=512,
                     masks={"block50": dict(kind="block", block=bs,
                                            block_mask=block_matrix_top_half(seed, 5, H, nb))})
+    if name == "swa576_d256":
+        # prefill of the SWA-vs-linear-attention article's speed-test layer (16 query heads on 4 K/V
+        # heads, head dim 256) over a 128K-token prompt: causal window of 576 keys, learned sink
+        H = 16
+        return dict(cfg=6, B=1, H=H, Hkv=4, L=131072, D=256, sink=head_sinks(seed, 6, H), rows=512,
+                    masks={"swa576": dict(kind="window", left=575, right=0, causal=True)})
     raise KeyError(name)
 
 
-WORKLOADS = ("tiny_chunk", "vit896", "vit1792", "lm_headwin", "blocksparse128k")
+WORKLOADS = ("tiny_chunk", "vit896", "vit1792", "lm_headwin", "blocksparse128k", "swa576_d256")
 
 
 # ---------------------------------------------------------------------------

@@ -376,13 +376,13 @@ def _grouped_as_bench(w, q, k, v):
     return {m: o.float().cpu().double().numpy() for m, o in zip(labels, outs)}
 
 
-@pytest.mark.parametrize("name", ["vit896", "vit1792", "lm_headwin", "blocksparse128k"])
+@pytest.mark.parametrize("name", ["vit896", "vit1792", "lm_headwin", "blocksparse128k", "swa576_d256"])
 def test_workloads_in_the_bench_launch(name):
     """The grouped [B, H, L, D] launch of each workload against the oracle: all rows up to 4096 tokens,
     512 seeded rows per head beyond."""
     w = gen.workload(name)
     print(f"[case] {name}: grouped launch as timed", flush=True)
-    q, k, v = gen.qkv_bf16(0, w["cfg"], w["B"], w["H"], w["L"], w["D"])
+    q, k, v = gen.qkv_bf16(0, w["cfg"], w["B"], w["H"], w["L"], w["D"], w["Hkv"])
     got = _grouped_as_bench(w, q, k, v)
     rows = None if w["rows"] is None else gen.sampled_rows(0, w["cfg"], w["H"], w["L"], w["rows"])
     for label, mask in w["masks"].items():

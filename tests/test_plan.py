@@ -405,3 +405,19 @@ def test_head_dim_256_is_forward_only(lib):
     assert lib.attn_bwd_lists(plan.handle, 4, ctypes.byref(nb), ctypes.byref(cp), ctypes.byref(ne), ctypes.byref(en),
                               ctypes.byref(ni), ctypes.byref(it)) == _lib.ATTN_E_UNSUPPORTED
     assert lib.attn_bwd_upload(plan.handle, 4, None, 0, None) == _lib.ATTN_E_UNSUPPORTED
+
+
+def test_swa576_d256_workload_pairs(lib):
+    """The 128K-token causal window of 576 keys (head dim 256): every head holds
+    sum_i min(i + 1, 576) = 576 * 577 / 2 + (L - 576) * 576 allowed pairs."""
+    w = workload("swa576_d256")
+    assert (w["H"], w["Hkv"], w["D"]) == (16, 4, 256)
+    mask = w["masks"]["swa576"]
+    plan = _lib.Plan(mask, w["L"], w["H"], w["D"])
+    per, tot = plan.pairs()
+    W, L = mask["left"] + 1, w["L"]
+    assert np.all(per == W * (W + 1) // 2 + (L - W) * W) and tot == per.sum()
+    # every query tile lists the key tiles its window touches: 10 or 11 of 64 keys, the diagonal PARTIAL
+    bm, bn, rp, kv, fl = plan.tiles()
+    n = np.diff(rp)
+    assert n.max() <= -(-(bm + W - 1) // bn) + 1 and n[w["H"] * 8 - 1] >= 10
