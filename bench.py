@@ -116,13 +116,18 @@ _SAMPLER = r"""
 import json, subprocess, sys
 for line in sys.stdin:
     try:
-        r = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True, timeout=20)
+        r = subprocess.run(["amd-smi", "metric", "-c", "-p", "--json"], capture_output=True, text=True, timeout=20)
         d = json.loads(r.stdout)
-        c = (d["gpu_data"] if isinstance(d, dict) else d)[0]["clock"]
+        g0 = (d["gpu_data"] if isinstance(d, dict) else d)[0]
+        c = g0["clock"]
         gfx = [float(v["clk"]["value"]) for k, v in c.items() if k.startswith("gfx") and isinstance(v, dict)]
         mem = [float(v["clk"]["value"]) for k, v in c.items() if k.startswith("mem") and isinstance(v, dict)]
+        try:
+            watts = float(g0["power"]["socket_power"]["value"])
+        except (KeyError, TypeError, ValueError):
+            watts = None
         out = dict(gfx_mhz_mean=sum(gfx) / len(gfx) if gfx else None, gfx_mhz_min=min(gfx) if gfx else None,
-                   gfx_mhz_max=max(gfx) if gfx else None, mem_mhz=mem[0] if mem else None)
+                   gfx_mhz_max=max(gfx) if gfx else None, mem_mhz=mem[0] if mem else None, socket_watts=watts)
     except Exception:
         out = None
     sys.stdout.write(json.dumps(out) + "\n")
@@ -131,7 +136,8 @@ for line in sys.stdin:
 
 
 class ClockSampler:
-    """GPU clocks from amd-smi through the helper process (best effort; None when unavailable)."""
+    """GPU clocks and socket power from amd-smi through the helper process (best effort; None when
+    unavailable)."""
 
     def __init__(self, enabled: bool):
         self.proc = None
@@ -306,8 +312,9 @@ launches when the working set fits the last-level cache).
     return path
 
 
-def _clocks_under_load(setup, layout, sampler, seconds=1.0):
-    """Sample the clocks while about `seconds` of the workload's launches are queued on the GPU."""
+def _clocks_under_load(setup, layout, sampler, seconds=3.0):
+    """Sample the clocks and power while about `seconds` of the workload's launches are queued on
+    the GPU (the sample is taken two thirds of the way in, once power and clocks have settled)."""
     import torch
     from block_sparse_softmax_amd import bind_group
     q, k, v = setup["dev"]
@@ -322,7 +329,7 @@ def _clocks_under_load(setup, layout, sampler, seconds=1.0):
     one = max(time.perf_counter() - t0, 1e-4)
     for _ in range(max(1, int(seconds / one))):
         group()
-    time.sleep(min(0.3, seconds / 3))
+    time.sleep(2.0 * seconds / 3)
     c = sampler()
     torch.cuda.synchronize()
     return c
@@ -786,6 +793,7 @@ def _run(args, sampler):
             pk = PEAK_BF16_TFLOPS * c["gfx_mhz_mean"] / 2400.0
             roof["peak_at_load_clock"] = pk
             roof["frac_at_load_clock"] = roof["achieved"] / pk
+            roof["socket_watts_under_load"] = c.get("socket_watts")
 
     cpu = None if args.no_cpu_baseline else _cpu_baseline(setup)
 
