@@ -62,20 +62,20 @@ LLC_BYTES = 256 * 2**20       # MI355X last-level (Infinity) cache
 FLUSH_BYTES = 512 * 2**20     # scratch rewritten between launches to evict it
 CSRC = os.path.join(ROOT, "block_sparse_softmax_amd", "csrc")
 # source of each head dim's forward kernel, and the headers every forward kernel includes
-KERNEL_SRC = {64: "attn_fwd.hip", 80: "attn_fwd.hip", 128: "attn_fwd_pp.hip", 256: "attn_fwd_d256.hip"}
+KERNEL_SRC = {"swizzled": "attn_fwd.hip", "pingpong": "attn_fwd_pp.hip", "single": "attn_fwd_sg.hip"}
 KERNEL_HEADERS = ("fwd_common.hpp", "tile_common.hpp", "kernels.hpp")
 DEFAULT_WORKLOAD = "blocksparse128k"
 
 
-def _kernel_hash(D: int) -> str:
-    """Hash of the forward kernel's source at head dim D (its file and the shared headers)."""
+def _kernel_hash(kind: str) -> str:
+    """Hash of a forward kernel's source (its file and the shared headers); kind as Plan.kernel()."""
     h = hashlib.sha256()
-    for f in (KERNEL_SRC[D], *KERNEL_HEADERS):
+    for f in (KERNEL_SRC[kind], *KERNEL_HEADERS):
         h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def _traffic_from_profile(workload: str, mask: str, D: int):
+def _traffic_from_profile(workload: str, mask: str, kind: str):
     """HBM bytes per launch from the committed counter summary, if it was taken on this kernel source."""
     path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_{mask}_traffic.txt")
     if not os.path.exists(path):
@@ -83,7 +83,7 @@ def _traffic_from_profile(workload: str, mask: str, D: int):
     txt = open(path).read()
     m = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
     b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m or not b or m.group(1) != _kernel_hash(D):
+    if not m or not b or m.group(1) != _kernel_hash(kind):
         return None
     return float(b.group(1))
 
@@ -181,8 +181,17 @@ def calibrate_copy(mib: int, steps: int, device: str) -> dict:
     return {"calibrate_copy_bytes": n, "copies": steps}
 
 
-def _kernel_name(D: int) -> str:
-    return {128: "attn_fwd_pp_kernel", 256: "attn_fwd_d256_kernel"}.get(D, f"attn_fwd_kernel<{D}")
+def _kernel_name(kind: str, D: int) -> str:
+    """Name (prefix) of the forward kernel of this kind and head dim in profiler output."""
+    return {"pingpong": "attn_fwd_pp_kernel", "single": f"attn_fwd_sg_kernel<{D}"}.get(kind, f"attn_fwd_kernel<{D}")
+
+
+def _workload_kernel(w) -> tuple:
+    """(kind, name) of the forward kernel that runs the workload's launch (host-side plan only)."""
+    from block_sparse_softmax_amd._lib import Plan
+    m = next(iter(w["masks"].values()))
+    kind = Plan(m, w["L"], w["H"], w["D"]).kernel()
+    return kind, _kernel_name(kind, w["D"])
 
 
 def _counter_values(run_dir: str, counter: str, kernel: str):
@@ -211,7 +220,7 @@ def traffic_summary(workload: str, pmc_dir: str, copy_mib: int = 1024, out_dir: 
     if len(w["masks"]) != 1:
         raise SystemExit("traffic summaries cover single-mask workloads")
     label = next(iter(w["masks"]))
-    kern = _kernel_name(w["D"])
+    kind, kern = _workload_kernel(w)
     run = (f"python3 bench.py --workload {workload} --quick --no-cpu-baseline --no-clocks --steps 3 --warmup 1 "
            "--reps 3")
     copy = f"python3 bench.py --calibrate-copy {copy_mib} --steps 3"
@@ -236,7 +245,7 @@ Commands (from the repository root, one MI355X; each counter in its own pass), t
 {cmds}
 ```
 
-kernel_source_sha256_16: {_kernel_hash(w["D"])}
+kernel_source_sha256_16: {_kernel_hash(kind)}
 
 Calibration with a plain {copy_mib} MiB device copy ({kib:,.0f} KiB read and written):
 
@@ -268,7 +277,7 @@ def trace_summary(workload: str, trace_dir: str, out_dir: str | None = None) -> 
     from block_sparse_softmax_amd import inputs as gen
     from block_sparse_softmax_amd._lib import Plan
     w = gen.workload(workload)
-    kern = _kernel_name(w["D"])
+    kind, kern = _workload_kernel(w)
     durs, name = [], None
     for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
         with open(path) as f:
@@ -295,7 +304,7 @@ Command (from the repository root, one MI355X), then
 {cmd}
 ```
 
-kernel_source_sha256_16: {_kernel_hash(w["D"])}
+kernel_source_sha256_16: {_kernel_hash(kind)}
 
 | kernel | calls | average | median | min | max |
 |---|---|---|---|---|---|
@@ -477,9 +486,12 @@ def _roofline(setup, group, total_flops, workload):
     w = setup["w"]
     achieved = total_flops / (group["avg_ms"] * 1e-3) / 1e12
     label = "+".join(group["masks"])
+    # a grouped launch runs the ping-pong kernel only when every plan picks it
+    kinds = [m["pm"].plan.kernel() for m in setup["masks"]]
+    kind = kinds[0] if all(k == kinds[0] for k in kinds) else "single"
     return dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                frac=achieved / PEAK_BF16_TFLOPS, traffic=_traffic_from_profile(workload, label, w["D"]),
-                kernel=(_kernel_name(w["D"]) + (">" if w["D"] < 128 else "") +
+                frac=achieved / PEAK_BF16_TFLOPS, traffic=_traffic_from_profile(workload, label, kind),
+                kernel=(_kernel_name(kind, w["D"]) + (">" if kind != "pingpong" else "") +
                         f" ({workload}: {', '.join(group['masks'])})"),
                 avg_launch_ms=group["avg_ms"], median_launch_ms=group["median_ms"],
                 frac_at_median=total_flops / (group["median_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS)

@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "ATTN_OK", -1: "ATTN_E_INVAL", -2: "ATTN_E_UNSUPPORTED", -3: 
 
 # every symbol the header declares
 EXPORTS = ("attn_masked_fwd", "attn_masked_fwd_noalloc", "attn_workspace_bytes", "attn_workspace_release", "attn_plan_create", "attn_plan_tiles",
-           "attn_plan_pairs", "attn_plan_schedule", "attn_plan_workspace_bytes", "attn_plan_upload",
+           "attn_plan_pairs", "attn_plan_schedule", "attn_plan_kernel", "attn_plan_workspace_bytes", "attn_plan_upload",
            "attn_masked_fwd_plan", "attn_masked_fwd_group", "attn_rr_workspace_bytes", "attn_rr_search",
            "attn_reorder_tokens", "attn_masked_fwd_lse", "attn_bwd_workspace_bytes", "attn_bwd_lists",
            "attn_bwd_upload",
@@ -94,6 +94,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "attn_plan_tiles": [plan_p, P(i32), P(i32), P(i64), P(i64), P(P(i32)), P(P(i32)), P(P(ctypes.c_uint8))],
             "attn_plan_pairs": [plan_p, P(i64), P(i64)],
             "attn_plan_schedule": [plan_p, P(i64), P(P(i32))],
+            "attn_plan_kernel": [plan_p, P(i32)],
             "attn_plan_workspace_bytes": [plan_p, P(sz)],
             "attn_plan_upload": [plan_p, vp, sz, vp],
             "attn_masked_fwd_plan": [plan_p, P(AttnTensor), P(AttnTensor), P(AttnTensor), vp, P(AttnTensor), P(Launch)],
@@ -225,6 +226,13 @@ class Plan:
         it = ctypes.POINTER(ctypes.c_int32)()
         _check(lib.attn_plan_schedule(self._h, ctypes.byref(n), ctypes.byref(it)))
         return np.ctypeslib.as_array(it, shape=(n.value, 8)).copy() if n.value else np.zeros((0, 8), np.int32)
+
+    def kernel(self) -> str:
+        """Forward kernel of the plan's launches: "swizzled" (d 64, 80), "single" or "pingpong"."""
+        lib = load_library()
+        k = ctypes.c_int32()
+        _check(lib.attn_plan_kernel(self._h, ctypes.byref(k)))
+        return {0: "swizzled", 1: "single", 2: "pingpong"}[k.value]
 
     def bwd_lists(self, kv_heads: int):
         """Transposed lists of the backward: (n_blocks, col_ptr, entries, items (n, 8))."""

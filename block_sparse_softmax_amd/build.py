@@ -33,8 +33,8 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 # forward kernels: d = 64/80 (attn_fwd.hip, also the split-row merge and the
-# dispatch), d = 128 (attn_fwd_pp.hip), d = 256 (attn_fwd_d256.hip)
-HIP_SOURCES = ["attn_fwd.hip", "attn_fwd_pp.hip", "attn_fwd_d256.hip", "attn_bwd.hip", "rr_search.hip",
+# dispatch), d = 128 long rows (attn_fwd_pp.hip), d = 128 short rows and d = 256 (attn_fwd_sg.hip)
+HIP_SOURCES = ["attn_fwd.hip", "attn_fwd_pp.hip", "attn_fwd_sg.hip", "attn_bwd.hip", "rr_search.hip",
                "reorder.hip", "decode.hip"]
 HOST_SOURCES = ["plan.cpp", "capi.cpp", "plan_cache.cpp"]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",

@@ -12,8 +12,9 @@
 //
 // This file: attn_fwd_kernel (d = 64 and 80), the merge of split rows and the
 // launch for every head dim; d = 128 runs attn_fwd_pp_kernel (attn_fwd_pp.hip:
-// two wave groups in ping-pong) and d = 256 attn_fwd_d256_kernel
-// (attn_fwd_d256.hip).
+// two wave groups in ping-pong) for long rows and attn_fwd_sg_kernel
+// (attn_fwd_sg.hip: one wave group, two work-groups per CU) for short ones,
+// d = 256 attn_fwd_sg_kernel.
 //
 // Layout of the work in attn_fwd_kernel (per work-group: 4 waves x 32 query rows):
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16.  K (A operand) comes from LDS,
@@ -795,10 +796,11 @@ hipError_t launch_d(const GroupParams& g, int blocks, int B, hipStream_t stream,
   // the extended launch attaches the events to the kernel's own dispatch
   hipEvent_t stop1 = merges > 0 ? nullptr : stop;
   hipError_t e = hipSuccess;
-  if constexpr (D == 128) {
-    e = launch_fwd_pp(g, grid, prefix, stream, start, stop1);
-  } else if constexpr (D == 256) {
-    e = launch_fwd_d256(g, grid, prefix, stream, start, stop1);
+  if constexpr (D == 128 || D == 256) {
+    bool pingpong = D == 128;
+    for (int j = 0; j < g.n_jobs; ++j) pingpong = pingpong && g.job[j].pingpong != 0;
+    e = pingpong ? launch_fwd_pp(g, grid, prefix, stream, start, stop1)
+                 : launch_fwd_sg(g, D, grid, prefix, stream, start, stop1);
   } else {
     if (prefix) hipExtLaunchKernelGGL((attn_fwd_kernel<D, true>), grid, dim3(kThreads), 0, stream, start, stop1, 0, g);
     else hipExtLaunchKernelGGL((attn_fwd_kernel<D, false>), grid, dim3(kThreads), 0, stream, start, stop1, 0, g);

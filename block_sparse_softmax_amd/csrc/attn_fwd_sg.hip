@@ -1,18 +1,23 @@
-// Structured-mask softmax attention forward, head dim 256, for gfx950 (the
-// grouped-query layer of the sliding-window-vs-linear-attention article's
-// speed test: 16 query heads on 4 key/value heads).  The computation is
+// Structured-mask softmax attention forward for head dims 128 and 256 on
+// gfx950, one wave group per work-group.  The computation is
 // attn_fwd_kernel's (attn_fwd.hip): the exact tiled softmax over the item's
 // listed key tiles, sink in the denominator, PARTIAL-tile masking, split rows.
 //
-// At d = 256 a wave's 32 query rows hold 64 registers of Q fragments and 128
-// of fp32 accumulators, so the kernel runs one wave per SIMD: 4 waves x 32
-// rows per work-group, one work-group per CU (136 KB of LDS), registers
-// beyond 256 in AGPRs.  Each 64-key tile runs S^T = K Q^T (32 MFMAs), the
-// mask (PARTIAL tiles), the softmax and O^T += V^T P^T (32 MFMAs, with the
-// exponentials of the next 16 keys beside the MFMAs of the previous 16) in
-// turn; the copies of tile j+1 stream into the other LDS buffers meanwhile.
-// LDS tiles use the padded layout of Lds<256>: copy instruction i carries
-// rows i and i + 32 (512 bytes each) into 1 KiB plus a pad.
+// 4 waves x 32 query rows per work-group.  Each 64-key tile runs
+// S^T = K Q^T (2 d / 16 MFMAs), the mask (PARTIAL tiles), the softmax and
+// O^T += V^T P^T (d / 8 MFMAs, with the exponentials of the next 16 keys
+// beside the MFMAs of the previous 16) in turn, while the copies of the next
+// listed tile stream into the other LDS buffers.
+//   * d = 128: two work-groups per CU, so that one work-group's first tiles
+//     and epilogue overlap the other's MFMAs.  This is the kernel for items of
+//     a few tiles (short windows, small chunks); long items run the ping-pong
+//     kernel (attn_fwd_pp.hip).
+//   * d = 256 (the grouped-query layer of the sliding-window-vs-linear-
+//     attention article's speed test: 16 query heads on 4 key/value heads):
+//     a wave's 32 rows hold 64 registers of Q fragments and 128 of fp32
+//     accumulators, so one work-group per CU, registers beyond 256 in AGPRs.
+// LDS tiles use the padded layout of Lds<D>: copy instruction i carries rows
+// i, i + NI, ... (1024 / (2 d) rows of 2 d bytes) into 1 KiB plus a pad.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -29,18 +34,21 @@ namespace {
 
 using namespace dev;
 
-template <bool PREFIX>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_d256_kernel(const GroupParams g) {
-  constexpr int D = 256;
+template <int D, bool PREFIX>
+__global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void attn_fwd_sg_kernel(const GroupParams g) {
   using S = Shape<D>;
   using L = Lds<D>;
-  static_assert(L::PADDED && L::NI == 32, "padded d = 256 tiles: 32 copy instructions of two rows");
+  static_assert(L::PADDED && (D == 128 || D == 256), "padded tiles of head dim 128 or 256");
+  constexpr int NI = L::NI;          // copy instructions per tile
+  constexpr int RB = 2 * D;          // bytes of a row
+  constexpr int CPR = D / 8;         // 16-byte chunks of a row
+  constexpr int PAIRS = S::DT / 4;   // PV MFMAs per pair of exponentials of the next 16 keys
   constexpr int64_t kSlotFloats = partial_slot_floats(D);
   constexpr int kSlotM = 4 * S::DT * 16 * 64;
   constexpr int kSlotL = kSlotM + 4 * 64;
   static_assert(kSlotL + 4 * 64 == kSlotFloats, "partial slot layout");
-  constexpr int NQ = 2 * S::KS;  // 32 QK MFMAs per tile
-  constexpr int NP = 4 * S::DT;  // 32 PV MFMAs per tile
+  constexpr int NQ = 2 * S::KS;  // QK MFMAs per tile
+  constexpr int NP = 4 * S::DT;  // PV MFMAs per tile
   __shared__ __attribute__((aligned(1024))) unsigned char smem[L::BYTES];
 
   const int lane = threadIdx.x & 63;
@@ -126,35 +134,39 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_d256_kernel(const GroupP
   }
   auto ref_of = [&]() __attribute__((always_inline)) { return m_run == -INFINITY ? 0.f : m_run; };
 
-  // ---- LDS addressing (padded rows; Lds<256>) ----
-  const int kbase_off = l31 * L::kKBlk + 16 * h2;   // row l31 (+32 per key half: +512), chunk 2 ks + h2
+  // ---- LDS addressing (padded rows; Lds<D>): row r sits in block r mod NI at (r / NI) * RB ----
+  // K fragment: key row l31 (+32 for the second key half: + 32 RB / NI bytes), chunk 2 ks + h2
+  const int kbase_off = (l31 % NI) * L::kKBlk + (l31 / NI) * RB + 16 * h2;
+  constexpr int kHalfOff = 32 / NI * RB;
+  // V^T fragment: source lane (j, c) of each 16-lane group reads key row 16 t + 8 u + 4 h2 + j,
+  // columns 32 dt + 16 dhalf + 4 c .. +3 (u = 0, 1: the two transposed reads)
   const int tr_j = (lane & 15) >> 2, tr_c = lane & 3, dhalf = (lane >> 4) & 1;
   const int vbase_off = (4 * h2 + tr_j) * L::kVBlk + 32 * dhalf + 8 * tr_c;
   auto kfrag = [&](int set, int i) __attribute__((always_inline)) {  // QK step i: k-step i/2, key half i%2
-    return *reinterpret_cast<const bf16x8*>(smem + L::buf_off(set) + kbase_off + 32 * (i >> 1) + (i & 1) * 512);
+    return *reinterpret_cast<const bf16x8*>(smem + L::buf_off(set) + kbase_off + 32 * (i >> 1) + (i & 1) * kHalfOff);
   };
   auto vfrag = [&](int set, int i) __attribute__((always_inline)) {  // PV step i: keys 16 t .., O^T tile dt
     const int t = i / S::DT, dt = i % S::DT;
-    const unsigned char* src =
-        smem + L::buf_off(2 + set) + (t & 1) * 16 * L::kVBlk + (t >> 1) * 512 + vbase_off + 64 * dt;
+    const unsigned char* src = smem + L::buf_off(2 + set) + ((16 * t) % NI) * L::kVBlk + (16 * t / NI) * RB +
+                               vbase_off + 64 * dt;
     const s16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src));
     const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(src + 8 * L::kVBlk));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  // ---- LDS-DMA: waves 0-1 copy K tiles, waves 2-3 V tiles, 16 instructions each ----
+  // ---- LDS-DMA: waves 0-1 copy K tiles, waves 2-3 V tiles, NI / 2 instructions each ----
   const int dma_tensor = wave >> 1;
   const uint32_t dma_row_bytes =
       static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(dma_tensor ? v_row_bytes : k_row_bytes)));
   const unsigned char* dma_base = dma_tensor ? vbase : kbase;
   const uint32_t smem_lds = lds_addr(smem);
-  // lane l of instruction i copies chunk l mod 32 of row i + 32 (l / 32)
-  const uint32_t goff = static_cast<uint32_t>(32 * (lane >> 5)) * dma_row_bytes + 16 * (lane & 31);
+  // lane l of instruction i copies chunk l mod CPR of row i + NI (l / CPR)
+  const uint32_t goff = static_cast<uint32_t>(NI * (lane / CPR)) * dma_row_bytes + 16 * (lane % CPR);
   const uint32_t blk_bytes = dma_tensor ? L::kVBlk : L::kKBlk;
   auto issue_tile = [&](int kt, int set) __attribute__((always_inline)) {
     const uint32_t kv0 = static_cast<uint32_t>(kt * kBN);
     const uint64_t tb = uniform_u64(reinterpret_cast<uint64_t>(dma_base) + static_cast<uint64_t>(kv0) * dma_row_bytes);
-    constexpr int kPer = 16;
+    constexpr int kPer = NI / 2;
     const int i0 = (wave & 1) * kPer;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(smem_lds + L::buf_off(2 * dma_tensor + set) + i0 * blk_bytes);
     if (static_cast<int>(kv0) + kBN <= p.L) {
@@ -165,8 +177,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_d256_kernel(const GroupP
       const int last = p.L - 1 - static_cast<int>(kv0);
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        const int row = i0 + i + 32 * (lane >> 5);
-        dma16(tb, min(row, last) * dma_row_bytes + 16 * (lane & 31), dst + i * blk_bytes);
+        const int row = i0 + i + NI * (lane / CPR);
+        dma16(tb, min(row, last) * dma_row_bytes + 16 * (lane % CPR), dst + i * blk_bytes);
       }
     }
   };
@@ -250,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_d256_kernel(const GroupP
       const int t = i / S::DT, dt = i % S::DT;
       if (i + 2 < NP) va[i + 2] = vfrag(set, i + 2);
       acc[dt] = mfma32(va[i], pb[t], acc[dt]);
-      if (t + 1 < 4 && (dt & 1) == 1) exp_pair(t + 1, dt >> 1);
+      if (t + 1 < 4 && (dt + 1) % PAIRS == 0) exp_pair(t + 1, dt / PAIRS);
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run += rs;
@@ -407,10 +419,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_d256_kernel(const GroupP
 
 }  // namespace
 
-hipError_t launch_fwd_d256(const GroupParams& g, dim3 grid, bool prefix, hipStream_t stream, hipEvent_t start,
-                           hipEvent_t stop) {
-  if (prefix) hipExtLaunchKernelGGL((attn_fwd_d256_kernel<true>), grid, dim3(kThreads), 0, stream, start, stop, 0, g);
-  else hipExtLaunchKernelGGL((attn_fwd_d256_kernel<false>), grid, dim3(kThreads), 0, stream, start, stop, 0, g);
+hipError_t launch_fwd_sg(const GroupParams& g, int D, dim3 grid, bool prefix, hipStream_t stream, hipEvent_t start,
+                         hipEvent_t stop) {
+  if (D == 128) {
+    if (prefix) hipExtLaunchKernelGGL((attn_fwd_sg_kernel<128, true>), grid, dim3(kThreads), 0, stream, start, stop, 0, g);
+    else hipExtLaunchKernelGGL((attn_fwd_sg_kernel<128, false>), grid, dim3(kThreads), 0, stream, start, stop, 0, g);
+  } else if (D == 256) {
+    if (prefix) hipExtLaunchKernelGGL((attn_fwd_sg_kernel<256, true>), grid, dim3(kThreads), 0, stream, start, stop, 0, g);
+    else hipExtLaunchKernelGGL((attn_fwd_sg_kernel<256, false>), grid, dim3(kThreads), 0, stream, start, stop, 0, g);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -138,6 +138,7 @@ attn_status make_job(const attn_plan& p, const attn_tensor* q, const attn_tensor
   f.right = static_cast<int32_t>(p.right);
   f.prefix = static_cast<int32_t>(std::min<int64_t>(p.prefix, p.L));
   f.kv_group = static_cast<int32_t>(p.H / hkv);
+  f.pingpong = p.pingpong ? 1 : 0;
   *out = f;
   *queue_len = static_cast<int32_t>(n_items / 8);
   return ATTN_OK;
@@ -248,6 +249,13 @@ attn_status attn_plan_schedule(const attn_plan* p, int64_t* n_items, const int32
   if (!p) { set_error("plan is NULL"); return ATTN_E_INVAL; }
   if (n_items) *n_items = static_cast<int64_t>(p->items.size());
   if (items) *items = reinterpret_cast<const int32_t*>(p->items.data());
+  return ATTN_OK;
+}
+
+attn_status attn_plan_kernel(const attn_plan* p, int32_t* kernel) {
+  if (!p || !kernel) { set_error("plan or kernel is NULL"); return ATTN_E_INVAL; }
+  *kernel = p->D == 128 ? (p->pingpong ? ATTN_KERNEL_PINGPONG : ATTN_KERNEL_SINGLE)
+                        : (p->D == 256 ? ATTN_KERNEL_SINGLE : ATTN_KERNEL_SWIZZLED);
   return ATTN_OK;
 }
 

@@ -1,5 +1,6 @@
 // Pieces shared by the forward kernels: attn_fwd.hip (d = 64, 80 and the
-// split-row merge), attn_fwd_pp.hip (d = 128) and attn_fwd_d256.hip (d = 256).
+// split-row merge), attn_fwd_pp.hip (d = 128, long rows) and attn_fwd_sg.hip
+// (d = 128 short rows, d = 256).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,10 +43,10 @@ struct Lds {
 
 // Main kernels of the d = 128 and d = 256 forward over `grid` (one work item
 // per work-group, as laid out by the plan); launch_fwd queues the split-row
-// merge after them.
+// merge after them.  launch_fwd_sg takes D = 128 or 256.
 hipError_t launch_fwd_pp(const GroupParams& g, dim3 grid, bool prefix, hipStream_t stream, hipEvent_t start,
                          hipEvent_t stop);
-hipError_t launch_fwd_d256(const GroupParams& g, dim3 grid, bool prefix, hipStream_t stream, hipEvent_t start,
-                           hipEvent_t stop);
+hipError_t launch_fwd_sg(const GroupParams& g, int D, dim3 grid, bool prefix, hipStream_t stream, hipEvent_t start,
+                         hipEvent_t stop);
 
 }  // namespace bss

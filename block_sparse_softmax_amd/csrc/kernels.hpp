@@ -41,6 +41,7 @@ struct FwdParams {
   int32_t chunk, right;
   int32_t prefix;             // prefix tokens added to every row's set (0 = none)
   int32_t kv_group;           // query heads per K/V head (grouped-query attention; 1 = MHA)
+  int32_t pingpong;           // head dim 128: the plan picks the two-group kernel (long rows)
   float* lse;                 // optional [B][H][L]: row log-sum-exp (natural log), -inf for empty rows
 };
 

@@ -234,6 +234,7 @@ void compile_blocks(attn_plan& p) {
 // rounds whose item costs are uneven is dealt longest-first to the
 // least-loaded queue instead.  Queues are padded to equal length with null
 // items.
+constexpr double kPingPongMinTiles = 32.0;  // d = 128: mean row cost (tiles) from which the ping-pong kernel runs
 constexpr double kMinPiece = 12.0;     // tiles: below this a piece's merge costs more than it saves
 constexpr double kPieceOverhead = 2.0; // tiles: writing the partial state and the merge
 constexpr int kMaxPieces = 16;
@@ -314,6 +315,7 @@ void schedule(attn_plan& p) {
   std::iota(heads.begin(), heads.end(), 0);
   std::stable_sort(heads.begin(), heads.end(),
                    [&](int64_t a, int64_t b) { return head_cost[a] > head_cost[b]; });
+  p.pingpong = p.D == 128 && total >= kPingPongMinTiles * static_cast<double>(rows);
 
   // unsplit schedule (batch > 1)
   std::vector<Item> whole(rows);

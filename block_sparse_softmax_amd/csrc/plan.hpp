@@ -117,6 +117,10 @@ struct attn_plan {
   // kXcds equal-length queues
   std::vector<bss::Item> items, items_unsplit;
   int64_t n_partial_slots = 0;
+  // forward kernel of head dim 128: the two-group ping-pong kernel when the
+  // rows are long on average, else the single-group kernel (two work-groups
+  // per CU, for short rows)
+  bool pingpong = false;
   std::vector<bss::MergeRow> merge_rows;  // split rows of `items`, merged after the launch
   std::vector<int32_t> kv_entries;    // (kv_tile << 1) | full, in canonical order
   std::vector<int32_t> head_left32;   // [H]

@@ -211,6 +211,20 @@ attn_status attn_plan_pairs(const attn_plan* plan, int64_t* pairs_per_head, int6
 attn_status attn_plan_schedule(const attn_plan* plan, int64_t* n_items, const int32_t** items);
 
 /*
+ * Forward kernel the plan's launches run (for profiling and tests):
+ *   ATTN_KERNEL_SWIZZLED  head dims 64, 80: one wave group, XOR-swizzled LDS
+ *                         tiles, two tiles in flight per iteration;
+ *   ATTN_KERNEL_SINGLE    head dims 128 (rows of fewer than about 32 tiles on
+ *                         average: two work-groups per CU) and 256;
+ *   ATTN_KERNEL_PINGPONG  head dim 128 with long rows: two wave groups per
+ *                         work-group taking alternate tiles, MFMA and softmax
+ *                         phases alternating between the two waves of a SIMD.
+ * A grouped launch runs the ping-pong kernel only when all its plans do.
+ */
+enum { ATTN_KERNEL_SWIZZLED = 0, ATTN_KERNEL_SINGLE = 1, ATTN_KERNEL_PINGPONG = 2 };
+attn_status attn_plan_kernel(const attn_plan* plan, int32_t* kernel);
+
+/*
  * Device bytes a launch needs in the workspace: the plan's image (tile lists,
  * schedules, the list of split rows) followed, for batch-1 launches, by the
  * partial states of split rows.  Launches that share a workspace must not

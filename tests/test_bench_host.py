@@ -75,14 +75,14 @@ def test_traffic_summary_scales_by_the_copy(tmp_path):
     pmc = tmp_path / "pmc"
     _write_counters(pmc / "FETCH_SIZE_copy", "FETCH_SIZE", "copyBuffer", [512 * 1024] * 3)     # half of 1 GiB
     _write_counters(pmc / "WRITE_SIZE_copy", "WRITE_SIZE", "copyBuffer", [1024 * 1024] * 3)
-    k = "void bss::(anonymous namespace)::attn_fwd_d256_kernel<false>(bss::GroupParams)"
+    k = "void bss::(anonymous namespace)::attn_fwd_sg_kernel<256, false>(bss::GroupParams)"
     _write_counters(pmc / "FETCH_SIZE_swa576_d256", "FETCH_SIZE", k, [100.0, 300.0, 200.0])
     _write_counters(pmc / "WRITE_SIZE_swa576_d256", "WRITE_SIZE", k, [50.0, 50.0, 70.0])
     path = bench.traffic_summary("swa576_d256", str(pmc), out_dir=str(tmp_path))
     txt = open(path).read()
     assert os.path.basename(path) == "attn_fwd_swa576_d256_swa576_traffic.txt"
     assert "hbm_bytes_per_launch: %d" % ((200.0 * 2 + 50.0) * 1024) in txt
-    assert f"kernel_source_sha256_16: {bench._kernel_hash(256)}" in txt
+    assert f"kernel_source_sha256_16: {bench._kernel_hash('single')}" in txt
     alg = 2 * 131072 * 256 * (2 * 16 + 2 * 4)
     assert f"algorithmic_bytes_per_launch: {alg}" in txt
     with pytest.raises(SystemExit):

@@ -173,6 +173,34 @@ def test_v_ones_probe_and_determinism():
     assert np.array_equal(got, got2)
 
 
+KERNELS_128 = [
+    # (mask, L, kernel the plan picks at head dim 128)
+    (dict(kind="full"), 2200, "pingpong"),
+    (dict(kind="full", causal=True), 2500, "single"),
+    (dict(kind="window", left=300, right=0, causal=True), 1800, "single"),
+    (dict(kind="chunk", chunk=1024, causal=True), 3000, "single"),
+    (dict(kind="window", left=2000, right=2000), 2600, "pingpong"),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(KERNELS_128)))
+def test_both_head_dim_128_kernels(ci):
+    """Head dim 128 runs the single-group kernel for short rows and the ping-pong kernel for long
+    ones (the plan decides); both against the oracle, with a sink, batch 2 (unsplit) and batch 1
+    (split rows)."""
+    from block_sparse_softmax_amd import _lib
+    mask, L, kind = KERNELS_128[ci]
+    H, D = 2, 128
+    assert _lib.Plan(mask, L, H, D).kernel() == kind
+    sink = np.random.default_rng(700 + ci).standard_normal(H).astype(np.float32)
+    for B in (2, 1):
+        print(f"[case] d128 {kind} {mask} L={L} B={B}", flush=True)
+        q, k, v = _random_case(710 + ci, B, H, L, D)
+        got = _run_gpu(q, k, v, mask, sink, layout="bhld")
+        ref = attention(q, k, v, mask, sink=sink)["out"]
+        _compare(got, ref, f"d128-{kind}-{ci}-B{B}")
+
+
 def _offset_case(seed, H, L, D, first_sign):
     """Q, K with a shared direction u: the first 64 keys score about first_sign * 40 (log2 units) against
     every query, all other keys about -first_sign * 40, plus N(0, 1) noise in every element."""

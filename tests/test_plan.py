@@ -421,3 +421,16 @@ def test_swa576_d256_workload_pairs(lib):
     bm, bn, rp, kv, fl = plan.tiles()
     n = np.diff(rp)
     assert n.max() <= -(-(bm + W - 1) // bn) + 1 and n[w["H"] * 8 - 1] >= 10
+
+
+def test_forward_kernel_choice(lib):
+    """Head dims 64 and 80 run the swizzled kernel, 256 the single-group one; at 128 the plan picks
+    the ping-pong kernel when its rows hold 32 tiles or more on average (schedule cost)."""
+    assert _lib.Plan(dict(kind="full"), 1024, 2, 64).kernel() == "swizzled"
+    assert _lib.Plan(dict(kind="full"), 1024, 2, 80).kernel() == "swizzled"
+    assert _lib.Plan(dict(kind="full"), 4096, 2, 256).kernel() == "single"
+    assert _lib.Plan(dict(kind="full"), 2048, 2, 128).kernel() == "pingpong"      # 32 tiles per row
+    assert _lib.Plan(dict(kind="full"), 1984, 2, 128).kernel() == "single"        # 31
+    assert _lib.Plan(dict(kind="window", left=575, right=0, causal=True), 131072, 4, 128).kernel() == "single"
+    w = workload("blocksparse128k")
+    assert _lib.Plan(w["masks"]["block50"], w["L"], w["H"], w["D"]).kernel() == "pingpong"
