@@ -15,7 +15,9 @@ from typing import Optional
 
 import numpy as np
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbss_attn.so")
+# BSS_ATTN_CHECKED=1 loads the checked build (forward kernels with range checks; see attn_checks)
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "libbss_attn_checked.so" if os.environ.get("BSS_ATTN_CHECKED") == "1" else "libbss_attn.so")
 
 ATTN_OK, ATTN_E_INVAL, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP, ATTN_E_NOMEM = 0, -1, -2, -3, -4, -5
 KINDS = {"full": 0, "chunk": 1, "window": 2, "block": 3}
@@ -28,7 +30,7 @@ EXPORTS = ("attn_masked_fwd", "attn_masked_fwd_noalloc", "attn_workspace_bytes",
            "attn_masked_fwd_plan", "attn_masked_fwd_group", "attn_rr_workspace_bytes", "attn_rr_search",
            "attn_reorder_tokens", "attn_masked_fwd_lse", "attn_bwd_workspace_bytes", "attn_bwd_lists",
            "attn_bwd_upload",
-           "attn_masked_bwd", "attn_decode_workspace_bytes", "attn_decode_fwd",
+           "attn_masked_bwd", "attn_decode_workspace_bytes", "attn_decode_fwd", "attn_checks",
            "attn_plan_destroy", "attn_last_error", "attn_version")
 
 
@@ -113,6 +115,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "attn_decode_workspace_bytes": [P(AttnTensor), P(AttnTensor), i64, P(DecodeDesc), P(sz)],
             "attn_decode_fwd": [P(AttnTensor), P(AttnTensor), P(AttnTensor), vp, i64, P(DecodeDesc), vp,
                                 P(AttnTensor), P(Launch)],
+            "attn_checks": [P(i32), P(ctypes.c_uint32), i32],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -124,6 +127,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.attn_version.restype = ctypes.c_char_p
         _lib = lib
         return lib
+
+
+def checks(clear: bool = True):
+    """(enabled, bits) of the loaded library's range checks (attn_checks); synchronize first."""
+    lib = load_library()
+    en, bits = ctypes.c_int32(), ctypes.c_uint32()
+    _check(lib.attn_checks(ctypes.byref(en), ctypes.byref(bits), 1 if clear else 0))
+    return bool(en.value), int(bits.value)
 
 
 def _check(status: int):

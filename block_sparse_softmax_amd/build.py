@@ -18,6 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbss_attn.so")
+LIB_CHECKED = os.path.join(PKG, "libbss_attn_checked.so")   # forward kernels with range checks
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HIP_FLAGS = [
@@ -37,6 +38,7 @@ HIP_FLAGS = [
 HIP_SOURCES = ["attn_fwd.hip", "attn_fwd_pp.hip", "attn_fwd_sg.hip", "attn_bwd.hip", "rr_search.hip",
                "reorder.hip", "decode.hip"]
 HOST_SOURCES = ["plan.cpp", "capi.cpp", "plan_cache.cpp"]
+CHECKED_SOURCES = ["attn_fwd.hip", "attn_fwd_pp.hip", "attn_fwd_sg.hip"]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
               f"-I{ROCM}/include"]
 
@@ -50,22 +52,30 @@ def _run(cmd):
 
 
 def build(verbose: bool = False) -> str:
+    """Build LIB and LIB_CHECKED (the forward kernels with BSS_CHECKED range checks, everything else
+    shared); returns LIB."""
     hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
-    os.makedirs(BUILD, exist_ok=True)
+    checked_dir = os.path.join(BUILD, "checked")
+    os.makedirs(checked_dir, exist_ok=True)
     inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
     objs = [os.path.join(BUILD, os.path.splitext(f)[0] + ".o") for f in HIP_SOURCES + HOST_SOURCES]
+    checked = {f: os.path.join(checked_dir, os.path.splitext(f)[0] + ".o") for f in CHECKED_SOURCES}
     jobs = [[hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, f), "-o", o] for f, o in zip(HIP_SOURCES, objs)]
     jobs += [["g++", *HOST_FLAGS, *inc, "-c", os.path.join(CSRC, f), "-o", o]
              for f, o in zip(HOST_SOURCES, objs[len(HIP_SOURCES):])]
+    jobs += [[hipcc, *HIP_FLAGS, "-DBSS_CHECKED", *inc, "-c", os.path.join(CSRC, f), "-o", o]
+             for f, o in checked.items()]
     with ThreadPoolExecutor(8) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    tmp = LIB + ".tmp"
-    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+    objs_checked = [checked.get(f, o) for f, o in zip(HIP_SOURCES + HOST_SOURCES, objs)]
+    for lib, ob in ((LIB, objs), (LIB_CHECKED, objs_checked)):
+        tmp = lib + ".tmp"
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *ob])
+        os.replace(tmp, lib)
     return LIB
 
 

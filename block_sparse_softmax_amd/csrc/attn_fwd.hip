@@ -95,6 +95,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(const GroupParams
   const int4 split = reinterpret_cast<const int4*>(p.items)[2 * item_idx + 1];
   const int head = __builtin_amdgcn_readfirstlane(item.x);
   if (head < 0) return;  // queue padding
+  if constexpr (kChecked) {
+    if (!item_checked(p, item, split)) return;
+  }
   const int qtile = __builtin_amdgcn_readfirstlane(item.y);
   const int e_begin = __builtin_amdgcn_readfirstlane(item.z);
   const int e_end = __builtin_amdgcn_readfirstlane(item.w);
@@ -732,6 +735,13 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(const GroupParams 
   const int qtile = __builtin_amdgcn_readfirstlane(row.y);
   const int slot0 = __builtin_amdgcn_readfirstlane(row.z);
   const int npieces = __builtin_amdgcn_readfirstlane(row.w);
+  if constexpr (kChecked) {
+    const uint32_t bits = merge_row_violations(head, qtile, slot0, npieces, p.H, p.L, p.n_slots);
+    if (bits != 0) {
+      if (threadIdx.x == 0 && p.check != nullptr) atomicOr(p.check, bits);
+      return;
+    }
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h2 = lane >> 5, l31 = lane & 31;
@@ -818,7 +828,43 @@ hipError_t launch_d(const GroupParams& g, int blocks, int B, hipStream_t stream,
 // only the address hipGetSymbolAddress returns (per device) is passed on.
 static __device__ __align__(256) unsigned char scratch[kFwdScratchBytes];
 
+// Violation bits of the checked build's range checks (one word per device).
+static __device__ uint32_t check_word;
+
+// The current device's address of check_word (looked up once per device).
+hipError_t check_word_addr(uint32_t** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static uint32_t* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(check_word));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<uint32_t*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
+
+bool checked_build() { return kChecked; }
+
+hipError_t check_bits(uint32_t* bits, bool clear) {
+  uint32_t* w = nullptr;
+  hipError_t e = check_word_addr(&w);
+  if (e != hipSuccess) return e;
+  e = hipMemcpy(bits, w, sizeof(uint32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess || !clear) return e;
+  const uint32_t zero = 0;
+  return hipMemcpy(w, &zero, sizeof(uint32_t), hipMemcpyHostToDevice);
+}
 
 hipError_t fwd_scratch(void** ptr, size_t* bytes) {
   constexpr int kMaxDevices = 64;
@@ -852,11 +898,21 @@ hipError_t launch_fwd(const GroupParams& g, int D, int B, hipStream_t stream, hi
     if (e == hipSuccess && stop != nullptr) e = hipEventRecord(stop, stream);
     return e;
   }
+  const GroupParams* gp = &g;
+  GroupParams gc;
+  if constexpr (dev::kChecked) {  // the kernels report range violations into the device's check word
+    uint32_t* w = nullptr;
+    hipError_t e = check_word_addr(&w);
+    if (e != hipSuccess) return e;
+    gc = g;
+    for (int j = 0; j < gc.n_jobs; ++j) gc.job[j].check = w;
+    gp = &gc;
+  }
   switch (D) {
-    case 64: return launch_d<64>(g, static_cast<int>(blocks), B, stream, start, stop);
-    case 80: return launch_d<80>(g, static_cast<int>(blocks), B, stream, start, stop);
-    case 128: return launch_d<128>(g, static_cast<int>(blocks), B, stream, start, stop);
-    case 256: return launch_d<256>(g, static_cast<int>(blocks), B, stream, start, stop);
+    case 64: return launch_d<64>(*gp, static_cast<int>(blocks), B, stream, start, stop);
+    case 80: return launch_d<80>(*gp, static_cast<int>(blocks), B, stream, start, stop);
+    case 128: return launch_d<128>(*gp, static_cast<int>(blocks), B, stream, start, stop);
+    case 256: return launch_d<256>(*gp, static_cast<int>(blocks), B, stream, start, stop);
     default: return hipErrorInvalidValue;
   }
 }

@@ -67,6 +67,9 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void attn_fwd_sg_kernel
   const int4 split = reinterpret_cast<const int4*>(p.items)[2 * item_idx + 1];
   const int head = __builtin_amdgcn_readfirstlane(item.x);
   if (head < 0) return;  // queue padding
+  if constexpr (kChecked) {
+    if (!item_checked(p, item, split)) return;
+  }
   const int qtile = __builtin_amdgcn_readfirstlane(item.y);
   const int e_begin = __builtin_amdgcn_readfirstlane(item.z);
   const int e_end = __builtin_amdgcn_readfirstlane(item.w);

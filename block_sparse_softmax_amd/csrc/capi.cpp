@@ -139,6 +139,8 @@ attn_status make_job(const attn_plan& p, const attn_tensor* q, const attn_tensor
   f.prefix = static_cast<int32_t>(std::min<int64_t>(p.prefix, p.L));
   f.kv_group = static_cast<int32_t>(p.H / hkv);
   f.pingpong = p.pingpong ? 1 : 0;
+  f.n_entries = static_cast<int32_t>(p.kv_entries.size());
+  f.n_slots = split ? static_cast<int32_t>(p.n_partial_slots) : 0;
   *out = f;
   *queue_len = static_cast<int32_t>(n_items / 8);
   return ATTN_OK;
@@ -249,6 +251,14 @@ attn_status attn_plan_schedule(const attn_plan* p, int64_t* n_items, const int32
   if (!p) { set_error("plan is NULL"); return ATTN_E_INVAL; }
   if (n_items) *n_items = static_cast<int64_t>(p->items.size());
   if (items) *items = reinterpret_cast<const int32_t*>(p->items.data());
+  return ATTN_OK;
+}
+
+attn_status attn_checks(int32_t* enabled, uint32_t* bits, int32_t clear) {
+  if (enabled) *enabled = checked_build() ? 1 : 0;
+  if (!bits) return ATTN_OK;
+  hipError_t e = check_bits(bits, clear != 0);
+  if (e != hipSuccess) return hip_fail(e, "reading the check word");
   return ATTN_OK;
 }
 

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "checks.hpp"
 #include "kernels.hpp"
 #include "tile_common.hpp"
 
@@ -38,6 +39,36 @@ struct Lds {
   // buffers 0-1 hold K tiles, 2-3 V tiles
   __device__ static constexpr int buf_off(int buf) { return buf < 2 ? buf * KT : 2 * KT + (buf - 2) * VT; }
 };
+
+#ifdef BSS_CHECKED
+constexpr bool kChecked = true;
+#else
+constexpr bool kChecked = false;
+#endif
+
+// Checked build, at the top of a forward kernel (every wave of the work-group
+// runs it, before any barrier): false, with the violations recorded in the
+// launch's check word, when the item's fields, the pointers it needs or the
+// key tiles it lists are out of range; the work-group then returns without
+// touching memory through them.
+__device__ inline bool item_checked(const FwdParams& p, int4 item, int4 split) {
+  const ItemFields f{item.x, item.y, item.z, item.w, split.x, split.y, split.z};
+  uint32_t bits = item_violations(f, p.H, p.L, p.n_entries, p.n_slots);
+  if (f.npieces > 1 && p.partials == nullptr) bits |= kCheckPointer;
+  if (p.kind == kMaskWindow && p.head_left == nullptr) bits |= kCheckPointer;
+  if (p.q == nullptr || p.k == nullptr || p.v == nullptr || p.o == nullptr || p.kv == nullptr) bits |= kCheckPointer;
+  if (bits == 0) {
+    for (int e = f.begin; e < f.end; ++e) {
+      if (!entry_in_range(p.kv[e], p.L)) {
+        bits |= kCheckEntry;
+        break;
+      }
+    }
+  }
+  if (bits == 0) return true;
+  if (threadIdx.x == 0 && p.check != nullptr) atomicOr(p.check, bits);
+  return false;
+}
 
 }  // namespace dev
 

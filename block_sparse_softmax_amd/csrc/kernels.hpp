@@ -42,6 +42,9 @@ struct FwdParams {
   int32_t prefix;             // prefix tokens added to every row's set (0 = none)
   int32_t kv_group;           // query heads per K/V head (grouped-query attention; 1 = MHA)
   int32_t pingpong;           // head dim 128: the plan picks the two-group kernel (long rows)
+  int32_t n_entries;          // list entries of the plan's image (range checks of the checked build)
+  int32_t n_slots;            // partial-state slots of this launch (0 without split rows)
+  uint32_t* check;            // violation bits of the checked build (set by launch_fwd)
   float* lse;                 // optional [B][H][L]: row log-sum-exp (natural log), -inf for empty rows
 };
 
@@ -69,6 +72,12 @@ hipError_t launch_fwd(const GroupParams& g, int D, int B, hipStream_t stream, hi
 // device with hipGetSymbolAddress) and its size.
 constexpr size_t kFwdScratchBytes = size_t(32) << 20;
 hipError_t fwd_scratch(void** ptr, size_t* bytes);
+
+// Checked build (BSS_CHECKED): whether the kernels carry range checks, and the
+// current device's violation bits (read after the device has finished the
+// launches; `clear` zeroes them).  Without the checks the bits stay 0.
+bool checked_build();
+hipError_t check_bits(uint32_t* bits, bool clear);
 
 // Backward pass (attn_bwd.hip).
 struct BwdParams {

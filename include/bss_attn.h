@@ -469,6 +469,22 @@ attn_status attn_decode_fwd(const attn_tensor* q, const attn_tensor* k_cache, co
 /* Free a plan (NULL is allowed). */
 void attn_plan_destroy(attn_plan* plan);
 
+/*
+ * Range checks of the checked build (libbss_attn_checked.so, built from the
+ * same sources with BSS_CHECKED): before a forward work-group or split-row
+ * merge touches memory, it checks its work item (head, query tile, list range,
+ * piece and partial slot), the key tiles the item lists and the pointers it
+ * needs against the launch's sizes; on a violation it ORs these bits into the
+ * device's check word and returns without computing:
+ *   1 head, 2 query tile, 4 list range, 8 piece or slot, 16 listed key tile,
+ *   32 split-row record, 64 NULL pointer.
+ * *enabled (optional): 1 in the checked build, 0 otherwise (bits stay 0).
+ * *bits (optional): the current device's check word; the caller synchronizes
+ * the launches first.  clear != 0 zeroes the word after reading it.
+ * Errors: ATTN_E_HIP.
+ */
+attn_status attn_checks(int32_t* enabled, uint32_t* bits, int32_t clear);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* attn_last_error(void);
 

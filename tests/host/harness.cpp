@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "bss_attn.h"
+#include "checks.hpp"
 #include "mock_hip.hpp"
 #include "plan.hpp"
 #include "plan_cache.hpp"
@@ -66,6 +67,48 @@ void check_image(const attn_plan& p) {
     CHECK(m.npieces >= 2 && m.slot >= 0 && m.slot + m.npieces <= p.n_partial_slots);
   }
   CHECK(p.layout.bytes <= p.layout.total);
+  // the checked build's kernel-side range checks pass on every compiled image
+  // (split schedule with the plan's partial slots, unsplit with none)
+  const int32_t L = static_cast<int32_t>(p.L), H = static_cast<int32_t>(p.H);
+  for (int pass = 0; pass < 2; ++pass) {
+    const auto& items = pass == 0 ? p.items : p.items_unsplit;
+    const int32_t slots = pass == 0 ? static_cast<int32_t>(p.n_partial_slots) : 0;
+    for (const bss::Item& it : items) {
+      if (it.head < 0) continue;
+      const bss::ItemFields f{it.head, it.qtile, it.begin, it.end, it.slot, it.piece, it.npieces};
+      CHECK(bss::item_violations(f, H, L, static_cast<int32_t>(nnz), slots) == 0);
+    }
+  }
+  for (int32_t e : p.kv_entries) CHECK(bss::entry_in_range(e, L));
+  for (const bss::MergeRow& m : p.merge_rows)
+    CHECK(bss::merge_row_violations(m.head, m.qtile, m.slot, m.npieces, H, L,
+                                    static_cast<int32_t>(p.n_partial_slots)) == 0);
+}
+
+// The checks flag each kind of planted violation, and only that kind.
+void test_range_check_predicates() {
+  const int32_t H = 4, L = 1000, nnz = 50, slots = 6;  // 8 query tiles, 16 key tiles
+  const bss::ItemFields ok{1, 7, 10, 20, 2, 1, 3};
+  CHECK(bss::item_violations(ok, H, L, nnz, slots) == 0);
+  auto with = [&](auto edit) { bss::ItemFields f = ok; edit(f); return bss::item_violations(f, H, L, nnz, slots); };
+  CHECK(with([](bss::ItemFields& f) { f.head = 4; }) == bss::kCheckHead);
+  CHECK(with([](bss::ItemFields& f) { f.head = -2; }) == bss::kCheckHead);
+  CHECK(with([](bss::ItemFields& f) { f.qtile = 8; }) == bss::kCheckQTile);
+  CHECK(with([](bss::ItemFields& f) { f.qtile = -1; }) == bss::kCheckQTile);
+  CHECK(with([](bss::ItemFields& f) { f.end = 51; }) == bss::kCheckRange);
+  CHECK(with([](bss::ItemFields& f) { f.begin = 21; }) == bss::kCheckRange);
+  CHECK(with([](bss::ItemFields& f) { f.begin = -1; }) == bss::kCheckRange);
+  CHECK(with([](bss::ItemFields& f) { f.piece = 3; }) == bss::kCheckPiece);
+  CHECK(with([](bss::ItemFields& f) { f.npieces = 0; f.piece = 0; }) == bss::kCheckPiece);
+  CHECK(with([](bss::ItemFields& f) { f.slot0 = 4; }) == bss::kCheckPiece);    // slots 4..6 of 6
+  CHECK(with([](bss::ItemFields& f) { f.slot0 = 3; }) == 0);                    // slots 3..5
+  CHECK(with([](bss::ItemFields& f) { f.npieces = 1; f.piece = 0; f.slot0 = 99; }) == 0);  // unsplit: no slot
+  CHECK(with([](bss::ItemFields& f) { f.head = 9; f.end = 99; }) == (bss::kCheckHead | bss::kCheckRange));
+  CHECK(bss::entry_in_range((15 << 1) | 1, L) && !bss::entry_in_range(16 << 1, L) && !bss::entry_in_range(-1, L));
+  CHECK(bss::merge_row_violations(3, 7, 4, 2, H, L, slots) == 0);
+  CHECK(bss::merge_row_violations(3, 7, 5, 2, H, L, slots) == bss::kCheckMergeRow);
+  CHECK(bss::merge_row_violations(3, 7, 0, 1, H, L, slots) == bss::kCheckMergeRow);
+  CHECK(bss::merge_row_violations(4, 0, 0, 2, H, L, slots) == bss::kCheckMergeRow);
 }
 
 attn_tensor fake_tensor(uintptr_t addr, int64_t B, int64_t L, int64_t H, int64_t D) {
@@ -305,6 +348,7 @@ int main() {
   test_backward_records();
   test_noalloc();
   test_images_in_bounds();
+  test_range_check_predicates();
   if (g_failures) {
     std::printf("%d check(s) failed\n", g_failures);
     return 1;

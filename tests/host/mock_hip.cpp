@@ -49,6 +49,13 @@ hipError_t launch_reorder(const ReorderParams&, hipStream_t, hipEvent_t, hipEven
 hipError_t launch_decode(const DecodeParams&, int, hipStream_t, hipEvent_t, hipEvent_t) { return hipSuccess; }
 
 // the library's static scratch, at a fixed fake device address
+bool checked_build() { return false; }
+
+hipError_t check_bits(uint32_t* bits, bool) {
+  *bits = 0;
+  return hipSuccess;
+}
+
 hipError_t fwd_scratch(void** ptr, size_t* bytes) {
   *ptr = reinterpret_cast<void*>(mock::kScratchAddr);
   *bytes = kFwdScratchBytes;

@@ -33,6 +33,22 @@ def test_library_exports_every_declared_symbol(lib):
     assert lib.attn_version().decode().startswith("bss_attn")
 
 
+def test_checked_library_exports_the_same_symbols():
+    """The checked build (range checks in the forward kernels) loads and exports every declared symbol
+    too; its attn_checks reports the checks enabled (no GPU call: only the flag is asked for)."""
+    import ctypes
+    from block_sparse_softmax_amd.build import LIB_CHECKED
+    if not os.path.exists(LIB_CHECKED):
+        pytest.skip("checked build missing")
+    chk = ctypes.CDLL(LIB_CHECKED)
+    for name in _lib.EXPORTS:
+        assert hasattr(chk, name), name
+    en = ctypes.c_int32(-1)
+    assert chk.attn_checks(ctypes.byref(en), None, 0) == 0 and en.value == 1
+    en.value = -1
+    assert _lib.load_library().attn_checks(ctypes.byref(en), None, 0) == 0 and en.value == 0
+
+
 def _compare(mask, L, H, D=64):
     plan = _lib.Plan(mask, L, H, D)
     bm, bn, rp, kv, fl = plan.tiles()
