@@ -195,8 +195,8 @@ def _workload_kernel(w) -> tuple:
 
 
 def _counter_values(run_dir: str, counter: str, kernel: str):
-    """Per-dispatch values of `counter` for kernels whose name contains `kernel`, from the
-    counter_collection.csv files rocprofv3 wrote under run_dir."""
+    """Per-dispatch values of `counter` for kernels whose name contains `kernel`, in dispatch order,
+    from the counter_collection.csv files rocprofv3 wrote under run_dir."""
     import csv
     import glob
     vals = []
@@ -204,39 +204,46 @@ def _counter_values(run_dir: str, counter: str, kernel: str):
         with open(path) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]:
-                    vals.append(float(r["Counter_Value"]))
+                    vals.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
     if not vals:
         raise SystemExit(f"no {counter} values for {kernel} under {run_dir}")
-    return vals
+    return [v for _, v in sorted(vals)]
+
+
+# the counter passes run bench.py with --steps 3 --warmup 1: the kernel's first four dispatches are the
+# grouped launch (one dispatch for all masks of the workload); the per-mask launches follow
+TRAFFIC_RUN_ARGS = "--quick --no-cpu-baseline --no-clocks --steps 3 --warmup 1 --reps 3"
+GROUPED_DISPATCHES = slice(1, 4)   # the timed steps (the warm-up dispatch is left out)
 
 
 def traffic_summary(workload: str, pmc_dir: str, copy_mib: int = 1024, out_dir: str | None = None) -> str:
-    """Write profiles/attn_fwd_<workload>_<mask>_traffic.txt from four rocprofv3 counter passes under
+    """Write profiles/attn_fwd_<workload>_<masks>_traffic.txt from four rocprofv3 counter passes under
     pmc_dir (FETCH_SIZE and WRITE_SIZE of the workload's launches and of a plain copy of copy_mib MiB,
-    each scaled so that the copy reads as its known size).  Single-mask workloads only."""
+    each scaled so that the copy reads as its known size): HBM bytes of the workload's grouped launch
+    (median of its timed dispatches)."""
     import statistics
     from block_sparse_softmax_amd import inputs as gen
     w = gen.workload(workload)
-    if len(w["masks"]) != 1:
-        raise SystemExit("traffic summaries cover single-mask workloads")
-    label = next(iter(w["masks"]))
+    label = "+".join(w["masks"])
     kind, kern = _workload_kernel(w)
-    run = (f"python3 bench.py --workload {workload} --quick --no-cpu-baseline --no-clocks --steps 3 --warmup 1 "
-           "--reps 3")
+    run = f"python3 bench.py --workload {workload} {TRAFFIC_RUN_ARGS}"
     copy = f"python3 bench.py --calibrate-copy {copy_mib} --steps 3"
     kib = copy_mib * 1024.0
     fc = statistics.median(_counter_values(os.path.join(pmc_dir, "FETCH_SIZE_copy"), "FETCH_SIZE", "copyBuffer"))
     wc = statistics.median(_counter_values(os.path.join(pmc_dir, "WRITE_SIZE_copy"), "WRITE_SIZE", "copyBuffer"))
     fs, ws = kib / fc, kib / wc
-    fv = _counter_values(os.path.join(pmc_dir, f"FETCH_SIZE_{workload}"), "FETCH_SIZE", kern)
-    wv = _counter_values(os.path.join(pmc_dir, f"WRITE_SIZE_{workload}"), "WRITE_SIZE", kern)
+    fv = _counter_values(os.path.join(pmc_dir, f"FETCH_SIZE_{workload}"), "FETCH_SIZE", kern)[GROUPED_DISPATCHES]
+    wv = _counter_values(os.path.join(pmc_dir, f"WRITE_SIZE_{workload}"), "WRITE_SIZE", kern)[GROUPED_DISPATCHES]
     f, wr = statistics.median(fv), statistics.median(wv)
     hbm = (f * fs + wr * ws) * 1024
-    alg = _io_bytes(w)
+    alg = _io_bytes(w) * len(w["masks"])
     cmds = "\n".join(
         f"rocprofv3 --pmc {c} --output-format csv -d {pmc_dir}/{c}_{tag} -o run -- {cmd}"
         for tag, cmd in ((workload, run), ("copy", copy)) for c in ("FETCH_SIZE", "WRITE_SIZE"))
-    txt = f"""# {kern}, {workload} launch ({label}) — HBM traffic per launch
+    shown = kern + (">" if "<" in kern else "")
+    txt = f"""# {shown}, {workload} grouped launch ({label}) — HBM traffic per launch
+
+{WORKLOADS[workload]}.
 
 Commands (from the repository root, one MI355X; each counter in its own pass), then
 `python3 bench.py --traffic-summary {pmc_dir} --workload {workload}`:
@@ -252,13 +259,13 @@ Calibration with a plain {copy_mib} MiB device copy ({kib:,.0f} KiB read and wri
 - FETCH_SIZE reads {fc:.1f} KiB per copy -> scale {fs:.4f}
 - WRITE_SIZE reads {wc:.1f} KiB per copy -> scale {ws:.4f}
 
-Launches of the run (median of {len(fv)}):
+The grouped launch (one dispatch of {shown} for all masks; median of the {len(fv)} timed dispatches):
 
 - FETCH_SIZE {f:.1f} KiB raw -> {f * 1024 * fs / 1e6:.2f} MB
 - WRITE_SIZE {wr:.1f} KiB raw -> {wr * 1024 * ws / 1e6:.2f} MB
 
 hbm_bytes_per_launch: {hbm:.0f}
-algorithmic_bytes_per_launch: {alg}  (Q, K, V read once and O written once, bf16)
+algorithmic_bytes_per_launch: {alg}  (per mask: Q, K, V read once and O written once, bf16)
 ratio: {hbm / alg:.3f}
 """
     path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"attn_fwd_{workload}_{label}_traffic.txt")
@@ -267,35 +274,54 @@ ratio: {hbm / alg:.3f}
     return path
 
 
-def trace_summary(workload: str, trace_dir: str, out_dir: str | None = None) -> str:
-    """Write profiles/<kernel>_<workload>_stats.md from a rocprofv3 --kernel-trace --stats run of
-    this workload under trace_dir (the command below): the forward kernel's calls and durations,
-    and the throughput at the average duration."""
+TRACE_RUN_ARGS = "--quick --no-cpu-baseline --no-clocks --steps 10 --warmup 2 --reps 10"
+TRACE_GROUPED = slice(2, 12)   # the timed grouped launches of a TRACE_RUN_ARGS run
+
+
+def _kernel_rows(path_glob: str, kernel: str):
+    """(dispatch id, kernel name, duration ms) of kernels whose name contains `kernel`, dispatch order."""
     import csv
     import glob
+    out = []
+    for path in glob.glob(path_glob, recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if kernel in r["Kernel_Name"]:
+                    out.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6))
+    return sorted(out)
+
+
+def trace_summary(workload: str, trace_dir: str, out_dir: str | None = None) -> str:
+    """Write profiles/<kernel>_<workload>_stats.md from a rocprofv3 --kernel-trace --stats run of this
+    workload under trace_dir (the command below): the grouped launch's timed dispatches of the forward
+    kernel (all masks of the workload in one dispatch) and the throughput at their average duration."""
     import statistics
     from block_sparse_softmax_amd import inputs as gen
     from block_sparse_softmax_amd._lib import Plan
     w = gen.workload(workload)
     kind, kern = _workload_kernel(w)
-    durs, name = [], None
-    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
-        with open(path) as f:
-            for r in csv.DictReader(f):
-                if kern in r["Kernel_Name"]:
-                    name = name or r["Kernel_Name"]
-                    durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
-    if not durs:
+    rows = _kernel_rows(os.path.join(trace_dir, "**", "*kernel_trace.csv"), kern)
+    if not rows:
         raise SystemExit(f"no {kern} dispatches under {trace_dir}")
+    name = rows[0][1]
+    durs = [d for _, _, d in rows[TRACE_GROUPED]]
+    merges = [d for _, _, d in _kernel_rows(os.path.join(trace_dir, "**", "*kernel_trace.csv"),
+                                           "attn_merge_kernel")]
     pairs = sum(int(Plan(m, w["L"], w["H"], w["D"]).pairs()[1]) for m in w["masks"].values())
     flops = 4.0 * w["D"] * pairs * w["B"]
     avg, med = statistics.mean(durs), statistics.median(durs)
     tf = flops / (avg * 1e-3) / 1e12
     cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o run -- python3 bench.py "
-           f"--workload {workload} --quick --no-cpu-baseline --no-clocks --steps 10 --warmup 2 --reps 10")
-    txt = f"""# {kern}, {workload} — kernel trace
+           f"--workload {workload} {TRACE_RUN_ARGS}")
+    merge_line = ""
+    if merges:
+        merge_line = (f"\nThe run also holds {len(merges)} dispatches of the split-row merge "
+                      f"(attn_merge_kernel), {statistics.mean(merges) * 1e3:.1f} us on average.\n")
+    shown = kern + (">" if "<" in kern else "")
+    txt = f"""# {shown}, {workload} — kernel trace
 
-{WORKLOADS[workload]}.
+{WORKLOADS[workload]}; masks {", ".join(w["masks"])} in one grouped launch.
 
 Command (from the repository root, one MI355X), then
 `python3 bench.py --trace-summary {trace_dir} --workload {workload}`:
@@ -306,16 +332,106 @@ Command (from the repository root, one MI355X), then
 
 kernel_source_sha256_16: {_kernel_hash(kind)}
 
-| kernel | calls | average | median | min | max |
+| kernel | timed grouped dispatches | average | median | min | max |
 |---|---|---|---|---|---|
-| {name} | {len(durs)} | {avg:.3f} ms | {med:.3f} ms | {min(durs):.3f} ms | {max(durs):.3f} ms |
+| {name} | {len(durs)} | {avg:.4f} ms | {med:.4f} ms | {min(durs):.4f} ms | {max(durs):.4f} ms |
 
-Effective throughput at the average duration: {flops / 1e12:.3f} TFLOP (4 d per allowed pair) / {avg:.3f} ms =
-{tf:.1f} TFLOP/s = {tf / PEAK_BF16_TFLOPS:.3f} of the {PEAK_BF16_TFLOPS} TFLOP/s bf16 peak.  The calls are the
-warm-up, timed and per-launch-protocol launches of the command (the last with a cache flush between
-launches when the working set fits the last-level cache).
+Effective throughput at the average duration: {flops / 1e12:.4f} TFLOP (4 d per allowed pair) / {avg:.4f} ms =
+{tf:.1f} TFLOP/s = {tf / PEAK_BF16_TFLOPS:.3f} of the {PEAK_BF16_TFLOPS} TFLOP/s bf16 peak.  The kernel's
+{len(rows)} dispatches of the run are 2 warm-up and 10 timed grouped launches (summarised here), then the
+per-launch protocol (each mask alone, with a cache flush between launches when the working set fits the
+last-level cache).
+{merge_line}"""
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"{kern.split('<')[0]}_{workload}_stats.md")
+    with open(path, "w") as fh:
+        fh.write(txt)
+    return path
+
+
+def kernels_summary(trace_dir: str, name: str, run_args: str, out_dir: str | None = None) -> str:
+    """Write profiles/<name>_kernels.md: every kernel of a rocprofv3 --kernel-trace run of
+    `python3 bench.py <run_args>` under trace_dir, with its dispatch count and durations."""
+    import statistics
+    rows = _kernel_rows(os.path.join(trace_dir, "**", "*kernel_trace.csv"), "")
+    by = {}
+    for _, kname, d in rows:
+        by.setdefault(kname, []).append(d)
+    cmd = f"rocprofv3 --kernel-trace --stats --output-format csv -d {trace_dir} -o run -- python3 bench.py {run_args}"
+    lines = [f"# Kernels of `bench.py {run_args}` — kernel trace", "",
+             "Command (from the repository root, one MI355X), then",
+             f"`python3 bench.py --kernels-summary {trace_dir} --summary-name {name} --run-args \"{run_args}\"`:",
+             "", "```", cmd, "```", "",
+             "Source hashes (sha256[:16]): " + ", ".join(
+                 f"{k} {_kernel_hash(k)}" for k in KERNEL_SRC), "",
+             "| kernel | calls | average (us) | median (us) | min (us) | max (us) | total (ms) |",
+             "|---|---|---|---|---|---|---|"]
+    for kname, ds in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        short = kname.replace("void ", "").replace("(anonymous namespace)::", "")
+        short = short.split("(bss::")[0].split("(")[0] if "bss::" in short else short[:90]
+        lines.append(f"| {short} | {len(ds)} | {statistics.mean(ds) * 1e3:.1f} | {statistics.median(ds) * 1e3:.1f} "
+                     f"| {min(ds) * 1e3:.1f} | {max(ds) * 1e3:.1f} | {sum(ds):.2f} |")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"{name}_kernels.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    return path
+
+
+def counters_summary(workload: str, pmc_dir: str, out_dir: str | None = None) -> str:
+    """Write profiles/<kernel>_<workload>_counters.md from two rocprofv3 passes under pmc_dir: MFMA
+    utilisation and counted bf16 MFMA work (MfmaUtil, SQ_INSTS_VALU_MFMA_MOPS_BF16), L2 hits and misses
+    (TCC_HIT_sum, TCC_MISS_sum), each the median over the grouped launch's timed dispatches."""
+    import statistics
+    from block_sparse_softmax_amd import inputs as gen
+    from block_sparse_softmax_amd._lib import Plan
+    w = gen.workload(workload)
+    kind, kern = _workload_kernel(w)
+
+    def med(tag, counter):
+        return statistics.median(_counter_values(os.path.join(pmc_dir, f"{tag}_{workload}"), counter,
+                                                 kern)[GROUPED_DISPATCHES])
+    util = med("mfma", "MfmaUtil")
+    mops = med("mfma", "SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512
+    hit, miss = med("l2", "TCC_HIT_sum"), med("l2", "TCC_MISS_sum")
+    listed = 0
+    pairs = 0
+    for m in w["masks"].values():
+        plan = Plan(m, w["L"], w["H"], w["D"])
+        bm, bn, _, kv_tile, _ = plan.tiles()
+        listed += len(kv_tile) * bm * bn
+        pairs += int(plan.pairs()[1])
+    # per listed pair: 2 d for the score, 2 d' for the value mix, d' = d rounded up to 32 (the
+    # output tiles of the value MFMAs; d = 80 runs 96 rows)
+    d_out = 32 * ((w["D"] + 31) // 32)
+    listed_flops = 2.0 * (w["D"] + d_out) * listed * w["B"]
+    alg = 4.0 * w["D"] * pairs * w["B"]
+    run = f"python3 bench.py --workload {workload} {TRAFFIC_RUN_ARGS}"
+    shown = kern + (">" if "<" in kern else "")
+    txt = f"""# {shown}, {workload} grouped launch — MFMA utilisation, MFMA work, L2 hit rate
+
+{WORKLOADS[workload]}.
+
+Commands (from the repository root, one MI355X; one pass each), then
+`python3 bench.py --counters-summary {pmc_dir} --workload {workload}`:
+
+```
+rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 --output-format csv -d {pmc_dir}/mfma_{workload} -o run -- {run}
+rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum --output-format csv -d {pmc_dir}/l2_{workload} -o run -- {run}
+```
+
+kernel_source_sha256_16: {_kernel_hash(kind)}
+
+Per grouped launch (median of the timed dispatches):
+
+| measure | value |
+|---|---|
+| MfmaUtil (rocprofv3's derived metric: SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs) | {util:.1f} % |
+| MFMA work counted (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) | {mops / 1e12:.4f} TFLOP |
+| MFMA work of the listed 128 x 64 tiles (2 d + 2 d' per pair, d' = {d_out}) | {listed_flops / 1e12:.4f} TFLOP |
+| algorithmic work (4 d per allowed pair) | {alg / 1e12:.4f} TFLOP |
+| L2 hits / misses (TCC_HIT_sum, TCC_MISS_sum) | {hit / 1e9:.3f} G / {miss / 1e9:.3f} G |
+| L2 hit rate | {100 * hit / max(hit + miss, 1):.1f} % |
 """
-    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"{kern}_{workload}_stats.md")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"{kern.split('<')[0]}_{workload}_counters.md")
     with open(path, "w") as fh:
         fh.write(txt)
     return path
@@ -748,6 +864,12 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB mebibytes (counter calibration)")
     ap.add_argument("--reps", type=int, default=20, help="launches per mask in the per-launch protocol")
+    ap.add_argument("--kernels-summary", default=None, metavar="DIR",
+                    help="summarise every kernel of a rocprofv3 kernel trace under DIR into profiles/ (no GPU)")
+    ap.add_argument("--summary-name", default="bench", help=argparse.SUPPRESS)
+    ap.add_argument("--run-args", default="", help=argparse.SUPPRESS)
+    ap.add_argument("--counters-summary", default=None, metavar="DIR",
+                    help="summarise rocprofv3 MFMA and L2 counter passes under DIR into profiles/ (no GPU)")
     ap.add_argument("--trace-summary", default=None, metavar="DIR",
                     help="summarise a rocprofv3 kernel trace of the workload under DIR into profiles/ (no GPU)")
     ap.add_argument("--traffic-summary", default=None, metavar="DIR",
@@ -758,6 +880,12 @@ def main(argv=None):
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
               "(the kernel shards by head with no exchange; see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+    if args.kernels_summary:
+        print(kernels_summary(args.kernels_summary, args.summary_name, args.run_args))
+        return
+    if args.counters_summary:
+        print(counters_summary(args.workload, args.counters_summary))
+        return
     if args.trace_summary:
         print(trace_summary(args.workload, args.trace_summary))
         return
@@ -776,6 +904,11 @@ def main(argv=None):
         sampler.close()
 
 
+def _progress(msg: str):
+    """One line per phase on stderr (the JSON result goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def _run(args, sampler):
     import torch
     device = torch.device(args.device)
@@ -790,7 +923,9 @@ def _run(args, sampler):
         return
 
     flusher = _Flusher(device)
+    _progress(f"setting up {args.workload}")
     setup = _setup(args.workload, device, args.layout)
+    _progress(f"timing {args.workload}")
     if args.only:
         setup["masks"] = [m for m in setup["masks"] if m["label"] == args.only]
     wall, per_group, per_mask, gc = _time(setup, args.steps, args.warmup, args.layout,
@@ -807,19 +942,23 @@ def _run(args, sampler):
             roof["frac_at_load_clock"] = roof["achieved"] / pk
             roof["socket_watts_under_load"] = c.get("socket_watts")
 
+    if not args.no_cpu_baseline:
+        _progress("cpu baseline (oracle on sampled rows)")
     cpu = None if args.no_cpu_baseline else _cpu_baseline(setup)
 
     extra = {}
     if not args.quick:
         if args.workload == "blocksparse128k":
             q, k, _ = setup["dev"]
+            _progress("pattern search")
             extra["rr_search128k"] = _bench_rr(q, k, 5, 1, args.layout)
             del q, k
         del setup
         torch.cuda.empty_cache()
-        for name in ("vit896", "vit1792", "lm_headwin", "blocksparse128k"):
+        for name in ("vit896", "vit1792", "lm_headwin", "blocksparse128k", "swa576_d256"):
             if name == args.workload:
                 continue
+            _progress(f"extra workload {name}")
             s2, r2, tf2, ms2, g2 = _workload_block(name, device, args.layout, max(5, args.steps // 2),
                                                    args.warmup, flusher, warm_s=0.2)
             extra[name] = dict(workload=WORKLOADS[name], ms_per_step=ms2, tflops=tf2 / (ms2 * 1e-3) / 1e12,
@@ -830,7 +969,9 @@ def _run(args, sampler):
             del s2
             torch.cuda.empty_cache()
         for name in ("vit896", "lm_headwin"):
+            _progress(f"backward {name}")
             extra[f"backward_{name}"] = _bench_bwd(name, device, 5, args.layout)
+        _progress("decode workloads")
         from block_sparse_softmax_amd.inputs import DECODE_WORKLOADS
         for name in DECODE_WORKLOADS:
             extra[name] = _bench_decode(name, device, 10)
