@@ -701,6 +701,31 @@ namespace {
 
 constexpr int kRrTileQ = 128;    // sampled queries per work-group of the scores kernel
 
+// Workspace of the search, 256-byte aligned parts: sampled queries (rows of
+// D bf16), stride-summed keys (hi then lo: rows of 2 D bf16 + 16 bytes), the
+// squared norms of the key aggregates by 8-dim piece, the heads' largest
+// key-aggregate norm, 1 / row sum, the query tiles to
+// recompute, and the per (key block, row) sums of the single pass.
+struct RrLayout {
+  size_t qs, ks, knorm2, kmax, linv, flags, u, total;
+};
+static RrLayout rr_layout(int64_t B, int64_t H, int64_t ns_pad, int64_t D, int64_t nb) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t bh = static_cast<size_t>(B) * static_cast<size_t>(H);
+  const size_t rows = bh * static_cast<size_t>(ns_pad);
+  RrLayout l{};
+  size_t o = 0;
+  l.qs = o; o = up(o + rows * static_cast<size_t>(D) * 2);
+  l.ks = o; o = up(o + rows * static_cast<size_t>(4 * D + 16));
+  l.knorm2 = o; o = up(o + rows * static_cast<size_t>(D / 8) * 4);
+  l.kmax = o; o = up(o + bh * 4);
+  l.linv = o; o = up(o + rows * 4);
+  l.flags = o; o = up(o + bh * static_cast<size_t>(ns_pad / kRrTileQ) * 4);
+  l.u = o; o = up(o + rows * static_cast<size_t>(nb) * 4);
+  l.total = o;
+  return l;
+}
+
 // Validate a search request and fill the kernel parameters (pointers except the workspace).
 static attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const attn_rr_params* prm, RrParams* out,
                        size_t* ws_bytes) {
@@ -753,8 +778,7 @@ static attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const 
   p.protect_last = prm->protect_last;
   p.kv_group = static_cast<int32_t>(H / k->H);
   *out = p;
-  // sampled queries (rows of D bf16), then stride-summed keys (rows of D bf16 + 16 pad bytes)
-  *ws_bytes = static_cast<size_t>(B) * H * ns_pad * (2 * D + (4 * D + 16));  // queries, then hi/lo key sums
+  *ws_bytes = rr_layout(B, H, ns_pad, D, nb).total;
   return ATTN_OK;
 }
 
@@ -876,8 +900,16 @@ attn_status attn_rr_search(const attn_tensor* q, const attn_tensor* k, const att
       return ATTN_E_WORKSPACE;
     }
     if (!aligned16(launch->workspace)) { set_error("workspace must be 16-byte aligned"); return ATTN_E_INVAL; }
-    p.qs = static_cast<uint16_t*>(launch->workspace);
-    p.ks = p.qs + static_cast<size_t>(p.B) * p.H * p.ns_pad * p.D;
+    const RrLayout lay = rr_layout(p.B, p.H, p.ns_pad, p.D, p.nb);
+    uint8_t* ws = static_cast<uint8_t*>(launch->workspace);
+    p.qs = reinterpret_cast<uint16_t*>(ws + lay.qs);
+    p.ks = reinterpret_cast<uint16_t*>(ws + lay.ks);
+    p.knorm2 = reinterpret_cast<float*>(ws + lay.knorm2);
+    p.kmax = reinterpret_cast<uint32_t*>(ws + lay.kmax);
+    p.linv = reinterpret_cast<float*>(ws + lay.linv);
+    p.flags = reinterpret_cast<int32_t*>(ws + lay.flags);
+    p.u = reinterpret_cast<float*>(ws + lay.u);
+    p.gate = 0;
     p.score = static_cast<float*>(block_score);
     p.bmask = static_cast<uint8_t*>(block_mask);
     hipError_t e = launch_rr_search(p, static_cast<hipStream_t>(launch->stream),

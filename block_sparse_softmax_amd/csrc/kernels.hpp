@@ -142,9 +142,16 @@ struct RrParams {
   int32_t B, H, L, D, S, Bs;
   int32_t ns, ns_pad, nb, protect_last;
   int32_t kv_group;           // query heads per K head (grouped-query attention)
+  // single-pass scores (workspace)
+  float* knorm2;              // [B][H][ns_pad][D / 8]: |stride sum|^2 by 8-dim piece
+  uint32_t* kmax;             // [B][H]: largest |stride sum| of the head, as float bits
+  float* linv;                // [B][H][ns_pad]: 1 / (row sum against the row's fixed reference)
+  int32_t* flags;             // [B][H][ns_pad / 128]: query tiles that need the two-pass recompute
+  float* u;                   // [B][H][nb][ns_pad]: per (key block, row) sums against the reference
+  int32_t gate;               // two-pass kernel: 1 = only the flagged query tiles
 };
 
-// Queue the three search kernels on `stream`; non-null events are recorded
+// Queue the search kernels on `stream`; non-null events are recorded
 // before the first and after the last.
 hipError_t launch_rr_search(const RrParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 

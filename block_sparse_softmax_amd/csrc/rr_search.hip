@@ -10,12 +10,20 @@
 //           relative: the importance GEMM then runs on the matrix cores with
 //           the key aggregate at fp32 accuracy (hi and lo are two k-ranges of
 //           one product against the same query fragments).
+//   kmax    the largest norm of the head's key aggregates.
 //   scores  the stride importance I = q . ksum / (S sqrt(d)) (Eq. 8) on
-//           v_mfma_f32_32x32x16_bf16, in two passes over the causal key
-//           strides j <= i: pass 1 keeps each row's running max and sum
-//           (Eq. 9's softmax denominator), pass 2 recomputes I, normalises
-//           and sums the probabilities straight into block scores S_mn
-//           (Eq. 10).  The stride-level matrix is never stored.
+//           v_mfma_f32_32x32x16_bf16, in ONE pass over the causal key
+//           strides j <= i: each row's probabilities are taken against a
+//           fixed reference r >= every I of the row (|q| |ksum|max, Cauchy-
+//           Schwarz), so the pass sums 2^(I - r) per (row, key block) and per
+//           row without knowing the row's max; the per-block sums go to the
+//           workspace (the stride-level matrix never exists).
+//   norm    S_mn = sum over the rows i of block m of u_in / l_i (Eq. 9-10).
+//   recompute  rows whose sum against r underflows (r far above the row's
+//           max: keys with large norms orthogonal to the query) are redone,
+//           per query tile, by the two-pass kernel: pass 1 keeps each row's
+//           running max and sum, pass 2 recomputes I, normalises and sums
+//           the probabilities into block scores.
 //   select  per query block m: of S_m,n (n <= m) ordered descending (ties to
 //           the lower n), keep the shortest prefix whose mass reaches tau
 //           times the row's mass (Eq. 11), found by a threshold search rather
@@ -90,6 +98,7 @@ __global__ __launch_bounds__(256) void rr_prep_kernel(const RrParams p) {
   const int j = static_cast<int>(row % p.ns_pad);
   const int bh = static_cast<int>(row / p.ns_pad);
   const int h = bh % p.H, b = bh / p.H;
+  if (j == 0 && c == 0) p.kmax[bh] = 0u;     // folded into by rr_kmax_kernel (next in the stream)
   bf16x8 qo = {}, ko = {}, kl = {};
   if (j < p.ns) {
     const int pos = j * p.S + (p.S - 1 - (h % p.S));
@@ -101,11 +110,17 @@ __global__ __launch_bounds__(256) void rr_prep_kernel(const RrParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += static_cast<float>(x[e]);
     }
+    float n2 = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       ko[e] = static_cast<__bf16>(acc[e]);
       kl[e] = static_cast<__bf16>(acc[e] - static_cast<float>(ko[e]));  // the difference is exact in fp32
+      const float x = static_cast<float>(ko[e]) + static_cast<float>(kl[e]);
+      n2 = __builtin_fmaf(x, x, n2);
     }
+    p.knorm2[t] = n2;                          // this piece's share of |hi + lo|^2 (rows of D / 8 pieces)
+  } else {
+    p.knorm2[t] = 0.f;
   }
   *reinterpret_cast<bf16x8*>(p.qs + row * p.D + 8 * c) = qo;
   uint16_t* kdst = p.ks + row * (2 * p.D + 8);                       // rows of 4 D + 16 bytes
@@ -142,6 +157,7 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p)
   const bf16x8* qs = reinterpret_cast<const bf16x8*>(p.qs) + bh_row * CPR;
   const unsigned char* ksb = reinterpret_cast<const unsigned char*>(p.ks) + bh_row * PITCH;
 
+  if (p.gate && p.flags[(static_cast<int64_t>(b) * p.H + h) * n_tiles + tile] == 0) return;  // whole work-group
   const int q0 = tile * kRrQ + 32 * wave;    // this wave's first sampled query
   const int qi = q0 + (lane & 31);           // this lane's query (column of I^T)
   const int half = lane >> 5;
@@ -295,6 +311,225 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p)
   }
 }
 
+// ---------------------------------------------------------------- kmax ----
+// One thread per stride row: |hi + lo| of the row (the aggregate the products
+// see) from rr_prep's per-piece squares, the largest over the wave, folded
+// into the head's word with an atomic max of the float's bits (norms are >= 0,
+// so the bits order like the values).  A wave never spans two heads: a head
+// has ns_pad rows, a multiple of 128.
+__global__ __launch_bounds__(256) void rr_kmax_kernel(const RrParams p) {
+  const int cpr = p.D / 8;
+  const int64_t rows = static_cast<int64_t>(p.B) * p.H * p.ns_pad;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  float n2 = 0.f;
+  if (row < rows) {
+    const float* pr = p.knorm2 + row * cpr;
+    for (int c = 0; c < cpr; ++c) n2 += pr[c];
+  }
+  float nrm = __builtin_sqrtf(n2);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) nrm = fmaxf(nrm, __shfl_xor(nrm, off));
+  if ((threadIdx.x & 63) == 0 && row < rows) atomicMax(p.kmax + row / p.ns_pad, __float_as_uint(nrm));
+}
+
+// ------------------------------------------------------ scores, one pass ----
+// The layout of rr_scores_kernel (128 sampled queries per work-group, key
+// strides staged 64 at a time, chunks of 32); one pass instead of two.  Lane
+// l's row i takes the reference r_i = |q_i| kmax scale (1 + 2^-8): every
+// computed I_ij scale is at most r_i (Cauchy-Schwarz, the products and sums'
+// rounding far inside the margin), so 2^(I_ij scale - r_i) <= 1 and the row's
+// sum l_i and its per-key-block sums u_in can be accumulated against r_i from
+// the first stride on.  u_in goes to the workspace ([key block][row], one
+// coalesced 128-byte store per wave and block); 1 / l_i too.  A row whose
+// l_i is below 2^-40 (r_i more than 40 + log2 of its strides above its max)
+// flags its query tile for the two-pass recompute.
+template <int D, int R>
+__global__ __launch_bounds__(kRrThreads) void rr_scores1p_kernel(const RrParams p) {
+  constexpr int KS = D / 16;
+  constexpr int PITCH = 4 * D + 16;
+  constexpr int CPR = D / 8;
+  constexpr int STAGE = 2 * kChunk;
+  constexpr int SBYTES = STAGE * PITCH;
+  constexpr int NI = SBYTES / 1024;
+  constexpr int NW_HI = (NI + 3) / 4, NW_LO = NI / 4;
+  constexpr int NBUF = (3 * SBYTES <= 80 * 1024) ? 3 : 2;
+  constexpr int AHEAD = NBUF - 1;
+  constexpr int KB = kChunk / R;             // key blocks in a chunk
+  static_assert(SBYTES % 1024 == 0, "a stage is whole 1 KiB copies");
+  static_assert(NW_HI < 16, "vmcnt immediate");
+  static_assert(R == 8 || R == 16 || R == 32, "strides per block");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * SBYTES];
+  __shared__ int bad_wave[4];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n_tiles = p.ns_pad / kRrQ;
+  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.x);  // longest (latest) tiles first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = static_cast<int64_t>(b) * p.H + h;
+  const int64_t bh_row = bh * p.ns_pad;
+  const bf16x8* qs = reinterpret_cast<const bf16x8*>(p.qs) + bh_row * CPR;
+  const unsigned char* ksb = reinterpret_cast<const unsigned char*>(p.ks) + bh_row * PITCH;
+
+  const int q0 = tile * kRrQ + 32 * wave;
+  const int qi = q0 + (lane & 31);
+  const int half = lane >> 5;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qf[s] = qs[static_cast<int64_t>(qi) * CPR + 2 * s + half];
+  const bool q_valid = qi < p.ns;
+  // the row's reference (log2 units): |q| over both halves of the lane pair
+  float qn2 = 0.f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qn2 = __builtin_fmaf(static_cast<float>(qf[s][e]), static_cast<float>(qf[s][e]), qn2);
+  }
+  qn2 = halves_sum32(qn2);
+  const float kmx = __uint_as_float(p.kmax[bh]);
+  const float rref = __builtin_sqrtf(qn2) * kmx * p.scale_log2 * (1.f + 0x1p-8f);
+
+  const int last_chunk_wg = (tile * kRrQ + kRrQ - 1) / kChunk;
+  const int last_chunk = q0 / kChunk;
+  const int n_chunks = last_chunk_wg + 1;
+  const int n_stage = n_chunks / 2;
+
+  const uint32_t smem_lds = dev::lds_addr(smem);
+  const int nw = (NI - wave + 3) / 4;
+  auto issue_stage = [&](int st) __attribute__((always_inline)) {
+    const uint64_t src = dev::uniform_u64(reinterpret_cast<uint64_t>(ksb) + static_cast<uint64_t>(st) * SBYTES);
+    const uint32_t dst = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+        static_cast<int>(smem_lds + (st % NBUF) * SBYTES)));
+#pragma unroll
+    for (int i = 0; i < NW_HI; ++i) {
+      const int ins = wave + 4 * i;
+      if (ins < NI) dev::dma16(src + static_cast<uint64_t>(ins) * 1024, 16 * lane, dst + ins * 1024);
+    }
+  };
+  auto wait_stage = [&](bool next_in_flight) __attribute__((always_inline)) {
+    if (!next_in_flight) dev::wait_vmcnt<0>();
+    else if (nw == NW_HI) dev::wait_vmcnt<NW_HI>();
+    else dev::wait_vmcnt<NW_LO>();
+  };
+  auto chunk_scores = [&](int buf, int sub) __attribute__((always_inline)) {
+    f32x16 acc = {};
+    const unsigned char* base = smem + buf * SBYTES + (sub * kChunk + (lane & 31)) * PITCH + half * 16;
+#pragma unroll
+    for (int s = 0; s < 2 * KS; ++s) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(base + 32 * s);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s % KS], acc, 0, 0, 0);
+    }
+    return acc;
+  };
+  auto key_of = [&](int c, int r) __attribute__((always_inline)) { return c * kChunk + 8 * (r >> 2) + 4 * half + (r & 3); };
+
+  float l_run = 0.f;                         // the row's sum against rref (both halves: equal in l and l ^ 32)
+  float* ucol = p.u + bh * p.nb * static_cast<int64_t>(p.ns_pad) + qi;
+  issue_stage(0);
+  if (AHEAD > 1 && n_stage > 1) issue_stage(1);
+  for (int st = 0; st < n_stage; ++st) {
+    wait_stage(AHEAD > 1 && st + 1 < n_stage);
+    __syncthreads();
+    if (st + AHEAD < n_stage) issue_stage(st + AHEAD);
+    const int buf = st % NBUF;
+    f32x16 accs[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+      if (2 * st + sub <= last_chunk) accs[sub] = chunk_scores(buf, sub);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int c = 2 * st + sub;
+      if (c <= last_chunk) {
+        const f32x16& acc = accs[sub];
+        const bool open = c < last_chunk && q0 + 31 < p.ns;
+        float bs[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) bs[kb] = 0.f;
+        if (open) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            bs[(8 * (r >> 2) + 4 * half + (r & 3)) / R] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], p.scale_log2, -rref));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = key_of(c, r);
+            const float pr = (q_valid && j <= qi) ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], p.scale_log2, -rref)) : 0.f;
+            bs[(8 * (r >> 2) + 4 * half + (r & 3)) / R] += pr;
+          }
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const float v = halves_sum32(bs[kb]);
+          l_run += v;
+          const int kblk = (c * kChunk) / R + kb;
+          if (half == 0 && kblk < p.nb) ucol[static_cast<int64_t>(kblk) * p.ns_pad] = v;
+        }
+      }
+    }
+  }
+  if (half == 0) p.linv[bh_row + qi] = (q_valid && l_run > 0.f) ? 1.f / l_run : 0.f;
+  const bool bad = q_valid && !(l_run >= 0x1p-40f);
+  const uint64_t any_bad = __builtin_amdgcn_ballot_w64(bad);
+  if (lane == 0) bad_wave[wave] = any_bad != 0 ? 1 : 0;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    p.flags[bh * n_tiles + tile] = bad_wave[0] | bad_wave[1] | bad_wave[2] | bad_wave[3];
+}
+
+// ---------------------------------------------------------------- norm ----
+// S_mn = sum over the rows i of query block m (i < ns) of u_in / l_i, for the
+// causal pairs n <= m, by 64 x 64 tiles of (m, n): thread (m, n mod 4) sums
+// its block's R rows for every fourth n of the tile (R contiguous floats of
+// u, adjacent m adjacent), the tile is transposed through LDS and stored as
+// rows of S.  Pairs n > m are left to the select kernel (it zeroes them).
+template <int R>
+__global__ __launch_bounds__(256) void rr_norm_kernel(const RrParams p) {
+  constexpr int T = 64;
+  __shared__ float tl[T][T + 1];             // [n][m]
+  int x = static_cast<int>(blockIdx.x), mt = 0;
+  while ((mt + 1) * (mt + 2) / 2 <= x) ++mt; // tile pairs (mt, nt <= mt) in order
+  const int nt = x - mt * (mt + 1) / 2;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = static_cast<int64_t>(b) * p.H + h;
+  const int ml = threadIdx.x % T, nsub = threadIdx.x / T;
+  const int m = mt * T + ml;
+  // a block's rows are whole float4s of u (R and ns_pad are multiples of 4); rows at or past ns
+  // carry 1 / l = 0 (they hold no sampled query)
+  float linv[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = m * R + r;
+    linv[r] = (m < p.nb && i < p.ns) ? p.linv[bh * p.ns_pad + i] : 0.f;
+  }
+  const bool m_ok = m < p.nb && m * R < p.ns;
+#pragma unroll 2
+  for (int nn = nsub; nn < T; nn += 4) {
+    const int n = nt * T + nn;
+    float s = 0.f;
+    if (m_ok && n <= m) {
+      const float4* urow = reinterpret_cast<const float4*>(
+          p.u + (bh * p.nb + n) * static_cast<int64_t>(p.ns_pad) + static_cast<int64_t>(m) * R);
+#pragma unroll
+      for (int r4 = 0; r4 < R / 4; ++r4) {
+        if (m * R + 4 * r4 < p.ns_pad) {
+          const float4 v = urow[r4];
+          s = __builtin_fmaf(v.x, linv[4 * r4], s);
+          s = __builtin_fmaf(v.y, linv[4 * r4 + 1], s);
+          s = __builtin_fmaf(v.z, linv[4 * r4 + 2], s);
+          s = __builtin_fmaf(v.w, linv[4 * r4 + 3], s);
+        }
+      }
+    }
+    tl[nn][ml] = s;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < T * T; idx += 256) {
+    const int a = idx / T, c = idx % T;      // tile row (m) and column (n)
+    const int m2 = mt * T + a, n2 = nt * T + c;
+    if (m2 < p.nb && n2 <= m2) p.score[(bh * p.nb + m2) * p.nb + n2] = tl[c][a];
+  }
+}
+
 // -------------------------------------------------------------- select ----
 // One wave per (query block m, head, batch), four block rows per work-group.
 // Eq. 11 keeps the shortest prefix of the row's causal blocks, ordered by
@@ -373,16 +608,32 @@ __global__ __launch_bounds__(kRrThreads) void rr_select_kernel(const RrParams p)
   }
 }
 
+// One pass, the normalisation, then the two-pass kernel on the flagged query
+// tiles only (its work-groups for other tiles return at once).
+template <int D, int R>
+hipError_t launch_scores_r(const RrParams& p, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(p.ns_pad / kRrQ), static_cast<unsigned>(p.H), static_cast<unsigned>(p.B));
+  hipLaunchKernelGGL((rr_scores1p_kernel<D, R>), grid, dim3(kRrThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int mt = (p.nb + 63) / 64;
+  const dim3 ngrid(static_cast<unsigned>(mt * (mt + 1) / 2), static_cast<unsigned>(p.H), static_cast<unsigned>(p.B));
+  hipLaunchKernelGGL((rr_norm_kernel<R>), ngrid, dim3(256), 0, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  RrParams g = p;
+  g.gate = 1;
+  hipLaunchKernelGGL((rr_scores_kernel<D, R>), grid, dim3(kRrThreads), 0, stream, g);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_scores(const RrParams& p, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(p.ns_pad / kRrQ), static_cast<unsigned>(p.H), static_cast<unsigned>(p.B));
   switch (p.Bs / p.S) {
-    case 8: hipLaunchKernelGGL((rr_scores_kernel<D, 8>), grid, dim3(kRrThreads), 0, stream, p); break;
-    case 16: hipLaunchKernelGGL((rr_scores_kernel<D, 16>), grid, dim3(kRrThreads), 0, stream, p); break;
-    case 32: hipLaunchKernelGGL((rr_scores_kernel<D, 32>), grid, dim3(kRrThreads), 0, stream, p); break;
+    case 8: return launch_scores_r<D, 8>(p, stream);
+    case 16: return launch_scores_r<D, 16>(p, stream);
+    case 32: return launch_scores_r<D, 32>(p, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -392,6 +643,9 @@ hipError_t launch_rr_search(const RrParams& p, hipStream_t stream, hipEvent_t st
   if (start != nullptr && (e = hipEventRecord(start, stream)) != hipSuccess) return e;
   const int64_t n = static_cast<int64_t>(p.B) * p.H * p.ns_pad * (p.D / 8);
   hipLaunchKernelGGL(rr_prep_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t rows = static_cast<int64_t>(p.B) * p.H * p.ns_pad;
+  hipLaunchKernelGGL(rr_kmax_kernel, dim3(static_cast<unsigned>((rows + 255) / 256)), dim3(256), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   switch (p.D) {
     case 64: e = launch_scores<64>(p, stream); break;

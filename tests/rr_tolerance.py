@@ -19,10 +19,15 @@ the oracle (ks = stride sums, Q = sampled queries, I = Eq. 8, P = Eq. 9):
                   a tree, so the longest chain of fp32 additions behind a denominator or a block
                   score is about n_row / 32 + 40 (n_row = the row's key strides); with the
                   exponential's and the normalisation's own rounding the relative error is at most
-                  (ceil(n_row / 32) + 64) u; plus an absolute 1e-30 R for probabilities that flush
-                  to zero.
+                  (ceil(n_row / 32) + 64) u.
+* flushed terms:  the single pass takes every probability against a fixed reference r_i above the
+                  row's max (|q| times the largest key-aggregate norm, Cauchy-Schwarz); a row whose
+                  sum against r_i is below 2^-40 is recomputed by the two-pass method, so r_i exceeds
+                  the row's max by at most 40 + log2(n_row) <= 57 log2 units, and a term that flushes
+                  (2^(I - r) below 2^-126) is a probability below 2^-69; a block sums R^2 <= 2^10 of
+                  them: at most 2^-59 per block score, covered by 2^-58 R.
 
-tol_mn = T_mn + (ceil(n_row / 32) + 64) u S_mn + 1e-30 R.
+tol_mn = T_mn + (ceil(n_row / 32) + 64) u S_mn + 2^-58 R.
 """
 
 from __future__ import annotations
@@ -64,5 +69,5 @@ def score_tolerance(q, k, S: int, Bs: int, h: int, b: int = 0, query_blocks=None
         chain = -(-(rows + 1) // 32) + 64
         W = P * (np.expm1(2 * eps) + chain * U32)[:, None]
         kb = (np.arange(ns) * S) // Bs
-        tol[m] = np.bincount(kb, weights=W.sum(axis=0), minlength=nb)[:nb] + 1e-30 * R
+        tol[m] = np.bincount(kb, weights=W.sum(axis=0), minlength=nb)[:nb] + 2.0 ** -58 * R
     return tol

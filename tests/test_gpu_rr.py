@@ -165,3 +165,36 @@ def test_rr_search_grouped_keys():
         for m in range(L // Bs - 1):
             if _check_row(bm[0, h, m, : m + 1], s_ref[m, : m + 1], tau, float(tol[m].sum())):
                 assert np.array_equal(bm[0, h, m], b_ref[m]), (h, m)
+
+
+@pytest.mark.parametrize("L,H,big", [(8192, 1, 20.0), (8192, 1, 25.0), (2048, 2, 400.0)])
+def test_rr_search_recompute_path(L, H, big):
+    """Queries live in the first half of the head dim; one key of some strides carries a large component
+    in the second half, orthogonal to every query.  Those keys put the single pass's fixed reference
+    (|q| times the largest key-aggregate norm) far above the rows' maxima: rows whose sum against it
+    falls below 2^-40 send their 128-row query tile to the two-pass recompute.  On the CPU these inputs
+    flag no tile (big = 20: the reference about 35 log2 units above the maxima), 6 of 8 tiles (25) and
+    every tile (400); the scores must match the oracle within the derived bound in all three."""
+    from block_sparse_softmax_amd import rr_search
+    D, S, Bs, tau = 128, 8, 64, 0.9
+    rng = np.random.default_rng(int(big))
+    q = rng.standard_normal((1, H, L, D))
+    q[..., D // 2:] = 0.0
+    k = rng.standard_normal((1, H, L, D))
+    hot = rng.choice(L, size=L // 64, replace=False)
+    k[:, :, hot, D // 2:] += big * rng.standard_normal((1, H, hot.size, D // 2))
+    q, k = (gen.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k))
+    print(f"[case] rr search recompute path L={L} big={big}", flush=True)
+    bm, sc = rr_search(_dev(q), _dev(k), S, Bs, tau, layout="bhld")
+    torch.cuda.synchronize()
+    bm, sc = bm.cpu().numpy(), sc.cpu().numpy().astype(np.float64)
+    nb = L // Bs
+    for h in range(H):
+        s_ref, b_ref = rr_oracle(q, k, S, Bs, tau, h=h)
+        tol = score_tolerance(q, k, S, Bs, h)
+        err = np.abs(sc[0, h] - s_ref)
+        assert np.all(err <= tol), (h, float((err - tol).max()))
+        np.testing.assert_allclose(sc[0, h].sum(axis=1), Bs // S, rtol=1e-5)   # every row's mass is there
+        for m in range(nb - 1):
+            if _check_row(bm[0, h, m, : m + 1], s_ref[m, : m + 1], tau, float(tol[m].sum())):
+                assert np.array_equal(bm[0, h, m], b_ref[m]), (h, m)
