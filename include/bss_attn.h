@@ -366,7 +366,13 @@ attn_status attn_masked_bwd(const attn_plan* plan, const attn_tensor* q, const a
  * The stride importance runs on bf16 MFMA with fp32 accumulation; each stride
  * sum of the keys is formed in fp32 and carried as a pair of bf16 values
  * (hi + lo, the fp32 sum to about 2^-16 relative), so the products see the
- * key aggregate at fp32 accuracy.  The selection compares fp32 sums.
+ * key aggregate at fp32 accuracy.  One pass over the key strides takes each
+ * row's probabilities against a fixed reference above every score of the row
+ * (|q| times the head's largest key-aggregate norm); rows whose sum against it
+ * underflows are recomputed exactly by a two-pass kernel.  The selection
+ * compares fp32 sums.  The workspace holds the per (key block, row) sums of
+ * the pass: 4 bytes per sampled row and key block (2 GiB at 128K tokens,
+ * 32 heads, stride 8, block 128).
  */
 typedef struct {
   int64_t stride;             /* S >= 1                                                   */
