@@ -699,11 +699,11 @@ attn_status attn_masked_bwd(const attn_plan* p, const attn_tensor* q, const attn
 
 namespace {
 
-constexpr int kRrTileQ = 128;    // sampled queries per work-group of the scores kernel
+constexpr int kRrTileQ = 128;    // sampled queries per work-group of the two-pass scores kernel (twice that for the single pass)
 
 // Workspace of the search, 256-byte aligned parts: sampled queries (rows of
 // D bf16), stride-summed keys (hi then lo: rows of 2 D bf16 + 16 bytes), the
-// squared norms of the key aggregates by 8-dim piece, the heads' largest
+// squared norms of the key aggregates (one per row), the heads' largest
 // key-aggregate norm, 1 / row sum, the query tiles to
 // recompute, and the per (key block, row) sums of the single pass.
 struct RrLayout {
@@ -717,7 +717,7 @@ static RrLayout rr_layout(int64_t B, int64_t H, int64_t ns_pad, int64_t D, int64
   size_t o = 0;
   l.qs = o; o = up(o + rows * static_cast<size_t>(D) * 2);
   l.ks = o; o = up(o + rows * static_cast<size_t>(4 * D + 16));
-  l.knorm2 = o; o = up(o + rows * static_cast<size_t>(D / 8) * 4);
+  l.knorm2 = o; o = up(o + rows * 4);
   l.kmax = o; o = up(o + bh * 4);
   l.linv = o; o = up(o + rows * 4);
   l.flags = o; o = up(o + bh * static_cast<size_t>(ns_pad / kRrTileQ) * 4);
@@ -762,7 +762,7 @@ static attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const 
     return ATTN_E_UNSUPPORTED;
   }
   const int64_t ns = L / S;
-  const int64_t ns_pad = (ns + kRrTileQ - 1) / kRrTileQ * kRrTileQ;
+  const int64_t ns_pad = (ns + 2 * kRrTileQ - 1) / (2 * kRrTileQ) * (2 * kRrTileQ);  // single pass: 256-row tiles
   RrParams p{};
   p.q = static_cast<const uint16_t*>(q->data);
   p.k = static_cast<const uint16_t*>(k->data);

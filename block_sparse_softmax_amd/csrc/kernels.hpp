@@ -143,7 +143,7 @@ struct RrParams {
   int32_t ns, ns_pad, nb, protect_last;
   int32_t kv_group;           // query heads per K head (grouped-query attention)
   // single-pass scores (workspace)
-  float* knorm2;              // [B][H][ns_pad][D / 8]: |stride sum|^2 by 8-dim piece
+  float* knorm2;              // [B][H][ns_pad]: |hi + lo|^2 of each stride-summed key row
   uint32_t* kmax;             // [B][H]: largest |stride sum| of the head, as float bits
   float* linv;                // [B][H][ns_pad]: 1 / (row sum against the row's fixed reference)
   int32_t* flags;             // [B][H][ns_pad / 128]: query tiles that need the two-pass recompute

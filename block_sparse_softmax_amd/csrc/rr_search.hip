@@ -42,6 +42,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "kernels.hpp"
 #include "tile_common.hpp"
@@ -83,24 +84,28 @@ __device__ __forceinline__ float halves_sum32(float v) {
 }
 
 // ---------------------------------------------------------------- prep ----
-// One thread per (batch, head, stride row of the padded table, 8-dim chunk).
+// One thread per (batch, head, stride row of the padded table, 8-dim chunk),
+// a row's chunks on P lanes in a row (P = D / 8 rounded up to a power of two;
+// lanes past D / 8 only join the norm's reduction).
 // A stride-summed key row holds hi (D bf16) then lo (D bf16); rows are
 // 4 D + 16 bytes apart (the last 16 bytes are never written or read): a run
 // of rows is then byte for byte the padded LDS layout of the scores kernel
-// and is copied with LDS-DMA as it is.
+// and is copied with LDS-DMA as it is.  The row's |hi + lo|^2 (the aggregate
+// the products see) is summed over its lanes and stored once per row.
+template <int P>
 __global__ __launch_bounds__(256) void rr_prep_kernel(const RrParams p) {
   const int cpr = p.D / 8;
-  const int64_t n = static_cast<int64_t>(p.B) * p.H * p.ns_pad * cpr;
+  const int64_t n = static_cast<int64_t>(p.B) * p.H * p.ns_pad * P;   // a multiple of 64: whole waves
   const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (t >= n) return;
-  const int c = static_cast<int>(t % cpr);
-  const int64_t row = t / cpr;
+  const int c = static_cast<int>(t % P);
+  const int64_t row = t / P;
   const int j = static_cast<int>(row % p.ns_pad);
   const int bh = static_cast<int>(row / p.ns_pad);
   const int h = bh % p.H, b = bh / p.H;
-  if (j == 0 && c == 0) p.kmax[bh] = 0u;     // folded into by rr_kmax_kernel (next in the stream)
   bf16x8 qo = {}, ko = {}, kl = {};
-  if (j < p.ns) {
+  float n2 = 0.f;
+  if (j < p.ns && c < cpr) {
     const int pos = j * p.S + (p.S - 1 - (h % p.S));
     qo = *reinterpret_cast<const bf16x8*>(p.q + b * p.q_sb + static_cast<int64_t>(pos) * p.q_sl + h * p.q_sh + 8 * c);
     float acc[8] = {};
@@ -110,7 +115,6 @@ __global__ __launch_bounds__(256) void rr_prep_kernel(const RrParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] += static_cast<float>(x[e]);
     }
-    float n2 = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       ko[e] = static_cast<__bf16>(acc[e]);
@@ -118,14 +122,16 @@ __global__ __launch_bounds__(256) void rr_prep_kernel(const RrParams p) {
       const float x = static_cast<float>(ko[e]) + static_cast<float>(kl[e]);
       n2 = __builtin_fmaf(x, x, n2);
     }
-    p.knorm2[t] = n2;                          // this piece's share of |hi + lo|^2 (rows of D / 8 pieces)
-  } else {
-    p.knorm2[t] = 0.f;
   }
-  *reinterpret_cast<bf16x8*>(p.qs + row * p.D + 8 * c) = qo;
-  uint16_t* kdst = p.ks + row * (2 * p.D + 8);                       // rows of 4 D + 16 bytes
-  *reinterpret_cast<bf16x8*>(kdst + 8 * c) = ko;
-  *reinterpret_cast<bf16x8*>(kdst + p.D + 8 * c) = kl;
+#pragma unroll
+  for (int off = 1; off < P; off <<= 1) n2 += __shfl_xor(n2, off);
+  if (c == 0) p.knorm2[row] = n2;
+  if (c < cpr) {
+    *reinterpret_cast<bf16x8*>(p.qs + row * p.D + 8 * c) = qo;
+    uint16_t* kdst = p.ks + row * (2 * p.D + 8);                     // rows of 4 D + 16 bytes
+    *reinterpret_cast<bf16x8*>(kdst + 8 * c) = ko;
+    *reinterpret_cast<bf16x8*>(kdst + p.D + 8 * c) = kl;
+  }
 }
 
 // -------------------------------------------------------------- scores ----
@@ -312,39 +318,39 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p)
 }
 
 // ---------------------------------------------------------------- kmax ----
-// One thread per stride row: |hi + lo| of the row (the aggregate the products
-// see) from rr_prep's per-piece squares, the largest over the wave, folded
-// into the head's word with an atomic max of the float's bits (norms are >= 0,
-// so the bits order like the values).  A wave never spans two heads: a head
-// has ns_pad rows, a multiple of 128.
+// One work-group per (batch, head): the largest |hi + lo| over the head's
+// rows (padding rows are 0), stored as the float's bits.
 __global__ __launch_bounds__(256) void rr_kmax_kernel(const RrParams p) {
-  const int cpr = p.D / 8;
-  const int64_t rows = static_cast<int64_t>(p.B) * p.H * p.ns_pad;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  float n2 = 0.f;
-  if (row < rows) {
-    const float* pr = p.knorm2 + row * cpr;
-    for (int c = 0; c < cpr; ++c) n2 += pr[c];
-  }
-  float nrm = __builtin_sqrtf(n2);
+  __shared__ float wmax[4];
+  const int64_t bh = static_cast<int64_t>(blockIdx.y) * p.H + blockIdx.x;
+  const float* n2 = p.knorm2 + bh * p.ns_pad;
+  float m = 0.f;
+  for (int r = threadIdx.x; r < p.ns_pad; r += 256) m = fmaxf(m, n2[r]);
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) nrm = fmaxf(nrm, __shfl_xor(nrm, off));
-  if ((threadIdx.x & 63) == 0 && row < rows) atomicMax(p.kmax + row / p.ns_pad, __float_as_uint(nrm));
+  for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    p.kmax[bh] = __float_as_uint(__builtin_sqrtf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
 }
 
 // ------------------------------------------------------ scores, one pass ----
-// The layout of rr_scores_kernel (128 sampled queries per work-group, key
-// strides staged 64 at a time, chunks of 32); one pass instead of two.  Lane
-// l's row i takes the reference r_i = |q_i| kmax scale (1 + 2^-8): every
-// computed I_ij scale is at most r_i (Cauchy-Schwarz, the products and sums'
-// rounding far inside the margin), so 2^(I_ij scale - r_i) <= 1 and the row's
-// sum l_i and its per-key-block sums u_in can be accumulated against r_i from
-// the first stride on.  u_in goes to the workspace ([key block][row], one
-// coalesced 128-byte store per wave and block); 1 / l_i too.  A row whose
-// l_i is below 2^-40 (r_i more than 40 + log2 of its strides above its max)
-// flags its query tile for the two-pass recompute.
+// 256 sampled queries per work-group, 64 per wave as two sets of 32 (rows
+// q0 .. q0+31 and q0+32 .. q0+63 of the wave): every K fragment read from LDS
+// feeds one MFMA per set, so a staged 64-stride stage serves twice the
+// products of the two-pass kernel's layout.  Key strides staged 64 at a time
+// as there, chunks of 32.  Lane l's rows take the reference
+// r_i = |q_i| kmax scale (1 + 2^-8): every computed I_ij scale is at most r_i
+// (Cauchy-Schwarz, the products' and sums' rounding far inside the margin), so
+// 2^(I_ij scale - r_i) <= 1 and the row's sum l_i and its per-key-block sums
+// u_in can be accumulated against r_i from the first stride on.  u_in goes to
+// the workspace ([key block][row], one coalesced 128-byte store per set and
+// block); 1 / l_i too.  A row whose l_i is below 2^-40 (r_i more than
+// 40 + log2 of its strides above its max) flags its 128-row query tile for
+// the two-pass recompute.
+constexpr int kRrQ1 = 256;    // sampled queries per work-group of the single pass
 template <int D, int R>
-__global__ __launch_bounds__(kRrThreads) void rr_scores1p_kernel(const RrParams p) {
+__global__ __launch_bounds__(kRrThreads, 2) void rr_scores1p_kernel(const RrParams p) {
   constexpr int KS = D / 16;
   constexpr int PITCH = 4 * D + 16;
   constexpr int CPR = D / 8;
@@ -363,35 +369,42 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores1p_kernel(const RrParams 
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n_tiles = p.ns_pad / kRrQ;
-  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.x);  // longest (latest) tiles first
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t bh = static_cast<int64_t>(b) * p.H + h;
+  const int n_tiles = p.ns_pad / kRrQ1;
+  // one flat grid, tile-major: every head's longest (latest) tiles go first
+  // and the short ones fill the tail
+  const int nbh = p.B * p.H;
+  const int tile = n_tiles - 1 - static_cast<int>(blockIdx.x) / nbh;
+  const int64_t bh = static_cast<int>(blockIdx.x) % nbh;
   const int64_t bh_row = bh * p.ns_pad;
   const bf16x8* qs = reinterpret_cast<const bf16x8*>(p.qs) + bh_row * CPR;
   const unsigned char* ksb = reinterpret_cast<const unsigned char*>(p.ks) + bh_row * PITCH;
 
-  const int q0 = tile * kRrQ + 32 * wave;
-  const int qi = q0 + (lane & 31);
+  const int q0 = tile * kRrQ1 + 64 * wave;   // this wave's first sampled query
   const int half = lane >> 5;
-  bf16x8 qf[KS];
-#pragma unroll
-  for (int s = 0; s < KS; ++s) qf[s] = qs[static_cast<int64_t>(qi) * CPR + 2 * s + half];
-  const bool q_valid = qi < p.ns;
-  // the row's reference (log2 units): |q| over both halves of the lane pair
-  float qn2 = 0.f;
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qn2 = __builtin_fmaf(static_cast<float>(qf[s][e]), static_cast<float>(qf[s][e]), qn2);
-  }
-  qn2 = halves_sum32(qn2);
   const float kmx = __uint_as_float(p.kmax[bh]);
-  const float rref = __builtin_sqrtf(qn2) * kmx * p.scale_log2 * (1.f + 0x1p-8f);
+  int qi[2];
+  bool q_valid[2];
+  float rref[2];
+  bf16x8 qf[2][KS];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    qi[g] = q0 + 32 * g + (lane & 31);
+    q_valid[g] = qi[g] < p.ns;
+    float qn2 = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qf[g][s] = qs[static_cast<int64_t>(qi[g]) * CPR + 2 * s + half];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        qn2 = __builtin_fmaf(static_cast<float>(qf[g][s][e]), static_cast<float>(qf[g][s][e]), qn2);
+    }
+    qn2 = halves_sum32(qn2);                  // |q|^2 over both halves of the lane pair
+    rref[g] = __builtin_sqrtf(qn2) * kmx * p.scale_log2 * (1.f + 0x1p-8f);
+  }
 
-  const int last_chunk_wg = (tile * kRrQ + kRrQ - 1) / kChunk;
-  const int last_chunk = q0 / kChunk;
-  const int n_chunks = last_chunk_wg + 1;
+  const int last_chunk_wg = (tile * kRrQ1 + kRrQ1 - 1) / kChunk;
+  const int last0 = q0 / kChunk;              // set g's diagonal chunk is last0 + g
+  const int n_chunks = last_chunk_wg + 1;     // a multiple of 8
   const int n_stage = n_chunks / 2;
 
   const uint32_t smem_lds = dev::lds_addr(smem);
@@ -411,69 +424,195 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores1p_kernel(const RrParams 
     else if (nw == NW_HI) dev::wait_vmcnt<NW_HI>();
     else dev::wait_vmcnt<NW_LO>();
   };
-  auto chunk_scores = [&](int buf, int sub) __attribute__((always_inline)) {
-    f32x16 acc = {};
+  // I^T tiles of chunk (buf, sub) for the sets that reach it (set 0 stops one chunk earlier)
+  auto chunk_scores = [&](int buf, int sub, bool both, f32x16* acc) __attribute__((always_inline)) {
+    acc[0] = f32x16{};
+    acc[1] = f32x16{};
     const unsigned char* base = smem + buf * SBYTES + (sub * kChunk + (lane & 31)) * PITCH + half * 16;
 #pragma unroll
     for (int s = 0; s < 2 * KS; ++s) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(base + 32 * s);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s % KS], acc, 0, 0, 0);
+      if (both) acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][s % KS], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[1][s % KS], acc[1], 0, 0, 0);
     }
-    return acc;
   };
   auto key_of = [&](int c, int r) __attribute__((always_inline)) { return c * kChunk + 8 * (r >> 2) + 4 * half + (r & 3); };
+  // Key block (within a chunk) of accumulator register r: the half and low
+  // row bits add less than 8 <= R strides, so only 8 (r / 4) decides it.
+  auto kb_of = [](int r) constexpr { return (8 * (r >> 2)) / R; };
 
-  float l_run = 0.f;                         // the row's sum against rref (both halves: equal in l and l ^ 32)
-  float* ucol = p.u + bh * p.nb * static_cast<int64_t>(p.ns_pad) + qi;
-  issue_stage(0);
-  if (AHEAD > 1 && n_stage > 1) issue_stage(1);
-  for (int st = 0; st < n_stage; ++st) {
+  float l_run[2] = {0.f, 0.f};               // the rows' sums against rref (equal in lanes l and l ^ 32)
+  float* ucol[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) ucol[g] = p.u + bh * p.nb * static_cast<int64_t>(p.ns_pad) + qi[g];
+  // chunk c's per-block sums of both sets: both halves combined, added to the rows' sums, stored
+  auto finish = [&](int c, float (&bsx)[2][KB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const float v = halves_sum32(bsx[g][kb]);
+        l_run[g] += v;
+        const int kblk = (c * kChunk) / R + kb;
+        if (half == 0 && kblk < p.nb) ucol[g][static_cast<int64_t>(kblk) * p.ns_pad] = v;
+      }
+  };
+
+  // Stages whose two chunks lie wholly before both sets' rows (every row of
+  // the wave valid) run software-pipelined: a chunk's MFMAs are interleaved
+  // step by step with the exponentials of the chunk before it, so matrix and
+  // vector work of one wave overlap.  The sums keep chunk and register order.
+  constexpr int NS = 2 * KS;                 // MFMA steps per chunk (hi and lo k-ranges)
+  auto mfma_exp = [&](const unsigned char* base, f32x16 (&acc)[2], const f32x16 (&accx)[2], float (&bsx)[2][KB],
+                      auto&& side) __attribute__((always_inline)) {
+    acc[0] = f32x16{};
+    acc[1] = f32x16{};
+    bf16x8 kf = *reinterpret_cast<const bf16x8*>(base);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      bf16x8 kn{};
+      if (s + 1 < NS) kn = *reinterpret_cast<const bf16x8*>(base + 32 * (s + 1));
+      // one MFMA, then that set's share of the other chunk's exponentials: the
+      // vector work issues while the MFMA runs.  The sums are pinned at each
+      // step (without it they sink below the chunk's MFMAs, to their first use).
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[g][s % KS], acc[g], 0, 0, 0);
+#pragma unroll
+        for (int r = s * 16 / NS; r < (s + 1) * 16 / NS; ++r)
+          bsx[g][kb_of(r)] += __builtin_amdgcn_exp2f(__builtin_fmaf(accx[g][r], p.scale_log2, -rref[g]));
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) __asm__ volatile("" : "+v"(bsx[g][kb]));
+        if (g == 1) side(s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      kf = kn;
+    }
+  };
+  auto exp_only = [&](const f32x16 (&accx)[2], float (&bsx)[2][KB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        bsx[g][kb_of(r)] += __builtin_amdgcn_exp2f(__builtin_fmaf(accx[g][r], p.scale_log2, -rref[g]));
+  };
+  const int n_open = (q0 + 63 < p.ns) ? last0 / 2 : 0;
+  f32x16 accp[2];                            // the pending chunk's scores (none yet: exp2 of -inf adds 0)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) accp[0][r] = accp[1][r] = -__builtin_inff();
+
+  auto next_stage = [&](int st) __attribute__((always_inline)) {
     wait_stage(AHEAD > 1 && st + 1 < n_stage);
     __syncthreads();
     if (st + AHEAD < n_stage) issue_stage(st + AHEAD);
+  };
+  issue_stage(0);
+  if (AHEAD > 1 && n_stage > 1) issue_stage(1);
+  // In pipelined stages the copies of stage st + AHEAD are spread over the
+  // first chunk's MFMA steps (one per two steps; a wave's last copy, which
+  // not every wave has, after them) instead of issued in a burst.
+  static_assert(NS / 2 >= NW_LO, "a copy every second step");
+  auto no_side = [](int) {};
+  auto pipelined = [&](int st, auto copies) __attribute__((always_inline)) {
+    const unsigned char* base = smem + (st % NBUF) * SBYTES + (lane & 31) * PITCH + half * 16;
+    uint64_t src = 0;
+    uint32_t dst = 0;
+    if constexpr (decltype(copies)::value) {
+      const int sn = st + AHEAD;
+      src = dev::uniform_u64(reinterpret_cast<uint64_t>(ksb) + static_cast<uint64_t>(sn) * SBYTES);
+      dst = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(smem_lds + (sn % NBUF) * SBYTES)));
+    }
+    auto copy = [&](int s) __attribute__((always_inline)) {
+      if constexpr (decltype(copies)::value) {
+        if (s % 2 == 0 && s / 2 < NW_LO) {
+          const int ins = wave + 4 * (s / 2);
+          dev::dma16(src + static_cast<uint64_t>(ins) * 1024, 16 * lane, dst + ins * 1024);
+        }
+      }
+    };
+    float bsp[2][KB] = {}, bsa[2][KB] = {};
+    f32x16 acca[2], accb[2];
+    mfma_exp(base, acca, accp, bsp, copy);              // chunk 2 st; exponentials of 2 st - 1
+    if constexpr (decltype(copies)::value) {
+      if (NW_HI > NW_LO && wave + 4 * NW_LO < NI)
+        dev::dma16(src + static_cast<uint64_t>(wave + 4 * NW_LO) * 1024, 16 * lane, dst + (wave + 4 * NW_LO) * 1024);
+    }
+    if (st > 0) finish(2 * st - 1, bsp);
+    mfma_exp(base + kChunk * PITCH, accb, acca, bsa, no_side);  // chunk 2 st + 1; exponentials of 2 st
+    finish(2 * st, bsa);
+    accp[0] = accb[0];
+    accp[1] = accb[1];
+  };
+  int st = 0;
+  for (; st < n_open; ++st) {
+    wait_stage(AHEAD > 1 && st + 1 < n_stage);
+    __syncthreads();
+    if (st + AHEAD < n_stage) pipelined(st, std::true_type{});
+    else pipelined(st, std::false_type{});
+  }
+  if (n_open > 0) {                                     // the last pipelined chunk
+    float bsp[2][KB] = {};
+    exp_only(accp, bsp);
+    finish(2 * n_open - 1, bsp);
+  }
+  for (; st < n_stage; ++st) {
+    next_stage(st);
     const int buf = st % NBUF;
-    f32x16 accs[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-      if (2 * st + sub <= last_chunk) accs[sub] = chunk_scores(buf, sub);
+    f32x16 accs[2][2];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int c = 2 * st + sub;
-      if (c <= last_chunk) {
-        const f32x16& acc = accs[sub];
-        const bool open = c < last_chunk && q0 + 31 < p.ns;
+      if (c <= last0 + 1) chunk_scores(buf, sub, c <= last0, accs[sub]);
+    }
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int c = 2 * st + sub;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        if (c > last0 + g) continue;            // no stride of this chunk precedes the set's rows
+        const f32x16& acc = accs[sub][g];
+        const bool open = c < last0 + g && q0 + 32 * g + 31 < p.ns;
         float bs[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) bs[kb] = 0.f;
         if (open) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            bs[(8 * (r >> 2) + 4 * half + (r & 3)) / R] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], p.scale_log2, -rref));
+            bs[kb_of(r)] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], p.scale_log2, -rref[g]));
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int j = key_of(c, r);
-            const float pr = (q_valid && j <= qi) ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], p.scale_log2, -rref)) : 0.f;
-            bs[(8 * (r >> 2) + 4 * half + (r & 3)) / R] += pr;
+            const float pr = (q_valid[g] && j <= qi[g])
+                                 ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], p.scale_log2, -rref[g]))
+                                 : 0.f;
+            bs[kb_of(r)] += pr;
           }
         }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           const float v = halves_sum32(bs[kb]);
-          l_run += v;
+          l_run[g] += v;
           const int kblk = (c * kChunk) / R + kb;
-          if (half == 0 && kblk < p.nb) ucol[static_cast<int64_t>(kblk) * p.ns_pad] = v;
+          if (half == 0 && kblk < p.nb) ucol[g][static_cast<int64_t>(kblk) * p.ns_pad] = v;
         }
       }
     }
   }
-  if (half == 0) p.linv[bh_row + qi] = (q_valid && l_run > 0.f) ? 1.f / l_run : 0.f;
-  const bool bad = q_valid && !(l_run >= 0x1p-40f);
+  bool bad = false;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    if (half == 0) p.linv[bh_row + qi[g]] = (q_valid[g] && l_run[g] > 0.f) ? 1.f / l_run[g] : 0.f;
+    bad = bad || (q_valid[g] && !(l_run[g] >= 0x1p-40f));
+  }
   const uint64_t any_bad = __builtin_amdgcn_ballot_w64(bad);
   if (lane == 0) bad_wave[wave] = any_bad != 0 ? 1 : 0;
   __syncthreads();
-  if (threadIdx.x == 0)
-    p.flags[bh * n_tiles + tile] = bad_wave[0] | bad_wave[1] | bad_wave[2] | bad_wave[3];
+  if (threadIdx.x == 0) {                     // waves 0-1 cover 128-row tile 2 tile, waves 2-3 the next
+    const int64_t f = bh * (p.ns_pad / kRrQ) + 2 * tile;
+    p.flags[f] = bad_wave[0] | bad_wave[1];
+    p.flags[f + 1] = bad_wave[2] | bad_wave[3];
+  }
 }
 
 // ---------------------------------------------------------------- norm ----
@@ -612,8 +751,9 @@ __global__ __launch_bounds__(kRrThreads) void rr_select_kernel(const RrParams p)
 // tiles only (its work-groups for other tiles return at once).
 template <int D, int R>
 hipError_t launch_scores_r(const RrParams& p, hipStream_t stream) {
+  const dim3 grid1(static_cast<unsigned>(p.ns_pad / kRrQ1 * p.H * p.B));
   const dim3 grid(static_cast<unsigned>(p.ns_pad / kRrQ), static_cast<unsigned>(p.H), static_cast<unsigned>(p.B));
-  hipLaunchKernelGGL((rr_scores1p_kernel<D, R>), grid, dim3(kRrThreads), 0, stream, p);
+  hipLaunchKernelGGL((rr_scores1p_kernel<D, R>), grid1, dim3(kRrThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int mt = (p.nb + 63) / 64;
@@ -641,11 +781,13 @@ hipError_t launch_scores(const RrParams& p, hipStream_t stream) {
 hipError_t launch_rr_search(const RrParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   hipError_t e;
   if (start != nullptr && (e = hipEventRecord(start, stream)) != hipSuccess) return e;
-  const int64_t n = static_cast<int64_t>(p.B) * p.H * p.ns_pad * (p.D / 8);
-  hipLaunchKernelGGL(rr_prep_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t rows = static_cast<int64_t>(p.B) * p.H * p.ns_pad;
-  hipLaunchKernelGGL(rr_kmax_kernel, dim3(static_cast<unsigned>((rows + 255) / 256)), dim3(256), 0, stream, p);
+  const dim3 pgrid(static_cast<unsigned>((rows * (p.D == 64 ? 8 : 16) + 255) / 256));
+  if (p.D == 64) hipLaunchKernelGGL(rr_prep_kernel<8>, pgrid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL(rr_prep_kernel<16>, pgrid, dim3(256), 0, stream, p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(rr_kmax_kernel, dim3(static_cast<unsigned>(p.H), static_cast<unsigned>(p.B)), dim3(256), 0,
+                     stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   switch (p.D) {
     case 64: e = launch_scores<64>(p, stream); break;
