@@ -704,10 +704,11 @@ constexpr int kRrTileQ = 128;    // sampled queries per work-group of the two-pa
 // Workspace of the search, 256-byte aligned parts: sampled queries (rows of
 // D bf16), stride-summed keys (hi then lo: rows of 2 D bf16 + 16 bytes), the
 // squared norms of the key aggregates (one per row), the heads' largest
-// key-aggregate norm, 1 / row sum, the query tiles to
-// recompute, and the per (key block, row) sums of the single pass.
+// key-aggregate norm, the query tiles to recompute, and the per (key block,
+// row) sums of the single pass.  Rows: nb R (every query block's strides,
+// nb R >= floor(L / S)) rounded up to whole 256-row tiles.
 struct RrLayout {
-  size_t qs, ks, knorm2, kmax, linv, flags, u, total;
+  size_t qs, ks, knorm2, kmax, flags, u, total;
 };
 static RrLayout rr_layout(int64_t B, int64_t H, int64_t ns_pad, int64_t D, int64_t nb) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -719,7 +720,6 @@ static RrLayout rr_layout(int64_t B, int64_t H, int64_t ns_pad, int64_t D, int64
   l.ks = o; o = up(o + rows * static_cast<size_t>(4 * D + 16));
   l.knorm2 = o; o = up(o + rows * 4);
   l.kmax = o; o = up(o + bh * 4);
-  l.linv = o; o = up(o + rows * 4);
   l.flags = o; o = up(o + bh * static_cast<size_t>(ns_pad / kRrTileQ) * 4);
   l.u = o; o = up(o + rows * static_cast<size_t>(nb) * 4);
   l.total = o;
@@ -762,7 +762,7 @@ static attn_status rr_prepare(const attn_tensor* q, const attn_tensor* k, const 
     return ATTN_E_UNSUPPORTED;
   }
   const int64_t ns = L / S;
-  const int64_t ns_pad = (ns + 2 * kRrTileQ - 1) / (2 * kRrTileQ) * (2 * kRrTileQ);  // single pass: 256-row tiles
+  const int64_t ns_pad = (nb * R + 2 * kRrTileQ - 1) / (2 * kRrTileQ) * (2 * kRrTileQ);  // 256-row tiles
   RrParams p{};
   p.q = static_cast<const uint16_t*>(q->data);
   p.k = static_cast<const uint16_t*>(k->data);
@@ -906,7 +906,6 @@ attn_status attn_rr_search(const attn_tensor* q, const attn_tensor* k, const att
     p.ks = reinterpret_cast<uint16_t*>(ws + lay.ks);
     p.knorm2 = reinterpret_cast<float*>(ws + lay.knorm2);
     p.kmax = reinterpret_cast<uint32_t*>(ws + lay.kmax);
-    p.linv = reinterpret_cast<float*>(ws + lay.linv);
     p.flags = reinterpret_cast<int32_t*>(ws + lay.flags);
     p.u = reinterpret_cast<float*>(ws + lay.u);
     p.gate = 0;

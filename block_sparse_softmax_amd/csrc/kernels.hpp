@@ -145,7 +145,6 @@ struct RrParams {
   // single-pass scores (workspace)
   float* knorm2;              // [B][H][ns_pad]: |hi + lo|^2 of each stride-summed key row
   uint32_t* kmax;             // [B][H]: largest |stride sum| of the head, as float bits
-  float* linv;                // [B][H][ns_pad]: 1 / (row sum against the row's fixed reference)
   int32_t* flags;             // [B][H][ns_pad / 128]: query tiles that need the two-pass recompute
   float* u;                   // [B][H][nb][ns_pad]: per (key block, row) sums against the reference
   int32_t gate;               // two-pass kernel: 1 = only the flagged query tiles

@@ -17,8 +17,9 @@
 //           fixed reference r >= every I of the row (|q| |ksum|max, Cauchy-
 //           Schwarz), so the pass sums 2^(I - r) per (row, key block) and per
 //           row without knowing the row's max; the per-block sums go to the
-//           workspace (the stride-level matrix never exists).
-//   norm    S_mn = sum over the rows i of block m of u_in / l_i (Eq. 9-10).
+//           workspace (the stride-level matrix never exists), and once a
+//           wave's rows are done it reads its own sums back and writes
+//           S_mn = sum over the rows i of block m of u_in / l_i (Eq. 9-10).
 //   recompute  rows whose sum against r underflows (r far above the row's
 //           max: keys with large norms orthogonal to the query) are redone,
 //           per query tile, by the two-pass kernel: pass 1 keeps each row's
@@ -30,13 +31,14 @@
 //           than a sort, and every causal block of the last query block
 //           (Eq. 12).
 //
-// Layout of the scores kernel: a work-group of 4 waves takes 128 consecutive
-// sampled queries of one (batch, head); wave w owns queries 32w..32w+31 of
-// them.  The stride-summed keys are staged in LDS 64 at a time, three stages
-// in flight, shared by the 4 waves, and used in chunks of 32.  I^T = Ksum
-// Q^T: the key chunk is the A operand (from LDS), the sampled queries the B
-// operand (in registers), so lane l holds query l mod 32 and 16 of the
-// chunk's 32 key strides.
+// Layout of the two-pass scores kernel: a work-group of 4 waves takes 128
+// consecutive sampled queries of one (batch, head); wave w owns queries
+// 32w..32w+31 of them.  The stride-summed keys are staged in LDS 64 at a
+// time, up to three stages in flight, shared by the 4 waves, and used in
+// chunks of 32.  I^T = Ksum Q^T: the key chunk is the A operand (from LDS),
+// the sampled queries the B operand (in registers), so lane l holds query
+// l mod 32 and 16 of the chunk's 32 key strides.  The single pass uses the
+// same staging with 256 queries per work-group (two sets of 32 per wave).
 
 #include <hip/hip_runtime.h>
 
@@ -366,6 +368,7 @@ __global__ __launch_bounds__(kRrThreads, 2) void rr_scores1p_kernel(const RrPara
   static_assert(R == 8 || R == 16 || R == 32, "strides per block");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * SBYTES];
   __shared__ int bad_wave[4];
+  __shared__ float linv_s[4][64];            // 1 / l of each wave's rows
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -454,7 +457,7 @@ __global__ __launch_bounds__(kRrThreads, 2) void rr_scores1p_kernel(const RrPara
         const float v = halves_sum32(bsx[g][kb]);
         l_run[g] += v;
         const int kblk = (c * kChunk) / R + kb;
-        if (half == 0 && kblk < p.nb) ucol[g][static_cast<int64_t>(kblk) * p.ns_pad] = v;
+        if (half == 0 && kblk < p.nb) __builtin_nontemporal_store(v, ucol[g] + static_cast<int64_t>(kblk) * p.ns_pad);
       }
   };
 
@@ -594,16 +597,65 @@ __global__ __launch_bounds__(kRrThreads, 2) void rr_scores1p_kernel(const RrPara
           const float v = halves_sum32(bs[kb]);
           l_run[g] += v;
           const int kblk = (c * kChunk) / R + kb;
-          if (half == 0 && kblk < p.nb) ucol[g][static_cast<int64_t>(kblk) * p.ns_pad] = v;
+          if (half == 0 && kblk < p.nb) __builtin_nontemporal_store(v, ucol[g] + static_cast<int64_t>(kblk) * p.ns_pad);
         }
       }
     }
   }
+  // Block scores of the wave's rows: S_mn = sum over the rows i of block m of
+  // u_in / l_i for n <= m, from the per-block sums this wave stored (read
+  // back by the wave that wrote them).  Lane (j, b) takes block b of the
+  // wave's 64 / R and key blocks n = j, j + R, ...: it reads the block's R
+  // row sums for n (contiguous), scales them by the rows' 1 / l (shared
+  // through LDS) and adds them in row order.  The table has a row for every
+  // block's rows (rows at or past ns hold 0 and 1 / l = 0), so every S_mn with
+  // n <= m < nb is written here; rows of flagged tiles are rewritten by the
+  // recompute.
+  constexpr int MB = 64 / R;                 // query blocks of a wave
   bool bad = false;
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    if (half == 0) p.linv[bh_row + qi[g]] = (q_valid[g] && l_run[g] > 0.f) ? 1.f / l_run[g] : 0.f;
+    const float li = (q_valid[g] && l_run[g] > 0.f) ? 1.f / l_run[g] : 0.f;
     bad = bad || (q_valid[g] && !(l_run[g] >= 0x1p-40f));
+    if (half == 0) linv_s[wave][32 * g + lane] = li;
+  }
+  __threadfence_block();                     // this wave's stores of u before its loads of them
+  __syncthreads();
+  {
+    const int bl = lane % MB, j = lane / MB;
+    const int m = q0 / R + bl;
+    float lr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) lr[r] = linv_s[wave][bl * R + r];
+    const int n_row = min(m, p.nb - 1);
+    const int n_end = min((q0 + 63) / R, p.nb - 1);     // the wave's last block
+    const float* ublk = p.u + bh * p.nb * static_cast<int64_t>(p.ns_pad) + q0 + bl * R;
+    float* srow = p.score + (bh * p.nb + m) * static_cast<int64_t>(p.nb);
+    constexpr int U = 4;                     // key blocks in flight per lane
+    for (int n0 = 0; n0 <= n_end; n0 += U * R) {
+      using v4f = float __attribute__((ext_vector_type(4)));
+      v4f v[U][R / 4];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {          // every load issued, at a block the rows have written
+        const v4f* src = reinterpret_cast<const v4f*>(
+            ublk + static_cast<int64_t>(min(n0 + k * R + j, n_row)) * p.ns_pad);
+#pragma unroll
+        for (int r4 = 0; r4 < R / 4; ++r4) v[k][r4] = __builtin_nontemporal_load(src + r4);
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int n = n0 + k * R + j;
+        float sm = 0.f;
+#pragma unroll
+        for (int r4 = 0; r4 < R / 4; ++r4) {
+          sm = __builtin_fmaf(v[k][r4].x, lr[4 * r4], sm);
+          sm = __builtin_fmaf(v[k][r4].y, lr[4 * r4 + 1], sm);
+          sm = __builtin_fmaf(v[k][r4].z, lr[4 * r4 + 2], sm);
+          sm = __builtin_fmaf(v[k][r4].w, lr[4 * r4 + 3], sm);
+        }
+        if (n <= n_row && m < p.nb) srow[n] = sm;
+      }
+    }
   }
   const uint64_t any_bad = __builtin_amdgcn_ballot_w64(bad);
   if (lane == 0) bad_wave[wave] = any_bad != 0 ? 1 : 0;
@@ -612,60 +664,6 @@ __global__ __launch_bounds__(kRrThreads, 2) void rr_scores1p_kernel(const RrPara
     const int64_t f = bh * (p.ns_pad / kRrQ) + 2 * tile;
     p.flags[f] = bad_wave[0] | bad_wave[1];
     p.flags[f + 1] = bad_wave[2] | bad_wave[3];
-  }
-}
-
-// ---------------------------------------------------------------- norm ----
-// S_mn = sum over the rows i of query block m (i < ns) of u_in / l_i, for the
-// causal pairs n <= m, by 64 x 64 tiles of (m, n): thread (m, n mod 4) sums
-// its block's R rows for every fourth n of the tile (R contiguous floats of
-// u, adjacent m adjacent), the tile is transposed through LDS and stored as
-// rows of S.  Pairs n > m are left to the select kernel (it zeroes them).
-template <int R>
-__global__ __launch_bounds__(256) void rr_norm_kernel(const RrParams p) {
-  constexpr int T = 64;
-  __shared__ float tl[T][T + 1];             // [n][m]
-  int x = static_cast<int>(blockIdx.x), mt = 0;
-  while ((mt + 1) * (mt + 2) / 2 <= x) ++mt; // tile pairs (mt, nt <= mt) in order
-  const int nt = x - mt * (mt + 1) / 2;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int64_t bh = static_cast<int64_t>(b) * p.H + h;
-  const int ml = threadIdx.x % T, nsub = threadIdx.x / T;
-  const int m = mt * T + ml;
-  // a block's rows are whole float4s of u (R and ns_pad are multiples of 4); rows at or past ns
-  // carry 1 / l = 0 (they hold no sampled query)
-  float linv[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int i = m * R + r;
-    linv[r] = (m < p.nb && i < p.ns) ? p.linv[bh * p.ns_pad + i] : 0.f;
-  }
-  const bool m_ok = m < p.nb && m * R < p.ns;
-#pragma unroll 2
-  for (int nn = nsub; nn < T; nn += 4) {
-    const int n = nt * T + nn;
-    float s = 0.f;
-    if (m_ok && n <= m) {
-      const float4* urow = reinterpret_cast<const float4*>(
-          p.u + (bh * p.nb + n) * static_cast<int64_t>(p.ns_pad) + static_cast<int64_t>(m) * R);
-#pragma unroll
-      for (int r4 = 0; r4 < R / 4; ++r4) {
-        if (m * R + 4 * r4 < p.ns_pad) {
-          const float4 v = urow[r4];
-          s = __builtin_fmaf(v.x, linv[4 * r4], s);
-          s = __builtin_fmaf(v.y, linv[4 * r4 + 1], s);
-          s = __builtin_fmaf(v.z, linv[4 * r4 + 2], s);
-          s = __builtin_fmaf(v.w, linv[4 * r4 + 3], s);
-        }
-      }
-    }
-    tl[nn][ml] = s;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < T * T; idx += 256) {
-    const int a = idx / T, c = idx % T;      // tile row (m) and column (n)
-    const int m2 = mt * T + a, n2 = nt * T + c;
-    if (m2 < p.nb && n2 <= m2) p.score[(bh * p.nb + m2) * p.nb + n2] = tl[c][a];
   }
 }
 
@@ -747,8 +745,8 @@ __global__ __launch_bounds__(kRrThreads) void rr_select_kernel(const RrParams p)
   }
 }
 
-// One pass, the normalisation, then the two-pass kernel on the flagged query
-// tiles only (its work-groups for other tiles return at once).
+// The single pass (block scores included), then the two-pass kernel on the
+// flagged query tiles only (its work-groups for other tiles return at once).
 template <int D, int R>
 hipError_t launch_scores_r(const RrParams& p, hipStream_t stream) {
   const dim3 grid1(static_cast<unsigned>(p.ns_pad / kRrQ1 * p.H * p.B));
@@ -756,10 +754,6 @@ hipError_t launch_scores_r(const RrParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((rr_scores1p_kernel<D, R>), grid1, dim3(kRrThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int mt = (p.nb + 63) / 64;
-  const dim3 ngrid(static_cast<unsigned>(mt * (mt + 1) / 2), static_cast<unsigned>(p.H), static_cast<unsigned>(p.B));
-  hipLaunchKernelGGL((rr_norm_kernel<R>), ngrid, dim3(256), 0, stream, p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   RrParams g = p;
   g.gate = 1;
   hipLaunchKernelGGL((rr_scores_kernel<D, R>), grid, dim3(kRrThreads), 0, stream, g);

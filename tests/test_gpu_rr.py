@@ -78,6 +78,7 @@ CASES = [
     (4096, 4, 128, 8, 128, 0.5, "planted"),
     (2048, 2, 64, 8, 128, 1.0, "random"),      # tau = 1: every block with mass
     (8200, 1, 64, 1, 8, 0.5, "planted"),       # 1025 blocks per row (the select kernel's wide variant)
+    (2052, 2, 64, 8, 128, 0.9, "random"),      # 256 strides; the 17th block holds no sampled query
 ]
 
 

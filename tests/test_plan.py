@@ -382,8 +382,8 @@ def test_rr_workspace_and_argument_errors_without_gpu(lib):
     256-byte aligned: the sampled queries (rows of d bf16), the stride-summed keys (rows of 2 d bf16,
     the hi and lo halves, plus 16 pad bytes), one float per key row (its squared norm),
     one float per (batch, head) (the largest key-aggregate
-    norm), one float per row (1 / row sum), one int per 128-row query tile (recompute flag) and one float
-    per (key block, row) (the single pass's per-block sums); floor(L / S) rows padded to a multiple of 256."""
+    norm), one int per 128-row query tile (recompute flag) and one float
+    per (key block, row) (the single pass's per-block sums); one row per stride of every block (nb R >= floor(L / S)) padded to a multiple of 256."""
     import ctypes
     from block_sparse_softmax_amd._lib import AttnTensor, RrParams
 
@@ -402,13 +402,15 @@ def test_rr_workspace_and_argument_errors_without_gpu(lib):
         up = lambda x: -(-x // 256) * 256
         bh = B * H
         return (up(bh * rows * 2 * D) + up(bh * rows * (4 * D + 16)) + up(bh * rows * 4)
-                + up(bh * 4) + up(bh * rows * 4)
+                + up(bh * 4)
                 + up(bh * (rows // 128) * 4) + up(bh * rows * nb * 4))
 
     assert ws(view(1, 131072, 32, 128), RrParams(8, 128, 0.9, 1)) == (0, expect(1, 32, 16384, 128, 1024))
     assert expect(1, 32, 16384, 128, 1024) > 2 * 2 ** 30      # the single pass's block sums: 2 GiB at 128K
-    # 1030 // 4 = 257 strides -> 512 rows (a multiple of 256); 9 key blocks
+    # 9 key blocks of 32 strides -> 288 rows -> 512 (a multiple of 256)
     assert ws(view(2, 1030, 3, 80), RrParams(4, 128, 0.5, 0)) == (0, expect(2, 3, 512, 80, 9))
+    # 16388 // 8 = 2048 strides, a whole number of 256-row tiles, but 129 blocks of 16 strides need 2064 rows
+    assert ws(view(1, 16388, 1, 64), RrParams(8, 128, 0.9, 1)) == (0, expect(1, 1, 2304, 64, 129))
     assert ws(view(1, 4096, 2, 96), RrParams(8, 128, 0.9, 1))[0] == _lib.ATTN_E_UNSUPPORTED   # head dim
     assert ws(view(1, 4096, 2, 64), RrParams(8, 100, 0.9, 1))[0] == _lib.ATTN_E_INVAL         # Bs % S != 0
     assert ws(view(1, 4096, 2, 64), RrParams(8, 512, 0.9, 1))[0] == _lib.ATTN_E_UNSUPPORTED   # Bs / S = 64
