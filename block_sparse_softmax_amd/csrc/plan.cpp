@@ -231,13 +231,15 @@ void compile_blocks(attn_plan& p) {
 // better than dealing a head's rows to all XCDs for the 16K-token windows and
 // the 128K-token block masks).  A queue short enough to run in a few rounds of
 // its work-groups is ordered by descending cost.  A launch of at most two
-// rounds whose item costs are uneven is dealt longest-first to the
-// least-loaded queue instead.  Queues are padded to equal length with null
-// items.
+// rounds whose item costs are uneven gives whole heads to XCDs, longest
+// first to the least-loaded one, when that balances the XCDs within 5 %
+// (else its items are dealt longest first to the least-loaded queue).
+// Queues are padded to equal length with null items.
 constexpr double kPingPongMinTiles = 32.0;  // d = 128: mean row cost (tiles) from which the ping-pong kernel runs
 constexpr double kMinPiece = 12.0;     // tiles: below this a piece's merge costs more than it saves
 constexpr double kPieceOverhead = 2.0; // tiles: writing the partial state and the merge
 constexpr int kMaxPieces = 16;
+constexpr double kHeadSpread = 1.05;   // largest XCD load / mean for whole heads per XCD
 
 std::vector<Item> layout_queues(const std::vector<int64_t>& head_order, const std::vector<Item>& all,
                                 const std::vector<double>& icost) {
@@ -260,15 +262,36 @@ std::vector<Item> layout_queues(const std::vector<int64_t>& head_order, const st
   }
   const bool uneven = !seq.empty() && cmax > 1.5 * csum / static_cast<double>(seq.size());
   if (uneven && seq.size() <= static_cast<size_t>(2 * kSlots)) {
-    // at most two rounds of work-groups: longest first over all queues (LPT)
-    std::stable_sort(seq.begin(), seq.end(), [&](int64_t a, int64_t b) { return icost[a] > icost[b]; });
+    // At most two rounds of work-groups.  Whole heads go to XCDs, longest
+    // first to the least-loaded one, so that a head's key/value tiles are
+    // read into one L2 only; if that leaves an XCD more than kHeadSpread
+    // above the mean, items go longest first over all queues instead (LPT).
+    std::vector<double> hc(H, 0.0);
+    for (int64_t i : seq) hc[all[i].head] += icost[i];
+    std::vector<int64_t> hs(head_order);
+    std::stable_sort(hs.begin(), hs.end(), [&](int64_t a, int64_t b) { return hc[a] > hc[b]; });
     std::vector<double> load(kXcds, 0.0);
-    for (int64_t i : seq) {
+    std::vector<int> xcd_of(H, 0);
+    for (int64_t h : hs) {
       int x = 0;
       for (int y = 1; y < kXcds; ++y)
         if (load[y] < load[x]) x = y;
-      q[x].push_back(i);
-      load[x] += icost[i];
+      xcd_of[h] = x;
+      load[x] += hc[h];
+    }
+    const double lmax = *std::max_element(load.begin(), load.end());
+    if (H >= kXcds && lmax <= kHeadSpread * csum / kXcds) {
+      for (int64_t i : seq) q[xcd_of[all[i].head]].push_back(i);
+    } else {
+      std::stable_sort(seq.begin(), seq.end(), [&](int64_t a, int64_t b) { return icost[a] > icost[b]; });
+      std::fill(load.begin(), load.end(), 0.0);
+      for (int64_t i : seq) {
+        int x = 0;
+        for (int y = 1; y < kXcds; ++y)
+          if (load[y] < load[x]) x = y;
+        q[x].push_back(i);
+        load[x] += icost[i];
+      }
     }
   } else {
     // consecutive runs of equal cost: an XCD works through few heads at a time

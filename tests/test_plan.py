@@ -167,7 +167,8 @@ def test_schedule_covers_every_row_once(lib):
     """The batch-1 schedule: 8 equal-length XCD queues (padding items have head -1); every (head, query
     tile) row's list is covered exactly once, by one item or by pieces that cut it into contiguous ranges
     in piece order; split rows own distinct partial slots and split-row indices (their merge-list entry);
-    the queues carry equal cost."""
+    the queues carry equal cost: within twice the largest item's, or, where whole heads were given to
+    XCDs (each head's items in one queue), every queue within 5 % of the mean."""
     split_seen = {}
     for name in ("vit896", "vit1792", "lm_headwin"):
         w = workload(name)
@@ -197,12 +198,24 @@ def test_schedule_covers_every_row_once(lib):
             if slots:
                 assert sorted(slots) == list(range(len(slots))) and sorted(split_rows) == list(range(len(split_rows)))
             split_seen[(name, label)] = len(split_rows)
-            # per-XCD queues of equal total cost (within one item's cost)
+            # per-XCD queues of equal total cost
             q = items.reshape(8, -1, 8)
             cost = np.array([[0.0 if it[0] < 0 else 0.5 + _schedule_cost(fl, it[2], it[3]) + (2.0 if it[6] > 1 else 0.0)
                               for it in qq] for qq in q])
             tot = cost.sum(axis=1)
-            assert tot.max() - tot.min() <= 2 * cost.max() + 1e-9, (name, label, tot)
+            heads_per_queue = [set(qq[qq[:, 0] >= 0][:, 0].tolist()) for qq in q]
+            whole_heads = all(not (a & b) for i, a in enumerate(heads_per_queue) for b in heads_per_queue[i + 1:])
+            if whole_heads and name == "lm_headwin":
+                assert tot.max() <= 1.05 * tot.mean() + 1e-9, (name, label, tot)
+            else:
+                assert tot.max() - tot.min() <= 2 * cost.max() + 1e-9, (name, label, tot)
+    # the per-head windows (uneven rows, one round of work-groups) keep each head on one XCD
+    lw = workload("lm_headwin")
+    its = _lib.Plan(lw["masks"]["headwin"], lw["L"], lw["H"], lw["D"]).schedule().reshape(8, -1, 8)
+    owner = {}
+    for x in range(8):
+        for h in set(its[x][its[x][:, 0] >= 0][:, 0].tolist()):
+            assert owner.setdefault(h, x) == x, ("head on two XCDs", h)
     # uniform ViT masks are never split; the causal per-head windows are
     assert split_seen[("vit896", "full")] == 0 and split_seen[("vit1792", "full")] == 0
     assert split_seen[("vit1792", "swa512")] == 0
