@@ -371,8 +371,9 @@ attn_status attn_masked_bwd(const attn_plan* plan, const attn_tensor* q, const a
  * (|q| times the head's largest key-aggregate norm); rows whose sum against it
  * underflows are recomputed exactly by a two-pass kernel.  The selection
  * compares fp32 sums.  The workspace holds the per (key block, row) sums of
- * the pass: 4 bytes per sampled row and key block (2 GiB at 128K tokens,
- * 32 heads, stride 8, block 128).
+ * the pass: 4 bytes per row and key block, with a row for every stride of
+ * every block (Nb * block / stride rows, padded to a multiple of 256; 2 GiB at
+ * 128K tokens, 32 heads, stride 8, block 128).
  */
 typedef struct {
   int64_t stride;             /* S >= 1                                                   */
@@ -386,7 +387,7 @@ attn_status attn_rr_workspace_bytes(const attn_tensor* q, const attn_rr_params* 
 
 /*
  * Run the search on launch->stream (asynchronous; launch->workspace of at least
- * attn_rr_workspace_bytes; optional events bracket the three kernels).
+ * attn_rr_workspace_bytes; optional events bracket all of its kernels).
  *   q, k         : bf16 [B, L, H, D] device views (same shape; D in {64, 80, 128}).
  *   block_mask   : device uint8 [B][H][Nb][Nb], Nb = ceil(L / block): written
  *                  entirely (1 = compute the block pair; zero above the diagonal).
