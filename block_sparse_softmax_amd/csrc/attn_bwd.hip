@@ -53,6 +53,8 @@ namespace {
 
 using namespace dev;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // ---------------------------------------------------------------------------
 // prep: D_i, lse2_i; partial sink-gradient sums
 // ---------------------------------------------------------------------------
@@ -594,58 +596,159 @@ __global__ __launch_bounds__(kThreads, DkdvShape<D>::OCC) void bwd_dkdv_kernel(c
     const unsigned char* gt = qt + S::TILE;
     const float* stl = reinterpret_cast<const float*>(qt + T::STAT);
 
+    if constexpr (D == 128) {
+      // One wave per SIMD: the step's two 32-query chunks are software-
+      // pipelined so that the vector work of one chunk issues beside the
+      // MFMAs of the other:
+      //   S, dP of chunk 0;  S, dP of chunk 1 | P, dS of chunk 0;
+      //   dV, dK of chunk 0 | P, dS of chunk 1;  dV, dK of chunk 1.
+      // Each MFMA step takes one pair of P and dS values (packed to bf16 as
+      // the serial loop packs them); the packed words are pinned per step, so
+      // that the compiler does not sink the exponentials to their first use.
+      float4 l4[2][4], d4[2][4];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {  // 32-query chunks
-      // S = Qs K^T (log2 units), dP = dO V^T (rows: queries 32c .. +31; columns: the wave's keys)
-      f32x16 sc = f32x16{}, dp = f32x16{};
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int ks = 0; ks < S::KS; ++ks) {
-        sc = mfma32(row_frag<D>(qt, roffs[ks], c), kf[ks], sc);
-        dp = mfma32(row_frag<D>(gt, roffs[ks], c), vf[ks], dp);
-      }
-      // row r of the block is query 32c + 8 (r/4) + 4 h2 + r%4 of the step
-      float4 l4[4], d4[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        l4[g] = *reinterpret_cast<const float4*>(stl + 32 * c + 8 * g + 4 * h2);
-        d4[g] = *reinterpret_cast<const float4*>(stl + 64 + 32 * c + 8 * g + 4 * h2);
-      }
-      if (masked) {
+        for (int g = 0; g < 4; ++g) {
+          l4[c][g] = *reinterpret_cast<const float4*>(stl + 32 * c + 8 * g + 4 * h2);
+          d4[c][g] = *reinterpret_cast<const float4*>(stl + 64 + 32 * c + 8 * g + 4 * h2);
+        }
+      auto comp = [](const float4& v, int i) __attribute__((always_inline)) {
+        return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+      };
+      f32x16 sc[2], dp[2];
+      u32x4 pw[2][2], dw[2][2];               // P and dS of each chunk, bf16 pairs (B operands)
+      auto mask_chunk = [&](int c) __attribute__((always_inline)) {
+        if (!masked) return;
         const unsigned ubase = static_cast<unsigned>(row0 + 32 * c + 4 * h2 - qlo);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const unsigned u = ubase + 8 * (r >> 2) + (r & 3);
-          sc[r] = u >= static_cast<unsigned>(qwidth) ? -INFINITY : sc[r];
+          sc[c][r] = u >= static_cast<unsigned>(qwidth) ? -INFINITY : sc[c][r];
         }
-      }
-      bf16x8 pb[2], dsb[2];
+      };
+      // P and dS of chunk c, values r = 2 i, 2 i + 1
+      auto soft_pair = [&](int c, int i) __attribute__((always_inline)) {
+        float pr[2], ds[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float4& L4 = l4[r >> 2];
-        const float4& D4 = d4[r >> 2];
-        const float lr = (r & 3) == 0 ? L4.x : (r & 3) == 1 ? L4.y : (r & 3) == 2 ? L4.z : L4.w;
-        const float dr = (r & 3) == 0 ? D4.x : (r & 3) == 1 ? D4.y : (r & 3) == 2 ? D4.z : D4.w;
-        const float pr = __builtin_amdgcn_exp2f(sc[r] - lr);
-        pb[r >> 3][r & 7] = (__bf16)pr;
-        dsb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - dr));
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS (K dimension: 16-query steps 2c, 2c+1),
-      // at raised priority when two waves share a SIMD (as in the dQ kernel)
-      if constexpr (D != 128) {
-        __builtin_amdgcn_s_setprio(1);
+        for (int e = 0; e < 2; ++e) {
+          const int r = 2 * i + e;
+          pr[e] = __builtin_amdgcn_exp2f(sc[c][r] - comp(l4[c][r >> 2], r & 3));
+          ds[e] = pr[e] * (dp[c][r] - comp(d4[c][r >> 2], r & 3));
+        }
+        uint32_t wp = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)pr[0], (__bf16)pr[1]});
+        uint32_t wd = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)ds[0], (__bf16)ds[1]});
+        __asm__ volatile("" : "+v"(wp), "+v"(wd));
+        pw[c][i >> 2][i & 3] = wp;
+        dw[c][i >> 2][i & 3] = wd;
+      };
+      auto bop = [](const u32x4& w) __attribute__((always_inline)) { return __builtin_bit_cast(bf16x8, w); };
+
+      // The step as 32 operations of two MFMAs each: S, dP of chunk 0 (ks 0..7),
+      // of chunk 1, then dV, dK of chunk 0 ((t2, dt) pairs), of chunk 1.  Each
+      // operation's two LDS fragments are read kAhead operations before it.
+      constexpr int kOps = 4 * S::KS;
+      static_assert(2 * S::DT == S::KS, "dV/dK operations per chunk match S/dP ones at d = 128");
+      constexpr int kAhead = 3;
+      auto frags = [&](int j, bf16x8 (&f)[2]) __attribute__((always_inline)) {
+        if (j < 2 * S::KS) {
+          const int c = j / S::KS, ks = j % S::KS;
+          f[0] = row_frag<D>(qt, roffs[ks], c);
+          f[1] = row_frag<D>(gt, roffs[ks], c);
+        } else {
+          const int c = (j - 2 * S::KS) / S::KS, st = (j - 2 * S::KS) % S::KS;
+          const int t2 = st / S::DT, dt = st % S::DT;
+          f[0] = tr_frag<D>(gt, toff[dt][0], toff[dt][1], 2 * c + t2);
+          f[1] = tr_frag<D>(qt, toff[dt][0], toff[dt][1], 2 * c + t2);
+        }
+      };
+      bf16x8 fr[kOps][2];
+#pragma unroll
+      for (int j = 0; j < kAhead; ++j) frags(j, fr[j]);
+      sc[0] = f32x16{};
+      dp[0] = f32x16{};
+      sc[1] = f32x16{};
+      dp[1] = f32x16{};
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < kOps; ++j) {
+        if (j == S::KS) {
+          mask_chunk(0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (j == 2 * S::KS) {
+          mask_chunk(1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (j + kAhead < kOps) frags(j + kAhead, fr[j + kAhead]);
+        if (j < 2 * S::KS) {
+          const int c = j / S::KS, ks = j % S::KS;
+          sc[c] = mfma32(fr[j][0], kf[ks], sc[c]);
+          if (c == 1) soft_pair(0, ks);
+          dp[c] = mfma32(fr[j][1], vf[ks], dp[c]);
+        } else {
+          const int c = (j - 2 * S::KS) / S::KS, st = (j - 2 * S::KS) % S::KS;
+          const int t2 = st / S::DT, dt = st % S::DT;
+          dv[dt] = mfma32(fr[j][0], bop(pw[c][t2]), dv[dt]);
+          if (c == 0) soft_pair(1, st);
+          dk[dt] = mfma32(fr[j][1], bop(dw[c][t2]), dk[dt]);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-#pragma unroll
-        for (int dt = 0; dt < S::DT; ++dt) {
-          dv[dt] = mfma32(tr_frag<D>(gt, toff[dt][0], toff[dt][1], 2 * c + t2), pb[t2], dv[dt]);
-          dk[dt] = mfma32(tr_frag<D>(qt, toff[dt][0], toff[dt][1], 2 * c + t2), dsb[t2], dk[dt]);
+    } else {
+  #pragma unroll
+      for (int c = 0; c < 2; ++c) {  // 32-query chunks
+        // S = Qs K^T (log2 units), dP = dO V^T (rows: queries 32c .. +31; columns: the wave's keys)
+        f32x16 sc = f32x16{}, dp = f32x16{};
+  #pragma unroll
+        for (int ks = 0; ks < S::KS; ++ks) {
+          sc = mfma32(row_frag<D>(qt, roffs[ks], c), kf[ks], sc);
+          dp = mfma32(row_frag<D>(gt, roffs[ks], c), vf[ks], dp);
         }
-      }
-      if constexpr (D != 128) {
-        __builtin_amdgcn_s_setprio(0);
-        __builtin_amdgcn_sched_barrier(0);
+        // row r of the block is query 32c + 8 (r/4) + 4 h2 + r%4 of the step
+        float4 l4[4], d4[4];
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          l4[g] = *reinterpret_cast<const float4*>(stl + 32 * c + 8 * g + 4 * h2);
+          d4[g] = *reinterpret_cast<const float4*>(stl + 64 + 32 * c + 8 * g + 4 * h2);
+        }
+        if (masked) {
+          const unsigned ubase = static_cast<unsigned>(row0 + 32 * c + 4 * h2 - qlo);
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const unsigned u = ubase + 8 * (r >> 2) + (r & 3);
+            sc[r] = u >= static_cast<unsigned>(qwidth) ? -INFINITY : sc[r];
+          }
+        }
+        bf16x8 pb[2], dsb[2];
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float4& L4 = l4[r >> 2];
+          const float4& D4 = d4[r >> 2];
+          const float lr = (r & 3) == 0 ? L4.x : (r & 3) == 1 ? L4.y : (r & 3) == 2 ? L4.z : L4.w;
+          const float dr = (r & 3) == 0 ? D4.x : (r & 3) == 1 ? D4.y : (r & 3) == 2 ? D4.z : D4.w;
+          const float pr = __builtin_amdgcn_exp2f(sc[r] - lr);
+          pb[r >> 3][r & 7] = (__bf16)pr;
+          dsb[r >> 3][r & 7] = (__bf16)(pr * (dp[r] - dr));
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS (K dimension: 16-query steps 2c, 2c+1),
+        // at raised priority when two waves share a SIMD (as in the dQ kernel)
+        if constexpr (D != 128) {
+          __builtin_amdgcn_s_setprio(1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+  #pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+  #pragma unroll
+          for (int dt = 0; dt < S::DT; ++dt) {
+            dv[dt] = mfma32(tr_frag<D>(gt, toff[dt][0], toff[dt][1], 2 * c + t2), pb[t2], dv[dt]);
+            dk[dt] = mfma32(tr_frag<D>(qt, toff[dt][0], toff[dt][1], 2 * c + t2), dsb[t2], dk[dt]);
+          }
+        }
+        if constexpr (D != 128) {
+          __builtin_amdgcn_s_setprio(0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     if (s == 1) {
