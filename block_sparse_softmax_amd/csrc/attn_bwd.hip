@@ -58,54 +58,55 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 // prep: D_i, lse2_i; partial sink-gradient sums
 // ---------------------------------------------------------------------------
+// One work-group per (batch, head, query tile); a row's 16-byte chunks sit on
+// P adjacent lanes (P = D / 8 rounded up to a power of two, lanes past D / 8
+// idle), so every load and store of a pass is contiguous; D_i is summed per
+// lane over its 8 elements, then over the row's lanes.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams p) {
+  constexpr int CH = D / 8;                  // 16-byte chunks of a row
+  constexpr int P = CH <= 8 ? 8 : 16;        // lanes per row
+  constexpr int RPP = 256 / P;               // rows per pass
+  static_assert(CH <= P && kBM % RPP == 0, "row layout");
   const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const int i = qt * kBM + row;
-  float dsum = 0.f;
-  if (i < p.L) {
-    const unsigned char* o = reinterpret_cast<const unsigned char*>(p.o + b * p.o_sb + h * p.o_sh) +
-                             static_cast<int64_t>(i) * p.o_sl * 2 + half * D;
-    const unsigned char* g = reinterpret_cast<const unsigned char*>(p.dout + b * p.do_sb + h * p.do_sh) +
-                             static_cast<int64_t>(i) * p.do_sl * 2 + half * D;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + 16 * c);
-      const bf16x8 y = *reinterpret_cast<const bf16x8*>(g + 16 * c);
+  const int c = threadIdx.x % P, rsub = threadIdx.x / P;
+  const unsigned char* obase = reinterpret_cast<const unsigned char*>(p.o + b * p.o_sb + h * p.o_sh);
+  const unsigned char* gbase = reinterpret_cast<const unsigned char*>(p.dout + b * p.do_sb + h * p.do_sh);
+  const unsigned char* qbase = reinterpret_cast<const unsigned char*>(p.q + b * p.q_sb + h * p.q_sh);
+  unsigned char* qwbase = reinterpret_cast<unsigned char*>(p.qs) + (static_cast<int64_t>(b) * p.H + h) * p.L * (D * 2);
+  float* st = p.stat + (static_cast<int64_t>(b) * p.H + h) * 2 * p.Lpad;
+  const float sink2 = (p.dsink != nullptr && p.sink != nullptr) ? p.sink[h] * kLog2e : -INFINITY;
+  float t = 0.f;                             // this lane's share of the sink-gradient partial sum
+  for (int pass = 0; pass < kBM / RPP; ++pass) {
+    const int i = qt * kBM + pass * RPP + rsub;
+    float dsum = 0.f;
+    if (i < p.L && c < CH) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(obase + static_cast<int64_t>(i) * p.o_sl * 2 + 16 * c);
+      const bf16x8 y = *reinterpret_cast<const bf16x8*>(gbase + static_cast<int64_t>(i) * p.do_sl * 2 + 16 * c);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf((float)x[e], (float)y[e], dsum);
-    }
-  }
-  dsum += __shfl_xor(dsum, 1);
-  if (i < p.L) {  // this thread's half of the scaled query row
-    const unsigned char* qr = reinterpret_cast<const unsigned char*>(p.q + b * p.q_sb + h * p.q_sh) +
-                              static_cast<int64_t>(i) * p.q_sl * 2 + half * D;
-    unsigned char* qw = reinterpret_cast<unsigned char*>(p.qs) +
-                        ((static_cast<int64_t>(b) * p.H + h) * p.L + i) * (D * 2) + half * D;
+      // this lane's chunk of the scaled query row
+      const bf16x8 qx = *reinterpret_cast<const bf16x8*>(qbase + static_cast<int64_t>(i) * p.q_sl * 2 + 16 * c);
+      bf16x8 qy;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
-      bf16x8 y;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = (__bf16)((float)x[e] * p.scale_log2);
-      *reinterpret_cast<bf16x8*>(qw + 16 * c) = y;
+      for (int e = 0; e < 8; ++e) qy[e] = (__bf16)((float)qx[e] * p.scale_log2);
+      *reinterpret_cast<bf16x8*>(qwbase + static_cast<int64_t>(i) * (D * 2) + 16 * c) = qy;
     }
-  }
-  float lse2 = INFINITY;
-  if (i < p.L) {
-    const float lse = p.lse[(static_cast<int64_t>(b) * p.H + h) * p.L + i];
-    lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
-  }
-  float* st = p.stat + (static_cast<int64_t>(b) * p.H + h) * 2 * p.Lpad;
-  if (half == 0) {
-    st[i] = lse2;
-    st[p.Lpad + i] = i < p.L ? dsum : 0.f;
+#pragma unroll
+    for (int off = 1; off < P; off <<= 1) dsum += __shfl_xor(dsum, off);
+    if (c == 0) {
+      float lse2 = INFINITY;
+      if (i < p.L) {
+        const float lse = p.lse[(static_cast<int64_t>(b) * p.H + h) * p.L + i];
+        lse2 = lse == -INFINITY ? INFINITY : lse * kLog2e;
+      }
+      st[i] = lse2;
+      st[p.Lpad + i] = i < p.L ? dsum : 0.f;
+      // the sink's share of row i is exp2(s_aux log2 e - lse2_i)
+      if (i < p.L && sink2 > -INFINITY) t += __builtin_amdgcn_exp2f(sink2 - lse2) * dsum;
+    }
   }
   if (p.dsink == nullptr) return;
-  // the sink's share of row i is exp2(s_aux log2 e - lse2_i)
-  float t = 0.f;
-  if (half == 0 && i < p.L && p.sink != nullptr) t = __builtin_amdgcn_exp2f(p.sink[h] * kLog2e - lse2) * dsum;
   __shared__ float red[256];
   red[threadIdx.x] = t;
   __syncthreads();
