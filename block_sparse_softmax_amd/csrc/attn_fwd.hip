@@ -747,27 +747,64 @@ __global__ __launch_bounds__(kThreads) void attn_merge_kernel(const GroupParams 
   const int h2 = lane >> 5, l31 = lane & 31;
   const float* slots = p.partials + static_cast<int64_t>(slot0) * kSlotFloats;
 
+  // every piece's reference and sum first (one batch of loads), then the
+  // pieces' accumulators two at a time: piece i + 1's loads are in flight
+  // while piece i is added (pieces are still added in piece order)
+  constexpr int kMaxMerge = 16;              // pieces per split row (the plan's limit)
+  float mv[kMaxMerge], lv[kMaxMerge];
+#pragma unroll
+  for (int i = 0; i < kMaxMerge; ++i) {
+    mv[i] = i < npieces ? slots[static_cast<int64_t>(i) * kSlotFloats + kSlotM + wave * 64 + lane] : -INFINITY;
+    lv[i] = i < npieces ? slots[static_cast<int64_t>(i) * kSlotFloats + kSlotL + wave * 64 + lane] : 0.f;
+  }
   float mmax = -INFINITY;
-  for (int i = 0; i < npieces; ++i)
+#pragma unroll
+  for (int i = 0; i < kMaxMerge; ++i) mmax = fmaxf(mmax, mv[i]);
+  for (int i = kMaxMerge; i < npieces; ++i)  // beyond the plan's limit: read as needed
     mmax = fmaxf(mmax, slots[static_cast<int64_t>(i) * kSlotFloats + kSlotM + wave * 64 + lane]);
   f32x16 acc[S::DT];
 #pragma unroll
   for (int dt = 0; dt < S::DT; ++dt) acc[dt] = f32x16{};
   float lm = 0.f;
-  for (int i = 0; i < npieces; ++i) {
+  auto load_piece = [&](int i, float4 (&a)[S::DT * 4]) __attribute__((always_inline)) {
     const float* sp = slots + static_cast<int64_t>(i) * kSlotFloats;
-    const float mi = sp[kSlotM + wave * 64 + lane];
+#pragma unroll
+    for (int k = 0; k < S::DT * 4; ++k) a[k] = *reinterpret_cast<const float4*>(sp + ((wave * S::DT * 4 + k) * 64 + lane) * 4);
+  };
+  auto add_piece = [&](int i, const float4 (&a)[S::DT * 4]) __attribute__((always_inline)) {
+    float mi = mv[0], li = lv[0];
+#pragma unroll
+    for (int k = 1; k < kMaxMerge; ++k) {
+      mi = i == k ? mv[k] : mi;
+      li = i == k ? lv[k] : li;
+    }
+    if (i >= kMaxMerge) {
+      mi = slots[static_cast<int64_t>(i) * kSlotFloats + kSlotM + wave * 64 + lane];
+      li = slots[static_cast<int64_t>(i) * kSlotFloats + kSlotL + wave * 64 + lane];
+    }
     const float w = mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - mmax);
-    lm = __builtin_fmaf(w, sp[kSlotL + wave * 64 + lane], lm);
+    lm = __builtin_fmaf(w, li, lm);
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt) {
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
-        const float4 a = *reinterpret_cast<const float4*>(sp + (((wave * S::DT + dt) * 4 + gg) * 64 + lane) * 4);
-        acc[dt][4 * gg + 0] = __builtin_fmaf(w, a.x, acc[dt][4 * gg + 0]);
-        acc[dt][4 * gg + 1] = __builtin_fmaf(w, a.y, acc[dt][4 * gg + 1]);
-        acc[dt][4 * gg + 2] = __builtin_fmaf(w, a.z, acc[dt][4 * gg + 2]);
-        acc[dt][4 * gg + 3] = __builtin_fmaf(w, a.w, acc[dt][4 * gg + 3]);
+        const float4& x = a[dt * 4 + gg];
+        acc[dt][4 * gg + 0] = __builtin_fmaf(w, x.x, acc[dt][4 * gg + 0]);
+        acc[dt][4 * gg + 1] = __builtin_fmaf(w, x.y, acc[dt][4 * gg + 1]);
+        acc[dt][4 * gg + 2] = __builtin_fmaf(w, x.z, acc[dt][4 * gg + 2]);
+        acc[dt][4 * gg + 3] = __builtin_fmaf(w, x.w, acc[dt][4 * gg + 3]);
+      }
+    }
+  };
+  {
+    float4 b0[S::DT * 4], b1[S::DT * 4];
+    if (npieces > 0) load_piece(0, b0);
+    for (int i = 0; i < npieces; i += 2) {
+      if (i + 1 < npieces) load_piece(i + 1, b1);
+      add_piece(i, b0);
+      if (i + 1 < npieces) {
+        if (i + 2 < npieces) load_piece(i + 2, b0);
+        add_piece(i + 1, b1);
       }
     }
   }
