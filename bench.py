@@ -276,6 +276,7 @@ ratio: {hbm / alg:.3f}
 
 TRACE_RUN_ARGS = "--quick --no-cpu-baseline --no-clocks --steps 10 --warmup 2 --reps 10"
 TRACE_GROUPED = slice(2, 12)   # the timed grouped launches of a TRACE_RUN_ARGS run
+TRACE_REPS, TRACE_MASK_WARMUP = 10, 3   # then per mask: 3 untimed and 10 timed launches alone
 
 
 def _kernel_rows(path_glob: str, kernel: str):
@@ -318,6 +319,23 @@ def trace_summary(workload: str, trace_dir: str, out_dir: str | None = None) -> 
     if merges:
         merge_line = (f"\nThe run also holds {len(merges)} dispatches of the split-row merge "
                       f"(attn_merge_kernel), {statistics.mean(merges) * 1e3:.1f} us on average.\n")
+    # each mask alone: its timed dispatches of the per-launch protocol (kernel durations, so without
+    # the dispatch latency that the event-timed figures of the bench line include)
+    io = _io_bytes(w)
+    alone = ["", "Each mask alone (the per-launch protocol's timed dispatches; kernel durations):", "",
+             "| mask | dispatches | median | min | TFLOP/s at the median | algorithmic GB/s at the median | of 8 TB/s |",
+             "|---|---|---|---|---|---|---|"]
+    for mi, (label, m) in enumerate(w["masks"].items()):
+        s0 = TRACE_GROUPED.stop + mi * (TRACE_MASK_WARMUP + TRACE_REPS) + TRACE_MASK_WARMUP
+        ds = [d for _, _, d in rows[s0:s0 + TRACE_REPS]]
+        if len(ds) < TRACE_REPS:
+            continue
+        md = statistics.median(ds)
+        f_m = 4.0 * w["D"] * int(Plan(m, w["L"], w["H"], w["D"]).pairs()[1]) * w["B"]
+        alone.append(f"| {label} | {len(ds)} | {md * 1e3:.1f} us | {min(ds) * 1e3:.1f} us | "
+                     f"{f_m / (md * 1e-3) / 1e12:.1f} | {io / (md * 1e-3) / 1e9:.0f} | "
+                     f"{io / (md * 1e-3) / 1e9 / PEAK_HBM_GBS:.3f} |")
+    alone_txt = "\n".join(alone) + "\n" if len(alone) > 5 else ""
     shown = kern + (">" if "<" in kern else "")
     txt = f"""# {shown}, {workload} — kernel trace
 
@@ -341,7 +359,7 @@ Effective throughput at the average duration: {flops / 1e12:.4f} TFLOP (4 d per 
 {len(rows)} dispatches of the run are 2 warm-up and 10 timed grouped launches (summarised here), then the
 per-launch protocol (each mask alone, with a cache flush between launches when the working set fits the
 last-level cache).
-{merge_line}"""
+{alone_txt}{merge_line}"""
     path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"{kern.split('<')[0]}_{workload}_stats.md")
     with open(path, "w") as fh:
         fh.write(txt)
