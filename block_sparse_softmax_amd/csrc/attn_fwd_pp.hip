@@ -119,6 +119,11 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const GroupParams g
   const int64_t q_row_bytes = p.q_sl * 2, k_row_bytes = p.k_sl * 2, v_row_bytes = p.v_sl * 2,
                 o_row_bytes = p.o_sl * 2;
 
+  // kept in registers: read from the parameter block inside the loop, these
+  // would be reloaded after every barrier and copy (a scalar load and a wait
+  // that also drains the wave's LDS reads)
+  const int32_t* const kv_list = p.kv;
+  const int seq_len = p.L;
   const int n = e_end - e_begin;
   const int ng = (n - grp + 1) >> 1;  // this group's tiles: list entries e_begin + grp + 2 t
   const int N = (n + 1) >> 1;         // group A's count (group B has N or N - 1)
@@ -206,12 +211,12 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const GroupParams g
     const int i0 = (wq & 1) * kPer;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(
         smem_lds + (dma_tensor ? vbuf(set) : kbuf(set)) + i0 * blk_bytes);
-    if (static_cast<int>(kv0) + kBN <= p.L) {
+    if (static_cast<int>(kv0) + kBN <= seq_len) {
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
         dma16(tb + static_cast<uint64_t>(i0 + i) * dma_row_bytes, goff_pad, dst + i * blk_bytes);
     } else {  // ragged last tile: clamp rows past the end of the sequence (their keys are masked)
-      const int last = p.L - 1 - static_cast<int>(kv0);
+      const int last = seq_len - 1 - static_cast<int>(kv0);
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int row = i0 + i + 16 * (lane >> 4);
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(512, 1) void attn_fwd_pp_kernel(const GroupParams g
   };
   // list entry of this group's tile t (a uniform load; -1 past the group's end)
   auto entry = [&](int t) __attribute__((always_inline)) {
-    return t < ng ? __builtin_amdgcn_readfirstlane(p.kv[e_begin + grp + 2 * t]) : -1;
+    return t < ng ? __builtin_amdgcn_readfirstlane(kv_list[e_begin + grp + 2 * t]) : -1;
   };
   // pair t = (K_t, V_{t-1}) into set t mod 2: K-waves copy K_t, V-waves V_{t-1}
   auto issue_pair = [&](int t, int ent_k, int ent_v) __attribute__((always_inline)) {
