@@ -86,6 +86,10 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void attn_fwd_sg_kernel
   const int64_t q_row_bytes = p.q_sl * 2, k_row_bytes = p.k_sl * 2, v_row_bytes = p.v_sl * 2,
                 o_row_bytes = p.o_sl * 2;
   const int n = e_end - e_begin;
+  // kept in registers: read from the parameter block inside the loop, these
+  // would be reloaded after every barrier and copy
+  const int32_t* const kv_list = p.kv;
+  const int seq_len = p.L;
 
   // ---- this lane's query; Q fragments pre-scaled by softmax_scale * log2(e) ----
   const int qi = qtile * kBM + wave * 32 + l31;
@@ -172,12 +176,12 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void attn_fwd_sg_kernel
     constexpr int kPer = NI / 2;
     const int i0 = (wave & 1) * kPer;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(smem_lds + L::buf_off(2 * dma_tensor + set) + i0 * blk_bytes);
-    if (static_cast<int>(kv0) + kBN <= p.L) {
+    if (static_cast<int>(kv0) + kBN <= seq_len) {
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
         dma16(tb + static_cast<uint64_t>(i0 + i) * dma_row_bytes, goff, dst + i * blk_bytes);
     } else {  // ragged last tile: clamp rows past the end of the sequence (their keys are masked)
-      const int last = p.L - 1 - static_cast<int>(kv0);
+      const int last = seq_len - 1 - static_cast<int>(kv0);
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int row = i0 + i + NI * (lane / CPR);
@@ -272,14 +276,20 @@ __global__ __launch_bounds__(kThreads, D == 128 ? 2 : 1) void attn_fwd_sg_kernel
   };
 
   if (n > 0) {
-    int ent = __builtin_amdgcn_readfirstlane(p.kv[e_begin]);
-    int ent1 = n > 1 ? __builtin_amdgcn_readfirstlane(p.kv[e_begin + 1]) : 0;
+    int ent = __builtin_amdgcn_readfirstlane(kv_list[e_begin]);
+    int ent1 = n > 1 ? __builtin_amdgcn_readfirstlane(kv_list[e_begin + 1]) : 0;
+    // entry j + 2 is loaded at the top of iteration j and read into a scalar
+    // register at the top of iteration j + 1, after the tile's wait for its
+    // copies has also covered it (a load used at once would cost a round trip
+    // per tile)
+    int raw2 = n > 2 ? kv_list[e_begin + 2] : 0;
     issue_tile(ent >> 1, 0);
     if (unmasked(ent)) tile(0, ent, ent1, Bool<false>{}, Bool<true>{});
     else tile(0, ent, ent1, Bool<true>{}, Bool<true>{});
     for (int j = 1; j < n; ++j) {
       ent = ent1;
-      ent1 = j + 1 < n ? __builtin_amdgcn_readfirstlane(p.kv[e_begin + j + 1]) : 0;
+      ent1 = j + 1 < n ? __builtin_amdgcn_readfirstlane(raw2) : 0;
+      raw2 = j + 2 < n ? kv_list[e_begin + j + 2] : 0;
       if (unmasked(ent)) tile(j, ent, ent1, Bool<false>{}, Bool<false>{});
       else tile(j, ent, ent1, Bool<true>{}, Bool<false>{});
     }
