@@ -320,20 +320,24 @@ __global__ __launch_bounds__(kRrThreads) void rr_scores_kernel(const RrParams p)
 }
 
 // ---------------------------------------------------------------- kmax ----
-// One work-group per (batch, head): the largest |hi + lo| over the head's
-// rows (padding rows are 0), stored as the float's bits.
-__global__ __launch_bounds__(256) void rr_kmax_kernel(const RrParams p) {
-  __shared__ float wmax[4];
+// One work-group of 1024 threads per (batch, head): the largest |hi + lo|
+// over the head's rows (padding rows are 0), stored as the float's bits.
+__global__ __launch_bounds__(1024) void rr_kmax_kernel(const RrParams p) {
+  __shared__ float wmax[16];
   const int64_t bh = static_cast<int64_t>(blockIdx.y) * p.H + blockIdx.x;
   const float* n2 = p.knorm2 + bh * p.ns_pad;
   float m = 0.f;
-  for (int r = threadIdx.x; r < p.ns_pad; r += 256) m = fmaxf(m, n2[r]);
+  for (int r = threadIdx.x; r < p.ns_pad; r += 1024) m = fmaxf(m, n2[r]);
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0)
-    p.kmax[bh] = __float_as_uint(__builtin_sqrtf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
+  if (threadIdx.x == 0) {
+    float x = wmax[0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) x = fmaxf(x, wmax[w]);
+    p.kmax[bh] = __float_as_uint(__builtin_sqrtf(x));
+  }
 }
 
 // ------------------------------------------------------ scores, one pass ----
@@ -780,7 +784,7 @@ hipError_t launch_rr_search(const RrParams& p, hipStream_t stream, hipEvent_t st
   if (p.D == 64) hipLaunchKernelGGL(rr_prep_kernel<8>, pgrid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL(rr_prep_kernel<16>, pgrid, dim3(256), 0, stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(rr_kmax_kernel, dim3(static_cast<unsigned>(p.H), static_cast<unsigned>(p.B)), dim3(256), 0,
+  hipLaunchKernelGGL(rr_kmax_kernel, dim3(static_cast<unsigned>(p.H), static_cast<unsigned>(p.B)), dim3(1024), 0,
                      stream, p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   switch (p.D) {
