@@ -62,3 +62,18 @@ def test_blocks_are_consecutive_positions():
             cells = [where[t + u] for u in range(4)]
             rs, cs = {r for r, _ in cells}, {c for _, c in cells}
             assert len(rs) == 2 and len(cs) == 2 and min(rs) % 2 == 0 and min(cs) % 2 == 0
+
+
+def test_row_major_window_example_of_the_pages():
+    """The Factor 2 example of "Semantic Head Specialization ..." (the Factor 2 slides, panel (c) and the
+    right-hand example): on the 4 x 8 patch grid with 2 x 2 blocks, the row-major block order puts the
+    anchor token 23 so that its sliding window of 8 positions on each side (15 .. 31) lies in the rows
+    around it.  Worked by hand from the figure's definition: blocks are numbered left to right, then top to
+    bottom, four positions each; token 23 is the last position of block 5, which is block (1, 1), so it sits
+    at patch (3, 3); position 15 closes block 3 = block (0, 3) at patch (1, 7); positions 16 .. 31 fill
+    blocks (1, 0) .. (1, 3), i.e. exactly patch rows 2 and 3."""
+    pos = positions("block_row", 4, 8)
+    where = {int(pos[r, c]): (r, c) for r in range(4) for c in range(8)}
+    assert where[23] == (3, 3)
+    assert where[15] == (1, 7)
+    assert {where[t] for t in range(16, 32)} == {(r, c) for r in (2, 3) for c in range(8)}
