@@ -168,6 +168,31 @@ def test_rr_search_grouped_keys():
                 assert np.array_equal(bm[0, h, m], b_ref[m]), (h, m)
 
 
+def test_rr_search_batch():
+    """Batch 2 with different data per batch element (the single pass's grid walks batch and head in one
+    index): every (b, h) against the oracle of its own element, and the rows with a clear decision equal."""
+    from block_sparse_softmax_amd import rr_search
+    B, L, H, D, S, Bs, tau = 2, 2000, 2, 64, 8, 128, 0.9
+    print(f"[case] rr search batch B={B} L={L} H={H} D={D}", flush=True)
+    q, k = _random(88, B, H, L, D)
+    bm, sc = rr_search(_dev(q), _dev(k), S, Bs, tau, layout="bhld")
+    torch.cuda.synchronize()
+    bm, sc = bm.cpu().numpy(), sc.cpu().numpy().astype(np.float64)
+    nb = -(-L // Bs)
+    clear = 0
+    for b in range(B):
+        for h in range(H):
+            s_ref, b_ref = rr_oracle(q, k, S, Bs, tau, b=b, h=h)
+            tol = score_tolerance(q, k, S, Bs, h, b=b)
+            assert np.all(np.abs(sc[b, h] - s_ref) <= tol), (b, h)
+            assert np.all(bm[b, h, nb - 1] == 1)
+            for m in range(nb - 1):
+                if _check_row(bm[b, h, m, : m + 1], s_ref[m, : m + 1], tau, float(tol[m].sum())):
+                    clear += 1
+                    assert np.array_equal(bm[b, h, m], b_ref[m]), (b, h, m)
+    assert clear >= 0.5 * B * H * (nb - 1)
+
+
 @pytest.mark.parametrize("L,H,big", [(8192, 1, 20.0), (8192, 1, 25.0), (2048, 2, 400.0)])
 def test_rr_search_recompute_path(L, H, big):
     """Queries live in the first half of the head dim; one key of some strides carries a large component
