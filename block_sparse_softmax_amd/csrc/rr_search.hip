@@ -112,10 +112,20 @@ __global__ __launch_bounds__(256) void rr_prep_kernel(const RrParams p) {
     qo = *reinterpret_cast<const bf16x8*>(p.q + b * p.q_sb + static_cast<int64_t>(pos) * p.q_sl + h * p.q_sh + 8 * c);
     float acc[8] = {};
     const uint16_t* kr = p.k + b * p.k_sb + static_cast<int64_t>(j) * p.S * p.k_sl + (h / p.kv_group) * p.k_sh + 8 * c;
-    for (int s = 0; s < p.S; ++s) {
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(kr + static_cast<int64_t>(s) * p.k_sl);
+    // the stride's rows in batches of 8 loads issued together (one round trip
+    // per batch instead of one per row); the sum stays in row order
+    for (int s0 = 0; s0 < p.S; s0 += 8) {
+      bf16x8 x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += static_cast<float>(x[e]);
+      for (int u = 0; u < 8; ++u)
+        x[u] = *reinterpret_cast<const bf16x8*>(kr + static_cast<int64_t>(min(s0 + u, p.S - 1)) * p.k_sl);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (s0 + u < p.S) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += static_cast<float>(x[u][e]);
+        }
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
