@@ -221,10 +221,15 @@ void compile_blocks(attn_plan& p) {
 //
 // Cost of a (head, query tile) row: its listed tiles (a PARTIAL tile counts
 // 1.25 for the masking) plus 0.5 for the Q load and the epilogue.  Rows much
-// longer than the launch's fair share T = max(total / kSlots, kMinPiece) are
-// cut into pieces of about T tiles (batch 1 only), so that a causal or
-// per-head-window launch with about as many rows as resident work-groups is
-// not held up by its longest rows.  Items are then laid out as kXcds queues:
+// longer than T = max(total / (kPieceShare kSlots), kMinPiece) are cut into
+// pieces of about T tiles (batch 1 only), so that a causal or per-head-window
+// launch with about as many rows as resident work-groups is not held up by
+// its longest rows.  T is 1 / kPieceShare times the fair share of a resident
+// work-group: an item's prologue (item record, Q rows, first list entries and
+// copies: about three tiles' time) and the merge of a piece's partial state
+// cost more than the imbalance that longer pieces leave (per-head windows at
+// 4K tokens, pieces of 1, 1.1, 1.25, 1.33, 1.43, 1.67 times the fair share:
+// 80.4, 78.9, 78.5, 77.7, 75.9, 81.6 us).  Items are then laid out as kXcds queues:
 // heads in descending cost, rows of a head in descending cost, and the
 // sequence cut into kXcds consecutive runs of equal total cost (so the work
 // that shares an XCD's L2 comes from as few heads as possible; measured
@@ -237,6 +242,7 @@ void compile_blocks(attn_plan& p) {
 // Queues are padded to equal length with null items.
 constexpr double kPingPongMinTiles = 32.0;  // d = 128: mean row cost (tiles) from which the ping-pong kernel runs
 constexpr double kMinPiece = 12.0;     // tiles: below this a piece's merge costs more than it saves
+constexpr double kPieceShare = 0.7;    // pieces are sized for this fraction of the resident work-groups
 constexpr double kPieceOverhead = 2.0; // tiles: writing the partial state and the merge
 constexpr int kMaxPieces = 16;
 constexpr double kHeadSpread = 1.05;   // largest XCD load / mean for whole heads per XCD
@@ -348,7 +354,7 @@ void schedule(attn_plan& p) {
   p.items_unsplit = layout_queues(heads, whole, cost);
 
   // batch-1 schedule: long rows cut into pieces
-  const double share = std::max(total / kSlots, kMinPiece);
+  const double share = std::max(total / (kPieceShare * kSlots), kMinPiece);
   std::vector<Item> all;
   std::vector<double> icost;
   all.reserve(rows);
