@@ -61,14 +61,16 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 LLC_BYTES = 256 * 2**20       # MI355X last-level (Infinity) cache
 FLUSH_BYTES = 512 * 2**20     # scratch rewritten between launches to evict it
 CSRC = os.path.join(ROOT, "block_sparse_softmax_amd", "csrc")
-# source of each head dim's forward kernel, and the headers every forward kernel includes
+# source of each head dim's forward kernel, the headers every forward kernel includes, and the
+# scheduler (which work-group runs which tiles decides what the L2s share, hence the traffic)
 KERNEL_SRC = {"swizzled": "attn_fwd.hip", "pingpong": "attn_fwd_pp.hip", "single": "attn_fwd_sg.hip"}
-KERNEL_HEADERS = ("fwd_common.hpp", "tile_common.hpp", "kernels.hpp")
+KERNEL_HEADERS = ("fwd_common.hpp", "tile_common.hpp", "kernels.hpp", "plan.cpp")
 DEFAULT_WORKLOAD = "blocksparse128k"
 
 
 def _kernel_hash(kind: str) -> str:
-    """Hash of a forward kernel's source (its file and the shared headers); kind as Plan.kernel()."""
+    """Hash of a forward kernel's source (its file, the shared headers and the scheduler); kind as
+    Plan.kernel()."""
     h = hashlib.sha256()
     for f in (KERNEL_SRC[kind], *KERNEL_HEADERS):
         h.update(open(os.path.join(CSRC, f), "rb").read())
