@@ -133,6 +133,11 @@ SMALL = [
     (dict(kind="window", left=100, right=0, causal=True, prefix=5), 1, 600, 4, 2, 128, True),   # GQA + prefix
     (dict(kind="full", causal=True), 2, 300, 6, 2, 64, False),                                  # GQA 3:1
     (dict(kind="chunk", chunk=90, prefix=70), 1, 600, 2, 2, 80, False),
+    # sequences shorter than one tile: every tile is the ragged last one
+    (dict(kind="full", causal=True), 2, 1, 2, 2, 64, True),
+    (dict(kind="full"), 1, 2, 2, 2, 80, False),
+    (dict(kind="chunk", chunk=32), 1, 63, 2, 2, 128, True),
+    (dict(kind="window", left=3, right=0, causal=True), 1, 65, 2, 1, 128, False),
 ]
 
 

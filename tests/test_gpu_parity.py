@@ -451,3 +451,21 @@ def test_large_logit_spread(D, spread):
         got = _run_gpu(q, k, v, mask, layout="bhld")
         ref = attention(q, k, v, mask)["out"]
         _compare(got, ref, f"spread{spread:.0f}-D{D}-{mask['kind']}")
+
+
+@pytest.mark.parametrize("D", [64, 80, 128, 256])
+@pytest.mark.parametrize("L", [1, 2, 63, 65])
+def test_sequences_shorter_than_a_tile(D, L):
+    """Sequences of one token, two tokens and one either side of a 64-key tile: every key tile is the
+    ragged last one and every query tile is mostly past the end (rows clamped on load, never stored)."""
+    masks = [dict(kind="full"), dict(kind="full", causal=True),
+             dict(kind="window", left=3, right=0, causal=True), dict(kind="chunk", chunk=32)]
+    q, k, v = _random_case(900 + L + D, 2, 2, L, D)
+    sink = np.random.default_rng(L + D).standard_normal(2).astype(np.float32)
+    for mi, mask in enumerate(masks):
+        for layout in ("bhld", "blhd"):
+            print(f"[case] short L={L} D={D} {mask} {layout}", flush=True)
+            s = sink if mi % 2 else None
+            got = _run_gpu(q, k, v, mask, s, layout)
+            ref = attention(q, k, v, mask, sink=s)["out"]
+            _compare(got, ref, f"short-L{L}-D{D}-{mi}-{layout}")
